@@ -1,0 +1,88 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that at least one pin catches each.
+
+A mutation is a one-place source edit of ``oracle/moe_oracle.py``: the
+edited source is executed into a fresh module whose functions replace the
+real ones for the duration of the test.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle
+import oracle.moe_oracle as om
+from tests import pins
+
+MUTATIONS = {
+    "tie_break_higher_id": (
+        'order = np.argsort(-z32, axis=1, kind="stable")',
+        'order = z32.shape[1] - 1 - np.argsort(-z32[:, ::-1], axis=1, kind="stable")'),
+    "renorm_dropped": (
+        "    if renorm:\n        w = w / w.sum(axis=1, keepdims=True)\n    return ids",
+        "    return ids"),
+    "sigmoid_sign": (
+        "        p = 1.0 / (1.0 + np.exp(-z))\n    else:\n        raise ValueError(score)\n    w = np.take",
+        "        p = 1.0 / (1.0 + np.exp(z))\n    else:\n        raise ValueError(score)\n    w = np.take"),
+    "route_bwd_sign": ("dz[rows, ids] = w * (dw - inner)", "dz[rows, ids] = w * (dw + inner)"),
+    "route_bwd_sigmoid_renorm_missing_S": ("ds = (dw - inner) / S", "ds = (dw - inner)"),
+    "route_bwd_softmax_only_selected": ("dz = -p * inner", "dz = np.zeros_like(p)"),
+    "route_bwd_sigmoid_missing_derivative": (
+        "dz[rows, ids] = ds * s_sel * (1.0 - s_sel)", "dz[rows, ids] = ds * s_sel"),
+    "align_pads_empty_groups": (
+        "group_sizes = ((counts + align - 1) // align) * align",
+        "group_sizes = (counts // align + 1) * align"),
+    "unstable_group_order": ("r = offsets[e] + fill[e]", "r = offsets[e] + (counts[e] - 1 - fill[e])"),
+    "capacity_off_by_one": ("counts[e] < capacity:", "counts[e] <= capacity:"),
+    "gmm_wrong_group_weight": ("W = _f64(rhs[g])", "W = _f64(rhs[max(g - 1, 0)])"),
+    "gmm_ignores_partial": ("out = _f64(partial).copy()\n        M_out", "out = 0 * _f64(partial)\n        M_out"),
+    "tgmm_drops_last_row": (
+        "out[g] += _f64(lhs[start:start + n]).T @ _f64(rhs[start:start + n])",
+        "out[g] += _f64(lhs[start:start + n - 1]).T @ _f64(rhs[start:start + n - 1])"),
+    "swiglu_missing_z": ("return h0 * _sigmoid(h0) * _f64(h1)", "return _sigmoid(h0) * _f64(h1)"),
+    "swiglu_bwd_dropped_term": ("(1.0 + h0 * (1.0 - sg))", "(1.0 + h0 * sg)"),
+    "combine_bwd_missing_weight": ("d_ys[r] = w[t, j] * dy[t]", "d_ys[r] = dy[t]"),
+    "permute_bwd_overwrites": ("                dx[t] += d[r]", "                dx[t] = d[r]"),
+    "backward_d_wo_wrong_operand": ('d_wo = tgmm(fwd["act"], d_ys, gs)', 'd_wo = tgmm(fwd["h1"], d_ys, gs)'),
+    "backward_dx_second_gmm_not_accumulated": (
+        "d_xs = gmm(d_h1, wi_1, gs, trans_rhs=True, partial=d_xs)",
+        "d_xs = gmm(d_h1, wi_1, gs, trans_rhs=True)"),
+    "backward_d_wi_1_transposed_role": ("d_wi_1 = tgmm(xs, d_h1, gs)", "d_wi_1 = tgmm(xs, d_h0, gs)"),
+    "router_bwd_missing_term": (
+        'out["dx"] = dx + d_logits @ _f64(Wg).T', 'out["dx"] = dx'),
+}
+
+
+def _mutant_module(old, new):
+    src = inspect.getsource(om)
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _run_all_pins():
+    failures = []
+    for name in dir(pins):
+        if name.startswith("check_"):
+            try:
+                getattr(pins, name)()
+            except Exception as exc:   # AssertionError or a crash both count as caught
+                failures.append((name, type(exc).__name__))
+    return failures
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_mutation_is_caught(mutation, monkeypatch):
+    old, new = MUTATIONS[mutation]
+    mod = _mutant_module(old, new)
+    for fname in dir(om):
+        obj = getattr(om, fname)
+        if isinstance(obj, types.FunctionType) and obj.__module__ == om.__name__:
+            monkeypatch.setattr(oracle, fname, getattr(mod, fname), raising=False)
+    failures = _run_all_pins()
+    assert failures, f"no pin caught mutation {mutation}"
+
+
+def test_unmutated_passes():
+    assert _run_all_pins() == []
