@@ -1,0 +1,213 @@
+/*
+ * moe.h -- C ABI of libmoe.so, the MI355X (gfx950) MoE expert-FFN path.
+ *
+ * The operations follow four pages on the subject:
+ *   [TE-MoE]   TransformerEngine pull request "[JAX] Add an MoE Block (Layer)
+ *              that compound router, permutation, groupedGEMM and
+ *              communication": the block's sequence diagram (route -> dispatch
+ *              -> grouped GEMM x3 -> combine, and the mirrored backward), the
+ *              review of _combine_bwd, the align_size receive-buffer bound and
+ *              the commit notes on the SwiGLU projection outputs.
+ *   [MT-Chunk] MaxText pull request "Overlap moe comms with collective
+ *              matmul": gmm/tgmm with in-place partial-sum accumulation,
+ *              tgmm zero-initialised empty groups, the gmm backward rule.
+ *   [MT-GG]    MaxText pull request "[Draft] Integrate TE/JAX GroupedGEMM for
+ *              MoE": grouped vs batched GEMM, token dropping (Tests).
+ *   [MT-ES]    MaxText pull request "Onboard explicit sharding to deepseek":
+ *              gate projection shape and the expert weight layouts.
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or synchronises and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *     call enqueues its kernels on it and returns; results are valid in stream
+ *     order.
+ *   - Return value: MOE_OK (0), or a negative MOE_ERR_* when the host-side
+ *     argument check fails (nothing is launched in that case) or a launch
+ *     fails.  moe_status_string() gives the text.  No call aborts or throws.
+ *   - Data errors only the device can see (an expert id outside [0, E), group
+ *     sizes that are negative or overrun the buffer) never cause an
+ *     out-of-bounds access: the offending item is skipped and a MOE_DERR_* bit
+ *     is OR-ed into the caller's int32 word `err` (may be NULL).
+ *   - dtype codes: MOE_F32 or MOE_BF16 for activations and weights.  Expert
+ *     ids, group sizes and row maps are int32; logits and routing weights
+ *     are float32.  Lengths are int64.  Leading dimensions (ld_*) and strides
+ *     are in elements.  All matrices are row-major.
+ *   - Slot s = t*K + j is token t's j-th routing choice.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,         /* bad size, null pointer, misaligned pointer/stride */
+  MOE_ERR_DTYPE = -2,       /* unsupported dtype or dtype combination */
+  MOE_ERR_CAPACITY = -3,    /* a buffer is smaller than the static bound */
+  MOE_ERR_LAUNCH = -4,      /* the HIP runtime refused a launch */
+  MOE_ERR_WORKSPACE = -5    /* workspace too small or misaligned */
+};
+
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
+
+/* bits OR-ed into the device error word */
+enum {
+  MOE_DERR_EXPERT_ID = 1,   /* an expert id outside [0, E): that slot was dropped */
+  MOE_DERR_GROUP_SIZES = 2, /* negative group size or sum(group_sizes) > rows: clipped */
+  MOE_DERR_ROWS = 4         /* permuted rows exceed the output buffer: clipped */
+};
+
+const char* moe_status_string(int status);
+int moe_abi_version(void);  /* bumped on any signature change */
+
+/* ---------------------------------------------------------------- routing
+ * moe_route: top-K routing [TE-MoE, Description/Changes: fused top-K with
+ * optional sigmoid scoring].
+ *   z[t,e] = logits[t,e] + bias[e] in float32 (bias may be NULL; -inf
+ *   switches an expert off).  Experts are ranked by z descending; equal z
+ *   ranks the lower id first; topk_ids[t, j] is the j-th ranked expert.
+ *   score MOE_SOFTMAX: p = softmax over all E of z; MOE_SIGMOID: p = 1/(1+e^-z).
+ *   topk_w[t, j] = p of the j-th expert, divided by the sum over the K
+ *   selected when renorm != 0.
+ *   logits [T, E] f32, bias [E] f32 or NULL, topk_ids [T, K] i32,
+ *   topk_w [T, K] f32.  Requires 1 <= K <= E <= 1024.
+ */
+int moe_route(const float* logits, const float* bias, int64_t T, int E, int K, int score,
+              int renorm, int32_t* topk_ids, float* topk_w, void* stream);
+
+/* moe_route_bwd: d_logits [T, E] (fully written) from d_topk_w [T, K], with
+ * the selection topk_ids held fixed (the gate-kernel gradient path of the
+ * [TE-MoE] block backward).  Same logits/bias/score/renorm as the forward.
+ * d_logits is stored in dlogits_dtype (MOE_F32, or MOE_BF16 to feed a bf16
+ * router-GEMM backward); the arithmetic is float32.
+ *   softmax+renorm: dz_ej = w_j (dw_j - sum_i w_i dw_i), others 0
+ *   softmax:        dz_e  = p_e ([e = e_j] dw_j - sum_i p_ei dw_i), all e
+ *   sigmoid+renorm: dz_ej = s_j(1-s_j)(dw_j - sum_i w_i dw_i) / sum_i s_i
+ *   sigmoid:        dz_ej = dw_j s_j (1 - s_j)
+ */
+int moe_route_bwd(const float* logits, const float* bias, const int32_t* topk_ids,
+                  const float* d_topk_w, int64_t T, int E, int K, int score, int renorm,
+                  void* d_logits, int dlogits_dtype, void* stream);
+
+/* -------------------------------------------------------------- permutation
+ * moe_rows_bound: the static row count of the expert-sorted buffers:
+ *   capacity_layout: E*capacity;  align > 0: T*K + E*(align-1) (the
+ *   worst-case receive-buffer bound for align_size > 0 in the [TE-MoE]
+ *   review);  otherwise T*K.  Returns -1 on bad arguments.
+ */
+int64_t moe_rows_bound(int64_t T, int K, int E, int align, int capacity, int capacity_layout);
+
+/* Workspace bytes moe_permute needs (256-byte aligned device memory). */
+size_t moe_permute_workspace(int64_t T, int K, int E);
+
+/* moe_permute: group the routed slots by expert (the [TE-MoE] "global
+ * permute" with group_sizes and align_size; token dropping in router order
+ * as in the [MT-GG] Tests).
+ *   Router order is ascending slot s.  With capacity C > 0 a slot is kept iff
+ *   fewer than C earlier slots chose the same expert.  counts[e] = kept slots
+ *   of e.  group_sizes[e] = counts[e] rounded up to a multiple of align
+ *   (align > 0; 0 stays 0), or C for every expert in capacity_layout.
+ *   group_offsets[e] = sum of earlier group sizes, group_offsets[E] = total.
+ *   Inside a group the kept slots are in ascending s (stable), followed by
+ *   the group's padding rows.
+ *   row_of_slot[s] = destination row, -1 if dropped.  slot_of_row[r] = source
+ *   slot, -1 for padding rows (including every row >= group_offsets[E]).
+ *   x_sorted[r] = x[slot_of_row[r] / K], zero for padding rows.
+ *   x [T, D] and x_sorted [rows, D] in `dtype`; rows >= moe_rows_bound(...).
+ *   x_sorted may be NULL (index maps only).  Requires E <= 1024, K <= 64.
+ */
+int moe_permute(const void* x, int dtype, int64_t T, int64_t D, const int32_t* topk_ids, int K,
+                int E, int align, int capacity, int capacity_layout, void* x_sorted, int64_t rows,
+                int32_t* counts, int32_t* group_sizes, int32_t* group_offsets,
+                int32_t* row_of_slot, int32_t* slot_of_row, void* workspace, size_t ws_bytes,
+                int32_t* err, void* stream);
+
+/* moe_permute_bwd: d_x[t] (+)= sum_j d_x_sorted[row_of_slot[t*K+j]] over kept
+ * slots (adjoint of the row gather; the dispatch backward of [TE-MoE]).
+ * accumulate != 0 adds into d_x.  d_x_sorted [rows, D], d_x [T, D], both in
+ * `dtype`; sums are taken in float32.
+ */
+int moe_permute_bwd(const void* d_x_sorted, int dtype, int64_t T, int64_t D, int K, int64_t rows,
+                    const int32_t* row_of_slot, void* d_x, int accumulate, void* stream);
+
+/* ------------------------------------------------------------ grouped GEMMs
+ * moe_gmm: grouped GEMM [MT-Chunk; TE-MoE grouped_gemm].
+ *   For group g with rows [o_g, o_g + n_g), o_g = sum_{g'<g} n_g':
+ *     out[o_g + i, :] (+)= lhs[o_g + i, :Kdim] . B_g
+ *   where B_g = rhs + g*rhs_group_stride viewed as [Kdim, N] with row stride
+ *   ld_rhs (trans_rhs = 0), or as [N, Kdim] with row stride ld_rhs and used
+ *   transposed (trans_rhs = 1).
+ *   lhs: [M_lhs, Kdim] with row stride ld_lhs; out: [M_out, N] with row stride
+ *   ld_out, M_out <= M_lhs (lhs may be padded to a row tile while the output
+ *   is not).  accumulate != 0: out += product (in-place partial sum); rows
+ *   >= sum(group_sizes) are left untouched.  accumulate == 0: out = product;
+ *   rows in [sum(group_sizes), M_out) are zero-filled.
+ *   in_dtype is the dtype of lhs and rhs; MOE_BF16 runs on bf16 MFMA with
+ *   float32 accumulation; MOE_F32 runs in float32 FMA.  out_dtype is
+ *   MOE_F32 or MOE_BF16 (rounded to nearest even).
+ *   Requires Kdim, N, ld_* and strides to be multiples of 8 and 16-byte
+ *   aligned pointers.  G <= 4096.  If sum(group_sizes) > M_out the groups are
+ *   clipped at M_out and MOE_DERR_GROUP_SIZES is raised.
+ */
+int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
+            int64_t rhs_group_stride, int trans_rhs, const int32_t* group_sizes, int G,
+            int64_t Kdim, int64_t N, int in_dtype, void* out, int64_t M_out, int64_t ld_out,
+            int out_dtype, int accumulate, int32_t* err, void* stream);
+
+/* moe_tgmm: transposed grouped GEMM [MT-Chunk: tgmm, output
+ * (num_local_groups, in_size, out_size), zero-initialised empty groups].
+ *   out[g] (+)= lhs[rows of g, :Kdim]^T . rhs[rows of g, :N]   -> [Kdim, N]
+ *   lhs [M, Kdim] row stride ld_lhs; rhs [M, N] row stride ld_rhs; out[g]
+ *   at out + g*out_group_stride with row stride ld_out.  An empty group's
+ *   block is zero (accumulate == 0) or left unchanged (accumulate != 0).
+ *   Same dtype and alignment rules as moe_gmm.
+ */
+int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
+             const int32_t* group_sizes, int G, int64_t M, int64_t Kdim, int64_t N, int in_dtype,
+             void* out, int64_t ld_out, int64_t out_group_stride, int out_dtype, int accumulate,
+             int32_t* err, void* stream);
+
+/* -------------------------------------------------------------------- SwiGLU
+ * moe_swiglu: act = silu(h0) * h1, silu(z) = z / (1 + e^-z), computed in
+ * float32 (gate_proj_out / up_proj_out of the [TE-MoE] SwiGLU FFN).
+ * h0, h1 [rows, F] in h_dtype; act [rows, F] in act_dtype.
+ */
+int moe_swiglu(const void* h0, const void* h1, int h_dtype, int64_t rows, int64_t F, void* act,
+               int act_dtype, void* stream);
+
+/* moe_swiglu_bwd: d_h0 = d_act*h1*s*(1 + h0*(1 - s)), d_h1 = d_act*silu(h0),
+ * s = sigmoid(h0).  h0, h1 in h_dtype; d_act in d_dtype; d_h0, d_h1 in d_dtype.
+ */
+int moe_swiglu_bwd(const void* h0, const void* h1, int h_dtype, const void* d_act, int64_t rows,
+                   int64_t F, void* d_h0, void* d_h1, int d_dtype, void* stream);
+
+/* ------------------------------------------------------------------ combine
+ * moe_combine: y[t] = sum_j topk_w[t, j] * y_sorted[row_of_slot[t*K+j]] over
+ * kept slots, summed in float32 (the combine einsum "BKE,BK -> BE" of
+ * [TE-MoE]).  y_sorted [rows, D], y [T, D] in `dtype`.
+ */
+int moe_combine(const void* y_sorted, int dtype, int64_t T, int64_t D, int K, int64_t rows,
+                const int32_t* row_of_slot, const float* topk_w, void* y, void* stream);
+
+/* moe_combine_bwd: the hand-derived combine backward of [TE-MoE]:
+ *   d_y_sorted[r] = topk_w[s] * d_y[s / K] for r = row_of_slot[s];
+ *   rows no slot maps to (slot_of_row[r] = -1) are written as zero;
+ *   d_topk_w[s] = <d_y[s / K], y_sorted[row_of_slot[s]]> (float32 sum),
+ *   0 for a dropped slot.
+ *   d_y [T, D], y_sorted and d_y_sorted [rows, D] in `dtype`.
+ */
+int moe_combine_bwd(const void* d_y, const void* y_sorted, int dtype, int64_t T, int64_t D, int K,
+                    int64_t rows, const int32_t* row_of_slot, const int32_t* slot_of_row,
+                    const float* topk_w, void* d_y_sorted, float* d_topk_w, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,323 @@
+"""ctypes binding of libmoe.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls, takes torch
+tensors resident on the GPU (PyTorch provides device memory and the stream)
+and forwards raw pointers, sizes and strides.  Output tensors may be passed
+in; otherwise they are allocated with ``torch.empty`` on the input's device.
+All arithmetic happens in the HIP kernels.  If the shared library is
+missing, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
+
+# Entry points (name -> (restype, argtypes)); must match include/moe.h.
+_P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_abi_version": (_I, []),
+    "moe_route": (_I, [_P, _P, _L, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_route_bwd": (_I, [_P, _P, _P, _P, _L, _I, _I, _I, _I, _P, _I, _P]),
+    "moe_rows_bound": (_L, [_L, _I, _I, _I, _I, _I]),
+    "moe_permute_workspace": (_S, [_L, _I, _I]),
+    "moe_permute": (_I, [_P, _I, _L, _L, _P, _I, _I, _I, _I, _I, _P, _L, _P, _P, _P, _P, _P,
+                         _P, _S, _P, _P]),
+    "moe_permute_bwd": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _I, _P]),
+    "moe_gmm": (_I, [_P, _L, _L, _P, _L, _L, _I, _P, _I, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
+    "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
+    "moe_swiglu": (_I, [_P, _P, _I, _L, _L, _P, _I, _P]),
+    "moe_swiglu_bwd": (_I, [_P, _P, _I, _P, _L, _L, _P, _P, _I, _P]),
+    "moe_combine": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _P, _P]),
+    "moe_combine_bwd": (_I, [_P, _P, _I, _L, _L, _I, _L, _P, _P, _P, _P, _P, _P]),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def load():
+    """Load libmoe.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m mixture_experts_grouped_top_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = load().moe_status_string(rc).decode()
+        raise MoeError(f"{what} failed with status {rc}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise MoeError("tensor must be on the GPU")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise MoeError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dtype(code: int):
+    return torch.bfloat16 if code == MOE_BF16 else torch.float32
+
+
+def _score(score) -> int:
+    if score in ("softmax", MOE_SOFTMAX):
+        return MOE_SOFTMAX
+    if score in ("sigmoid", MOE_SIGMOID):
+        return MOE_SIGMOID
+    raise MoeError(f"unknown score function {score!r}")
+
+
+def _rowmajor(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise MoeError(f"{name} must be a 2-D view with unit column stride")
+    return t.stride(0)
+
+
+def _contig(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+
+
+# ----------------------------------------------------------------- routing
+
+def moe_route(logits, K: int, score="softmax", renorm: bool = True, bias=None,
+              topk_ids=None, topk_w=None, stream=None):
+    T, E = logits.shape
+    _contig(logits, "logits")
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _check(load().moe_route(_ptr(logits), _ptr(bias), T, E, K, _score(score), int(bool(renorm)),
+                            _ptr(topk_ids), _ptr(topk_w), _stream(stream)), "moe_route")
+    return topk_ids, topk_w
+
+
+def moe_route_bwd(logits, topk_ids, d_topk_w, score="softmax", renorm: bool = True, bias=None,
+                  d_logits=None, dtype=torch.float32, stream=None):
+    T, E = logits.shape
+    K = topk_ids.shape[1]
+    if d_logits is None:
+        d_logits = torch.empty((T, E), dtype=dtype, device=logits.device)
+    _check(load().moe_route_bwd(_ptr(logits), _ptr(bias), _ptr(topk_ids), _ptr(d_topk_w), T, E, K,
+                                _score(score), int(bool(renorm)), _ptr(d_logits),
+                                _dtype_code(d_logits), _stream(stream)), "moe_route_bwd")
+    return d_logits
+
+
+# ------------------------------------------------------------- permutation
+
+def moe_rows_bound(T: int, K: int, E: int, align: int = 0, capacity: int = 0,
+                   capacity_layout: bool = False) -> int:
+    r = load().moe_rows_bound(T, K, E, align, capacity, int(bool(capacity_layout)))
+    if r < 0:
+        raise MoeError("moe_rows_bound: invalid arguments")
+    return r
+
+
+def moe_permute_workspace(T: int, K: int, E: int) -> int:
+    return load().moe_permute_workspace(T, K, E)
+
+
+def moe_permute(x, topk_ids, E: int, align: int = 0, capacity: int = 0,
+                capacity_layout: bool = False, rows: Optional[int] = None, x_sorted=None,
+                with_rows: bool = True, err=None, workspace=None, out=None, stream=None):
+    """Returns dict(x_sorted, counts, group_sizes, group_offsets, row_of_slot,
+    slot_of_row).  ``rows`` defaults to moe_rows_bound(...); ``out`` may hold
+    preallocated index tensors under the same keys."""
+    T, K = topk_ids.shape
+    dev = topk_ids.device
+    if rows is None:
+        rows = moe_rows_bound(T, K, E, align, capacity, capacity_layout)
+    out = dict(out or {})
+    i32 = dict(dtype=torch.int32, device=dev)
+    counts = out.get("counts") if out.get("counts") is not None else torch.empty(E, **i32)
+    gsz = out.get("group_sizes") if out.get("group_sizes") is not None else torch.empty(E, **i32)
+    goff = out.get("group_offsets") if out.get("group_offsets") is not None else torch.empty(E + 1, **i32)
+    ros = out.get("row_of_slot") if out.get("row_of_slot") is not None else torch.empty(T * K, **i32)
+    sor = out.get("slot_of_row") if out.get("slot_of_row") is not None else torch.empty(rows, **i32)
+    D = 0
+    dt = MOE_BF16
+    if x is not None and with_rows:
+        T2, D = x.shape
+        assert T2 == T
+        _contig(x, "x")
+        dt = _dtype_code(x)
+        if x_sorted is None:
+            x_sorted = torch.empty((rows, D), dtype=x.dtype, device=dev)
+        _contig(x_sorted, "x_sorted")
+        assert x_sorted.shape[0] == rows and x_sorted.shape[1] == D
+    else:
+        x_sorted = None
+    ws_bytes = moe_permute_workspace(T, K, E)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check(load().moe_permute(_ptr(x) if x_sorted is not None else None, dt, T, D, _ptr(topk_ids),
+                              K, E, align, capacity, int(bool(capacity_layout)), _ptr(x_sorted),
+                              rows, _ptr(counts), _ptr(gsz), _ptr(goff), _ptr(ros), _ptr(sor),
+                              _ptr(workspace), workspace.numel(), _ptr(err), _stream(stream)),
+           "moe_permute")
+    return dict(x_sorted=x_sorted, counts=counts, group_sizes=gsz, group_offsets=goff,
+                row_of_slot=ros, slot_of_row=sor)
+
+
+def moe_permute_bwd(d_x_sorted, row_of_slot, T: int, K: int, d_x=None, accumulate: bool = False,
+                    stream=None):
+    rows, D = d_x_sorted.shape
+    _contig(d_x_sorted, "d_x_sorted")
+    if d_x is None:
+        d_x = torch.empty((T, D), dtype=d_x_sorted.dtype, device=d_x_sorted.device)
+    _contig(d_x, "d_x")
+    _check(load().moe_permute_bwd(_ptr(d_x_sorted), _dtype_code(d_x_sorted), T, D, K, rows,
+                                  _ptr(row_of_slot), _ptr(d_x), int(bool(accumulate)),
+                                  _stream(stream)), "moe_permute_bwd")
+    return d_x
+
+
+# ----------------------------------------------------------- grouped GEMMs
+
+def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: Optional[int] = None,
+            out_dtype=None, accumulate: bool = False, err=None, stream=None):
+    """out[rows of g] (+)= lhs[rows of g] . rhs[g] (rhs[g]: [K, N], or [N, K]
+    used transposed).  lhs and out may be strided 2-D views (unit column
+    stride); rhs a 3-D view with unit last stride."""
+    M_lhs, Kd = lhs.shape
+    ld_lhs = _rowmajor(lhs, "lhs")
+    if rhs.dim() != 3 or rhs.stride(2) != 1:
+        raise MoeError("rhs must be a 3-D view with unit last stride")
+    G = rhs.shape[0]
+    N = rhs.shape[1] if trans_rhs else rhs.shape[2]
+    if (rhs.shape[2] if trans_rhs else rhs.shape[1]) != Kd:
+        raise MoeError("contracting dimensions differ")
+    if group_sizes.numel() != G:
+        raise MoeError("group_sizes must have one entry per rhs group")
+    if lhs.dtype != rhs.dtype:
+        raise MoeError("lhs and rhs dtypes differ")
+    if out is None:
+        M_out = M_lhs if rows_out is None else rows_out
+        odt = lhs.dtype if out_dtype is None else out_dtype
+        out = torch.empty((M_out, N), dtype=odt, device=lhs.device)
+    M_out = out.shape[0]
+    ld_out = _rowmajor(out, "out")
+    _check(load().moe_gmm(_ptr(lhs), M_lhs, ld_lhs, _ptr(rhs), rhs.stride(1), rhs.stride(0),
+                          int(bool(trans_rhs)), _ptr(group_sizes), G, Kd, N, _dtype_code(lhs),
+                          _ptr(out), M_out, ld_out, _dtype_code(out), int(bool(accumulate)),
+                          _ptr(err), _stream(stream)), "moe_gmm")
+    return out
+
+
+def moe_tgmm(lhs, rhs, group_sizes, out=None, out_dtype=None, accumulate: bool = False, err=None,
+             stream=None):
+    """out[g] (+)= lhs[rows of g]^T . rhs[rows of g] -> [G, K, N]."""
+    M, Kd = lhs.shape
+    M2, N = rhs.shape
+    if M2 != M:
+        raise MoeError("lhs and rhs row counts differ")
+    G = group_sizes.numel()
+    if out is None:
+        odt = lhs.dtype if out_dtype is None else out_dtype
+        out = torch.empty((G, Kd, N), dtype=odt, device=lhs.device)
+    if out.dim() != 3 or out.stride(2) != 1 or out.shape[0] != G:
+        raise MoeError("out must be [G, K, N] with unit last stride")
+    _check(load().moe_tgmm(_ptr(lhs), _rowmajor(lhs, "lhs"), _ptr(rhs), _rowmajor(rhs, "rhs"),
+                           _ptr(group_sizes), G, M, Kd, N, _dtype_code(lhs), _ptr(out),
+                           out.stride(1), out.stride(0), _dtype_code(out), int(bool(accumulate)),
+                           _ptr(err), _stream(stream)), "moe_tgmm")
+    return out
+
+
+# ------------------------------------------------------------------ SwiGLU
+
+def moe_swiglu(h0, h1, act=None, act_dtype=None, stream=None):
+    _contig(h0, "h0")
+    _contig(h1, "h1")
+    rows, F = h0.shape
+    if act is None:
+        act = torch.empty((rows, F), dtype=h0.dtype if act_dtype is None else act_dtype,
+                          device=h0.device)
+    _check(load().moe_swiglu(_ptr(h0), _ptr(h1), _dtype_code(h0), rows, F, _ptr(act),
+                             _dtype_code(act), _stream(stream)), "moe_swiglu")
+    return act
+
+
+def moe_swiglu_bwd(h0, h1, d_act, d_h0=None, d_h1=None, stream=None):
+    rows, F = h0.shape
+    for t, n in ((h0, "h0"), (h1, "h1"), (d_act, "d_act")):
+        _contig(t, n)
+    if d_h0 is None:
+        d_h0 = torch.empty_like(d_act)
+    if d_h1 is None:
+        d_h1 = torch.empty_like(d_act)
+    _check(load().moe_swiglu_bwd(_ptr(h0), _ptr(h1), _dtype_code(h0), _ptr(d_act), rows, F,
+                                 _ptr(d_h0), _ptr(d_h1), _dtype_code(d_act), _stream(stream)),
+           "moe_swiglu_bwd")
+    return d_h0, d_h1
+
+
+# ----------------------------------------------------------------- combine
+
+def moe_combine(y_sorted, row_of_slot, topk_w, y=None, stream=None):
+    rows, D = y_sorted.shape
+    T, K = topk_w.shape
+    _contig(y_sorted, "y_sorted")
+    if y is None:
+        y = torch.empty((T, D), dtype=y_sorted.dtype, device=y_sorted.device)
+    _check(load().moe_combine(_ptr(y_sorted), _dtype_code(y_sorted), T, D, K, rows,
+                              _ptr(row_of_slot), _ptr(topk_w), _ptr(y), _stream(stream)),
+           "moe_combine")
+    return y
+
+
+def moe_combine_bwd(d_y, y_sorted, row_of_slot, slot_of_row, topk_w, d_y_sorted=None,
+                    d_topk_w=None, stream=None):
+    rows, D = y_sorted.shape
+    T, K = topk_w.shape
+    _contig(d_y, "d_y")
+    _contig(y_sorted, "y_sorted")
+    if d_y_sorted is None:
+        d_y_sorted = torch.empty_like(y_sorted)
+    if d_topk_w is None:
+        d_topk_w = torch.empty((T, K), dtype=torch.float32, device=d_y.device)
+    _check(load().moe_combine_bwd(_ptr(d_y), _ptr(y_sorted), _dtype_code(y_sorted), T, D, K, rows,
+                                  _ptr(row_of_slot), _ptr(slot_of_row), _ptr(topk_w),
+                                  _ptr(d_y_sorted), _ptr(d_topk_w), _stream(stream)),
+           "moe_combine_bwd")
+    return d_y_sorted, d_topk_w

@@ -1,0 +1,163 @@
+"""The MoE expert-FFN block as a fixed sequence of libmoe.so calls.
+
+``MoEPlan`` preallocates every buffer of one workload (sizes are static:
+the sorted buffers have the worst-case row count, so nothing depends on
+device-resident counts and no host synchronisation is needed), then
+``forward`` and ``backward`` only enqueue kernels on the current stream.
+
+The sequence mirrors the single hand-derived custom VJP of the
+TransformerEngine MoE block (route -> dispatch -> three grouped GEMMs ->
+combine, and the reverse for the backward) with the gmm backward rule of
+the MaxText "Overlap moe comms with collective matmul" pull request
+(d_lhs = gmm with the rhs transposed, d_rhs = tgmm, in-place partial sums).
+The up-projections can run as a loop over contracting-dim chunks of
+d_model accumulating into float32 partial sums (that pull request's
+chunked gmm).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+@dataclasses.dataclass(frozen=True)
+class MoEShape:
+    T: int
+    D: int
+    F: int
+    E: int
+    K: int
+    dtype: torch.dtype = torch.bfloat16
+    score: str = "softmax"
+    renorm: bool = True
+    align: int = 0
+    capacity: int = 0
+    capacity_layout: bool = False
+    n_chunks: int = 1
+    pad_rows_to: int = 0
+
+
+def _round_up(a: int, b: int) -> int:
+    return a if b <= 0 else ((a + b - 1) // b) * b
+
+
+class MoEPlan:
+    """Buffers and call sequence for one MoE FFN workload on one GPU."""
+
+    def __init__(self, shape: MoEShape, device="cuda", router: bool = True):
+        s = self.s = shape
+        B.load()
+        dev = torch.device(device)
+        self.device = dev
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        act = dict(dtype=s.dtype, device=dev)
+        self.rows = B.moe_rows_bound(s.T, s.K, s.E, s.align, s.capacity, s.capacity_layout)
+        self.lhs_rows = _round_up(self.rows, s.pad_rows_to)
+        part = f32 if s.n_chunks > 1 else act   # chunked up-projection keeps fp32 partials
+        self.router = router
+        self.gs_T = torch.tensor([s.T], **i32)
+        # forward
+        self.logits = torch.empty((s.T, s.E), **f32)
+        self.ids = torch.empty((s.T, s.K), **i32)
+        self.w = torch.empty((s.T, s.K), **f32)
+        self.idx = dict(counts=torch.empty(s.E, **i32), group_sizes=torch.empty(s.E, **i32),
+                        group_offsets=torch.empty(s.E + 1, **i32),
+                        row_of_slot=torch.empty(s.T * s.K, **i32),
+                        slot_of_row=torch.empty(self.lhs_rows, **i32))
+        self.ws = torch.empty(max(B.moe_permute_workspace(s.T, s.K, s.E), 256), dtype=torch.uint8,
+                              device=dev)
+        self.err = torch.zeros(1, **i32)
+        self.x_sorted = torch.empty((self.lhs_rows, s.D), **act)
+        self.h0 = torch.empty((self.rows, s.F), **part)
+        self.h1 = torch.empty((self.rows, s.F), **part)
+        self.act = torch.empty((self.rows, s.F), **act)
+        self.y_sorted = torch.empty((self.rows, s.D), **act)
+        self.y = torch.empty((s.T, s.D), **act)
+        # backward
+        self.d_y_sorted = torch.empty((self.rows, s.D), **act)
+        self.d_w = torch.empty((s.T, s.K), **f32)
+        self.d_act = torch.empty((self.rows, s.F), **act)
+        self.d_h0 = torch.empty((self.rows, s.F), **act)
+        self.d_h1 = torch.empty((self.rows, s.F), **act)
+        self.d_x_sorted = torch.empty((self.rows, s.D), **act)
+        self.dx = torch.empty((s.T, s.D), **act)
+        self.d_logits = torch.empty((s.T, s.E), **act)
+        self.d_wi_0 = torch.empty((s.E, s.D, s.F), **act)
+        self.d_wi_1 = torch.empty((s.E, s.D, s.F), **act)
+        self.d_wo = torch.empty((s.E, s.F, s.D), **act)
+        self.d_Wg = torch.empty((1, s.D, s.E), **act) if router else None
+
+    @property
+    def group_sizes(self):
+        return self.idx["group_sizes"]
+
+    def forward(self, x, wi_0, wi_1, wo, Wg=None, logits=None, bias=None, stream=None):
+        """y = sum_j w[t,j] FFN_{e(t,j)}(x[t]).  Either Wg (router GEMM on the
+        device) or precomputed float32 logits."""
+        s = self.s
+        if logits is None:
+            B.moe_gmm(x, Wg.unsqueeze(0), self.gs_T, out=self.logits, err=self.err, stream=stream)
+        else:
+            self.logits.copy_(logits)
+        B.moe_route(self.logits, s.K, s.score, s.renorm, bias, topk_ids=self.ids, topk_w=self.w,
+                    stream=stream)
+        B.moe_permute(x, self.ids, s.E, s.align, s.capacity, s.capacity_layout,
+                      rows=self.lhs_rows, x_sorted=self.x_sorted, err=self.err,
+                      workspace=self.ws, out=self.idx, stream=stream)
+        gs = self.group_sizes
+        if s.n_chunks > 1:
+            c = s.D // s.n_chunks
+            for i in range(s.n_chunks):
+                xs = self.x_sorted[:, i * c:(i + 1) * c]
+                B.moe_gmm(xs, wi_0[:, i * c:(i + 1) * c, :], gs, out=self.h0, accumulate=i > 0,
+                          err=self.err, stream=stream)
+                B.moe_gmm(xs, wi_1[:, i * c:(i + 1) * c, :], gs, out=self.h1, accumulate=i > 0,
+                          err=self.err, stream=stream)
+        else:
+            B.moe_gmm(self.x_sorted, wi_0, gs, out=self.h0, err=self.err, stream=stream)
+            B.moe_gmm(self.x_sorted, wi_1, gs, out=self.h1, err=self.err, stream=stream)
+        B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
+        B.moe_gmm(self.act, wo, gs, out=self.y_sorted, err=self.err, stream=stream)
+        B.moe_combine(self.y_sorted, self.idx["row_of_slot"], self.w, y=self.y, stream=stream)
+        return self.y
+
+    def backward(self, dy, x, wi_0, wi_1, wo, Wg=None, bias=None, stream=None):
+        """Gradients for upstream dy: fills dx, d_wi_0, d_wi_1, d_wo, d_logits
+        and (with the router) d_Wg."""
+        s = self.s
+        gs = self.group_sizes
+        ros, sor = self.idx["row_of_slot"], self.idx["slot_of_row"]
+        B.moe_combine_bwd(dy, self.y_sorted, ros, sor, self.w, d_y_sorted=self.d_y_sorted,
+                          d_topk_w=self.d_w, stream=stream)
+        B.moe_gmm(self.d_y_sorted, wo, gs, trans_rhs=True, out=self.d_act, err=self.err,
+                  stream=stream)
+        B.moe_tgmm(self.act, self.d_y_sorted, gs, out=self.d_wo, err=self.err, stream=stream)
+        B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
+                         stream=stream)
+        B.moe_gmm(self.d_h0, wi_0, gs, trans_rhs=True, out=self.d_x_sorted, err=self.err,
+                  stream=stream)
+        B.moe_gmm(self.d_h1, wi_1, gs, trans_rhs=True, out=self.d_x_sorted, accumulate=True,
+                  err=self.err, stream=stream)
+        xs = self.x_sorted[:self.rows]
+        B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream)
+        B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream)
+        B.moe_permute_bwd(self.d_x_sorted, ros, s.T, s.K, d_x=self.dx, stream=stream)
+        B.moe_route_bwd(self.logits, self.ids, self.d_w, s.score, s.renorm, bias,
+                        d_logits=self.d_logits, stream=stream)
+        if Wg is not None and self.router:
+            B.moe_tgmm(x, self.d_logits, self.gs_T, out=self.d_Wg, err=self.err, stream=stream)
+            B.moe_gmm(self.d_logits, Wg.unsqueeze(0), self.gs_T, trans_rhs=True, out=self.dx,
+                      accumulate=True, err=self.err, stream=stream)
+        return self.dx
+
+    def expert_flops(self, kept_rows: Optional[int] = None) -> float:
+        """Algorithmic expert-FFN flops of one forward+backward: 18 R D F with
+        R the kept routed rows (padding rows excluded)."""
+        s = self.s
+        R = s.T * s.K if kept_rows is None else kept_rows
+        return 18.0 * R * s.D * s.F

@@ -1,0 +1,399 @@
+// Dispatch (permute) and combine (unpermute) with their backward passes.
+//
+// Permute is a two-level, deterministic counting sort of the routed slots by
+// expert (the "global permute" of the TransformerEngine MoE block with
+// group_sizes and align_size padding; token dropping in router order from the
+// MaxText grouped-GEMM pull request's Tests):
+//   1. hist    per block of kSlots slots: per-expert counts (LDS atomics on
+//              integers, so order-free and exact); also marks every row of
+//              slot_of_row as padding (-1).
+//   2. scan    one workgroup: per expert, exclusive scan of the block counts
+//              over blocks (each block's base rank), capacity clip, align,
+//              exclusive scan over experts -> group offsets.
+//   3. rank    per block: stable rank of each slot among same-expert slots,
+//              from wave ballots over the bits of the expert id (peer mask,
+//              popcount below the lane) plus per-wave counts in LDS; writes
+//              row_of_slot and slot_of_row.
+//   4. gather  one wave per destination row: copy x[token] or write zeros.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSlots = 1024;          // slots per block in hist/rank
+constexpr int kMaxE = 1024;
+
+__device__ __forceinline__ void flag_error(int32_t* err, int bit) {
+  if (err) atomicOr(err, bit);
+}
+
+__global__ __launch_bounds__(kThreads) void permute_hist_kernel(
+    const int32_t* __restrict__ ids, int64_t TK, int E, int32_t* __restrict__ blockcounts,
+    int32_t* __restrict__ slot_of_row, int64_t rows, int32_t* err) {
+  __shared__ int hist[kMaxE];
+  for (int e = threadIdx.x; e < E; e += kThreads) hist[e] = 0;
+  __syncthreads();
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kSlots;
+  for (int i = threadIdx.x; i < kSlots; i += kThreads) {
+    const int64_t s = s0 + i;
+    if (s < TK) {
+      const int e = ids[s];
+      if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+      else flag_error(err, MOE_DERR_EXPERT_ID);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads)
+    blockcounts[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
+  // every row starts as padding; the rank pass overwrites the real ones
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; r < rows;
+       r += static_cast<int64_t>(gridDim.x) * kThreads)
+    slot_of_row[r] = -1;
+}
+
+// Inclusive scan over the 1024 threads of a block.
+__device__ int block_scan_incl(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int t = (lane < 16) ? wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int u = __shfl_up(t, o, 64);
+      if (lane >= o) t += u;
+    }
+    if (lane < 16) wsum[lane] = t;
+  }
+  __syncthreads();
+  if (w > 0) v += wsum[w - 1];
+  return v;
+}
+
+__global__ __launch_bounds__(1024) void permute_scan_kernel(
+    int32_t* __restrict__ blockcounts, int nblocks, int E, int align, int capacity,
+    int capacity_layout, int64_t rows, int32_t* __restrict__ counts,
+    int32_t* __restrict__ group_sizes, int32_t* __restrict__ group_offsets, int32_t* err) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x;
+  int kept = 0, gs = 0;
+  if (e < E) {
+    int run = 0;
+    for (int b = 0; b < nblocks; ++b) {
+      int32_t* p = blockcounts + static_cast<int64_t>(b) * E + e;
+      const int c = *p;
+      *p = run;  // becomes this block's base rank for expert e
+      run += c;
+    }
+    kept = (capacity > 0 && run > capacity) ? capacity : run;
+    if (capacity_layout) gs = capacity;
+    else if (align > 0) gs = ((kept + align - 1) / align) * align;
+    else gs = kept;
+  }
+  const int incl = block_scan_incl(gs, wsum);
+  if (e < E) {
+    counts[e] = kept;
+    group_sizes[e] = gs;
+    group_offsets[e] = incl - gs;
+    if (e == E - 1) {
+      group_offsets[E] = incl;
+      if (incl > rows) flag_error(err, MOE_DERR_ROWS);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void permute_rank_kernel(
+    const int32_t* __restrict__ ids, int64_t TK, int E, int nbits, int capacity,
+    const int32_t* __restrict__ blockbase, const int32_t* __restrict__ group_offsets,
+    int64_t rows, int32_t* __restrict__ row_of_slot, int32_t* __restrict__ slot_of_row) {
+  __shared__ int base[kMaxE];                     // running rank per expert
+  __shared__ int wcnt[kThreads / 64][kMaxE];      // this chunk's per-wave counts
+  __shared__ int goff[kMaxE];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    base[e] = blockbase[static_cast<int64_t>(blockIdx.x) * E + e];
+    goff[e] = group_offsets[e];
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kSlots;
+  for (int c0 = 0; c0 < kSlots; c0 += kThreads) {
+    for (int i = threadIdx.x; i < (kThreads / 64) * E; i += kThreads) wcnt[i / E][i % E] = 0;
+    __syncthreads();
+    const int64_t s = s0 + c0 + threadIdx.x;
+    int e = (s < TK) ? ids[s] : -1;
+    const bool valid = e >= 0 && e < E;
+    if (!valid) e = 0;
+    // lanes holding the same expert id: AND of per-bit ballots
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t m = __ballot(valid && ((e >> b) & 1));
+      peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    const int below = __popcll(peers & lt_mask);
+    const int cnt = __popcll(peers);
+    if (valid && below == cnt - 1) wcnt[w][e] = cnt;   // highest lane of each peer set
+    __syncthreads();
+    if (valid) {
+      int rank = base[e] + below;
+      for (int v = 0; v < w; ++v) rank += wcnt[v][e];
+      int64_t row = -1;
+      if (capacity == 0 || rank < capacity) {
+        row = static_cast<int64_t>(goff[e]) + rank;
+        if (row >= rows) row = -1;
+      }
+      row_of_slot[s] = static_cast<int32_t>(row);
+      if (row >= 0) slot_of_row[row] = static_cast<int32_t>(s);
+    } else if (s < TK) {
+      row_of_slot[s] = -1;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < E; i += kThreads) {
+      int add = 0;
+#pragma unroll
+      for (int v = 0; v < kThreads / 64; ++v) add += wcnt[v][i];
+      base[i] += add;
+    }
+    __syncthreads();
+  }
+}
+
+// One wave per destination row; nvec 16-byte vectors per row.
+__global__ __launch_bounds__(kThreads) void permute_gather_kernel(
+    const uint4* __restrict__ x, int64_t nvec, int K, const int32_t* __restrict__ slot_of_row,
+    int64_t rows, uint4* __restrict__ xs) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int s = slot_of_row[r];
+  uint4* dst = xs + r * nvec;
+  if (s < 0) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int64_t i = lane; i < nvec; i += 64) dst[i] = z;
+    return;
+  }
+  const uint4* src = x + static_cast<int64_t>(s / K) * nvec;
+  int64_t i = lane;
+  for (; i + 192 < nvec; i += 256) {
+    const uint4 a = src[i], b = src[i + 64], c = src[i + 128], d = src[i + 192];
+    dst[i] = a; dst[i + 64] = b; dst[i + 128] = c; dst[i + 192] = d;
+  }
+  for (; i < nvec; i += 64) dst[i] = src[i];
+}
+
+// y[t] (+)= sum_j wt(t,j) * src[row_of_slot[t*K+j]]; one wave per token,
+// 8 elements per lane per step, float32 sums.
+template <typename T, bool WEIGHTED>
+__global__ __launch_bounds__(kThreads) void gather_sum_kernel(
+    const T* __restrict__ src, int64_t T_, int64_t D, int K, const int32_t* __restrict__ ros,
+    const float* __restrict__ wts, T* __restrict__ dst, int accumulate) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  for (int64_t c = static_cast<int64_t>(lane) * 8; c < D; c += 64 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    if (accumulate) load8(dst + t * D + c, acc);
+    for (int j = 0; j < K; ++j) {
+      const int r = ros[t * K + j];
+      if (r < 0) continue;
+      const float wv = WEIGHTED ? wts[t * K + j] : 1.0f;
+      float v[8];
+      load8(src + static_cast<int64_t>(r) * D + c, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wv, v[q], acc[q]);
+    }
+    store8(dst + t * D + c, acc);
+  }
+}
+
+// Row-centric combine backward: one wave per sorted row.  Blocks past the
+// row range zero d_w for dropped slots.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
+    const T* __restrict__ dy, const T* __restrict__ ys, int64_t D, int K, int64_t rows,
+    int64_t TK, const int32_t* __restrict__ ros, const int32_t* __restrict__ sor,
+    const float* __restrict__ wts, T* __restrict__ d_ys, float* __restrict__ d_w,
+    int64_t row_blocks) {
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x >= row_blocks) {
+    const int64_t s = (static_cast<int64_t>(blockIdx.x) - row_blocks) * kThreads + threadIdx.x;
+    if (s < TK && ros[s] < 0) d_w[s] = 0.f;
+    return;
+  }
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int s = sor[r];
+  T* out = d_ys + r * D;
+  if (s < 0) {
+    float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int64_t c = static_cast<int64_t>(lane) * 8; c < D; c += 512) store8(out + c, z);
+    return;
+  }
+  const float wv = wts[s];
+  const T* g = dy + static_cast<int64_t>(s / K) * D;
+  const T* yr = ys + r * D;
+  float dot = 0.f;
+  for (int64_t c = static_cast<int64_t>(lane) * 8; c < D; c += 512) {
+    float a[8], b[8], o[8];
+    load8(g + c, a);
+    load8(yr + c, b);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      o[q] = wv * a[q];
+      dot = fmaf(a[q], b[q], dot);
+    }
+    store8(out + c, o);
+  }
+  dot = wave_sum(dot);
+  if (lane == 0) d_w[s] = dot;
+}
+
+}  // namespace
+
+static int64_t rows_bound(int64_t T, int K, int E, int align, int capacity, int capacity_layout) {
+  if (T < 0 || K < 1 || E < 1 || align < 0 || capacity < 0) return -1;
+  if (capacity_layout) return capacity > 0 ? static_cast<int64_t>(E) * capacity : -1;
+  return T * K + (align > 0 ? static_cast<int64_t>(E) * (align - 1) : 0);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+MOE_API int64_t moe_rows_bound(int64_t T, int K, int E, int align, int capacity,
+                               int capacity_layout) {
+  return moe::rows_bound(T, K, E, align, capacity, capacity_layout);
+}
+
+MOE_API size_t moe_permute_workspace(int64_t T, int K, int E) {
+  if (T < 0 || K < 1 || E < 1) return 0;
+  const int64_t nb = (T * K + kSlots - 1) / kSlots;
+  const size_t bytes = static_cast<size_t>(nb > 0 ? nb : 1) * E * sizeof(int32_t);
+  return (bytes + 255) & ~static_cast<size_t>(255);
+}
+
+MOE_API int moe_permute(const void* x, int dtype, int64_t T, int64_t D, const int32_t* topk_ids,
+                        int K, int E, int align, int capacity, int capacity_layout,
+                        void* x_sorted, int64_t rows, int32_t* counts, int32_t* group_sizes,
+                        int32_t* group_offsets, int32_t* row_of_slot, int32_t* slot_of_row,
+                        void* workspace, size_t ws_bytes, int32_t* err, void* stream) {
+  if (T < 0 || D < 0 || K < 1 || K > 64 || E < 1 || E > kMaxE || align < 0 || capacity < 0)
+    return MOE_ERR_ARG;
+  if (capacity_layout && capacity <= 0) return MOE_ERR_ARG;
+  const int64_t bound = moe::rows_bound(T, K, E, align, capacity, capacity_layout);
+  if (rows < bound) return MOE_ERR_CAPACITY;
+  if (!topk_ids || !counts || !group_sizes || !group_offsets || !row_of_slot || !slot_of_row)
+    return MOE_ERR_ARG;
+  if (rows > INT32_MAX || T * K > INT32_MAX) return MOE_ERR_ARG;
+  const int eb = elem_bytes(dtype);
+  if (x_sorted) {
+    if (!eb) return MOE_ERR_DTYPE;
+    if ((T > 0 && !x) || (D * eb) % 16 || !aligned16(x) || !aligned16(x_sorted))
+      return MOE_ERR_ARG;
+  }
+  if (ws_bytes < moe_permute_workspace(T, K, E) || !workspace ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t TK = T * K;
+  const int nb = static_cast<int>((TK + kSlots - 1) / kSlots);
+  int32_t* blockcounts = static_cast<int32_t*>(workspace);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  // at least one block, so that counts are zeroed and padding rows marked
+  // even when there are no slots
+  const int nbh = nb > 0 ? nb : 1;
+  hipLaunchKernelGGL(permute_hist_kernel, dim3(nbh), dim3(kThreads), 0, st, topk_ids, TK, E,
+                     blockcounts, slot_of_row, rows, err);
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, st, blockcounts, nbh, E, align,
+                     capacity, capacity_layout, rows, counts, group_sizes, group_offsets, err);
+  if (nb > 0)
+    hipLaunchKernelGGL(permute_rank_kernel, dim3(nb), dim3(kThreads), 0, st, topk_ids, TK, E,
+                       nbits, capacity, blockcounts, group_offsets, rows, row_of_slot,
+                       slot_of_row);
+  if (x_sorted && rows > 0 && D > 0) {
+    const int64_t nvec = D * eb / 16;
+    const int64_t blocks = (rows + 3) / 4;
+    hipLaunchKernelGGL(permute_gather_kernel, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, st, static_cast<const uint4*>(x), nvec, K, slot_of_row,
+                       rows, static_cast<uint4*>(x_sorted));
+  }
+  return launch_status();
+}
+
+template <bool W>
+static int gather_sum(const void* src, int dtype, int64_t T, int64_t D, int K,
+                      const int32_t* ros, const float* w, void* dst, int accumulate,
+                      hipStream_t st) {
+  const unsigned blocks = static_cast<unsigned>((T + 3) / 4);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL((gather_sum_kernel<bf16_t, W>), dim3(blocks), dim3(kThreads), 0, st,
+                       static_cast<const bf16_t*>(src), T, D, K, ros, w,
+                       static_cast<bf16_t*>(dst), accumulate);
+  else
+    hipLaunchKernelGGL((gather_sum_kernel<float, W>), dim3(blocks), dim3(kThreads), 0, st,
+                       static_cast<const float*>(src), T, D, K, ros, w, static_cast<float*>(dst),
+                       accumulate);
+  return launch_status();
+}
+
+MOE_API int moe_permute_bwd(const void* d_x_sorted, int dtype, int64_t T, int64_t D, int K,
+                            int64_t rows, const int32_t* row_of_slot, void* d_x, int accumulate,
+                            void* stream) {
+  if (T < 0 || D < 0 || K < 1 || rows < 0) return MOE_ERR_ARG;
+  if (!elem_bytes(dtype)) return MOE_ERR_DTYPE;
+  if (T == 0 || D == 0) return MOE_OK;
+  if (!d_x_sorted || !row_of_slot || !d_x || D % 8 || !aligned16(d_x_sorted) || !aligned16(d_x))
+    return MOE_ERR_ARG;
+  return gather_sum<false>(d_x_sorted, dtype, T, D, K, row_of_slot, nullptr, d_x, accumulate,
+                           static_cast<hipStream_t>(stream));
+}
+
+MOE_API int moe_combine(const void* y_sorted, int dtype, int64_t T, int64_t D, int K,
+                        int64_t rows, const int32_t* row_of_slot, const float* topk_w, void* y,
+                        void* stream) {
+  if (T < 0 || D < 0 || K < 1 || rows < 0) return MOE_ERR_ARG;
+  if (!elem_bytes(dtype)) return MOE_ERR_DTYPE;
+  if (T == 0 || D == 0) return MOE_OK;
+  if (!y_sorted || !row_of_slot || !topk_w || !y || D % 8 || !aligned16(y_sorted) ||
+      !aligned16(y))
+    return MOE_ERR_ARG;
+  return gather_sum<true>(y_sorted, dtype, T, D, K, row_of_slot, topk_w, y, 0,
+                          static_cast<hipStream_t>(stream));
+}
+
+MOE_API int moe_combine_bwd(const void* d_y, const void* y_sorted, int dtype, int64_t T,
+                            int64_t D, int K, int64_t rows, const int32_t* row_of_slot,
+                            const int32_t* slot_of_row, const float* topk_w, void* d_y_sorted,
+                            float* d_topk_w, void* stream) {
+  if (T < 0 || D < 0 || K < 1 || rows < 0) return MOE_ERR_ARG;
+  if (!elem_bytes(dtype)) return MOE_ERR_DTYPE;
+  if (!d_y || !y_sorted || !row_of_slot || !slot_of_row || !topk_w || !d_y_sorted || !d_topk_w)
+    return (T == 0 && rows == 0) ? MOE_OK : MOE_ERR_ARG;
+  if (D % 8 || !aligned16(d_y) || !aligned16(y_sorted) || !aligned16(d_y_sorted))
+    return MOE_ERR_ARG;
+  const int64_t TK = T * K;
+  const int64_t row_blocks = (rows + 3) / 4;
+  const int64_t slot_blocks = (TK + kThreads - 1) / kThreads;
+  const unsigned grid = static_cast<unsigned>(row_blocks + slot_blocks);
+  if (grid == 0) return MOE_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, st,
+                       static_cast<const bf16_t*>(d_y), static_cast<const bf16_t*>(y_sorted), D,
+                       K, rows, TK, row_of_slot, slot_of_row, topk_w,
+                       static_cast<bf16_t*>(d_y_sorted), d_topk_w, row_blocks);
+  else
+    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(grid), dim3(kThreads), 0, st,
+                       static_cast<const float*>(d_y), static_cast<const float*>(y_sorted), D, K,
+                       rows, TK, row_of_slot, slot_of_row, topk_w,
+                       static_cast<float*>(d_y_sorted), d_topk_w, row_blocks);
+  return launch_status();
+}

@@ -1,0 +1,105 @@
+// SwiGLU gating of the expert FFN and its backward, elementwise over
+// [rows, F] with 8 elements per thread per step (HBM-bound).  The two inputs
+// are the gate and up projection outputs named in the TransformerEngine MoE
+// block pull request's commit notes (gate_proj_out, up_proj_out).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <typename TH, typename TA>
+__global__ __launch_bounds__(256) void swiglu_kernel(const TH* __restrict__ h0,
+                                                     const TH* __restrict__ h1, int64_t n8,
+                                                     TA* __restrict__ act) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float a[8], b[8], o[8];
+    load8(h0 + i * 8, a);
+    load8(h1 + i * 8, b);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = a[q] / (1.0f + expf(-a[q])) * b[q];
+    store8(act + i * 8, o);
+  }
+}
+
+template <typename TH, typename TD>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const TH* __restrict__ h0,
+                                                         const TH* __restrict__ h1,
+                                                         const TD* __restrict__ da, int64_t n8,
+                                                         TD* __restrict__ d0,
+                                                         TD* __restrict__ d1) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8;
+       i += static_cast<int64_t>(gridDim.x) * 256) {
+    float a[8], b[8], g[8], o0[8], o1[8];
+    load8(h0 + i * 8, a);
+    load8(h1 + i * 8, b);
+    load8(da + i * 8, g);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float s = 1.0f / (1.0f + expf(-a[q]));
+      o0[q] = g[q] * b[q] * s * (1.0f + a[q] * (1.0f - s));
+      o1[q] = g[q] * a[q] * s;
+    }
+    store8(d0 + i * 8, o0);
+    store8(d1 + i * 8, o1);
+  }
+}
+
+unsigned grid_for(int64_t n8) {
+  int64_t g = (n8 + 255) / 256;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 16;
+  if (g > cap) g = cap;
+  return static_cast<unsigned>(g < 1 ? 1 : g);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+MOE_API int moe_swiglu(const void* h0, const void* h1, int h_dtype, int64_t rows, int64_t F,
+                       void* act, int act_dtype, void* stream) {
+  if (rows < 0 || F < 0) return MOE_ERR_ARG;
+  if (!elem_bytes(h_dtype) || !elem_bytes(act_dtype)) return MOE_ERR_DTYPE;
+  const int64_t n = rows * F;
+  if (n == 0) return MOE_OK;
+  if (!h0 || !h1 || !act || n % 8 || !aligned16(h0) || !aligned16(h1) || !aligned16(act))
+    return MOE_ERR_ARG;
+  const int64_t n8 = n / 8;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned g = grid_for(n8);
+#define SW(TH, TA)                                                                         \
+  hipLaunchKernelGGL((swiglu_kernel<TH, TA>), dim3(g), dim3(256), 0, st,                  \
+                     static_cast<const TH*>(h0), static_cast<const TH*>(h1), n8, static_cast<TA*>(act))
+  if (h_dtype == MOE_BF16 && act_dtype == MOE_BF16) SW(bf16_t, bf16_t);
+  else if (h_dtype == MOE_BF16) SW(bf16_t, float);
+  else if (act_dtype == MOE_BF16) SW(float, bf16_t);
+  else SW(float, float);
+#undef SW
+  return launch_status();
+}
+
+MOE_API int moe_swiglu_bwd(const void* h0, const void* h1, int h_dtype, const void* d_act,
+                           int64_t rows, int64_t F, void* d_h0, void* d_h1, int d_dtype,
+                           void* stream) {
+  if (rows < 0 || F < 0) return MOE_ERR_ARG;
+  if (!elem_bytes(h_dtype) || !elem_bytes(d_dtype)) return MOE_ERR_DTYPE;
+  const int64_t n = rows * F;
+  if (n == 0) return MOE_OK;
+  if (!h0 || !h1 || !d_act || !d_h0 || !d_h1 || n % 8 || !aligned16(h0) || !aligned16(h1) ||
+      !aligned16(d_act) || !aligned16(d_h0) || !aligned16(d_h1))
+    return MOE_ERR_ARG;
+  const int64_t n8 = n / 8;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned g = grid_for(n8);
+#define SWB(TH, TD)                                                                          \
+  hipLaunchKernelGGL((swiglu_bwd_kernel<TH, TD>), dim3(g), dim3(256), 0, st,                \
+                     static_cast<const TH*>(h0), static_cast<const TH*>(h1),                 \
+                     static_cast<const TD*>(d_act), n8, static_cast<TD*>(d_h0), static_cast<TD*>(d_h1))
+  if (h_dtype == MOE_BF16 && d_dtype == MOE_BF16) SWB(bf16_t, bf16_t);
+  else if (h_dtype == MOE_BF16) SWB(bf16_t, float);
+  else if (d_dtype == MOE_BF16) SWB(float, bf16_t);
+  else SWB(float, float);
+#undef SWB
+  return launch_status();
+}

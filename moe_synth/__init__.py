@@ -86,7 +86,7 @@ WORKLOADS = {
                  capacity=22, logits="uniform"),
         Workload("mini_chunked", 333, 512, 160, 16, 4, "bf16", "softmax", True,
                  zipf_s=1.5, n_forced_empty=3, n_chunks=4, pad_rows_to=128),
-        Workload("mini_align8", 257, 128, 96, 12, 3, "bf16", "softmax", True,
+        Workload("mini_align8", 257, 128, 96, 16, 3, "bf16", "softmax", True,
                  align=8, zipf_s=1.2, n_forced_empty=2),
     ]
 }

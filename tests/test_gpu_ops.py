@@ -1,0 +1,285 @@
+"""Each C-ABI entry point against the float64 oracle, element by element, on
+seeded inputs that span several tiles, ragged tails and the degenerate
+cases (empty groups, one-row groups, no rows, ties, dropped slots)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+import oracle
+from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, dev, dev_i32, host, max_rel, poison)
+
+pytestmark = pytest.mark.gpu
+
+MODES = [("softmax", True), ("softmax", False), ("sigmoid", True), ("sigmoid", False)]
+
+
+def _topk_ids(g, T, E, K, off=()):
+    """K distinct experts per token from a Zipf-skewed distribution (Gumbel
+    top-k), never choosing the experts in `off`."""
+    p = 1.0 / np.arange(1, E + 1) ** 1.2
+    logp = np.log(p / p.sum())
+    logp[list(off)] = -np.inf
+    gum = g.gumbel(size=(T, E))
+    return np.argsort(-(logp[None, :] + gum), axis=1, kind="stable")[:, :K].astype(np.int32)
+
+
+# ---------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("E,K", [(8, 2), (33, 3), (64, 8), (256, 8), (1024, 4), (5, 5), (1, 1)])
+@pytest.mark.parametrize("score,renorm", MODES)
+def test_route(gpu_lib, E, K, score, renorm):
+    g = np.random.default_rng(1000 * E + K)
+    T = 301
+    z = (g.standard_normal((T, E)) * 2).astype(np.float32)
+    z[::5] = np.round(z[::5])                 # rows full of exact ties
+    bias = None
+    if E >= 8:
+        bias = (-1.2 * np.log(g.permutation(E) + 1.0)).astype(np.float32)
+        bias[[0, E - 1]] = -np.inf
+    ids, w = gpu_lib.moe_route(dev(z), K, score, renorm,
+                               bias=None if bias is None else dev(bias))
+    oi, ow = oracle.route(z, K, score, renorm, bias)
+    assert (host(ids) == oi).all()
+    assert_close(host(w), ow, TOL_F32, "topk_w")
+
+
+@pytest.mark.parametrize("E,K", [(8, 2), (64, 8), (256, 8), (9, 1)])
+@pytest.mark.parametrize("score,renorm", MODES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_route_bwd(gpu_lib, E, K, score, renorm, dtype):
+    g = np.random.default_rng(7 * E + K)
+    T = 257
+    z = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    bias = (-np.log(np.arange(1, E + 1))).astype(np.float32)
+    dw = g.standard_normal((T, K)).astype(np.float32)
+    oi, _ = oracle.route(z, K, score, renorm, bias)
+    d = gpu_lib.moe_route_bwd(dev(z), dev_i32(oi), dev(dw), score, renorm, bias=dev(bias),
+                              dtype=dtype)
+    want = oracle.route_bwd(z, oi, dw, score, renorm, bias)
+    assert_close(host(d), want, TOL_F32 if dtype == torch.float32 else TOL_BF16, "d_logits")
+
+
+# ------------------------------------------------------------- permutation
+
+PERMUTE_CASES = [
+    # T, K, E, align, capacity, capacity_layout, extra rows, forced-empty experts
+    (300, 2, 8, 0, 0, False, 0, (0,)),
+    (1500, 2, 8, 0, 0, False, 0, ()),          # several histogram blocks
+    (700, 8, 256, 128, 0, False, 0, (0, 5, 255)),
+    (257, 3, 12, 8, 0, False, 5, (11,)),       # buffer larger than the bound
+    (2000, 1, 64, 0, 20, False, 0, (3,)),      # dropping, compact layout
+    (2000, 1, 64, 0, 20, True, 0, (3,)),       # dropping, capacity layout
+    (2000, 2, 64, 16, 30, False, 0, ()),       # dropping + align
+    (100, 1, 1, 0, 0, False, 0, ()),           # one expert
+    (0, 2, 8, 0, 0, False, 0, ()),             # no tokens
+    (3000, 4, 1024, 16, 0, False, 0, (1023,)),
+]
+
+
+@pytest.mark.parametrize("case", PERMUTE_CASES, ids=[str(c[:7]) for c in PERMUTE_CASES])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_permute(gpu_lib, case, dtype):
+    T, K, E, a, C, lay, extra, off = case
+    g = np.random.default_rng(T + 31 * E + K)
+    ids = _topk_ids(g, T, E, K, off) if T else np.zeros((0, K), np.int32)
+    D = 136
+    x = g.standard_normal((T, D)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        x = ms.bf16_round(x)
+    rows = oracle.rows_bound(T, K, E, a, C, lay) + extra
+    want = oracle.permute(x, ids, E, a, C, lay, rows=rows)
+    xs = poison(torch.empty((rows, D), dtype=dtype, device="cuda"))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = gpu_lib.moe_permute(dev(x, dtype), dev_i32(ids), E, a, C, lay, rows=rows, x_sorted=xs,
+                              err=err)
+    for k in ("counts", "group_sizes", "group_offsets", "row_of_slot", "slot_of_row"):
+        assert (host(got[k]) == want[k]).all(), k
+    assert (host(xs) == want["x_sorted"]).all()      # a copy: bit-exact
+    assert host(err)[0] == 0
+
+
+def test_permute_invalid_ids_flagged(gpu_lib):
+    g = np.random.default_rng(5)
+    T, K, E = 200, 2, 8
+    ids = _topk_ids(g, T, E, K)
+    ids[3, 1] = E
+    ids[77, 0] = -1
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = gpu_lib.moe_permute(None, dev_i32(ids), E, err=err)
+    ros = host(got["row_of_slot"])
+    assert host(err)[0] & gpu_lib.MOE_DERR_EXPERT_ID
+    assert ros[3 * K + 1] == -1 and ros[77 * K] == -1
+    real = ros[ros >= 0]
+    assert sorted(real.tolist()) == list(range(T * K - 2))
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, TOL_F32), (torch.bfloat16, TOL_BF16)])
+@pytest.mark.parametrize("case", [(300, 2, 8, 0, 0, False), (400, 8, 64, 16, 0, False),
+                                  (900, 1, 32, 0, 20, False), (900, 1, 32, 0, 20, True)])
+def test_combine_and_backward(gpu_lib, dtype, tol, case):
+    T, K, E, a, C, lay = case
+    g = np.random.default_rng(T * K)
+    D = 264
+    ids = _topk_ids(g, T, E, K, (1,))
+    P = oracle.permute(None, ids, E, a, C, lay)
+    rows = P["slot_of_row"].size
+    ys = g.standard_normal((rows, D)).astype(np.float32)
+    dy = g.standard_normal((T, D)).astype(np.float32)
+    dxs = g.standard_normal((rows, D)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        ys, dy, dxs = ms.bf16_round(ys), ms.bf16_round(dy), ms.bf16_round(dxs)
+    w = g.random((T, K)).astype(np.float32)
+    ros, sor = dev_i32(P["row_of_slot"]), dev_i32(P["slot_of_row"])
+    y = gpu_lib.moe_combine(dev(ys, dtype), ros, dev(w))
+    assert_close(host(y), oracle.combine(ys, P["row_of_slot"], w, T, K), tol, "combine")
+    d_ys = poison(torch.empty((rows, D), dtype=dtype, device="cuda"))
+    d_w = poison(torch.empty((T, K), dtype=torch.float32, device="cuda"))
+    gpu_lib.moe_combine_bwd(dev(dy, dtype), dev(ys, dtype), ros, sor, dev(w), d_y_sorted=d_ys,
+                            d_topk_w=d_w)
+    w_ys, w_dw = oracle.combine_bwd(dy, ys, P["row_of_slot"], w, rows)
+    assert_close(host(d_ys), w_ys, tol, "d_y_sorted")
+    assert_close(host(d_w), w_dw, TOL_F32, "d_topk_w")
+    dx = gpu_lib.moe_permute_bwd(dev(dxs, dtype), ros, T, K)
+    assert_close(host(dx), oracle.permute_bwd(dxs, P["row_of_slot"], T, K), tol, "permute_bwd")
+    base = g.standard_normal((T, D)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        base = ms.bf16_round(base)
+    dx2 = dev(base, dtype)
+    gpu_lib.moe_permute_bwd(dev(dxs, dtype), ros, T, K, d_x=dx2, accumulate=True)
+    assert_close(host(dx2), base + oracle.permute_bwd(dxs, P["row_of_slot"], T, K), tol,
+                 "permute_bwd accumulate")
+
+
+# ------------------------------------------------------------ grouped GEMMs
+
+GS = {
+    "ragged": [130, 0, 257, 1, 64, 0, 300],
+    "empty_first": [0, 0, 128, 256],
+    "one_group": [517],
+    "all_empty": [0, 0, 0],
+    "aligned": [128, 256, 0, 384],
+}
+
+GMM_CASES = [
+    # groups, Kdim, N, extra lhs rows, out rows short of lhs, trans, in, out, accumulate
+    ("ragged", 192, 136, 7, 0, False, "bf16", "f32", False),
+    ("ragged", 192, 136, 7, 0, True, "bf16", "f32", False),
+    ("ragged", 200, 256, 0, 0, False, "bf16", "bf16", False),
+    ("ragged", 512, 128, 3, 0, True, "bf16", "bf16", False),
+    ("empty_first", 64, 264, 0, 0, False, "bf16", "f32", True),
+    ("empty_first", 64, 264, 0, 0, True, "bf16", "f32", True),
+    ("one_group", 136, 8, 0, 0, False, "bf16", "f32", False),     # router-like, N = 8
+    ("one_group", 8, 136, 0, 0, True, "bf16", "bf16", True),      # Kdim = 8
+    ("all_empty", 64, 128, 9, 0, False, "bf16", "f32", False),
+    ("aligned", 128, 128, 128, 100, False, "bf16", "f32", True),  # padded lhs, shorter out
+    ("ragged", 72, 40, 5, 0, False, "f32", "f32", False),
+    ("ragged", 72, 40, 5, 0, True, "f32", "f32", True),
+    ("one_group", 96, 8, 0, 0, False, "f32", "f32", False),
+    ("aligned", 64, 24, 64, 30, True, "f32", "bf16", False),
+]
+
+
+def _draw(g, shape, dt):
+    a = g.standard_normal(shape).astype(np.float32)
+    return ms.bf16_round(a) if dt == "bf16" else a
+
+
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.mark.parametrize("case", GMM_CASES, ids=[f"{c[0]}-{c[1]}x{c[2]}-t{int(c[5])}-{c[6]}{c[7]}-a{int(c[8])}" for c in GMM_CASES])
+def test_gmm(gpu_lib, case):
+    name, Kd, N, extra, short, trans, it, ot, acc = case
+    gs = np.array(GS[name], dtype=np.int32)
+    G = len(gs)
+    g = np.random.default_rng(Kd * 1000 + N + extra)
+    M_lhs = int(gs.sum()) + extra
+    M_out = M_lhs - short
+    lhs = _draw(g, (M_lhs, Kd), it)
+    rhs = _draw(g, (G, N, Kd) if trans else (G, Kd, N), it)
+    P = _draw(g, (M_out, N), ot) if acc else None
+    out = dev(P, TD[ot]) if acc else poison(torch.empty((M_out, N), dtype=TD[ot], device="cuda"))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gpu_lib.moe_gmm(dev(lhs, TD[it]), dev(rhs, TD[it]), dev_i32(gs), trans_rhs=trans, out=out,
+                    accumulate=acc, err=err)
+    want = oracle.gmm(lhs, rhs, gs, trans_rhs=trans, partial=P, rows_out=M_out)
+    got = host(out)
+    tol = TOL_F32 if ot == "f32" else TOL_BF16
+    assert_close(got, want, tol, "gmm")
+    S = int(gs.sum())
+    if acc:
+        assert (got[S:] == P[S:]).all()           # rows past the groups untouched
+    else:
+        assert (got[S:] == 0).all()               # rows past the groups zero-filled
+    assert host(err)[0] == 0
+
+
+def test_gmm_strided_chunks(gpu_lib):
+    """Contracting-dim chunks of a wider lhs and rhs (views with ld > K),
+    accumulated in place into a float32 partial sum = the unchunked product."""
+    g = np.random.default_rng(3)
+    gs = np.array([100, 0, 37, 200], dtype=np.int32)
+    G, D, N, n = 4, 512, 136, 4
+    M_lhs = 384                                   # padded to a 128-row tile
+    x = ms.bf16_round(g.standard_normal((M_lhs, D)).astype(np.float32))
+    w = ms.bf16_round(g.standard_normal((G, D, N)).astype(np.float32))
+    xd, wd = dev(x, torch.bfloat16), dev(w, torch.bfloat16)
+    out = poison(torch.empty((int(gs.sum()), N), dtype=torch.float32, device="cuda"))
+    c = D // n
+    for i in range(n):
+        gpu_lib.moe_gmm(xd[:, i * c:(i + 1) * c], wd[:, i * c:(i + 1) * c, :], dev_i32(gs), out=out,
+                        accumulate=i > 0)
+    want = oracle.gmm(x, w, gs, rows_out=int(gs.sum()))
+    assert_close(host(out), want, TOL_F32, "chunked gmm")
+
+
+TGMM_CASES = [
+    ("ragged", 136, 128, "bf16", "f32", False),
+    ("ragged", 64, 72, "bf16", "bf16", True),
+    ("empty_first", 200, 264, "bf16", "f32", True),
+    ("one_group", 128, 8, "bf16", "f32", False),
+    ("all_empty", 64, 64, "bf16", "f32", False),
+    ("all_empty", 64, 64, "bf16", "f32", True),
+    ("ragged", 40, 24, "f32", "f32", False),
+    ("aligned", 16, 48, "f32", "f32", True),
+]
+
+
+@pytest.mark.parametrize("case", TGMM_CASES, ids=[f"{c[0]}-{c[1]}x{c[2]}-{c[3]}{c[4]}-a{int(c[5])}" for c in TGMM_CASES])
+def test_tgmm(gpu_lib, case):
+    name, Kd, N, it, ot, acc = case
+    gs = np.array(GS[name], dtype=np.int32)
+    G = len(gs)
+    g = np.random.default_rng(Kd * 7 + N)
+    M = int(gs.sum()) + 5
+    lhs = _draw(g, (M, Kd), it)
+    rhs = _draw(g, (M, N), it)
+    P = _draw(g, (G, Kd, N), ot) if acc else None
+    out = dev(P, TD[ot]) if acc else poison(torch.empty((G, Kd, N), dtype=TD[ot], device="cuda"))
+    gpu_lib.moe_tgmm(dev(lhs, TD[it]), dev(rhs, TD[it]), dev_i32(gs), out=out, accumulate=acc)
+    want = oracle.tgmm(lhs, rhs, gs, partial=P)
+    got = host(out)
+    assert_close(got, want, TOL_F32 if ot == "f32" else TOL_BF16, "tgmm")
+    for gg in range(G):
+        if gs[gg] == 0:
+            assert (got[gg] == (P[gg] if acc else 0)).all(), "empty group"
+
+
+# ------------------------------------------------------------------ SwiGLU
+
+@pytest.mark.parametrize("hd,ad", [("bf16", "bf16"), ("f32", "bf16"), ("f32", "f32")])
+def test_swiglu(gpu_lib, hd, ad):
+    g = np.random.default_rng(11)
+    rows, F = 333, 136
+    h0 = _draw(g, (rows, F), hd) * 3
+    h0 = ms.bf16_round(h0) if hd == "bf16" else h0
+    h1 = _draw(g, (rows, F), hd)
+    da = _draw(g, (rows, F), ad)
+    act = gpu_lib.moe_swiglu(dev(h0, TD[hd]), dev(h1, TD[hd]), act_dtype=TD[ad])
+    tol = TOL_F32 if ad == "f32" else TOL_BF16
+    assert_close(host(act), oracle.swiglu(h0, h1), tol, "swiglu")
+    d0, d1 = gpu_lib.moe_swiglu_bwd(dev(h0, TD[hd]), dev(h1, TD[hd]), dev(da, TD[ad]))
+    w0, w1 = oracle.swiglu_bwd(h0, h1, da)
+    assert_close(host(d0), w0, tol, "d_h0")
+    assert_close(host(d1), w1, tol, "d_h1")
