@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""MoE expert-FFN forward+backward throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+
+A step is one pass of the whole path over one batch of synthetic input:
+router GEMM, top-k routing, permute, the up-projection grouped GEMMs,
+SwiGLU, the down-projection grouped GEMM and the weighted combine, then the
+hand-derived backward (combine backward, grouped GEMMs with the rhs
+transposed, transposed grouped GEMMs for the expert weight gradients,
+SwiGLU backward, permute backward, routing backward and the router GEMM
+backward).  Inputs are resident in HBM before the timed region starts.
+
+`value` is expert-FFN TFLOP/s: 18 * R * d_model * d_ff algorithmic flops per
+step (R = kept routed rows; padding rows and the router GEMM excluded)
+divided by the step time.  Prints ONE JSON line on stdout; everything else
+goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE FFN fwd+bwd grouped-GEMM TFLOP/s and % of bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="mixtral")
+    p.add_argument("--cpu-tokens", type=int, default=2048,
+                   help="tokens of the workload the CPU oracle baseline runs on")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-kernel-events", action="store_true",
+                   help="do not bracket the expert GEMM launches with events")
+    return p.parse_args()
+
+
+def gen_inputs(w, threads: int):
+    """Seeded inputs (CPU), generated per expert in parallel."""
+    import numpy as np
+    import moe_synth as ms
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        futs = {name: [ex.submit(ms.gen_expert_weight, w, name, e) for e in range(w.E)]
+                for name in ("wi_0", "wi_1", "wo")}
+        x = ms.gen_x(w)
+        dy = ms.gen_dy(w)
+        Wg = ms.gen_gate(w) if w.logits == "gemm" else None
+        logits = ms.gen_uniform_logits(w) if w.logits == "uniform" else None
+        bias = ms.gen_logit_bias(w)
+        weights = {k: [f.result() for f in v] for k, v in futs.items()}
+    log(f"[bench] generated inputs in {time.time() - t0:.1f}s")
+    return dict(x=x, dy=dy, Wg=Wg, logits=logits, bias=bias, **weights)
+
+
+def to_gpu(inp, dtype):
+    import numpy as np
+    import torch
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        return t.to(dtype) if dtype != torch.float32 else t
+
+    out = {k: up(inp[k]) if inp[k] is not None else None for k in ("x", "dy", "Wg")}
+    for k in ("wi_0", "wi_1", "wo"):
+        out[k] = torch.stack([up(a) for a in inp[k]])
+    for k in ("logits", "bias"):   # float32 router inputs
+        out[k] = torch.from_numpy(inp[k]).cuda() if inp[k] is not None else None
+    return out
+
+
+class LaunchRecorder:
+    """Brackets launches with events on the stream they are issued on."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.items = []
+        self.active = False
+
+    def __call__(self, kind, flops):
+        rec = self
+
+        class _Ctx:
+            def __enter__(self_):
+                if rec.active:
+                    self_.s = rec.torch.cuda.Event(enable_timing=True)
+                    self_.s.record(rec.torch.cuda.current_stream())
+
+            def __exit__(self_, *exc):
+                if rec.active:
+                    e = rec.torch.cuda.Event(enable_timing=True)
+                    e.record(rec.torch.cuda.current_stream())
+                    rec.items.append((kind, flops, self_.s, e))
+                return False
+        return _Ctx()
+
+    def summary(self):
+        agg = {}
+        for kind, flops, s, e in self.items:
+            ms = s.elapsed_time(e)
+            a = agg.setdefault(kind, dict(launches=0, ms=0.0, flops=0.0))
+            a["launches"] += 1
+            a["ms"] += ms
+            a["flops"] += flops
+        for a in agg.values():
+            a["avg_ms"] = a["ms"] / a["launches"]
+            a["tflops"] = a["flops"] / (a["ms"] * 1e-3) / 1e12
+        return agg
+
+
+# Kernel symbol behind each recorded launch kind for the bf16 workloads
+# (the rocprofv3 summary is matched on this name).
+KERNEL_NAME = {
+    "gmm_nn": "gmm_bf16_kernel<128, 128, false, unsigned short>",
+    "gmm_nt": "gmm_bf16_kernel<128, 128, true, unsigned short>",
+    "tgmm": "tgmm_bf16_kernel<128, 128, unsigned short>",
+    "gmm_up_chunk": "gmm_bf16_kernel<128, 128, false, float>",
+}
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "mixture_experts_grouped_top_amd", "csrc", "gmm.hip")
+    with open(src, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kind: str):
+    """HBM bytes per launch of the dominant kernel from the committed PMC
+    summary, or None if absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "gmm_mixtral_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = d.get("kernels", {}).get(kind)
+    if not k or d.get("gmm_source_sha256_16") != kernel_source_digest():
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, tokens: int):
+    """The float64 oracle, as it stands, on the first `tokens` tokens."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    T = min(tokens, w.T)
+    sl = slice(0, T)
+    wi0, wi1, wo = (np.stack(inp[k]) for k in ("wi_0", "wi_1", "wo"))
+    kw = dict(score=w.score, renorm=w.renorm, bias=inp["bias"])
+    t0 = time.perf_counter()
+    f = oracle.moe_forward(inp["x"][sl], wi0, wi1, wo, w.K, Wg=inp["Wg"],
+                           logits=None if inp["logits"] is None else inp["logits"][sl],
+                           align=w.align, capacity=w.capacity, n_chunks=w.n_chunks, **kw)
+    oracle.moe_backward(f, inp["dy"][sl], inp["x"][sl], wi0, wi1, wo, w.K, Wg=inp["Wg"], **kw)
+    dt = time.perf_counter() - t0
+    R = int((f["perm"]["row_of_slot"] >= 0).sum())
+    flops = 18.0 * R * w.D * w.F
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 oracle forward+backward on the first {T} of {w.T} tokens "
+                      f"({R} routed rows, all {w.E} experts) of the same workload; "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import moe_synth as ms
+    import mixture_experts_grouped_top_amd as moe
+
+    moe.load()
+    w = ms.get_workload(args.workload)
+    dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    threads = min(16, len(os.sched_getaffinity(0)))
+    inp = gen_inputs(w, threads)
+    g = to_gpu(inp, dtype)
+    shape = moe.MoEShape(T=w.T, D=w.D, F=w.F, E=w.E, K=w.K, dtype=dtype, score=w.score,
+                         renorm=w.renorm, align=w.align, capacity=w.capacity,
+                         n_chunks=w.n_chunks, pad_rows_to=w.pad_rows_to)
+    plan = moe.MoEPlan(shape)
+
+    def step():
+        plan.forward(g["x"], g["wi_0"], g["wi_1"], g["wo"], Wg=g["Wg"], logits=g["logits"],
+                     bias=g["bias"])
+        plan.backward(g["dy"], g["x"], g["wi_0"], g["wi_1"], g["wo"], Wg=g["Wg"], bias=g["bias"])
+
+    # one untimed step to learn the kept row count (dropping) for the flop count
+    step()
+    torch.cuda.synchronize()
+    R = int(plan.idx["counts"].sum().item())
+    plan.kept_rows_override = R
+    for _ in range(max(0, args.warmup - 1)):
+        step()
+    rec = LaunchRecorder()
+    if not args.no_kernel_events:
+        plan.recorder = rec
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    rec.active = True
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    rec.active = False
+    ms_step = start.elapsed_time(end) / args.steps
+    err = int(plan.err.item())
+    flops = 18.0 * R * w.D * w.F
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    log(f"[bench] {args.workload}: {ms_step:.3f} ms/step, {tflops:.1f} TFLOP/s, R={R}, err={err}")
+
+    kernels = rec.summary()
+    roofline = None
+    if kernels:
+        kind = max(kernels, key=lambda k: kernels[k]["ms"])
+        k = kernels[kind]
+        ach = k["tflops"]
+        traffic = traffic_from_profiles(kind)
+        roofline = {"bound": "mfma", "kernel": KERNEL_NAME.get(kind, kind),
+                    "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                    "avg_launch_ms": round(k["avg_ms"], 4),
+                    "flops_per_launch": k["flops"] / k["launches"]}
+        for kk, v in kernels.items():
+            log(f"[bench]   {kk:12s} {v['launches']:4d} launches  avg {v['avg_ms']:.3f} ms  "
+                f"{v['tflops']:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(w, inp, args.cpu_tokens)
+        log(f"[bench] cpu baseline: {cpu} ({time.time() - t0:.1f}s)")
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights; no dataset)",
+        "config": {"workload": w.name, "tokens": w.T, "d_model": w.D, "d_ff": w.F,
+                   "experts": w.E, "top_k": w.K, "score": w.score, "renorm": w.renorm,
+                   "align_size": w.align, "capacity": w.capacity, "chunks": w.n_chunks,
+                   "routed_rows": R},
+        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device_error_flags": err,
+        "kernels": {k: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
+                        "tflops": round(v["tflops"], 2)} for k, v in kernels.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

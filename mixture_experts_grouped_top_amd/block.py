@@ -16,6 +16,7 @@ chunked gmm).
 """
 from __future__ import annotations
 
+import contextlib
 import dataclasses
 from typing import Optional
 
@@ -90,11 +91,29 @@ class MoEPlan:
         self.d_wi_0 = torch.empty((s.E, s.D, s.F), **act)
         self.d_wi_1 = torch.empty((s.E, s.D, s.F), **act)
         self.d_wo = torch.empty((s.E, s.F, s.D), **act)
-        self.d_Wg = torch.empty((1, s.D, s.E), **act) if router else None
+        # router weight gradient kept in float32 (a [D, E] reduction over all tokens)
+        self.d_Wg = torch.empty((1, s.D, s.E), **f32) if router else None
+        self.recorder = None   # optional callable(kind, flops) -> context manager
+
+    def _rec(self, kind: str, flops: float):
+        if self.recorder is None:
+            return contextlib.nullcontext()
+        return self.recorder(kind, flops)
 
     @property
     def group_sizes(self):
         return self.idx["group_sizes"]
+
+    # Routed rows the expert GEMMs must process (the algorithmic work); set
+    # by the caller when dropping makes it smaller than T*K (it is only used
+    # to label recorded launches with their flops).
+    kept_rows_override: Optional[int] = None
+
+    @property
+    def kept_rows(self) -> int:
+        if self.kept_rows_override is not None:
+            return self.kept_rows_override
+        return self.s.T * self.s.K
 
     def forward(self, x, wi_0, wi_1, wo, Wg=None, logits=None, bias=None, stream=None):
         """y = sum_j w[t,j] FFN_{e(t,j)}(x[t]).  Either Wg (router GEMM on the
@@ -110,19 +129,25 @@ class MoEPlan:
                       rows=self.lhs_rows, x_sorted=self.x_sorted, err=self.err,
                       workspace=self.ws, out=self.idx, stream=stream)
         gs = self.group_sizes
+        R = self.kept_rows
         if s.n_chunks > 1:
             c = s.D // s.n_chunks
             for i in range(s.n_chunks):
                 xs = self.x_sorted[:, i * c:(i + 1) * c]
-                B.moe_gmm(xs, wi_0[:, i * c:(i + 1) * c, :], gs, out=self.h0, accumulate=i > 0,
-                          err=self.err, stream=stream)
-                B.moe_gmm(xs, wi_1[:, i * c:(i + 1) * c, :], gs, out=self.h1, accumulate=i > 0,
-                          err=self.err, stream=stream)
+                with self._rec("gmm_up_chunk", 2.0 * R * c * s.F):
+                    B.moe_gmm(xs, wi_0[:, i * c:(i + 1) * c, :], gs, out=self.h0,
+                              accumulate=i > 0, err=self.err, stream=stream)
+                with self._rec("gmm_up_chunk", 2.0 * R * c * s.F):
+                    B.moe_gmm(xs, wi_1[:, i * c:(i + 1) * c, :], gs, out=self.h1,
+                              accumulate=i > 0, err=self.err, stream=stream)
         else:
-            B.moe_gmm(self.x_sorted, wi_0, gs, out=self.h0, err=self.err, stream=stream)
-            B.moe_gmm(self.x_sorted, wi_1, gs, out=self.h1, err=self.err, stream=stream)
+            with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+                B.moe_gmm(self.x_sorted, wi_0, gs, out=self.h0, err=self.err, stream=stream)
+            with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+                B.moe_gmm(self.x_sorted, wi_1, gs, out=self.h1, err=self.err, stream=stream)
         B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
-        B.moe_gmm(self.act, wo, gs, out=self.y_sorted, err=self.err, stream=stream)
+        with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+            B.moe_gmm(self.act, wo, gs, out=self.y_sorted, err=self.err, stream=stream)
         B.moe_combine(self.y_sorted, self.idx["row_of_slot"], self.w, y=self.y, stream=stream)
         return self.y
 
@@ -131,21 +156,28 @@ class MoEPlan:
         and (with the router) d_Wg."""
         s = self.s
         gs = self.group_sizes
+        R = self.kept_rows
         ros, sor = self.idx["row_of_slot"], self.idx["slot_of_row"]
         B.moe_combine_bwd(dy, self.y_sorted, ros, sor, self.w, d_y_sorted=self.d_y_sorted,
                           d_topk_w=self.d_w, stream=stream)
-        B.moe_gmm(self.d_y_sorted, wo, gs, trans_rhs=True, out=self.d_act, err=self.err,
-                  stream=stream)
-        B.moe_tgmm(self.act, self.d_y_sorted, gs, out=self.d_wo, err=self.err, stream=stream)
+        with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+            B.moe_gmm(self.d_y_sorted, wo, gs, trans_rhs=True, out=self.d_act, err=self.err,
+                      stream=stream)
+        with self._rec("tgmm", 2.0 * R * s.D * s.F):
+            B.moe_tgmm(self.act, self.d_y_sorted, gs, out=self.d_wo, err=self.err, stream=stream)
         B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
                          stream=stream)
-        B.moe_gmm(self.d_h0, wi_0, gs, trans_rhs=True, out=self.d_x_sorted, err=self.err,
-                  stream=stream)
-        B.moe_gmm(self.d_h1, wi_1, gs, trans_rhs=True, out=self.d_x_sorted, accumulate=True,
-                  err=self.err, stream=stream)
+        with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+            B.moe_gmm(self.d_h0, wi_0, gs, trans_rhs=True, out=self.d_x_sorted, err=self.err,
+                      stream=stream)
+        with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+            B.moe_gmm(self.d_h1, wi_1, gs, trans_rhs=True, out=self.d_x_sorted,
+                      accumulate=True, err=self.err, stream=stream)
         xs = self.x_sorted[:self.rows]
-        B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream)
-        B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream)
+        with self._rec("tgmm", 2.0 * R * s.D * s.F):
+            B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream)
+        with self._rec("tgmm", 2.0 * R * s.D * s.F):
+            B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream)
         B.moe_permute_bwd(self.d_x_sorted, ros, s.T, s.K, d_x=self.dx, stream=stream)
         B.moe_route_bwd(self.logits, self.ids, self.d_w, s.score, s.renorm, bias,
                         d_logits=self.d_logits, stream=stream)

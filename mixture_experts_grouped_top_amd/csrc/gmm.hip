@@ -547,18 +547,30 @@ MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* 
     return MOE_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == MOE_BF16) {
-    const int64_t upper = ((M_out + kBM - 1) / kBM + G) * ((N + kBN - 1) / kBN);
-    const unsigned grid = persistent_grid(upper, 2);
     const bf16_t* A = static_cast<const bf16_t*>(lhs);
     const bf16_t* B = static_cast<const bf16_t*>(rhs);
-#define GMM(TR, TO)                                                                            \
-  hipLaunchKernelGGL((gmm_bf16_kernel<kBM, kBN, TR, TO>), dim3(grid), dim3(NT), 0, st, A, ld_lhs, \
+#define GMM(BMV, TR, TO)                                                                        \
+  hipLaunchKernelGGL((gmm_bf16_kernel<BMV, kBN, TR, TO>), dim3(grid), dim3(NT), 0, st, A, ld_lhs, \
                      B, ld_rhs, rhs_group_stride, group_sizes, G, Kdim, N, static_cast<TO*>(out), \
                      M_out, ld_out, accumulate, err)
-    if (trans_rhs) {
-      if (out_dtype == MOE_BF16) GMM(true, bf16_t); else GMM(true, float);
+    if (Kdim <= BK) {
+      // one contraction step: a taller row tile amortises the rhs tile
+      constexpr int kTall = 256;
+      const int64_t upper = ((M_out + kTall - 1) / kTall + G) * ((N + kBN - 1) / kBN);
+      const unsigned grid = persistent_grid(upper, 1);
+      if (trans_rhs) {
+        if (out_dtype == MOE_BF16) GMM(kTall, true, bf16_t); else GMM(kTall, true, float);
+      } else {
+        if (out_dtype == MOE_BF16) GMM(kTall, false, bf16_t); else GMM(kTall, false, float);
+      }
     } else {
-      if (out_dtype == MOE_BF16) GMM(false, bf16_t); else GMM(false, float);
+      const int64_t upper = ((M_out + kBM - 1) / kBM + G) * ((N + kBN - 1) / kBN);
+      const unsigned grid = persistent_grid(upper, 2);
+      if (trans_rhs) {
+        if (out_dtype == MOE_BF16) GMM(kBM, true, bf16_t); else GMM(kBM, true, float);
+      } else {
+        if (out_dtype == MOE_BF16) GMM(kBM, false, bf16_t); else GMM(kBM, false, float);
+      }
     }
 #undef GMM
   } else {

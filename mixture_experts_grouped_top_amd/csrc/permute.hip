@@ -289,8 +289,9 @@ MOE_API int moe_permute(const void* x, int dtype, int64_t T, int64_t D, const in
   if (capacity_layout && capacity <= 0) return MOE_ERR_ARG;
   const int64_t bound = moe::rows_bound(T, K, E, align, capacity, capacity_layout);
   if (rows < bound) return MOE_ERR_CAPACITY;
-  if (!topk_ids || !counts || !group_sizes || !group_offsets || !row_of_slot || !slot_of_row)
-    return MOE_ERR_ARG;
+  if (!counts || !group_sizes || !group_offsets) return MOE_ERR_ARG;
+  if (T * K > 0 && (!topk_ids || !row_of_slot)) return MOE_ERR_ARG;
+  if (rows > 0 && !slot_of_row) return MOE_ERR_ARG;
   if (rows > INT32_MAX || T * K > INT32_MAX) return MOE_ERR_ARG;
   const int eb = elem_bytes(dtype);
   if (x_sorted) {

@@ -125,9 +125,22 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
     return bf16_from_bits(bf16_bits(a))
 
 
-def _store(w: Workload, a: np.ndarray) -> np.ndarray:
-    a = a.astype(np.float32, copy=False)
-    return bf16_round(a) if w.dtype == "bf16" else a
+def _bf16_round_inplace(a: np.ndarray) -> np.ndarray:
+    """bf16_round without temporaries of the full size but one."""
+    u = a.view(np.uint32)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    u += t
+    u &= np.uint32(0xFFFF0000)
+    return a
+
+
+def _store(w: Workload, a: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if scale is not None:
+        a *= np.float32(scale)
+    return _bf16_round_inplace(a) if w.dtype == "bf16" else a
 
 
 # ---- tensors ----------------------------------------------------------------
@@ -143,7 +156,7 @@ def gen_gate(w: Workload, seed: Optional[int] = None) -> np.ndarray:
     """Router kernel Wg [D, E] ~ N(0, w_std^2)."""
     s = w.seed if seed is None else seed
     g = stream(s, w.name, "gate")
-    return _store(w, g.standard_normal((w.D, w.E), dtype=np.float32) * np.float32(w.w_std))
+    return _store(w, g.standard_normal((w.D, w.E), dtype=np.float32), w.w_std)
 
 
 def gen_expert_weight(w: Workload, name: str, e: int, seed: Optional[int] = None) -> np.ndarray:
@@ -151,7 +164,7 @@ def gen_expert_weight(w: Workload, name: str, e: int, seed: Optional[int] = None
     s = w.seed if seed is None else seed
     shape = (w.F, w.D) if name == "wo" else (w.D, w.F)
     g = stream(s, w.name, name, e)
-    return _store(w, g.standard_normal(shape, dtype=np.float32) * np.float32(w.w_std))
+    return _store(w, g.standard_normal(shape, dtype=np.float32), w.w_std)
 
 
 def gen_expert_weights(w: Workload, name: str, seed: Optional[int] = None) -> np.ndarray:
