@@ -48,131 +48,12 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;      // contraction elements per step
-
-__device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
-constexpr int NT = 256;     // threads per workgroup
+constexpr int NT = 256;     // threads per workgroup (4 waves)
 constexpr int kMaxG = 1024;
 
-__device__ __forceinline__ int lds_off(int x, int c) {
-  return x * (BK * 2) + ((c ^ (x & 7) ^ ((x >> 3) & 7)) << 4);
-}
-
-// Element (x, k) at src[x * ld + k]: contraction contiguous.
-template <int X>
-struct RowK {
-  static constexpr int N = X * (BK / 8) / NT;
-  uint4 r[N];
-  __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int xv, int kv) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = threadIdx.x + i * NT, x = q >> 3, c = q & 7;
-      if (x < xv && c * 8 < kv) r[i] = *reinterpret_cast<const uint4*>(src + x * ld + c * 8);
-      else r[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int q = threadIdx.x + i * NT, x = q >> 3, c = q & 7;
-      *reinterpret_cast<uint4*>(lds + lds_off(x, c)) = r[i];
-    }
-  }
-};
-
-// Element (x, k) at src[k * ld + x]: contraction is the row index.
-template <int X>
-struct ColK {
-  static constexpr int XQ = X / 8;
-  static constexpr int N = (BK / 4) * XQ / NT;
-  uint4 r[N][4];
-  __device__ __forceinline__ void load(const bf16_t* src, int64_t ld, int xv, int kv) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int u = threadIdx.x + i * NT, xq = u % XQ, kq = u / XQ;
-#pragma unroll
-      for (int kr = 0; kr < 4; ++kr) {
-        const int k = 4 * kq + kr;
-        if (k < kv && xq * 8 < xv)
-          r[i][kr] = *reinterpret_cast<const uint4*>(src + k * ld + xq * 8);
-        else
-          r[i][kr] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int u = threadIdx.x + i * NT, xq = u % XQ, kq = u / XQ;
-      const uint32_t a[4] = {r[i][0].x, r[i][0].y, r[i][0].z, r[i][0].w};
-      const uint32_t b[4] = {r[i][1].x, r[i][1].y, r[i][1].z, r[i][1].w};
-      const uint32_t c[4] = {r[i][2].x, r[i][2].y, r[i][2].z, r[i][2].w};
-      const uint32_t d[4] = {r[i][3].x, r[i][3].y, r[i][3].z, r[i][3].w};
-#pragma unroll
-      for (int xi = 0; xi < 8; ++xi) {
-        const int dw = xi >> 1;
-        uint32_t lo, hi;
-        if (xi & 1) {
-          lo = (a[dw] >> 16) | (b[dw] & 0xFFFF0000u);
-          hi = (c[dw] >> 16) | (d[dw] & 0xFFFF0000u);
-        } else {
-          lo = (a[dw] & 0xFFFFu) | (b[dw] << 16);
-          hi = (c[dw] & 0xFFFFu) | (d[dw] << 16);
-        }
-        const int x = xq * 8 + xi;
-        *reinterpret_cast<uint2*>(lds + lds_off(x, kq >> 1) + ((kq & 1) << 3)) = make_uint2(lo, hi);
-      }
-    }
-  }
-};
-
-template <int BM, int BN>
-struct Mfma {
-  static constexpr int FM = BM / 64, FN = BN / 64;  // 32x32 tiles per wave
-  f32x16 acc[FM][FN];
-  __device__ __forceinline__ void zero() {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  }
-  __device__ __forceinline__ void step(const char* As, const char* Bs) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int xa = (w >> 1) * (BM / 2) + (lane & 31);
-    const int xb = (w & 1) * (BN / 2) + (lane & 31);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int c = 2 * s + (lane >> 5);
-      bf16x8 a[FM], b[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(xa + 32 * i, c));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(xb + 32 * j, c));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  }
-  // Visit every accumulator element with its (row, col) inside the tile.
-  template <typename F>
-  __device__ __forceinline__ void for_each(F&& f) const {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int r0 = (w >> 1) * (BM / 2) + 4 * (lane >> 5);
-    const int c0 = (w & 1) * (BN / 2) + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          f(r0 + 32 * i + 8 * (r >> 2) + (r & 3), c0 + 32 * j, acc[i][j][r]);
-  }
-};
+__device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
 // Wave 0 scans the group sizes: row_base[g] (rows clipped to max_rows) and,
 // if tile_base != nullptr, tile_base[g] = tiles of groups < g, where a group
@@ -241,95 +122,406 @@ __device__ void zero_rows(TO* out, int64_t ld, int64_t N, int64_t r0, int64_t r1
     for (int64_t c = threadIdx.x; c < N; c += NT) out[r * ld + c] = TO(0);
 }
 
-template <int BM, int BN, bool TRANS, typename TO>
-__global__ __launch_bounds__(NT) void gmm_bf16_kernel(
-    const bf16_t* __restrict__ lhs, int64_t ld_lhs, const bf16_t* __restrict__ rhs, int64_t ld_rhs,
-    int64_t rhs_gs, const int32_t* __restrict__ gsz, int G, int64_t Kdim, int64_t N,
-    TO* __restrict__ out, int64_t M_out, int64_t ld_out, int accumulate, int32_t* err) {
-  __shared__ __attribute__((aligned(16))) char smem[2][(BM + BN) * BK * 2];
+// ---------------------------------------------------------------- bf16 MFMA
+//
+// Workgroup tile TM x TN (TN = 256, or 128 for narrow or single-step
+// problems), contraction step TK = 64, two LDS stages.  Waves are arranged
+// 2 x 2, each owning a (TM/2) x (TN/2) block of 32 x 32 accumulators.
+//
+// LDS layouts (per stage, per operand), 16-byte chunks XOR-swizzled:
+//   contraction-contiguous operand ("row" tile): [x][TK], 128-byte rows;
+//     chunk c of row x sits at c ^ (x & 7) ^ ((x >> 3) & 3), so any 8
+//     consecutive rows of one MFMA operand read (ds_read_b128) cover all
+//     banks, and the swizzle repeats every 32 rows (fragment i of a wave is
+//     fragment 0 plus a constant offset).
+//   contraction-major operand ("col" tile): [TK][BX], BX*2-byte rows;
+//     chunk c of row k sits at c ^ 4 (k & 3), so the four rows x four chunks
+//     that a transposing read (ds_read_b64_tr_b16) touches in one half-wave
+//     are distinct banks.
+// Full contraction steps are copied global -> LDS by global_load_lds_dwordx4
+// (16 bytes per lane; each wave instruction fills 1 KB of LDS in lane order,
+// so a lane fetches the global chunk that the swizzle places at its slot).
+// These are issued through inline asm so that the only waits on them are
+// the explicit ones at the top of each step.  Rows/columns past the valid
+// extent are clamped to a valid address (their products land in output rows
+// or columns that are never stored).  A ragged last contraction step is
+// loaded through registers with zero fill.
+//
+// MFMA operand fragment for 32 x (k16 substep s): lane l holds x = x0 + l%32,
+// k = 16 s + 8 (l / 32) + 0..7.  From a row tile that is one 16-byte read;
+// from a col tile, two transposing reads: within each 16-lane group, lane
+// 4 r + q addresses row k + r, columns 4 q .. 4 q + 3 of the group's 16
+// columns, and receives its own column for the four rows.
+
+constexpr int TM = 256, TK = 64;
+constexpr int kStages = 2;
+constexpr int kOpBytes = 256 * TK * 2;      // one operand tile, one stage (32 KB)
+
+__device__ __forceinline__ int row_swz(int x) { return (x & 7) ^ ((x >> 3) & 3); }
+__device__ __forceinline__ int row_off(int x, int c) { return x * (TK * 2) + ((c ^ row_swz(x)) << 4); }
+__device__ __forceinline__ int col_swz(int k) { return (k & 3) << 2; }
+template <int BX>
+__device__ __forceinline__ int col_off(int k, int c) { return k * (BX * 2) + ((c ^ col_swz(k)) << 4); }
+
+// threadIdx.x hidden from the optimiser: per-tile index arithmetic derived
+// from it is recomputed inside the persistent tile loop instead of being
+// hoisted out of it and kept live in registers across every tile.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// One global_load_lds_dwordx4: lane i's 16 bytes from sbase + voff land at
+// LDS byte lds + 16 i.  sbase and lds are wave-uniform.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// An operand tile of BX x TK.  COLK: element (x, k) at base[k * ld + x];
+// otherwise at base[x * ld + k].
+template <bool COLK, int BX>
+struct Operand {
+  static constexpr int kBytes = BX * TK * 2;
+  static constexpr int NJ = kBytes / 1024 / 4;   // DMA instructions per wave per stage
+  static constexpr int NR = kBytes / 16 / NT;    // 16-byte chunks per thread (register path)
+  const bf16_t* base;
+  int64_t ld;
+  int xv;                 // valid x extent (>= 1)
+  uint32_t voff[NJ];      // byte offsets of this lane's DMA chunks
+
+  __device__ __forceinline__ void setup(const bf16_t* b, int64_t ld_, int xv_) {
+    base = b;
+    ld = ld_;
+    xv = xv_;
+    const int tid = opaque_tid();
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int byte = (w * NJ + j) * 1024 + lane * 16;
+      if (!COLK) {
+        const int x = byte / (TK * 2);
+        const int c = ((byte % (TK * 2)) >> 4) ^ row_swz(x);
+        const int xx = x < xv ? x : xv - 1;
+        voff[j] = static_cast<uint32_t>((xx * ld + c * 8) * 2);
+      } else {
+        const int k = byte / (BX * 2);
+        int c = ((byte % (BX * 2)) >> 4) ^ col_swz(k);
+        const int cmax = (xv - 1) >> 3;
+        if (c > cmax) c = cmax;
+        voff[j] = static_cast<uint32_t>((k * ld + c * 8) * 2);
+      }
+    }
+  }
+  __device__ __forceinline__ const bf16_t* step_base(int kt) const {
+    return COLK ? base + static_cast<int64_t>(kt) * TK * ld : base + static_cast<int64_t>(kt) * TK;
+  }
+  __device__ __forceinline__ void dma(int kt, uint32_t lds) const {
+    const void* sb = uniform_ptr(step_base(kt));
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dma16(sb, voff[j], lds + (w * NJ + j) * 1024);
+  }
+  // Register path for a partial step of kv < TK contraction elements.
+  __device__ __forceinline__ void tail_load(int kt, int kv, uint4 (&r)[NR]) const {
+    const bf16_t* b = step_base(kt);
+    const int tid = opaque_tid();
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int q = tid + i * NT;
+      bool ok;
+      const bf16_t* p;
+      if (!COLK) {
+        const int x = q >> 3, c = q & 7;
+        ok = x < xv && c * 8 < kv;
+        p = b + x * ld + c * 8;
+      } else {
+        const int k = q / (BX / 8), c = q % (BX / 8);
+        ok = k < kv && c * 8 < xv;
+        p = b + k * ld + c * 8;
+      }
+      r[i] = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void tail_store(char* lds, const uint4 (&r)[NR]) const {
+    const int tid = opaque_tid();
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int q = tid + i * NT;
+      int off;
+      if (!COLK) off = row_off(q >> 3, q & 7);
+      else off = col_off<BX>(q / (BX / 8), q % (BX / 8));
+      *reinterpret_cast<uint4*>(lds + off) = r[i];
+    }
+  }
+  // Per-lane byte offsets of this wave's MFMA fragments inside a stage tile.
+  // Fragment (i, s) covers x = xw + 32 i + lane % 32 and
+  // k = 16 s + 8 (lane / 32) + 0..7, where xw is the wave's first x.
+  //   row tile: at fb[s] + i * 32 * 128 (one 16-byte read)
+  //   col tile: at fb[i] + s * 16 * ROWB and + 4 * ROWB (two transposing
+  //             reads; within each 16-lane group lane 4 r + q addresses row
+  //             r, columns 4 q .. 4 q + 3, and receives its own column)
+  static constexpr int ROWB = BX * 2;
+  __device__ __forceinline__ static void frag_base(int xw, uint32_t (&fb)[4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (!COLK) {
+        fb[t] = static_cast<uint32_t>(row_off(xw + (lane & 31), 2 * t + (lane >> 5)));
+      } else {
+        const int g = lane >> 4, j = lane & 15;
+        const int k = 8 * (g >> 1) + (j >> 2);
+        const int xc = xw + 32 * t + 16 * (g & 1) + 4 * (j & 3);
+        fb[t] = static_cast<uint32_t>(col_off<BX>(k, xc >> 3) + ((xc & 7) << 1));
+      }
+    }
+  }
+  __device__ __forceinline__ static bf16x8 frag(const char* lds, const uint32_t (&fb)[4], int i, int s) {
+    if (!COLK) {
+      return *reinterpret_cast<const bf16x8*>(lds + fb[s] + i * 32 * (TK * 2));
+    } else {
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const char* p = lds + fb[i] + s * 16 * ROWB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * ROWB));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, v);
+    }
+  }
+};
+
+template <int TN>
+struct Acc {
+  static constexpr int FM = TM / 64, FN = TN / 64;
+  f32x16 v[FM][FN];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[i][j][r] = 0.f;
+  }
+  template <class OA, class OB>
+  __device__ __forceinline__ void step(const char* As, const char* Bs, const uint32_t (&fa)[4],
+                                       const uint32_t (&fbb)[4]) {
+#pragma unroll
+    for (int s = 0; s < TK / 16; ++s) {
+      bf16x8 a[FM], b[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a[i] = OA::frag(As, fa, i, s);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b[j] = OB::frag(Bs, fbb, j, s);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], v[i][j], 0, 0, 0);
+    }
+  }
+  // f(row, col, value) for every accumulator element (row/col inside the tile)
+  template <typename F>
+  __device__ __forceinline__ void for_each(F&& f) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r0 = (w >> 1) * (TM / 2) + 4 * (lane >> 5);
+    const int c0 = (w & 1) * (TN / 2) + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          f(r0 + 32 * i + 8 * (r >> 2) + (r & 3), c0 + 32 * j, v[i][j][r]);
+  }
+};
+
+struct MfmaArgs {
+  const bf16_t* lhs;
+  int64_t ld_lhs;
+  const bf16_t* rhs;
+  int64_t ld_rhs;
+  int64_t rhs_gs;        // gmm: rhs group stride
+  const int32_t* gsz;
+  int G;
+  int64_t M;             // gmm: output rows; tgmm: lhs/rhs rows
+  int64_t Kdim;
+  int64_t N;
+  void* out;
+  int64_t ld_out;
+  int64_t out_gs;        // tgmm: output group stride
+  int accumulate;
+  int32_t* err;
+};
+
+// Contraction over one tile: nfull DMA steps then an optional ragged step.
+template <class OA, class OB, int TN>
+__device__ __forceinline__ void contract(char (*smem)[2][kOpBytes], const OA& A, const OB& B,
+                                         int64_t Kc, Acc<TN>& acc, const uint32_t (&fa)[4],
+                                         const uint32_t (&fb)[4]) {
+  const int nfull = static_cast<int>(Kc / TK);
+  const int kv = static_cast<int>(Kc - static_cast<int64_t>(nfull) * TK);
+  acc.zero();
+  if (nfull > 0) {
+    A.dma(0, lds_addr(smem[0][0]));
+    B.dma(0, lds_addr(smem[0][1]));
+  }
+  for (int s = 0; s < nfull; ++s) {
+    __builtin_amdgcn_s_waitcnt(0);      // this stage's DMA has landed (only it is in flight)
+    __syncthreads();                    // ... for every wave; the other stage is free
+    if (s + 1 < nfull) {
+      A.dma(s + 1, lds_addr(smem[(s + 1) & 1][0]));
+      B.dma(s + 1, lds_addr(smem[(s + 1) & 1][1]));
+    }
+    acc.template step<OA, OB>(smem[s & 1][0], smem[s & 1][1], fa, fb);
+  }
+  if (kv > 0) {
+    // stage nfull & 1 was last read in step nfull - 2 (or by the previous
+    // tile), and every wave has passed a barrier since
+    {
+      uint4 t[OA::NR];
+      A.tail_load(nfull, kv, t);
+      A.tail_store(smem[nfull & 1][0], t);
+    }
+    {
+      uint4 t[OB::NR];
+      B.tail_load(nfull, kv, t);
+      B.tail_store(smem[nfull & 1][1], t);
+    }
+    __syncthreads();
+    acc.template step<OA, OB>(smem[nfull & 1][0], smem[nfull & 1][1], fa, fb);
+  }
+  __syncthreads();   // every wave is done with both stages before they are refilled
+}
+
+// Write the accumulator tile: for each of its FM 32-row slabs a wave stages
+// the slab (32 x TN/2 float32) in its own LDS region, then reads it back as
+// 8-column row chunks and stores them with 16-byte (bf16) or 32-byte (fp32)
+// accesses; rows >= rv and columns >= cv are skipped.  The LDS is the
+// operand stages, free once the contraction has ended with a barrier.
+template <int TN, typename TO>
+__device__ __forceinline__ void store_tile(const Acc<TN>& acc, char* lds, TO* o, int64_t ldo,
+                                           int rv, int cv, int accumulate) {
+  constexpr int WC = TN / 2;
+  constexpr int SROW = WC * 4 + 16;
+  constexpr int CPR = WC / 8;                 // 8-column chunks per slab row
+  const int tid = opaque_tid();
+  const int lane = tid & 63, w = tid >> 6;
+  char* slab = lds + w * 32 * SROW;
+  const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * WC;
+#pragma unroll
+  for (int i = 0; i < Acc<TN>::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < Acc<TN>::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = 32 * j + (lane & 31);
+        *reinterpret_cast<float*>(slab + row * SROW + col * 4) = acc.v[i][j][r];
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q = 0; q < 32 * CPR / 64; ++q) {
+      const int chunk = lane + 64 * q;
+      const int row = chunk / CPR, c8 = chunk % CPR;
+      const int grow = wr + 32 * i + row, gcol = wc + 8 * c8;
+      const float4 lo = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32);
+      const float4 hi = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (grow < rv && gcol < cv) {
+        TO* p = o + static_cast<int64_t>(grow) * ldo + gcol;
+        if (accumulate) {
+          float old[8];
+          load8(p, old);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += old[e];
+        }
+        store8(p, v);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  __syncthreads();   // the stages are refilled by the next tile
+}
+
+template <bool B_COLK, int TN, typename TO>
+__global__ __launch_bounds__(NT, 1) void gmm_mfma_kernel(MfmaArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kStages][2][kOpBytes];
   __shared__ int row_base[kMaxG + 1];
   __shared__ int tile_base[kMaxG + 1];
-  const int ntn = static_cast<int>((N + BN - 1) / BN);
-  scan_groups(gsz, G, M_out, BM, ntn, row_base, tile_base, blockIdx.x == 0 ? err : nullptr);
+  const int ntn = static_cast<int>((a.N + TN - 1) / TN);
+  scan_groups(a.gsz, a.G, a.M, TM, ntn, row_base, tile_base, blockIdx.x == 0 ? a.err : nullptr);
   __syncthreads();
-  const int total = tile_base[G];
-  const int nk = static_cast<int>((Kdim + BK - 1) / BK);
-
-  RowK<BM> la;
-  typename std::conditional<TRANS, RowK<BN>, ColK<BN>>::type lb;
-  Mfma<BM, BN> mm;
-
+  const int total = tile_base[a.G];
+  TO* out = static_cast<TO*>(a.out);
+  Operand<false, TM> A;
+  Operand<B_COLK, TN> B;
+  Acc<TN> acc;
+  uint32_t fa[4], fb[4];
+  Operand<false, TM>::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
+  Operand<B_COLK, TN>::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
   for (int it = 0;; ++it) {
     const int64_t tile = xcd_tile(it);
     if (tile >= total) break;
-    int lo = 0, hi = G - 1;  // largest g with tile_base[g] <= tile
+    int lo = 0, hi = a.G - 1;   // largest g with tile_base[g] <= tile
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (tile_base[mid] <= tile) lo = mid; else hi = mid - 1;
     }
     const int g = lo;
     const int rows_g = row_base[g + 1] - row_base[g];
-    const int mtiles = (rows_g + BM - 1) / BM;
+    const int mtiles = (rows_g + TM - 1) / TM;
     const int local = static_cast<int>(tile - tile_base[g]);
     const int nt = local / mtiles, mt = local % mtiles;
-    const int64_t row0 = row_base[g] + static_cast<int64_t>(mt) * BM;
-    const int rv = min(BM, rows_g - mt * BM);
-    const int64_t col0 = static_cast<int64_t>(nt) * BN;
-    const int cv = static_cast<int>(lmin(BN, N - col0));
-
-    const bf16_t* a_src = lhs + row0 * ld_lhs;
-    const bf16_t* b_src = TRANS ? rhs + g * rhs_gs + col0 * ld_rhs : rhs + g * rhs_gs + col0;
-    auto load_step = [&](int kt) {
-      const int64_t k0 = static_cast<int64_t>(kt) * BK;
-      const int kv = static_cast<int>(lmin(BK, Kdim - k0));
-      la.load(a_src + k0, ld_lhs, rv, kv);
-      if (TRANS) lb.load(b_src + k0, ld_rhs, cv, kv);
-      else lb.load(b_src + k0 * ld_rhs, ld_rhs, cv, kv);
-    };
-    mm.zero();
-    if (nk > 0) {
-      load_step(0);
-      la.store(smem[0]);
-      lb.store(smem[0] + BM * BK * 2);
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) load_step(kt + 1);
-        const char* buf = smem[kt & 1];
-        mm.step(buf, buf + BM * BK * 2);
-        if (kt + 1 < nk) {
-          char* nb = smem[(kt + 1) & 1];
-          la.store(nb);
-          lb.store(nb + BM * BK * 2);
-        }
-        __syncthreads();
-      }
-    }
-    TO* o = out + row0 * ld_out + col0;
-    mm.for_each([&](int r, int c, float v) {
-      if (r < rv && c < cv) store_out(o + static_cast<int64_t>(r) * ld_out + c, v, accumulate);
-    });
+    const int64_t row0 = row_base[g] + static_cast<int64_t>(mt) * TM;
+    const int rv = min(TM, rows_g - mt * TM);
+    const int64_t col0 = static_cast<int64_t>(nt) * TN;
+    const int cv = static_cast<int>(lmin(TN, a.N - col0));
+    A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, rv);
+    const bf16_t* bg = a.rhs + g * a.rhs_gs;
+    B.setup(B_COLK ? bg + col0 : bg + col0 * a.ld_rhs, a.ld_rhs, cv);
+    contract(smem, A, B, a.Kdim, acc, fa, fb);
+    store_tile(acc, &smem[0][0][0], out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate);
   }
-  if (!accumulate) zero_rows(out, ld_out, N, row_base[G], M_out);
+  if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
 }
 
-template <int BM, int BN, typename TO>
-__global__ __launch_bounds__(NT) void tgmm_bf16_kernel(
-    const bf16_t* __restrict__ lhs, int64_t ld_lhs, const bf16_t* __restrict__ rhs, int64_t ld_rhs,
-    const int32_t* __restrict__ gsz, int G, int64_t M, int64_t Kdim, int64_t N,
-    TO* __restrict__ out, int64_t ld_out, int64_t out_gs, int accumulate, int32_t* err) {
-  __shared__ __attribute__((aligned(16))) char smem[2][(BM + BN) * BK * 2];
+template <typename TO>
+__global__ __launch_bounds__(NT, 1) void tgmm_mfma_kernel(MfmaArgs a) {
+  constexpr int TN = 256;
+  __shared__ __attribute__((aligned(1024))) char smem[kStages][2][kOpBytes];
   __shared__ int row_base[kMaxG + 1];
-  scan_groups(gsz, G, M, BM, 1, row_base, nullptr, blockIdx.x == 0 ? err : nullptr);
+  scan_groups(a.gsz, a.G, a.M, TM, 1, row_base, nullptr, blockIdx.x == 0 ? a.err : nullptr);
   __syncthreads();
-  const int mtn = static_cast<int>((Kdim + BM - 1) / BM);
-  const int ntn = static_cast<int>((N + BN - 1) / BN);
+  const int mtn = static_cast<int>((a.Kdim + TM - 1) / TM);
+  const int ntn = static_cast<int>((a.N + TN - 1) / TN);
   const int64_t per_group = static_cast<int64_t>(mtn) * ntn;
-  const int64_t total = per_group * G;
-
-  ColK<BM> la;
-  ColK<BN> lb;
-  Mfma<BM, BN> mm;
-
+  const int64_t total = per_group * a.G;
+  TO* out = static_cast<TO*>(a.out);
+  Operand<true, TM> A;
+  Operand<true, TN> B;
+  Acc<TN> acc;
+  uint32_t fa[4], fb[4];
+  Operand<true, TM>::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
+  Operand<true, TN>::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
   for (int it = 0;; ++it) {
     const int64_t tile = xcd_tile(it);
     if (tile >= total) break;
@@ -338,42 +530,15 @@ __global__ __launch_bounds__(NT) void tgmm_bf16_kernel(
     const int nt = local / mtn, mt = local % mtn;
     const int64_t r0 = row_base[g];
     const int rows_g = row_base[g + 1] - row_base[g];
-    const int64_t m0 = static_cast<int64_t>(mt) * BM;
-    const int64_t n0 = static_cast<int64_t>(nt) * BN;
-    const int mv = static_cast<int>(lmin(BM, Kdim - m0));
-    const int nv = static_cast<int>(lmin(BN, N - n0));
-    TO* o = out + g * out_gs + m0 * ld_out + n0;
-    if (rows_g == 0 && accumulate) continue;   // partial sum unchanged
-    const int nk = (rows_g + BK - 1) / BK;
-    const bf16_t* a_src = lhs + r0 * ld_lhs + m0;
-    const bf16_t* b_src = rhs + r0 * ld_rhs + n0;
-    auto load_step = [&](int kt) {
-      const int k0 = kt * BK;
-      const int kv = min(BK, rows_g - k0);
-      la.load(a_src + static_cast<int64_t>(k0) * ld_lhs, ld_lhs, mv, kv);
-      lb.load(b_src + static_cast<int64_t>(k0) * ld_rhs, ld_rhs, nv, kv);
-    };
-    mm.zero();
-    if (nk > 0) {
-      load_step(0);
-      la.store(smem[0]);
-      lb.store(smem[0] + BM * BK * 2);
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) load_step(kt + 1);
-        const char* buf = smem[kt & 1];
-        mm.step(buf, buf + BM * BK * 2);
-        if (kt + 1 < nk) {
-          char* nb = smem[(kt + 1) & 1];
-          la.store(nb);
-          lb.store(nb + BM * BK * 2);
-        }
-        __syncthreads();
-      }
-    }
-    mm.for_each([&](int r, int c, float v) {
-      if (r < mv && c < nv) store_out(o + static_cast<int64_t>(r) * ld_out + c, v, accumulate);
-    });
+    if (rows_g == 0 && a.accumulate) continue;   // partial sum unchanged
+    const int64_t m0 = static_cast<int64_t>(mt) * TM, n0 = static_cast<int64_t>(nt) * TN;
+    const int mv = static_cast<int>(lmin(TM, a.Kdim - m0));
+    const int nv = static_cast<int>(lmin(TN, a.N - n0));
+    A.setup(a.lhs + r0 * a.ld_lhs + m0, a.ld_lhs, mv);
+    B.setup(a.rhs + r0 * a.ld_rhs + n0, a.ld_rhs, nv);
+    contract(smem, A, B, rows_g, acc, fa, fb);
+    store_tile(acc, &smem[0][0][0], out + g * a.out_gs + m0 * a.ld_out + n0, a.ld_out, mv, nv,
+               a.accumulate);
   }
 }
 
@@ -512,8 +677,6 @@ __global__ __launch_bounds__(NT) void tgmm_f32_kernel(
   }
 }
 
-constexpr int kBM = 128, kBN = 128;
-
 unsigned persistent_grid(int64_t upper_tiles, int per_cu) {
   int64_t g = static_cast<int64_t>(device_cu_count()) * per_cu;
   if (upper_tiles < g) g = upper_tiles;
@@ -522,6 +685,8 @@ unsigned persistent_grid(int64_t upper_tiles, int per_cu) {
 }
 
 bool mult8(int64_t v) { return v >= 0 && (v & 7) == 0; }
+
+constexpr int64_t kMaxLd = int64_t(1) << 22;   // keeps per-lane DMA byte offsets in 32 bits
 
 }  // namespace
 }  // namespace moe
@@ -542,34 +707,32 @@ MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* 
       !mult8(rhs_group_stride))
     return MOE_ERR_ARG;
   if (ld_lhs < Kdim || ld_out < N || ld_rhs < (trans_rhs ? Kdim : N)) return MOE_ERR_ARG;
+  if (ld_lhs > kMaxLd || ld_rhs > kMaxLd) return MOE_ERR_ARG;
   if (M_out == 0 || N == 0) return MOE_OK;
   if (!lhs || !rhs || !group_sizes || !out || !aligned16(lhs) || !aligned16(rhs) || !aligned16(out))
     return MOE_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == MOE_BF16) {
-    const bf16_t* A = static_cast<const bf16_t*>(lhs);
-    const bf16_t* B = static_cast<const bf16_t*>(rhs);
-#define GMM(BMV, TR, TO)                                                                        \
-  hipLaunchKernelGGL((gmm_bf16_kernel<BMV, kBN, TR, TO>), dim3(grid), dim3(NT), 0, st, A, ld_lhs, \
-                     B, ld_rhs, rhs_group_stride, group_sizes, G, Kdim, N, static_cast<TO*>(out), \
-                     M_out, ld_out, accumulate, err)
-    if (Kdim <= BK) {
-      // one contraction step: a taller row tile amortises the rhs tile
-      constexpr int kTall = 256;
-      const int64_t upper = ((M_out + kTall - 1) / kTall + G) * ((N + kBN - 1) / kBN);
-      const unsigned grid = persistent_grid(upper, 1);
+    MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
+               rhs_group_stride, group_sizes, G, M_out, Kdim, N, out, ld_out, 0, accumulate, err};
+    // narrow outputs and single-step contractions use a 256 x 128 tile
+    const bool narrow = N <= 128 || Kdim <= TK;
+    const int TNv = narrow ? 128 : 256;
+    const int64_t upper = ((M_out + TM - 1) / TM + G) * ((N + TNv - 1) / TNv);
+    const unsigned grid = persistent_grid(upper, 1);
+#define GMM(BC, TNV, TO) \
+  hipLaunchKernelGGL((gmm_mfma_kernel<BC, TNV, TO>), dim3(grid), dim3(NT), 0, st, a)
+    if (narrow) {
       if (trans_rhs) {
-        if (out_dtype == MOE_BF16) GMM(kTall, true, bf16_t); else GMM(kTall, true, float);
+        if (out_dtype == MOE_BF16) GMM(false, 128, bf16_t); else GMM(false, 128, float);
       } else {
-        if (out_dtype == MOE_BF16) GMM(kTall, false, bf16_t); else GMM(kTall, false, float);
+        if (out_dtype == MOE_BF16) GMM(true, 128, bf16_t); else GMM(true, 128, float);
       }
     } else {
-      const int64_t upper = ((M_out + kBM - 1) / kBM + G) * ((N + kBN - 1) / kBN);
-      const unsigned grid = persistent_grid(upper, 2);
       if (trans_rhs) {
-        if (out_dtype == MOE_BF16) GMM(kBM, true, bf16_t); else GMM(kBM, true, float);
+        if (out_dtype == MOE_BF16) GMM(false, 256, bf16_t); else GMM(false, 256, float);
       } else {
-        if (out_dtype == MOE_BF16) GMM(kBM, false, bf16_t); else GMM(kBM, false, float);
+        if (out_dtype == MOE_BF16) GMM(true, 256, bf16_t); else GMM(true, 256, float);
       }
     }
 #undef GMM
@@ -605,23 +768,20 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
     return MOE_ERR_ARG;
   if (ld_lhs < Kdim || ld_rhs < N || ld_out < N || out_group_stride < Kdim * ld_out)
     return MOE_ERR_ARG;
+  if (ld_lhs > kMaxLd || ld_rhs > kMaxLd) return MOE_ERR_ARG;
   if (Kdim == 0 || N == 0) return MOE_OK;
   if (!lhs || !rhs || !group_sizes || !out || !aligned16(lhs) || !aligned16(rhs) || !aligned16(out))
     return MOE_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == MOE_BF16) {
-    const int64_t upper = static_cast<int64_t>(G) * ((Kdim + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    const unsigned grid = persistent_grid(upper, 2);
-    const bf16_t* A = static_cast<const bf16_t*>(lhs);
-    const bf16_t* B = static_cast<const bf16_t*>(rhs);
+    MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
+               0, group_sizes, G, M, Kdim, N, out, ld_out, out_group_stride, accumulate, err};
+    const int64_t upper = static_cast<int64_t>(G) * ((Kdim + TM - 1) / TM) * ((N + 255) / 256);
+    const unsigned grid = persistent_grid(upper, 1);
     if (out_dtype == MOE_BF16)
-      hipLaunchKernelGGL((tgmm_bf16_kernel<kBM, kBN, bf16_t>), dim3(grid), dim3(NT), 0, st, A,
-                         ld_lhs, B, ld_rhs, group_sizes, G, M, Kdim, N, static_cast<bf16_t*>(out),
-                         ld_out, out_group_stride, accumulate, err);
+      hipLaunchKernelGGL(tgmm_mfma_kernel<bf16_t>, dim3(grid), dim3(NT), 0, st, a);
     else
-      hipLaunchKernelGGL((tgmm_bf16_kernel<kBM, kBN, float>), dim3(grid), dim3(NT), 0, st, A,
-                         ld_lhs, B, ld_rhs, group_sizes, G, M, Kdim, N, static_cast<float*>(out),
-                         ld_out, out_group_stride, accumulate, err);
+      hipLaunchKernelGGL(tgmm_mfma_kernel<float>, dim3(grid), dim3(NT), 0, st, a);
   } else {
     const int64_t upper = static_cast<int64_t>(G) * ((Kdim + FB - 1) / FB) * ((N + FB - 1) / FB);
     const unsigned grid = persistent_grid(upper, 4);
