@@ -102,6 +102,19 @@ __device__ void scan_groups(const int32_t* __restrict__ gsz, int G, int64_t max_
   if (bad && lane == 0 && err) atomicOr(err, MOE_DERR_GROUP_SIZES);
 }
 
+// Position of a group's local tile l among mt x nt tiles: column blocks of
+// kNB tiles, row-major inside a block (consecutive indices cover about
+// 32 / kNB row tiles x kNB column tiles, so the tiles that run together on
+// one XCD share both operand blocks in its L2).
+constexpr int kNB = 4;
+__device__ __forceinline__ void blocked_tile(int l, int mtiles, int ntiles, int& mt, int& nt) {
+  const int per = mtiles * kNB;
+  const int nb = l / per, rem = l - nb * per;
+  const int width = min(kNB, ntiles - nb * kNB);
+  mt = rem / width;
+  nt = nb * kNB + rem % width;
+}
+
 // Linear tile index of a persistent workgroup's it-th tile: the grid's
 // workgroups on XCD x (b % 8 == x) take a contiguous run of indices.
 __device__ __forceinline__ int64_t xcd_tile(int it) {
@@ -125,15 +138,16 @@ __device__ void zero_rows(TO* out, int64_t ld, int64_t N, int64_t r0, int64_t r1
 // ---------------------------------------------------------------- bf16 MFMA
 //
 // Workgroup tile TM x TN (TN = 256, or 128 for narrow or single-step
-// problems), contraction step TK = 64, two LDS stages.  Waves are arranged
+// problems), contraction step TK = 32, a ring of four LDS stages (up to
+// four steps of loads in flight).  Waves are arranged
 // 2 x 2, each owning a (TM/2) x (TN/2) block of 32 x 32 accumulators.
 //
 // LDS layouts (per stage, per operand), 16-byte chunks XOR-swizzled:
-//   contraction-contiguous operand ("row" tile): [x][TK], 128-byte rows;
-//     chunk c of row x sits at c ^ (x & 7) ^ ((x >> 3) & 3), so any 8
-//     consecutive rows of one MFMA operand read (ds_read_b128) cover all
-//     banks, and the swizzle repeats every 32 rows (fragment i of a wave is
-//     fragment 0 plus a constant offset).
+//   contraction-contiguous operand ("row" tile): [x][TK], 64-byte rows;
+//     chunk c of row x sits at c ^ ((x >> 1) & 3), so any 8 consecutive
+//     rows of one MFMA operand read (ds_read_b128) hit distinct banks, and
+//     the swizzle repeats every 8 rows (fragment i of a wave is fragment 0
+//     plus a constant offset).
 //   contraction-major operand ("col" tile): [TK][BX], BX*2-byte rows;
 //     chunk c of row k sits at c ^ 4 (k & 3), so the four rows x four chunks
 //     that a transposing read (ds_read_b64_tr_b16) touches in one half-wave
@@ -153,12 +167,20 @@ __device__ void zero_rows(TO* out, int64_t ld, int64_t N, int64_t r0, int64_t r1
 // 4 r + q addresses row k + r, columns 4 q .. 4 q + 3 of the group's 16
 // columns, and receives its own column for the four rows.
 
-constexpr int TM = 256, TK = 64;
-constexpr int kStages = 2;
-constexpr int kOpBytes = 256 * TK * 2;      // one operand tile, one stage (32 KB)
+constexpr int TM = 256, TK = 32;
+constexpr int kStages = 4;
+constexpr int kOpBytes = 256 * TK * 2;      // one operand tile, one stage (16 KB)
+constexpr int kCPR = TK / 8;                // 16-byte chunks per row of a row tile
 
-__device__ __forceinline__ int row_swz(int x) { return (x & 7) ^ ((x >> 3) & 3); }
+__device__ __forceinline__ int row_swz(int x) { return (x >> 1) & 3; }
 __device__ __forceinline__ int row_off(int x, int c) { return x * (TK * 2) + ((c ^ row_swz(x)) << 4); }
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 __device__ __forceinline__ int col_swz(int k) { return (k & 3) << 2; }
 template <int BX>
 __device__ __forceinline__ int col_off(int k, int c) { return k * (BX * 2) + ((c ^ col_swz(k)) << 4); }
@@ -246,7 +268,7 @@ struct Operand {
       bool ok;
       const bf16_t* p;
       if (!COLK) {
-        const int x = q >> 3, c = q & 7;
+        const int x = q / kCPR, c = q % kCPR;
         ok = x < xv && c * 8 < kv;
         p = b + x * ld + c * 8;
       } else {
@@ -263,7 +285,7 @@ struct Operand {
     for (int i = 0; i < NR; ++i) {
       const int q = tid + i * NT;
       int off;
-      if (!COLK) off = row_off(q >> 3, q & 7);
+      if (!COLK) off = row_off(q / kCPR, q % kCPR);
       else off = col_off<BX>(q / (BX / 8), q % (BX / 8));
       *reinterpret_cast<uint4*>(lds + off) = r[i];
     }
@@ -281,7 +303,7 @@ struct Operand {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if (!COLK) {
-        fb[t] = static_cast<uint32_t>(row_off(xw + (lane & 31), 2 * t + (lane >> 5)));
+        fb[t] = t < TK / 16 ? static_cast<uint32_t>(row_off(xw + (lane & 31), 2 * t + (lane >> 5))) : 0u;
       } else {
         const int g = lane >> 4, j = lane & 15;
         const int k = 8 * (g >> 1) + (j >> 2);
@@ -317,22 +339,25 @@ struct Acc {
 #pragma unroll
         for (int r = 0; r < 16; ++r) v[i][j][r] = 0.f;
   }
+  // Fragments of one k16 substep.
+  struct Frags {
+    bf16x8 a[FM], b[FN];
+  };
   template <class OA, class OB>
-  __device__ __forceinline__ void step(const char* As, const char* Bs, const uint32_t (&fa)[4],
-                                       const uint32_t (&fbb)[4]) {
+  __device__ __forceinline__ static void load(Frags& f, const char* As, const char* Bs,
+                                              const uint32_t (&fa)[4], const uint32_t (&fb)[4],
+                                              int sub) {
 #pragma unroll
-    for (int s = 0; s < TK / 16; ++s) {
-      bf16x8 a[FM], b[FN];
+    for (int i = 0; i < FM; ++i) f.a[i] = OA::frag(As, fa, i, sub);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = OA::frag(As, fa, i, s);
+    for (int j = 0; j < FN; ++j) f.b[j] = OB::frag(Bs, fb, j, sub);
+  }
+  __device__ __forceinline__ void mma(const Frags& f) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = OB::frag(Bs, fbb, j, s);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], v[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < FN; ++j)
+        v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], v[i][j], 0, 0, 0);
   }
   // f(row, col, value) for every accumulator element (row/col inside the tile)
   template <typename F>
@@ -368,44 +393,84 @@ struct MfmaArgs {
   int32_t* err;
 };
 
-// Contraction over one tile: nfull DMA steps then an optional ragged step.
+// Contraction over one tile: nfull DMA steps, then an optional ragged step.
+//
+// Software pipeline (TK = 32: two k16 substeps per stage):
+//   prologue: DMA stages 0..3; wait for stage 0; barrier; load frags(0, 0)
+//   step s:   load frags(s, 1); MFMAs(s, 0);
+//             wait for stage s + 1; barrier (also: all waves hold their
+//             frags of stage s, so its buffer is free); DMA stage s + 4
+//             into it; load frags(s + 1, 0);
+//             MFMAs(s, 1)
+// so MFMAs are queued whenever a wave waits at the barrier or on LDS.
 template <class OA, class OB, int TN>
 __device__ __forceinline__ void contract(char (*smem)[2][kOpBytes], const OA& A, const OB& B,
                                          int64_t Kc, Acc<TN>& acc, const uint32_t (&fa)[4],
                                          const uint32_t (&fb)[4]) {
+  static_assert(kStages == 4 && TK == 32, "pipeline written for 4 stages of two substeps");
   const int nfull = static_cast<int>(Kc / TK);
   const int kv = static_cast<int>(Kc - static_cast<int64_t>(nfull) * TK);
+  constexpr int PER = OA::NJ + OB::NJ;      // DMA instructions per thread per stage
+  typename Acc<TN>::Frags f0, f1;
   acc.zero();
+  __builtin_amdgcn_s_waitcnt(0);            // nothing from the previous tile is in flight
+#pragma unroll
+  for (int p = 0; p < kStages; ++p)
+    if (p < nfull) {
+      A.dma(p, lds_addr(smem[p][0]));
+      B.dma(p, lds_addr(smem[p][1]));
+    }
   if (nfull > 0) {
-    A.dma(0, lds_addr(smem[0][0]));
-    B.dma(0, lds_addr(smem[0][1]));
+    // stage 0 has landed once at most the later prologue stages are in flight
+    const int later = min(kStages - 1, nfull - 1);
+    if (later >= 3) wait_vmcnt<3 * PER>();
+    else if (later == 2) wait_vmcnt<2 * PER>();
+    else if (later == 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    Acc<TN>::template load<OA, OB>(f0, smem[0][0], smem[0][1], fa, fb, 0);
   }
   for (int s = 0; s < nfull; ++s) {
-    __builtin_amdgcn_s_waitcnt(0);      // this stage's DMA has landed (only it is in flight)
-    __syncthreads();                    // ... for every wave; the other stage is free
+    const int cur = s % kStages;
+    Acc<TN>::template load<OA, OB>(f1, smem[cur][0], smem[cur][1], fa, fb, 1);
+    acc.mma(f0);
     if (s + 1 < nfull) {
-      A.dma(s + 1, lds_addr(smem[(s + 1) & 1][0]));
-      B.dma(s + 1, lds_addr(smem[(s + 1) & 1][1]));
+      // stages s + 2 and s + 3 may still be in flight; s + 1 must have landed
+      const int later = min(2, nfull - 2 - s);
+      if (later >= 2) wait_vmcnt<2 * PER>();
+      else if (later == 1) wait_vmcnt<PER>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (s + kStages < nfull) {
+        A.dma(s + kStages, lds_addr(smem[cur][0]));
+        B.dma(s + kStages, lds_addr(smem[cur][1]));
+      }
+      const int nxt = (s + 1) % kStages;
+      Acc<TN>::template load<OA, OB>(f0, smem[nxt][0], smem[nxt][1], fa, fb, 0);
     }
-    acc.template step<OA, OB>(smem[s & 1][0], smem[s & 1][1], fa, fb);
+    acc.mma(f1);
   }
   if (kv > 0) {
-    // stage nfull & 1 was last read in step nfull - 2 (or by the previous
-    // tile), and every wave has passed a barrier since
+    // stage nfull % kStages was last read four steps ago (or by the previous
+    // tile) and no DMA targets it; other waves may still read stage nfull - 1
+    const int ts = nfull % kStages;
     {
       uint4 t[OA::NR];
       A.tail_load(nfull, kv, t);
-      A.tail_store(smem[nfull & 1][0], t);
+      A.tail_store(smem[ts][0], t);
     }
     {
       uint4 t[OB::NR];
       B.tail_load(nfull, kv, t);
-      B.tail_store(smem[nfull & 1][1], t);
+      B.tail_store(smem[ts][1], t);
     }
     __syncthreads();
-    acc.template step<OA, OB>(smem[nfull & 1][0], smem[nfull & 1][1], fa, fb);
+    Acc<TN>::template load<OA, OB>(f0, smem[ts][0], smem[ts][1], fa, fb, 0);
+    Acc<TN>::template load<OA, OB>(f1, smem[ts][0], smem[ts][1], fa, fb, 1);
+    acc.mma(f0);
+    acc.mma(f1);
   }
-  __syncthreads();   // every wave is done with both stages before they are refilled
+  __syncthreads();   // every wave is done with all stages before they are refilled
 }
 
 // Write the accumulator tile: for each of its FM 32-row slabs a wave stages
@@ -490,7 +555,8 @@ __global__ __launch_bounds__(NT, 1) void gmm_mfma_kernel(MfmaArgs a) {
     const int rows_g = row_base[g + 1] - row_base[g];
     const int mtiles = (rows_g + TM - 1) / TM;
     const int local = static_cast<int>(tile - tile_base[g]);
-    const int nt = local / mtiles, mt = local % mtiles;
+    int mt, nt;
+    blocked_tile(local, mtiles, ntn, mt, nt);
     const int64_t row0 = row_base[g] + static_cast<int64_t>(mt) * TM;
     const int rv = min(TM, rows_g - mt * TM);
     const int64_t col0 = static_cast<int64_t>(nt) * TN;
@@ -527,7 +593,8 @@ __global__ __launch_bounds__(NT, 1) void tgmm_mfma_kernel(MfmaArgs a) {
     if (tile >= total) break;
     const int g = static_cast<int>(tile / per_group);
     const int local = static_cast<int>(tile - g * per_group);
-    const int nt = local / mtn, mt = local % mtn;
+    int mt, nt;
+    blocked_tile(local, mtn, ntn, mt, nt);
     const int64_t r0 = row_base[g];
     const int rows_g = row_base[g + 1] - row_base[g];
     if (rows_g == 0 && a.accumulate) continue;   // partial sum unchanged
