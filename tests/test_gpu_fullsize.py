@@ -1,0 +1,195 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times (the same MoEPlan call sequence).
+
+The oracle cannot run the whole block at these sizes, so:
+  * routing and the permutation index maps are checked for every token
+    against the oracle (bit-exact ids, counts, group sizes, row maps);
+  * every intermediate and gradient of a few sampled experts (the largest
+    group, a small one, a middle one) is checked element by element
+    against the oracle run on just that group;
+  * the remaining outputs are checked through properties that hold at any
+    size (the combine is the weighted sum of the expert rows, the combine
+    backward scales dy and dots it with the expert rows, dx is the sum of
+    its rows' gradients plus the router term, weight gradients of empty
+    experts are zero, x_sorted rows are copies of their tokens).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_synth as ms
+import oracle
+from mixture_experts_grouped_top_amd import MoEPlan, MoEShape
+from tests.gpu_util import TOL_BF16, TOL_F32, TOL_GRAD, assert_close, host
+
+pytestmark = [pytest.mark.gpu]
+
+FULL = ["mixtral", "deepseek_v3", "token_drop", "chunked"]
+
+
+def f64(t):
+    return host(t).astype(np.float64)
+
+
+def sampled_experts(counts):
+    nz = np.where(counts > 0)[0]
+    order = nz[np.argsort(counts[nz], kind="stable")]
+    picks = {int(order[-1]), int(order[0]), int(order[len(order) // 2])}
+    return sorted(picks)
+
+
+@pytest.fixture(scope="module", params=FULL)
+def full(request):
+    w = ms.get_workload(request.param)
+    dev = ms.device_inputs(w, threads=16)
+    h = dev["host"]
+    shape = MoEShape(T=w.T, D=w.D, F=w.F, E=w.E, K=w.K, score=w.score, renorm=w.renorm,
+                     align=w.align, capacity=w.capacity, n_chunks=w.n_chunks,
+                     pad_rows_to=w.pad_rows_to)
+    plan = MoEPlan(shape)
+    plan.forward(dev["x"], dev["wi_0"], dev["wi_1"], dev["wo"], Wg=dev["Wg"],
+                 logits=dev["logits"], bias=dev["bias"])
+    plan.backward(dev["dy"], dev["x"], dev["wi_0"], dev["wi_1"], dev["wo"], Wg=dev["Wg"],
+                  bias=dev["bias"])
+    torch.cuda.synchronize()
+    # oracle routing and permutation for every token
+    if h["Wg"] is not None:
+        logits = oracle.router_logits(h["x"], h["Wg"])
+    else:
+        logits = h["logits"]
+    ids, wts = oracle.route(logits, w.K, w.score, w.renorm, h["bias"])
+    P = oracle.permute(None, ids, w.E, w.align, w.capacity, rows=plan.lhs_rows)
+    yield w, dev, plan, logits, ids, wts, P
+    del dev, plan
+    torch.cuda.empty_cache()
+
+
+def test_full_routing_and_permutation(full):
+    w, dev, plan, logits, ids, wts, P = full
+    h = dev["host"]
+    if h["Wg"] is not None:
+        assert_close(host(plan.logits), logits, TOL_F32, "logits")
+        z_o = oracle.biased_logits_f32(logits, h["bias"])
+        z_g = oracle.biased_logits_f32(host(plan.logits), h["bias"])
+        fin = np.isfinite(z_o)
+        eps = float(np.max(np.abs(z_g[fin].astype(np.float64) - z_o[fin])))
+        s = -np.sort(-z_o.astype(np.float64), axis=1)
+        gap = s[:, w.K - 1] - s[:, w.K]
+        assert np.min(gap[np.isfinite(gap)]) > 2 * eps, "seeded input has a near-tie selection"
+    assert (host(plan.ids) == ids).all()
+    assert_close(host(plan.w), wts, TOL_F32, "topk_w")
+    for k in ("counts", "group_sizes", "group_offsets", "row_of_slot", "slot_of_row"):
+        assert (host(plan.idx[k]) == P[k]).all(), k
+    # x_sorted rows are bit copies of their tokens; padding rows are zero
+    sor = plan.idx["slot_of_row"].long()
+    real = sor >= 0
+    tok = torch.where(real, sor // w.K, torch.zeros_like(sor))
+    want = torch.where(real[:, None], dev["x"][tok], torch.zeros_like(plan.x_sorted))
+    assert torch.equal(plan.x_sorted.view(torch.int16), want.view(torch.int16))
+    assert int(plan.err.item()) == 0
+    if w.n_forced_empty:
+        assert (P["counts"][ms.forced_empty_experts(w)] == 0).all()
+
+
+def _group_oracle(w, dev, P, wts, e):
+    """Forward and backward of expert e's rows in float64 (the oracle on one group)."""
+    h = dev["host"]
+    n = int(P["group_sizes"][e])
+    o = int(P["group_offsets"][e])
+    sor = P["slot_of_row"][o:o + n]
+    xs = np.zeros((n, w.D))
+    real = sor >= 0
+    xs[real] = h["x"][sor[real] // w.K]
+    wi0 = ms.gen_expert_weight(w, "wi_0", e)[None]
+    wi1 = ms.gen_expert_weight(w, "wi_1", e)[None]
+    wo = ms.gen_expert_weight(w, "wo", e)[None]
+    gs = [n]
+    if w.n_chunks > 1:
+        c = w.D // w.n_chunks
+        h0 = h1 = None
+        for i in range(w.n_chunks):
+            sl = slice(i * c, (i + 1) * c)
+            h0 = oracle.gmm(xs[:, sl], wi0[:, sl, :], gs, partial=h0)
+            h1 = oracle.gmm(xs[:, sl], wi1[:, sl, :], gs, partial=h1)
+    else:
+        h0 = oracle.gmm(xs, wi0, gs)
+        h1 = oracle.gmm(xs, wi1, gs)
+    act = oracle.swiglu(h0, h1)
+    ys = oracle.gmm(act, wo, gs)
+    ros = P["row_of_slot"].astype(np.int64)
+    local = np.where((ros >= o) & (ros < o + n), ros - o, -1)
+    d_ys, d_w = oracle.combine_bwd(h["dy"], ys, local, wts, n)
+    d_act = oracle.gmm(d_ys, wo, gs, trans_rhs=True)
+    d_wo = oracle.tgmm(act, d_ys, gs)
+    d_h0, d_h1 = oracle.swiglu_bwd(h0, h1, d_act)
+    d_xs = oracle.gmm(d_h1, wi1, gs, trans_rhs=True, partial=oracle.gmm(d_h0, wi0, gs, trans_rhs=True))
+    d_wi0 = oracle.tgmm(xs, d_h0, gs)
+    d_wi1 = oracle.tgmm(xs, d_h1, gs)
+    slots = np.where(local >= 0)[0]
+    return dict(o=o, n=n, h0=h0, h1=h1, act=act, y_sorted=ys, d_y_sorted=d_ys, d_act=d_act,
+                d_h0=d_h0, d_h1=d_h1, d_x_sorted=d_xs, d_wo=d_wo[0], d_wi_0=d_wi0[0],
+                d_wi_1=d_wi1[0], slots=slots, d_w=d_w.reshape(-1)[slots])
+
+
+def test_full_sampled_experts(full):
+    w, dev, plan, logits, ids, wts, P = full
+    for e in sampled_experts(P["counts"]):
+        g = _group_oracle(w, dev, P, wts, e)
+        o, n = g["o"], g["n"]
+        rows = slice(o, o + n)
+        for k in ("h0", "h1", "act", "y_sorted"):
+            assert_close(f64(getattr(plan, k)[rows]), g[k], TOL_BF16, f"{k} expert {e}")
+        for k in ("d_y_sorted", "d_act", "d_h0", "d_h1", "d_x_sorted"):
+            assert_close(f64(getattr(plan, k)[rows]), g[k], TOL_GRAD, f"{k} expert {e}")
+        for k in ("d_wo", "d_wi_0", "d_wi_1"):
+            assert_close(f64(getattr(plan, k)[e]), g[k], TOL_GRAD, f"{k} expert {e}")
+        assert_close(host(plan.d_w).reshape(-1)[g["slots"]], g["d_w"], TOL_GRAD, f"d_w expert {e}")
+
+
+def test_full_properties(full):
+    w, dev, plan, logits, ids, wts, P = full
+    K = w.K
+    ros = plan.idx["row_of_slot"].long().view(w.T, K)
+    kept = ros >= 0
+    safe = torch.where(kept, ros, torch.zeros_like(ros))
+    wgt = torch.where(kept, plan.w, torch.zeros_like(plan.w))
+    # combine: y = sum_j w * y_sorted[row]
+    ys = plan.y_sorted.float()[safe]                       # [T, K, D]
+    y_want = (wgt[:, :, None] * ys).sum(1)
+    assert_close(host(plan.y), host(y_want), TOL_BF16, "y = combine(y_sorted)")
+    # combine backward: d_y_sorted[row] = w dy[t]; d_w = <dy, y_sorted[row]>
+    dy = dev["dy"].float()
+    dys_want = torch.zeros_like(plan.d_y_sorted, dtype=torch.float32)
+    dys_want[safe[kept]] = (plan.w[:, :, None] * dy[:, None, :])[kept]
+    assert_close(host(plan.d_y_sorted), host(dys_want), TOL_BF16, "d_y_sorted")
+    dw_want = torch.where(kept, (ys * dy[:, None, :]).sum(-1), torch.zeros_like(plan.w))
+    assert_close(host(plan.d_w), host(dw_want), TOL_F32 * 10, "d_topk_w")
+    # dx = sum_j d_x_sorted[row] (+ d_logits Wg^T) on sampled tokens, float64
+    sample = np.random.default_rng(0).choice(w.T, size=64, replace=False)
+    r = host(plan.idx["row_of_slot"]).reshape(w.T, K)
+    rows = sorted({int(v) for v in r[sample].reshape(-1) if v >= 0})
+    pos = {v: i for i, v in enumerate(rows)}
+    dxs = f64(plan.d_x_sorted[torch.tensor(rows, device=plan.d_x_sorted.device)])
+    dx_want = np.zeros((len(sample), w.D))
+    for i, t in enumerate(sample):
+        for j in range(K):
+            if r[t, j] >= 0:
+                dx_want[i] += dxs[pos[int(r[t, j])]]
+    if dev["Wg"] is not None:
+        dx_want += f64(plan.d_logits)[sample] @ f64(dev["Wg"]).T
+        # router weight gradient: d_Wg = x^T d_logits (sampled columns)
+        dW = f64(dev["x"]).T @ f64(plan.d_logits)
+        assert_close(f64(plan.d_Wg)[0], dW, TOL_GRAD, "d_Wg")
+    assert_close(f64(plan.dx)[sample], dx_want, TOL_GRAD, "dx")
+    # routing gradient is supported on the selected experts (renormalised modes)
+    if w.renorm:
+        dl = f64(plan.d_logits)
+        mask = np.zeros_like(dl, dtype=bool)
+        np.put_along_axis(mask, ids.astype(np.int64), True, axis=1)
+        assert (dl[~mask] == 0).all()
+    # empty experts: zero weight gradients
+    empty = np.where(P["group_sizes"] == 0)[0]
+    for k in ("d_wo", "d_wi_0", "d_wi_1"):
+        t = getattr(plan, k)
+        for e in empty:
+            assert int(torch.count_nonzero(t[int(e)])) == 0, (k, e)
