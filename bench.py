@@ -50,6 +50,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="do not bracket the expert GEMM launches with events")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain row copy of known size (for scaling HBM counters)")
+    p.add_argument("--traffic-summary", nargs=4, metavar=("BENCH_FETCH", "BENCH_WRITE",
+                                                           "COPY_FETCH", "COPY_WRITE"),
+                   help="turn four rocprofv3 --pmc counter_collection.csv files into "
+                        "profiles/gmm_mixtral_traffic.json and exit")
     return p.parse_args()
 
 
@@ -96,7 +102,7 @@ class LaunchRecorder:
         self.items = []
         self.active = False
 
-    def __call__(self, kind, flops):
+    def __call__(self, kind, flops=0.0, nbytes=0.0):
         rec = self
 
         class _Ctx:
@@ -109,31 +115,33 @@ class LaunchRecorder:
                 if rec.active:
                     e = rec.torch.cuda.Event(enable_timing=True)
                     e.record(rec.torch.cuda.current_stream())
-                    rec.items.append((kind, flops, self_.s, e))
+                    rec.items.append((kind, flops, nbytes, self_.s, e))
                 return False
         return _Ctx()
 
     def summary(self):
         agg = {}
-        for kind, flops, s, e in self.items:
+        for kind, flops, nbytes, s, e in self.items:
             ms = s.elapsed_time(e)
-            a = agg.setdefault(kind, dict(launches=0, ms=0.0, flops=0.0))
+            a = agg.setdefault(kind, dict(launches=0, ms=0.0, flops=0.0, bytes=0.0))
             a["launches"] += 1
             a["ms"] += ms
             a["flops"] += flops
+            a["bytes"] += nbytes
         for a in agg.values():
             a["avg_ms"] = a["ms"] / a["launches"]
             a["tflops"] = a["flops"] / (a["ms"] * 1e-3) / 1e12
+            a["gbs"] = a["bytes"] / (a["ms"] * 1e-3) / 1e9
         return agg
 
 
 # Kernel symbol behind each recorded launch kind for the bf16 workloads
 # (the rocprofv3 summary is matched on this name).
 KERNEL_NAME = {
-    "gmm_nn": "gmm_bf16_kernel<128, 128, false, unsigned short>",
-    "gmm_nt": "gmm_bf16_kernel<128, 128, true, unsigned short>",
-    "tgmm": "tgmm_bf16_kernel<128, 128, unsigned short>",
-    "gmm_up_chunk": "gmm_bf16_kernel<128, 128, false, float>",
+    "gmm_nn": "gmm_mfma_kernel<true, 256, unsigned short>",
+    "gmm_nt": "gmm_mfma_kernel<false, 256, unsigned short>",
+    "tgmm": "tgmm_mfma_kernel<unsigned short>",
+    "gmm_up_chunk": "gmm_mfma_kernel<true, 256, float>",
 }
 
 
@@ -158,6 +166,72 @@ def traffic_from_profiles(kind: str):
     if not k or d.get("gmm_source_sha256_16") != kernel_source_digest():
         return None
     return k.get("hbm_bytes_per_launch")
+
+
+COPY_ROWS, COPY_COLS = 32768, 16384      # bf16 rows copied by the calibration run (1 GiB)
+COPY_KERNEL = "permute_gather_kernel"
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gmm_mixtral_traffic.json")
+
+
+def copy_calibration():
+    """A plain copy of known size: moe_permute with one expert and top-1 is
+    the identity permutation, so its row-gather kernel reads and writes
+    COPY_ROWS x COPY_COLS bf16 once each (1 GiB each way)."""
+    import torch
+    import mixture_experts_grouped_top_amd as moe
+    moe.load()
+    x = torch.ones((COPY_ROWS, COPY_COLS), dtype=torch.bfloat16, device="cuda")
+    ids = torch.zeros((COPY_ROWS, 1), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        moe.moe_permute(x, ids, 1)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {COPY_ROWS}x{COPY_COLS} bf16, 3 copies")
+
+
+def _pmc_per_dispatch(path, counter, name_part):
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter or name_part not in r["Kernel_Name"]:
+            continue
+        d = int(r["Dispatch_Id"])
+        per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+    return list(per.values())
+
+
+def traffic_summary(bench_fetch, bench_write, copy_fetch, copy_write):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB) per dispatch of each GEMM kernel,
+    scaled by known_bytes / measured_bytes of the copy kernel."""
+    known = COPY_ROWS * COPY_COLS * 2
+    cf = _pmc_per_dispatch(copy_fetch, "FETCH_SIZE", COPY_KERNEL)
+    cw = _pmc_per_dispatch(copy_write, "WRITE_SIZE", COPY_KERNEL)
+    f_fetch = known / (1024.0 * sum(cf) / len(cf))
+    f_write = known / (1024.0 * sum(cw) / len(cw))
+    out = {"gmm_source_sha256_16": kernel_source_digest(),
+           "calibration": {"copy_bytes_each_way": known, "fetch_scale": round(f_fetch, 4),
+                           "write_scale": round(f_write, 4), "kernel": COPY_KERNEL},
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_bench_fetch -o p "
+               "-- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-kernel-events",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_bench_write -o p "
+               "-- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-kernel-events",
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o p "
+               "-- python bench.py --copy-calibration",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o p "
+               "-- python bench.py --copy-calibration"],
+           "kernels": {}}
+    for kind, name in KERNEL_NAME.items():
+        f = _pmc_per_dispatch(bench_fetch, "FETCH_SIZE", name)
+        wv = _pmc_per_dispatch(bench_write, "WRITE_SIZE", name)
+        if not f or not wv:
+            continue
+        fk, wk = sum(f) / len(f), sum(wv) / len(wv)
+        out["kernels"][kind] = {
+            "dispatches": len(f), "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+            "hbm_bytes_per_launch": round(1024.0 * (fk * f_fetch + wk * f_write))}
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+    log(f"[bench] wrote {TRAFFIC_JSON}")
 
 
 def cpu_baseline(w, inp, tokens: int):
@@ -190,6 +264,12 @@ def cpu_baseline(w, inp, tokens: int):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
@@ -220,6 +300,7 @@ def main():
     torch.cuda.synchronize()
     R = int(plan.idx["counts"].sum().item())
     plan.kept_rows_override = R
+    plan.padded_rows_override = int(plan.idx["group_offsets"][-1].item())
     for _ in range(max(0, args.warmup - 1)):
         step()
     rec = LaunchRecorder()
@@ -243,9 +324,10 @@ def main():
 
     kernels = rec.summary()
     roofline = None
-    if kernels:
-        kind = max(kernels, key=lambda k: kernels[k]["ms"])
-        k = kernels[kind]
+    gemm = {k: v for k, v in kernels.items() if v["flops"] > 0}
+    if gemm:
+        kind = max(gemm, key=lambda k: gemm[k]["ms"])
+        k = gemm[kind]
         ach = k["tflops"]
         traffic = traffic_from_profiles(kind)
         roofline = {"bound": "mfma", "kernel": KERNEL_NAME.get(kind, kind),
@@ -253,9 +335,10 @@ def main():
                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                     "avg_launch_ms": round(k["avg_ms"], 4),
                     "flops_per_launch": k["flops"] / k["launches"]}
-        for kk, v in kernels.items():
-            log(f"[bench]   {kk:12s} {v['launches']:4d} launches  avg {v['avg_ms']:.3f} ms  "
-                f"{v['tflops']:.1f} TFLOP/s")
+    for kk, v in kernels.items():
+        rate = (f"{v['tflops']:.1f} TFLOP/s" if v["flops"] else
+                f"{v['gbs']:.0f} GB/s ({100 * v['gbs'] / PEAK_HBM_GBS:.0f}% of HBM)")
+        log(f"[bench]   {kk:12s} {v['launches']:4d} launches  avg {v['avg_ms']:.3f} ms  {rate}")
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
@@ -276,8 +359,13 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "device_error_flags": err,
-        "kernels": {k: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
-                        "tflops": round(v["tflops"], 2)} for k, v in kernels.items()},
+        "kernels": {k: ({"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
+                         "tflops": round(v["tflops"], 2)} if v["flops"] else
+                        {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
+                         "algorithmic_bytes": int(v["bytes"] / v["launches"]),
+                         "gbs": round(v["gbs"], 1),
+                         "hbm_frac": round(v["gbs"] / PEAK_HBM_GBS, 4)})
+                    for k, v in kernels.items()},
     }
     print(json.dumps(out), flush=True)
 

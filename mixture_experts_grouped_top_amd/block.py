@@ -93,12 +93,12 @@ class MoEPlan:
         self.d_wo = torch.empty((s.E, s.F, s.D), **act)
         # router weight gradient kept in float32 (a [D, E] reduction over all tokens)
         self.d_Wg = torch.empty((1, s.D, s.E), **f32) if router else None
-        self.recorder = None   # optional callable(kind, flops) -> context manager
+        self.recorder = None   # optional callable(kind, flops, bytes) -> context manager
 
-    def _rec(self, kind: str, flops: float):
+    def _rec(self, kind: str, flops: float = 0.0, nbytes: float = 0.0):
         if self.recorder is None:
             return contextlib.nullcontext()
-        return self.recorder(kind, flops)
+        return self.recorder(kind, flops, nbytes)
 
     @property
     def group_sizes(self):
@@ -115,6 +115,29 @@ class MoEPlan:
             return self.kept_rows_override
         return self.s.T * self.s.K
 
+    # Rows of the sorted buffers that belong to groups (kept rows plus
+    # align_size padding); only used to label recorded launches.
+    padded_rows_override: Optional[int] = None
+
+    @property
+    def padded_rows(self) -> int:
+        return self.rows if self.padded_rows_override is None else self.padded_rows_override
+
+    def _bytes(self) -> dict:
+        """Algorithmic HBM bytes of the memory-bound calls (each tensor read or
+        written once; ids and maps at 4 bytes per entry)."""
+        s = self.s
+        b = torch.finfo(s.dtype).bits // 8
+        bh = 4 if s.n_chunks > 1 else b
+        R, Rp, T, D, F, K = self.kept_rows, self.padded_rows, s.T, s.D, s.F, s.K
+        return dict(
+            permute=T * D * b + self.lhs_rows * D * b + T * K * 4 * 2 + self.lhs_rows * 4,
+            swiglu=2 * Rp * F * bh + Rp * F * b,
+            combine=R * D * b + T * D * b + T * K * 8,
+            combine_bwd=T * D * b + R * D * b + self.rows * D * b + T * K * 12 + self.rows * 4,
+            swiglu_bwd=2 * Rp * F * bh + 3 * Rp * F * b,
+            permute_bwd=R * D * b + T * D * b + T * K * 4)
+
     def forward(self, x, wi_0, wi_1, wo, Wg=None, logits=None, bias=None, stream=None):
         """y = sum_j w[t,j] FFN_{e(t,j)}(x[t]).  Either Wg (router GEMM on the
         device) or precomputed float32 logits."""
@@ -125,9 +148,11 @@ class MoEPlan:
             self.logits.copy_(logits)
         B.moe_route(self.logits, s.K, s.score, s.renorm, bias, topk_ids=self.ids, topk_w=self.w,
                     stream=stream)
-        B.moe_permute(x, self.ids, s.E, s.align, s.capacity, s.capacity_layout,
-                      rows=self.lhs_rows, x_sorted=self.x_sorted, err=self.err,
-                      workspace=self.ws, out=self.idx, stream=stream)
+        nb = self._bytes() if self.recorder is not None else {}
+        with self._rec("permute", nbytes=nb.get("permute", 0)):
+            B.moe_permute(x, self.ids, s.E, s.align, s.capacity, s.capacity_layout,
+                          rows=self.lhs_rows, x_sorted=self.x_sorted, err=self.err,
+                          workspace=self.ws, out=self.idx, stream=stream)
         gs = self.group_sizes
         R = self.kept_rows
         if s.n_chunks > 1:
@@ -145,10 +170,13 @@ class MoEPlan:
                 B.moe_gmm(self.x_sorted, wi_0, gs, out=self.h0, err=self.err, stream=stream)
             with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
                 B.moe_gmm(self.x_sorted, wi_1, gs, out=self.h1, err=self.err, stream=stream)
-        B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
+        with self._rec("swiglu", nbytes=nb.get("swiglu", 0)):
+            B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
         with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
             B.moe_gmm(self.act, wo, gs, out=self.y_sorted, err=self.err, stream=stream)
-        B.moe_combine(self.y_sorted, self.idx["row_of_slot"], self.w, y=self.y, stream=stream)
+        with self._rec("combine", nbytes=nb.get("combine", 0)):
+            B.moe_combine(self.y_sorted, self.idx["row_of_slot"], self.w, y=self.y,
+                          stream=stream)
         return self.y
 
     def backward(self, dy, x, wi_0, wi_1, wo, Wg=None, bias=None, stream=None):
@@ -158,15 +186,18 @@ class MoEPlan:
         gs = self.group_sizes
         R = self.kept_rows
         ros, sor = self.idx["row_of_slot"], self.idx["slot_of_row"]
-        B.moe_combine_bwd(dy, self.y_sorted, ros, sor, self.w, d_y_sorted=self.d_y_sorted,
-                          d_topk_w=self.d_w, stream=stream)
+        nb = self._bytes() if self.recorder is not None else {}
+        with self._rec("combine_bwd", nbytes=nb.get("combine_bwd", 0)):
+            B.moe_combine_bwd(dy, self.y_sorted, ros, sor, self.w, d_y_sorted=self.d_y_sorted,
+                              d_topk_w=self.d_w, stream=stream)
         with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
             B.moe_gmm(self.d_y_sorted, wo, gs, trans_rhs=True, out=self.d_act, err=self.err,
                       stream=stream)
         with self._rec("tgmm", 2.0 * R * s.D * s.F):
             B.moe_tgmm(self.act, self.d_y_sorted, gs, out=self.d_wo, err=self.err, stream=stream)
-        B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
-                         stream=stream)
+        with self._rec("swiglu_bwd", nbytes=nb.get("swiglu_bwd", 0)):
+            B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
+                             stream=stream)
         with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
             B.moe_gmm(self.d_h0, wi_0, gs, trans_rhs=True, out=self.d_x_sorted, err=self.err,
                       stream=stream)
@@ -178,7 +209,8 @@ class MoEPlan:
             B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream)
         with self._rec("tgmm", 2.0 * R * s.D * s.F):
             B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream)
-        B.moe_permute_bwd(self.d_x_sorted, ros, s.T, s.K, d_x=self.dx, stream=stream)
+        with self._rec("permute_bwd", nbytes=nb.get("permute_bwd", 0)):
+            B.moe_permute_bwd(self.d_x_sorted, ros, s.T, s.K, d_x=self.dx, stream=stream)
         B.moe_route_bwd(self.logits, self.ids, self.d_w, s.score, s.renorm, bias,
                         d_logits=self.d_logits, stream=stream)
         if Wg is not None and self.router:
