@@ -137,11 +137,12 @@ class LaunchRecorder:
 
 # Kernel symbol behind each recorded launch kind for the bf16 workloads
 # (the rocprofv3 summary is matched on this name).
+# These are the 256 x 256 tile variants the Mixtral-8x7B shape runs on.
 KERNEL_NAME = {
-    "gmm_nn": "gmm_mfma_kernel<true, 256, unsigned short>",
-    "gmm_nt": "gmm_mfma_kernel<false, 256, unsigned short>",
-    "tgmm": "tgmm_mfma_kernel<unsigned short>",
-    "gmm_up_chunk": "gmm_mfma_kernel<true, 256, float>",
+    "gmm_nn": "gmm_mfma_kernel<true, 256, 256, unsigned short>",
+    "gmm_nt": "gmm_mfma_kernel<false, 256, 256, unsigned short>",
+    "tgmm": "tgmm_mfma_kernel<256, unsigned short>",
+    "gmm_up_chunk": "gmm_mfma_kernel<true, 256, 256, float>",
 }
 
 
@@ -153,9 +154,12 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kind: str):
+def traffic_from_profiles(kind: str, workload: str):
     """HBM bytes per launch of the dominant kernel from the committed PMC
-    summary, or None if absent or taken on a different kernel source."""
+    summary (taken on the Mixtral-8x7B shape), or None if absent, taken on a
+    different kernel source or for another workload."""
+    if workload != "mixtral":
+        return None
     path = os.path.join(ROOT, "profiles", "gmm_mixtral_traffic.json")
     try:
         with open(path) as f:
@@ -329,8 +333,9 @@ def main():
         kind = max(gemm, key=lambda k: gemm[k]["ms"])
         k = gemm[kind]
         ach = k["tflops"]
-        traffic = traffic_from_profiles(kind)
-        roofline = {"bound": "mfma", "kernel": KERNEL_NAME.get(kind, kind),
+        traffic = traffic_from_profiles(kind, args.workload)
+        label = KERNEL_NAME.get(kind, kind) if args.workload == "mixtral" else kind
+        roofline = {"bound": "mfma", "kernel": label,
                     "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                     "avg_launch_ms": round(k["avg_ms"], 4),

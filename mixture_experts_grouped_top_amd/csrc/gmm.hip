@@ -167,9 +167,7 @@ __device__ void zero_rows(TO* out, int64_t ld, int64_t N, int64_t r0, int64_t r1
 // 4 r + q addresses row k + r, columns 4 q .. 4 q + 3 of the group's 16
 // columns, and receives its own column for the four rows.
 
-constexpr int TM = 256, TK = 32;
-constexpr int kStages = 4;
-constexpr int kOpBytes = 256 * TK * 2;      // one operand tile, one stage (16 KB)
+constexpr int TK = 32;
 constexpr int kCPR = TK / 8;                // 16-byte chunks per row of a row tile
 
 __device__ __forceinline__ int row_swz(int x) { return (x >> 1) & 3; }
@@ -327,7 +325,7 @@ struct Operand {
   }
 };
 
-template <int TN>
+template <int TM, int TN>
 struct Acc {
   static constexpr int FM = TM / 64, FN = TN / 64;
   f32x16 v[FM][FN];
@@ -394,104 +392,116 @@ struct MfmaArgs {
 };
 
 // Contraction over one tile: nfull DMA steps, then an optional ragged step.
+// LDS holds NS stages, each the A tile followed by the B tile.
 //
 // Software pipeline (TK = 32: two k16 substeps per stage):
-//   prologue: DMA stages 0..3; wait for stage 0; barrier; load frags(0, 0)
+//   prologue: DMA stages 0..NS-1; wait for stage 0; barrier; load frags(0, 0)
 //   step s:   load frags(s, 1); MFMAs(s, 0);
 //             wait for stage s + 1; barrier (also: all waves hold their
-//             frags of stage s, so its buffer is free); DMA stage s + 4
+//             frags of stage s, so its buffer is free); DMA stage s + NS
 //             into it; load frags(s + 1, 0);
 //             MFMAs(s, 1)
 // so MFMAs are queued whenever a wave waits at the barrier or on LDS.
-template <class OA, class OB, int TN>
-__device__ __forceinline__ void contract(char (*smem)[2][kOpBytes], const OA& A, const OB& B,
-                                         int64_t Kc, Acc<TN>& acc, const uint32_t (&fa)[4],
+template <int NS, class OA, class OB, class ACC>
+__device__ __forceinline__ void contract(char* lds, const OA& A, const OB& B, int64_t Kc,
+                                         ACC& acc, const uint32_t (&fa)[4],
                                          const uint32_t (&fb)[4]) {
-  static_assert(kStages == 4 && TK == 32, "pipeline written for 4 stages of two substeps");
+  static_assert(TK == 32 && NS >= 2 && NS <= 4, "pipeline written for 2..4 stages of two substeps");
+  constexpr int SB = OA::kBytes + OB::kBytes;
   const int nfull = static_cast<int>(Kc / TK);
   const int kv = static_cast<int>(Kc - static_cast<int64_t>(nfull) * TK);
   constexpr int PER = OA::NJ + OB::NJ;      // DMA instructions per thread per stage
-  typename Acc<TN>::Frags f0, f1;
+  typename ACC::Frags f0, f1;
   acc.zero();
   __builtin_amdgcn_s_waitcnt(0);            // nothing from the previous tile is in flight
 #pragma unroll
-  for (int p = 0; p < kStages; ++p)
+  for (int p = 0; p < NS; ++p)
     if (p < nfull) {
-      A.dma(p, lds_addr(smem[p][0]));
-      B.dma(p, lds_addr(smem[p][1]));
+      A.dma(p, lds_addr(lds + p * SB));
+      B.dma(p, lds_addr(lds + p * SB + OA::kBytes));
     }
   if (nfull > 0) {
     // stage 0 has landed once at most the later prologue stages are in flight
-    const int later = min(kStages - 1, nfull - 1);
+    const int later = min(NS - 1, nfull - 1);
     if (later >= 3) wait_vmcnt<3 * PER>();
     else if (later == 2) wait_vmcnt<2 * PER>();
     else if (later == 1) wait_vmcnt<PER>();
     else wait_vmcnt<0>();
     __syncthreads();
-    Acc<TN>::template load<OA, OB>(f0, smem[0][0], smem[0][1], fa, fb, 0);
+    ACC::template load<OA, OB>(f0, lds, lds + OA::kBytes, fa, fb, 0);
   }
   for (int s = 0; s < nfull; ++s) {
-    const int cur = s % kStages;
-    Acc<TN>::template load<OA, OB>(f1, smem[cur][0], smem[cur][1], fa, fb, 1);
+    const int cur = s % NS;
+    char* cs = lds + cur * SB;
+    ACC::template load<OA, OB>(f1, cs, cs + OA::kBytes, fa, fb, 1);
     acc.mma(f0);
     if (s + 1 < nfull) {
-      // stages s + 2 and s + 3 may still be in flight; s + 1 must have landed
-      const int later = min(2, nfull - 2 - s);
+      // stages s + 2 .. s + NS - 1 may still be in flight; s + 1 must have landed
+      const int later = min(NS - 2, nfull - 2 - s);
       if (later >= 2) wait_vmcnt<2 * PER>();
       else if (later == 1) wait_vmcnt<PER>();
       else wait_vmcnt<0>();
       __syncthreads();
-      if (s + kStages < nfull) {
-        A.dma(s + kStages, lds_addr(smem[cur][0]));
-        B.dma(s + kStages, lds_addr(smem[cur][1]));
+      if (s + NS < nfull) {
+        A.dma(s + NS, lds_addr(cs));
+        B.dma(s + NS, lds_addr(cs + OA::kBytes));
       }
-      const int nxt = (s + 1) % kStages;
-      Acc<TN>::template load<OA, OB>(f0, smem[nxt][0], smem[nxt][1], fa, fb, 0);
+      char* ns = lds + ((s + 1) % NS) * SB;
+      ACC::template load<OA, OB>(f0, ns, ns + OA::kBytes, fa, fb, 0);
     }
     acc.mma(f1);
   }
   if (kv > 0) {
-    // stage nfull % kStages was last read four steps ago (or by the previous
-    // tile) and no DMA targets it; other waves may still read stage nfull - 1
-    const int ts = nfull % kStages;
+    // stage nfull % NS was last read NS steps ago (or by the previous tile)
+    // and no DMA targets it; other waves may still read stage nfull - 1
+    char* ts = lds + (nfull % NS) * SB;
     {
       uint4 t[OA::NR];
       A.tail_load(nfull, kv, t);
-      A.tail_store(smem[ts][0], t);
+      A.tail_store(ts, t);
     }
     {
       uint4 t[OB::NR];
       B.tail_load(nfull, kv, t);
-      B.tail_store(smem[ts][1], t);
+      B.tail_store(ts + OA::kBytes, t);
     }
     __syncthreads();
-    Acc<TN>::template load<OA, OB>(f0, smem[ts][0], smem[ts][1], fa, fb, 0);
-    Acc<TN>::template load<OA, OB>(f1, smem[ts][0], smem[ts][1], fa, fb, 1);
+    ACC::template load<OA, OB>(f0, ts, ts + OA::kBytes, fa, fb, 0);
+    ACC::template load<OA, OB>(f1, ts, ts + OA::kBytes, fa, fb, 1);
     acc.mma(f0);
     acc.mma(f1);
   }
   __syncthreads();   // every wave is done with all stages before they are refilled
 }
 
+// Stages and LDS bytes of a TM x TN tile (128-row tiles keep three stages
+// so that two workgroups fit in one CU's LDS).
+template <int TM, int TN>
+struct Stages {
+  static constexpr int NS = (TN >= 384 || TM <= 128) ? 3 : 4;
+  static constexpr int kBytes = NS * (TM + TN) * TK * 2;
+};
+
 // Write the accumulator tile: for each of its FM 32-row slabs a wave stages
 // the slab (32 x TN/2 float32) in its own LDS region, then reads it back as
 // 8-column row chunks and stores them with 16-byte (bf16) or 32-byte (fp32)
 // accesses; rows >= rv and columns >= cv are skipped.  The LDS is the
 // operand stages, free once the contraction has ended with a barrier.
-template <int TN, typename TO>
-__device__ __forceinline__ void store_tile(const Acc<TN>& acc, char* lds, TO* o, int64_t ldo,
+template <int TM, int TN, typename TO>
+__device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO* o, int64_t ldo,
                                            int rv, int cv, int accumulate) {
   constexpr int WC = TN / 2;
   constexpr int SROW = WC * 4 + 16;
   constexpr int CPR = WC / 8;                 // 8-column chunks per slab row
   const int tid = opaque_tid();
   const int lane = tid & 63, w = tid >> 6;
+  static_assert(4 * 32 * SROW <= Stages<TM, TN>::kBytes, "epilogue slabs fit in the stage buffers");
   char* slab = lds + w * 32 * SROW;
   const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * WC;
 #pragma unroll
-  for (int i = 0; i < Acc<TN>::FM; ++i) {
+  for (int i = 0; i < Acc<TM, TN>::FM; ++i) {
 #pragma unroll
-    for (int j = 0; j < Acc<TN>::FN; ++j)
+    for (int j = 0; j < Acc<TM, TN>::FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -527,11 +537,19 @@ __device__ __forceinline__ void store_tile(const Acc<TN>& acc, char* lds, TO* o,
   __syncthreads();   // the stages are refilled by the next tile
 }
 
-template <bool B_COLK, int TN, typename TO>
-__global__ __launch_bounds__(NT, 1) void gmm_mfma_kernel(MfmaArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[kStages][2][kOpBytes];
-  __shared__ int row_base[kMaxG + 1];
-  __shared__ int tile_base[kMaxG + 1];
+// Largest group count a gmm tile variant supports: the 128-row variant
+// keeps its LDS (three stages + two group prefixes) within half a CU.
+constexpr int kMaxGShort = 1000;
+template <int TM>
+struct MaxG {
+  static constexpr int value = TM <= 128 ? kMaxGShort : kMaxG;
+};
+
+template <bool B_COLK, int TM, int TN, typename TO>
+__global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Stages<TM, TN>::kBytes];
+  __shared__ int row_base[MaxG<TM>::value + 1];
+  __shared__ int tile_base[MaxG<TM>::value + 1];
   const int ntn = static_cast<int>((a.N + TN - 1) / TN);
   scan_groups(a.gsz, a.G, a.M, TM, ntn, row_base, tile_base, blockIdx.x == 0 ? a.err : nullptr);
   __syncthreads();
@@ -539,7 +557,7 @@ __global__ __launch_bounds__(NT, 1) void gmm_mfma_kernel(MfmaArgs a) {
   TO* out = static_cast<TO*>(a.out);
   Operand<false, TM> A;
   Operand<B_COLK, TN> B;
-  Acc<TN> acc;
+  Acc<TM, TN> acc;
   uint32_t fa[4], fb[4];
   Operand<false, TM>::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
   Operand<B_COLK, TN>::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
@@ -564,16 +582,16 @@ __global__ __launch_bounds__(NT, 1) void gmm_mfma_kernel(MfmaArgs a) {
     A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, rv);
     const bf16_t* bg = a.rhs + g * a.rhs_gs;
     B.setup(B_COLK ? bg + col0 : bg + col0 * a.ld_rhs, a.ld_rhs, cv);
-    contract(smem, A, B, a.Kdim, acc, fa, fb);
-    store_tile(acc, &smem[0][0][0], out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate);
+    contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
+    store_tile(acc, smem, out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate);
   }
   if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
 }
 
-template <typename TO>
+template <int TN, typename TO>
 __global__ __launch_bounds__(NT, 1) void tgmm_mfma_kernel(MfmaArgs a) {
-  constexpr int TN = 256;
-  __shared__ __attribute__((aligned(1024))) char smem[kStages][2][kOpBytes];
+  constexpr int TM = 256;
+  __shared__ __attribute__((aligned(1024))) char smem[Stages<TM, TN>::kBytes];
   __shared__ int row_base[kMaxG + 1];
   scan_groups(a.gsz, a.G, a.M, TM, 1, row_base, nullptr, blockIdx.x == 0 ? a.err : nullptr);
   __syncthreads();
@@ -584,7 +602,7 @@ __global__ __launch_bounds__(NT, 1) void tgmm_mfma_kernel(MfmaArgs a) {
   TO* out = static_cast<TO*>(a.out);
   Operand<true, TM> A;
   Operand<true, TN> B;
-  Acc<TN> acc;
+  Acc<TM, TN> acc;
   uint32_t fa[4], fb[4];
   Operand<true, TM>::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
   Operand<true, TN>::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
@@ -603,8 +621,8 @@ __global__ __launch_bounds__(NT, 1) void tgmm_mfma_kernel(MfmaArgs a) {
     const int nv = static_cast<int>(lmin(TN, a.N - n0));
     A.setup(a.lhs + r0 * a.ld_lhs + m0, a.ld_lhs, mv);
     B.setup(a.rhs + r0 * a.ld_rhs + n0, a.ld_rhs, nv);
-    contract(smem, A, B, rows_g, acc, fa, fb);
-    store_tile(acc, &smem[0][0][0], out + g * a.out_gs + m0 * a.ld_out + n0, a.ld_out, mv, nv,
+    contract<Stages<TM, TN>::NS>(smem, A, B, rows_g, acc, fa, fb);
+    store_tile(acc, smem, out + g * a.out_gs + m0 * a.ld_out + n0, a.ld_out, mv, nv,
                a.accumulate);
   }
 }
@@ -782,24 +800,34 @@ MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* 
   if (in_dtype == MOE_BF16) {
     MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
                rhs_group_stride, group_sizes, G, M_out, Kdim, N, out, ld_out, 0, accumulate, err};
-    // narrow outputs and single-step contractions use a 256 x 128 tile
+    // narrow outputs and single-step contractions use a 256 x 128 tile;
+    // small groups (fewer than 512 rows per group on average) use 128-row
+    // tiles, two workgroups per CU
     const bool narrow = N <= 128 || Kdim <= TK;
+    const bool short_m = !narrow && G <= kMaxGShort && M_out < 512 * static_cast<int64_t>(G);
+    const int TMv = short_m ? 128 : 256;
     const int TNv = narrow ? 128 : 256;
-    const int64_t upper = ((M_out + TM - 1) / TM + G) * ((N + TNv - 1) / TNv);
-    const unsigned grid = persistent_grid(upper, 1);
-#define GMM(BC, TNV, TO) \
-  hipLaunchKernelGGL((gmm_mfma_kernel<BC, TNV, TO>), dim3(grid), dim3(NT), 0, st, a)
+    const int64_t upper = ((M_out + TMv - 1) / TMv + G) * ((N + TNv - 1) / TNv);
+    const unsigned grid = persistent_grid(upper, short_m ? 2 : 1);
+#define GMM(BC, TMV, TNV, TO) \
+  hipLaunchKernelGGL((gmm_mfma_kernel<BC, TMV, TNV, TO>), dim3(grid), dim3(NT), 0, st, a)
     if (narrow) {
       if (trans_rhs) {
-        if (out_dtype == MOE_BF16) GMM(false, 128, bf16_t); else GMM(false, 128, float);
+        if (out_dtype == MOE_BF16) GMM(false, 256, 128, bf16_t); else GMM(false, 256, 128, float);
       } else {
-        if (out_dtype == MOE_BF16) GMM(true, 128, bf16_t); else GMM(true, 128, float);
+        if (out_dtype == MOE_BF16) GMM(true, 256, 128, bf16_t); else GMM(true, 256, 128, float);
+      }
+    } else if (short_m) {
+      if (trans_rhs) {
+        if (out_dtype == MOE_BF16) GMM(false, 128, 256, bf16_t); else GMM(false, 128, 256, float);
+      } else {
+        if (out_dtype == MOE_BF16) GMM(true, 128, 256, bf16_t); else GMM(true, 128, 256, float);
       }
     } else {
       if (trans_rhs) {
-        if (out_dtype == MOE_BF16) GMM(false, 256, bf16_t); else GMM(false, 256, float);
+        if (out_dtype == MOE_BF16) GMM(false, 256, 256, bf16_t); else GMM(false, 256, 256, float);
       } else {
-        if (out_dtype == MOE_BF16) GMM(true, 256, bf16_t); else GMM(true, 256, float);
+        if (out_dtype == MOE_BF16) GMM(true, 256, 256, bf16_t); else GMM(true, 256, 256, float);
       }
     }
 #undef GMM
@@ -843,12 +871,12 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
   if (in_dtype == MOE_BF16) {
     MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
                0, group_sizes, G, M, Kdim, N, out, ld_out, out_group_stride, accumulate, err};
-    const int64_t upper = static_cast<int64_t>(G) * ((Kdim + TM - 1) / TM) * ((N + 255) / 256);
+    const int64_t upper = static_cast<int64_t>(G) * ((Kdim + 255) / 256) * ((N + 255) / 256);
     const unsigned grid = persistent_grid(upper, 1);
     if (out_dtype == MOE_BF16)
-      hipLaunchKernelGGL(tgmm_mfma_kernel<bf16_t>, dim3(grid), dim3(NT), 0, st, a);
+      hipLaunchKernelGGL((tgmm_mfma_kernel<256, bf16_t>), dim3(grid), dim3(NT), 0, st, a);
     else
-      hipLaunchKernelGGL(tgmm_mfma_kernel<float>, dim3(grid), dim3(NT), 0, st, a);
+      hipLaunchKernelGGL((tgmm_mfma_kernel<256, float>), dim3(grid), dim3(NT), 0, st, a);
   } else {
     const int64_t upper = static_cast<int64_t>(G) * ((Kdim + FB - 1) / FB) * ((N + FB - 1) / FB);
     const unsigned grid = persistent_grid(upper, 4);

@@ -159,6 +159,9 @@ GS = {
     "one_group": [517],
     "all_empty": [0, 0, 0],
     "aligned": [128, 256, 0, 384],
+    # more groups than the 128-row tile variant holds (1000): 256-row tiles
+    "many": [(i * 7) % 3 for i in range(1010)],
+    "max_groups": [(i * 5) % 4 for i in range(1024)],
 }
 
 GMM_CASES = [
@@ -177,6 +180,10 @@ GMM_CASES = [
     ("ragged", 72, 40, 5, 0, True, "f32", "f32", True),
     ("one_group", 96, 8, 0, 0, False, "f32", "f32", False),
     ("aligned", 64, 24, 64, 30, True, "f32", "bf16", False),
+    ("one_group", 96, 264, 0, 0, False, "bf16", "bf16", False),  # 256 x 256 tiles
+    ("one_group", 96, 264, 0, 0, True, "bf16", "f32", True),
+    ("many", 64, 136, 3, 0, False, "bf16", "bf16", False),
+    ("max_groups", 64, 136, 0, 0, True, "bf16", "f32", True),
 ]
 
 
@@ -243,6 +250,7 @@ TGMM_CASES = [
     ("all_empty", 64, 64, "bf16", "f32", True),
     ("ragged", 40, 24, "f32", "f32", False),
     ("aligned", 16, 48, "f32", "f32", True),
+    ("max_groups", 16, 136, "bf16", "f32", False),
 ]
 
 
