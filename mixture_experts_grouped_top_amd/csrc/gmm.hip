@@ -588,9 +588,8 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
   if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
 }
 
-template <int TN, typename TO>
-__global__ __launch_bounds__(NT, 1) void tgmm_mfma_kernel(MfmaArgs a) {
-  constexpr int TM = 256;
+template <int TM, int TN, typename TO>
+__global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void tgmm_mfma_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[Stages<TM, TN>::kBytes];
   __shared__ int row_base[kMaxG + 1];
   scan_groups(a.gsz, a.G, a.M, TM, 1, row_base, nullptr, blockIdx.x == 0 ? a.err : nullptr);
@@ -871,12 +870,20 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
   if (in_dtype == MOE_BF16) {
     MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
                0, group_sizes, G, M, Kdim, N, out, ld_out, out_group_stride, accumulate, err};
-    const int64_t upper = static_cast<int64_t>(G) * ((Kdim + 255) / 256) * ((N + 255) / 256);
-    const unsigned grid = persistent_grid(upper, 1);
-    if (out_dtype == MOE_BF16)
-      hipLaunchKernelGGL((tgmm_mfma_kernel<256, bf16_t>), dim3(grid), dim3(NT), 0, st, a);
-    else
-      hipLaunchKernelGGL((tgmm_mfma_kernel<256, float>), dim3(grid), dim3(NT), 0, st, a);
+    // short contractions (under 512 rows per group on average) leave each
+    // tile's epilogue exposed: 128-row tiles let two workgroups share a CU
+    const bool short_k = M < 512 * static_cast<int64_t>(G);
+    const int TMv = short_k ? 128 : 256;
+    const int64_t upper = static_cast<int64_t>(G) * ((Kdim + TMv - 1) / TMv) * ((N + 255) / 256);
+    const unsigned grid = persistent_grid(upper, short_k ? 2 : 1);
+#define TGMM(TMc, TOc) \
+  hipLaunchKernelGGL((tgmm_mfma_kernel<TMc, 256, TOc>), dim3(grid), dim3(NT), 0, st, a)
+    if (short_k) {
+      if (out_dtype == MOE_BF16) TGMM(128, bf16_t); else TGMM(128, float);
+    } else {
+      if (out_dtype == MOE_BF16) TGMM(256, bf16_t); else TGMM(256, float);
+    }
+#undef TGMM
   } else {
     const int64_t upper = static_cast<int64_t>(G) * ((Kdim + FB - 1) / FB) * ((N + FB - 1) / FB);
     const unsigned grid = persistent_grid(upper, 4);

@@ -251,6 +251,7 @@ TGMM_CASES = [
     ("ragged", 40, 24, "f32", "f32", False),
     ("aligned", 16, 48, "f32", "f32", True),
     ("max_groups", 16, 136, "bf16", "f32", False),
+    ("one_group", 264, 136, "bf16", "bf16", True),   # long contraction: 256-row tiles
 ]
 
 
