@@ -67,6 +67,71 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// Streaming (non-temporal) 16-byte accesses for data touched once: they
+// leave L2 capacity to data that is reused.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(uint4* p, uint4 v) {
+  const u32x4 q = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void unpack8(const uint4& q, float v[8]) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8_nt(const bf16_t* p, float v[8]) {
+  unpack8(ld_nt(reinterpret_cast<const uint4*>(p)), v);
+}
+__device__ __forceinline__ void load8_nt(const float* p, float v[8]) {
+  const uint4 a = ld_nt(reinterpret_cast<const uint4*>(p));
+  const uint4 b = ld_nt(reinterpret_cast<const uint4*>(p + 4));
+  v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+  v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+  v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+  v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+__device__ __forceinline__ void store8_nt(bf16_t* p, const float v[8]) {
+  st_nt(reinterpret_cast<uint4*>(p),
+        make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                   pack_bf16x2(v[6], v[7])));
+}
+__device__ __forceinline__ void store8_nt(float* p, const float v[8]) {
+  st_nt(reinterpret_cast<uint4*>(p), make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                __float_as_uint(v[2]), __float_as_uint(v[3])));
+  st_nt(reinterpret_cast<uint4*>(p + 4), make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                                    __float_as_uint(v[6]), __float_as_uint(v[7])));
+}
+
+// Eight elements as raw bits (one 16-byte chunk for bf16, two for float32),
+// loaded with a streaming hint; unpacked to float32 only after a batch of
+// loads has been issued.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  uint4 q;
+  __device__ __forceinline__ void load(const bf16_t* p) { q = ld_nt(reinterpret_cast<const uint4*>(p)); }
+  __device__ __forceinline__ void get(float v[8]) const { unpack8(q, v); }
+};
+template <> struct Raw8<float> {
+  uint4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = ld_nt(reinterpret_cast<const uint4*>(p));
+    b = ld_nt(reinterpret_cast<const uint4*>(p + 4));
+  }
+  __device__ __forceinline__ void get(float v[8]) const {
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  }
+};
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

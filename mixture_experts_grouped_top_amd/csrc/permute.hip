@@ -14,7 +14,8 @@
 //              from wave ballots over the bits of the expert id (peer mask,
 //              popcount below the lane) plus per-wave counts in LDS; writes
 //              row_of_slot and slot_of_row.
-//   4. gather  one wave per destination row: copy x[token] or write zeros.
+//   4. scatter one wave per token: read x[token] once, write it to the row
+//              of each kept slot; padding rows are zeroed.
 #include "common.h"
 
 namespace moe {
@@ -163,96 +164,165 @@ __global__ __launch_bounds__(kThreads) void permute_rank_kernel(
   }
 }
 
-// One wave per destination row; nvec 16-byte vectors per row.
-__global__ __launch_bounds__(kThreads) void permute_gather_kernel(
-    const uint4* __restrict__ x, int64_t nvec, int K, const int32_t* __restrict__ slot_of_row,
-    int64_t rows, uint4* __restrict__ xs) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int s = slot_of_row[r];
-  uint4* dst = xs + r * nvec;
-  if (s < 0) {
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    for (int64_t i = lane; i < nvec; i += 64) dst[i] = z;
-    return;
-  }
-  const uint4* src = x + static_cast<int64_t>(s / K) * nvec;
-  int64_t i = lane;
-  for (; i + 192 < nvec; i += 256) {
-    const uint4 a = src[i], b = src[i + 64], c = src[i + 128], d = src[i + 192];
-    dst[i] = a; dst[i + 64] = b; dst[i + 128] = c; dst[i + 192] = d;
-  }
-  for (; i < nvec; i += 64) dst[i] = src[i];
+// Rows r of a row-major matrix (nvec 16-byte chunks per row) whose
+// slot_of_row is negative are padding: zero them, one wave per row.
+__device__ __forceinline__ void zero_padding_row(const int32_t* __restrict__ sor, int64_t r,
+                                                 int64_t rows, int64_t nvec, uint4* __restrict__ m) {
+  if (r >= rows || sor[r] >= 0) return;
+  uint4* d = m + r * nvec;
+  for (int64_t i = threadIdx.x & 63; i < nvec; i += 64) st_nt(d + i, make_uint4(0, 0, 0, 0));
 }
 
-// y[t] (+)= sum_j wt(t,j) * src[row_of_slot[t*K+j]]; one wave per token,
-// 8 elements per lane per step, float32 sums.
-template <typename T, bool WEIGHTED>
+// A token's K (<= 64) slot rows, one per lane (lane j holds row_of_slot of
+// slot j, -1 past K); readlane(v, j) then yields slot j's row as a
+// wave-uniform value.
+__device__ __forceinline__ int slot_rows(const int32_t* __restrict__ rt, int K) {
+  const int lane = threadIdx.x & 63;
+  return lane < K ? rt[lane] : -1;
+}
+__device__ __forceinline__ int lane_value(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+__device__ __forceinline__ float lane_value(float v, int j) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+}
+
+// x -> x_sorted: one wave per token reads x[t] once (kU chunks of 16 bytes
+// per lane at a time) and writes it to the row of each of its kept slots;
+// workgroups past the token range zero the padding rows.
+constexpr int kU = 4;
+__global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
+    const uint4* __restrict__ x, int64_t nvec, int64_t T, int K, const int32_t* __restrict__ ros,
+    const int32_t* __restrict__ sor, int64_t rows, uint4* __restrict__ xs, int64_t token_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (static_cast<int64_t>(blockIdx.x) >= token_blocks) {
+    zero_padding_row(sor, wid - token_blocks * (kThreads / 64), rows, nvec, xs);
+    return;
+  }
+  const int64_t t = wid;
+  if (t >= T) return;
+  const uint4* src = x + t * nvec;
+  const int rl = slot_rows(ros + t * K, K);
+  for (int64_t i0 = lane; i0 < nvec; i0 += 64 * kU) {
+    uint4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (i0 + 64 * u < nvec) v[u] = ld_nt(src + i0 + 64 * u);
+    for (int j = 0; j < K; ++j) {
+      const int r = lane_value(rl, j);
+      if (r < 0) continue;
+      uint4* dst = xs + static_cast<int64_t>(r) * nvec;
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (i0 + 64 * u < nvec) st_nt(dst + i0 + 64 * u, v[u]);
+    }
+  }
+}
+
+// y[t] (+)= sum_j wt(t,j) * src[row_of_slot[t*K+j]]: one wave per token,
+// 8 elements per lane per chunk, float32 sums in slot order.  Source rows
+// are taken in batches of kJB whose loads are all issued before they are
+// summed; a dropped slot adds 0 (it loads row 0 when src has rows).
+// kJB (1, 2, 4 or 8) is the smallest of these that is >= min(K, 8).
+template <typename T, bool WEIGHTED, int kJB>
 __global__ __launch_bounds__(kThreads) void gather_sum_kernel(
-    const T* __restrict__ src, int64_t T_, int64_t D, int K, const int32_t* __restrict__ ros,
-    const float* __restrict__ wts, T* __restrict__ dst, int accumulate) {
+    const T* __restrict__ src, int64_t rows, int64_t T_, int64_t D, int K,
+    const int32_t* __restrict__ ros, const float* __restrict__ wts, T* __restrict__ dst,
+    int accumulate) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
   if (t >= T_) return;
+  const int rl = slot_rows(ros + t * K, K);
+  const float wl = WEIGHTED ? (lane < K ? wts[t * K + lane] : 0.f) : 1.f;
   for (int64_t c = static_cast<int64_t>(lane) * 8; c < D; c += 64 * 8) {
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
     if (accumulate) load8(dst + t * D + c, acc);
-    for (int j = 0; j < K; ++j) {
-      const int r = ros[t * K + j];
-      if (r < 0) continue;
-      const float wv = WEIGHTED ? wts[t * K + j] : 1.0f;
-      float v[8];
-      load8(src + static_cast<int64_t>(r) * D + c, v);
+    // with no source rows every slot is dropped and the sum is empty
+    for (int j0 = 0; rows > 0 && j0 < K; j0 += kJB) {
+      Raw8<T> raw[kJB];
+      float wv[kJB];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = fmaf(wv, v[q], acc[q]);
+      for (int q = 0; q < kJB; ++q) {
+        const int j = j0 + q;
+        const int r = j < K ? lane_value(rl, j) : -1;
+        wv[q] = r < 0 ? 0.f : (WEIGHTED ? lane_value(wl, j) : 1.f);
+        raw[q].load(src + static_cast<int64_t>(r < 0 ? 0 : r) * D + c);
+      }
+#pragma unroll
+      for (int q = 0; q < kJB; ++q) {
+        float v[8];
+        raw[q].get(v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wv[q], v[e], acc[e]);
+      }
     }
-    store8(dst + t * D + c, acc);
+    store8_nt(dst + t * D + c, acc);
   }
 }
 
-// Row-centric combine backward: one wave per sorted row.  Blocks past the
-// row range zero d_w for dropped slots.
-template <typename T>
+// Combine backward, one wave per token: for each batch of kJB slots, dy[t]
+// is read once per chunk, d_y_sorted[row] = w dy[t] is written and
+// d_w = <dy[t], y_sorted[row]> accumulated (per lane in chunk order, then
+// summed over the wave); dropped slots get d_w = 0 and write nothing
+// (their loads read row 0, which exists whenever rows > 0).
+// Workgroups past the token range zero the padding rows of d_y_sorted.
+template <typename T, int kJB>
 __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
-    const T* __restrict__ dy, const T* __restrict__ ys, int64_t D, int K, int64_t rows,
-    int64_t TK, const int32_t* __restrict__ ros, const int32_t* __restrict__ sor,
+    const T* __restrict__ dy, const T* __restrict__ ys, int64_t T_, int64_t D, int K,
+    const int32_t* __restrict__ ros, const int32_t* __restrict__ sor, int64_t rows,
     const float* __restrict__ wts, T* __restrict__ d_ys, float* __restrict__ d_w,
-    int64_t row_blocks) {
+    int64_t token_blocks) {
   const int lane = threadIdx.x & 63;
-  if (blockIdx.x >= row_blocks) {
-    const int64_t s = (static_cast<int64_t>(blockIdx.x) - row_blocks) * kThreads + threadIdx.x;
-    if (s < TK && ros[s] < 0) d_w[s] = 0.f;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (static_cast<int64_t>(blockIdx.x) >= token_blocks) {
+    zero_padding_row(sor, wid - token_blocks * (kThreads / 64), rows,
+                     D * static_cast<int64_t>(sizeof(T)) / 16, reinterpret_cast<uint4*>(d_ys));
     return;
   }
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int s = sor[r];
-  T* out = d_ys + r * D;
-  if (s < 0) {
-    float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int64_t c = static_cast<int64_t>(lane) * 8; c < D; c += 512) store8(out + c, z);
-    return;
-  }
-  const float wv = wts[s];
-  const T* g = dy + static_cast<int64_t>(s / K) * D;
-  const T* yr = ys + r * D;
-  float dot = 0.f;
-  for (int64_t c = static_cast<int64_t>(lane) * 8; c < D; c += 512) {
-    float a[8], b[8], o[8];
-    load8(g + c, a);
-    load8(yr + c, b);
+  const int64_t t = wid;
+  if (t >= T_) return;
+  const int rl = slot_rows(ros + t * K, K);
+  const float wl = lane < K ? wts[t * K + lane] : 0.f;
+  const T* g = dy + t * D;
+  for (int j0 = 0; j0 < K; j0 += kJB) {
+    int r[kJB];
+    float wv[kJB], dot[kJB];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      o[q] = wv * a[q];
-      dot = fmaf(a[q], b[q], dot);
+    for (int q = 0; q < kJB; ++q) {
+      const int j = j0 + q;
+      r[q] = j < K ? lane_value(rl, j) : -1;
+      wv[q] = r[q] >= 0 ? lane_value(wl, j) : 0.f;
+      dot[q] = 0.f;
     }
-    store8(out + c, o);
+    // with no rows every slot is dropped: only d_w = 0 is written
+    for (int64_t c = static_cast<int64_t>(lane) * 8; rows > 0 && c < D; c += 512) {
+      float a[8];
+      Raw8<T> raw[kJB];
+      load8(g + c, a);
+#pragma unroll
+      for (int q = 0; q < kJB; ++q)
+        raw[q].load(ys + static_cast<int64_t>(r[q] < 0 ? 0 : r[q]) * D + c);
+#pragma unroll
+      for (int q = 0; q < kJB; ++q) {
+        if (r[q] < 0) continue;
+        float b[8], o[8];
+        raw[q].get(b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[e] = wv[q] * a[e];
+          dot[q] = fmaf(a[e], b[e], dot[q]);
+        }
+        store8_nt(d_ys + static_cast<int64_t>(r[q]) * D + c, o);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kJB; ++q) {
+      if (j0 + q >= K) break;
+      const float sdot = wave_sum(dot[q]);
+      if (lane == 0) d_w[t * K + j0 + q] = r[q] >= 0 ? sdot : 0.f;
+    }
   }
-  dot = wave_sum(dot);
-  if (lane == 0) d_w[s] = dot;
 }
 
 }  // namespace
@@ -321,28 +391,69 @@ MOE_API int moe_permute(const void* x, int dtype, int64_t T, int64_t D, const in
                        slot_of_row);
   if (x_sorted && rows > 0 && D > 0) {
     const int64_t nvec = D * eb / 16;
-    const int64_t blocks = (rows + 3) / 4;
-    hipLaunchKernelGGL(permute_gather_kernel, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, st, static_cast<const uint4*>(x), nvec, K, slot_of_row,
-                       rows, static_cast<uint4*>(x_sorted));
+    const int64_t token_blocks = (T + 3) / 4;
+    const int64_t blocks = token_blocks + (rows + 3) / 4;
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, st, static_cast<const uint4*>(x), nvec, T, K,
+                       row_of_slot, slot_of_row, rows, static_cast<uint4*>(x_sorted),
+                       token_blocks);
   }
   return launch_status();
 }
 
+// Slot batch of the token-centric kernels for top-K routing.
+static int slot_batch(int K) { return K <= 1 ? 1 : K <= 2 ? 2 : K <= 4 ? 4 : 8; }
+
+template <typename T, bool W>
+static void launch_gather_sum(int jb, unsigned blocks, hipStream_t st, const void* src,
+                              int64_t rows, int64_t T_, int64_t D, int K, const int32_t* ros,
+                              const float* w, void* dst, int accumulate) {
+  const T* s = static_cast<const T*>(src);
+  T* d = static_cast<T*>(dst);
+#define GS(JB)                                                                             \
+  hipLaunchKernelGGL((gather_sum_kernel<T, W, JB>), dim3(blocks), dim3(kThreads), 0, st, s, \
+                     rows, T_, D, K, ros, w, d, accumulate)
+  switch (jb) {
+    case 1: GS(1); break;
+    case 2: GS(2); break;
+    case 4: GS(4); break;
+    default: GS(8); break;
+  }
+#undef GS
+}
+
 template <bool W>
-static int gather_sum(const void* src, int dtype, int64_t T, int64_t D, int K,
+static int gather_sum(const void* src, int dtype, int64_t rows, int64_t T, int64_t D, int K,
                       const int32_t* ros, const float* w, void* dst, int accumulate,
                       hipStream_t st) {
   const unsigned blocks = static_cast<unsigned>((T + 3) / 4);
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL((gather_sum_kernel<bf16_t, W>), dim3(blocks), dim3(kThreads), 0, st,
-                       static_cast<const bf16_t*>(src), T, D, K, ros, w,
-                       static_cast<bf16_t*>(dst), accumulate);
+    launch_gather_sum<bf16_t, W>(slot_batch(K), blocks, st, src, rows, T, D, K, ros, w, dst,
+                                 accumulate);
   else
-    hipLaunchKernelGGL((gather_sum_kernel<float, W>), dim3(blocks), dim3(kThreads), 0, st,
-                       static_cast<const float*>(src), T, D, K, ros, w, static_cast<float*>(dst),
-                       accumulate);
+    launch_gather_sum<float, W>(slot_batch(K), blocks, st, src, rows, T, D, K, ros, w, dst,
+                                accumulate);
   return launch_status();
+}
+
+template <typename T>
+static void launch_combine_bwd(int jb, unsigned grid, hipStream_t st, const void* d_y,
+                               const void* y_sorted, int64_t T_, int64_t D, int K,
+                               const int32_t* ros, const int32_t* sor, int64_t rows,
+                               const float* w, void* d_ys, float* d_w, int64_t token_blocks) {
+  const T* a = static_cast<const T*>(d_y);
+  const T* b = static_cast<const T*>(y_sorted);
+  T* o = static_cast<T*>(d_ys);
+#define CB(JB)                                                                            \
+  hipLaunchKernelGGL((combine_bwd_kernel<T, JB>), dim3(grid), dim3(kThreads), 0, st, a, b, \
+                     T_, D, K, ros, sor, rows, w, o, d_w, token_blocks)
+  switch (jb) {
+    case 1: CB(1); break;
+    case 2: CB(2); break;
+    case 4: CB(4); break;
+    default: CB(8); break;
+  }
+#undef CB
 }
 
 MOE_API int moe_permute_bwd(const void* d_x_sorted, int dtype, int64_t T, int64_t D, int K,
@@ -353,8 +464,8 @@ MOE_API int moe_permute_bwd(const void* d_x_sorted, int dtype, int64_t T, int64_
   if (T == 0 || D == 0) return MOE_OK;
   if (!d_x_sorted || !row_of_slot || !d_x || D % 8 || !aligned16(d_x_sorted) || !aligned16(d_x))
     return MOE_ERR_ARG;
-  return gather_sum<false>(d_x_sorted, dtype, T, D, K, row_of_slot, nullptr, d_x, accumulate,
-                           static_cast<hipStream_t>(stream));
+  return gather_sum<false>(d_x_sorted, dtype, rows, T, D, K, row_of_slot, nullptr, d_x,
+                           accumulate, static_cast<hipStream_t>(stream));
 }
 
 MOE_API int moe_combine(const void* y_sorted, int dtype, int64_t T, int64_t D, int K,
@@ -366,7 +477,7 @@ MOE_API int moe_combine(const void* y_sorted, int dtype, int64_t T, int64_t D, i
   if (!y_sorted || !row_of_slot || !topk_w || !y || D % 8 || !aligned16(y_sorted) ||
       !aligned16(y))
     return MOE_ERR_ARG;
-  return gather_sum<true>(y_sorted, dtype, T, D, K, row_of_slot, topk_w, y, 0,
+  return gather_sum<true>(y_sorted, dtype, rows, T, D, K, row_of_slot, topk_w, y, 0,
                           static_cast<hipStream_t>(stream));
 }
 
@@ -380,21 +491,15 @@ MOE_API int moe_combine_bwd(const void* d_y, const void* y_sorted, int dtype, in
     return (T == 0 && rows == 0) ? MOE_OK : MOE_ERR_ARG;
   if (D % 8 || !aligned16(d_y) || !aligned16(y_sorted) || !aligned16(d_y_sorted))
     return MOE_ERR_ARG;
-  const int64_t TK = T * K;
-  const int64_t row_blocks = (rows + 3) / 4;
-  const int64_t slot_blocks = (TK + kThreads - 1) / kThreads;
-  const unsigned grid = static_cast<unsigned>(row_blocks + slot_blocks);
+  const int64_t token_blocks = (T + 3) / 4;
+  const unsigned grid = static_cast<unsigned>(token_blocks + (rows + 3) / 4);
   if (grid == 0) return MOE_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bwd_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const bf16_t*>(d_y), static_cast<const bf16_t*>(y_sorted), D,
-                       K, rows, TK, row_of_slot, slot_of_row, topk_w,
-                       static_cast<bf16_t*>(d_y_sorted), d_topk_w, row_blocks);
+    launch_combine_bwd<bf16_t>(slot_batch(K), grid, st, d_y, y_sorted, T, D, K, row_of_slot,
+                               slot_of_row, rows, topk_w, d_y_sorted, d_topk_w, token_blocks);
   else
-    hipLaunchKernelGGL(combine_bwd_kernel<float>, dim3(grid), dim3(kThreads), 0, st,
-                       static_cast<const float*>(d_y), static_cast<const float*>(y_sorted), D, K,
-                       rows, TK, row_of_slot, slot_of_row, topk_w,
-                       static_cast<float*>(d_y_sorted), d_topk_w, row_blocks);
+    launch_combine_bwd<float>(slot_batch(K), grid, st, d_y, y_sorted, T, D, K, row_of_slot,
+                              slot_of_row, rows, topk_w, d_y_sorted, d_topk_w, token_blocks);
   return launch_status();
 }

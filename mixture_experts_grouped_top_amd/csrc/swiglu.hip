@@ -1,5 +1,5 @@
 // SwiGLU gating of the expert FFN and its backward, elementwise over
-// [rows, F] with 8 elements per thread per step (HBM-bound).  The two inputs
+// [rows, F], two groups of 8 elements per thread per step (HBM-bound).  The two inputs
 // are the gate and up projection outputs named in the TransformerEngine MoE
 // block pull request's commit notes (gate_proj_out, up_proj_out).
 #include "common.h"
@@ -7,18 +7,37 @@
 namespace moe {
 namespace {
 
+// Grid-stride over groups of kU x 8 elements per thread: all loads of a
+// group are issued (streaming hint) before any is used.
+constexpr int kU = 2;
+
 template <typename TH, typename TA>
 __global__ __launch_bounds__(256) void swiglu_kernel(const TH* __restrict__ h0,
                                                      const TH* __restrict__ h1, int64_t n8,
                                                      TA* __restrict__ act) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    float a[8], b[8], o[8];
-    load8(h0 + i * 8, a);
-    load8(h1 + i * 8, b);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256 * kU;
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 * kU + threadIdx.x; i0 < n8;
+       i0 += stride) {
+    Raw8<TH> ra[kU], rb[kU];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) o[q] = a[q] / (1.0f + expf(-a[q])) * b[q];
-    store8(act + i * 8, o);
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + 256 * u;
+      if (i < n8) {
+        ra[u].load(h0 + i * 8);
+        rb[u].load(h1 + i * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + 256 * u;
+      if (i >= n8) break;
+      float a[8], b[8], o[8];
+      ra[u].get(a);
+      rb[u].get(b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] = a[q] / (1.0f + expf(-a[q])) * b[q];
+      store8_nt(act + i * 8, o);
+    }
   }
 }
 
@@ -28,25 +47,42 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const TH* __restrict__ 
                                                          const TD* __restrict__ da, int64_t n8,
                                                          TD* __restrict__ d0,
                                                          TD* __restrict__ d1) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n8;
-       i += static_cast<int64_t>(gridDim.x) * 256) {
-    float a[8], b[8], g[8], o0[8], o1[8];
-    load8(h0 + i * 8, a);
-    load8(h1 + i * 8, b);
-    load8(da + i * 8, g);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256 * kU;
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 * kU + threadIdx.x; i0 < n8;
+       i0 += stride) {
+    Raw8<TH> ra[kU], rb[kU];
+    Raw8<TD> rg[kU];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float s = 1.0f / (1.0f + expf(-a[q]));
-      o0[q] = g[q] * b[q] * s * (1.0f + a[q] * (1.0f - s));
-      o1[q] = g[q] * a[q] * s;
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + 256 * u;
+      if (i < n8) {
+        ra[u].load(h0 + i * 8);
+        rb[u].load(h1 + i * 8);
+        rg[u].load(da + i * 8);
+      }
     }
-    store8(d0 + i * 8, o0);
-    store8(d1 + i * 8, o1);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + 256 * u;
+      if (i >= n8) break;
+      float a[8], b[8], g[8], o0[8], o1[8];
+      ra[u].get(a);
+      rb[u].get(b);
+      rg[u].get(g);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float s = 1.0f / (1.0f + expf(-a[q]));
+        o0[q] = g[q] * b[q] * s * (1.0f + a[q] * (1.0f - s));
+        o1[q] = g[q] * a[q] * s;
+      }
+      store8_nt(d0 + i * 8, o0);
+      store8_nt(d1 + i * 8, o1);
+    }
   }
 }
 
 unsigned grid_for(int64_t n8) {
-  int64_t g = (n8 + 255) / 256;
+  int64_t g = (n8 + 256 * kU - 1) / (256 * kU);
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 16;
   if (g > cap) g = cap;
   return static_cast<unsigned>(g < 1 ? 1 : g);
