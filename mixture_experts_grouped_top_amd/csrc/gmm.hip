@@ -250,6 +250,11 @@ struct Operand {
   __device__ __forceinline__ const bf16_t* step_base(int kt) const {
     return COLK ? base + static_cast<int64_t>(kt) * TK * ld : base + static_cast<int64_t>(kt) * TK;
   }
+  // DMA instruction j (< NJ) of step kt; sb = uniform_ptr(step_base(kt)).
+  __device__ __forceinline__ void dma_one(const void* sb, int j, uint32_t lds) const {
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    dma16(sb, voff[j], lds + (w * NJ + j) * 1024);
+  }
   __device__ __forceinline__ void dma(int kt, uint32_t lds) const {
     const void* sb = uniform_ptr(step_base(kt));
     const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -350,6 +355,20 @@ struct Acc {
 #pragma unroll
     for (int j = 0; j < FN; ++j) f.b[j] = OB::frag(Bs, fb, j, sub);
   }
+  template <class OA>
+  __device__ __forceinline__ static void load_a(Frags& f, const char* As, const uint32_t (&fa)[4],
+                                                int i, int sub) {
+    f.a[i] = OA::frag(As, fa, i, sub);
+  }
+  template <class OB>
+  __device__ __forceinline__ static void load_b(Frags& f, const char* Bs, const uint32_t (&fb)[4],
+                                                int j, int sub) {
+    f.b[j] = OB::frag(Bs, fb, j, sub);
+  }
+  __device__ __forceinline__ void mma_one(const Frags& f, int q) {
+    const int i = q / FN, j = q % FN;
+    v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], v[i][j], 0, 0, 0);
+  }
   __device__ __forceinline__ void mma(const Frags& f) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -433,8 +452,21 @@ __device__ __forceinline__ void contract(char* lds, const OA& A, const OB& B, in
   for (int s = 0; s < nfull; ++s) {
     const int cur = s % NS;
     char* cs = lds + cur * SB;
-    ACC::template load<OA, OB>(f1, cs, cs + OA::kBytes, fa, fb, 1);
-    acc.mma(f0);
+    {
+      // MFMAs(s, 0) with the fragment reads of (s, 1) spread between them
+      constexpr int NM = ACC::FM * ACC::FN;
+      constexpr int NO = ACC::FM + ACC::FN;
+#pragma unroll
+      for (int q = 0; q < NM; ++q) {
+        acc.mma_one(f0, q);
+#pragma unroll
+        for (int o = q * NO / NM; o < (q + 1) * NO / NM; ++o) {
+          if (o < ACC::FM) ACC::template load_a<OA>(f1, cs, fa, o, 1);
+          else ACC::template load_b<OB>(f1, cs + OA::kBytes, fb, o - ACC::FM, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     if (s + 1 < nfull) {
       // stages s + 2 .. s + NS - 1 may still be in flight; s + 1 must have landed
       const int later = min(NS - 2, nfull - 2 - s);
@@ -442,11 +474,32 @@ __device__ __forceinline__ void contract(char* lds, const OA& A, const OB& B, in
       else if (later == 1) wait_vmcnt<PER>();
       else wait_vmcnt<0>();
       __syncthreads();
-      if (s + NS < nfull) {
-        A.dma(s + NS, lds_addr(cs));
-        B.dma(s + NS, lds_addr(cs + OA::kBytes));
-      }
       char* ns = lds + ((s + 1) % NS) * SB;
+      if (s + NS < nfull) {
+        // MFMAs(s, 1) with the DMA of stage s + NS and the fragment reads of
+        // (s + 1, 0) spread between them, in this order: each DMA issue,
+        // which can wait for room in the load queue, then sits behind a
+        // running MFMA instead of idling the matrix unit
+        const void* sa = uniform_ptr(A.step_base(s + NS));
+        const void* sb = uniform_ptr(B.step_base(s + NS));
+        const uint32_t la = lds_addr(cs), lb = lds_addr(cs + OA::kBytes);
+        constexpr int NM = ACC::FM * ACC::FN;
+        constexpr int NO = OA::NJ + OB::NJ + ACC::FM + ACC::FN;
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          acc.mma_one(f1, q);
+#pragma unroll
+          for (int o = q * NO / NM; o < (q + 1) * NO / NM; ++o) {
+            if (o < ACC::FM) ACC::template load_a<OA>(f0, ns, fa, o, 0);
+            else if (o < ACC::FM + ACC::FN)
+              ACC::template load_b<OB>(f0, ns + OA::kBytes, fb, o - ACC::FM, 0);
+            else if (o < ACC::FM + ACC::FN + OA::NJ) A.dma_one(sa, o - ACC::FM - ACC::FN, la);
+            else B.dma_one(sb, o - ACC::FM - ACC::FN - OA::NJ, lb);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
+      }
       ACC::template load<OA, OB>(f0, ns, ns + OA::kBytes, fa, fb, 0);
     }
     acc.mma(f1);
