@@ -218,6 +218,9 @@ template <bool COLK, int BX>
 struct Operand {
   static constexpr int kBytes = BX * TK * 2;
   static constexpr int NJ = kBytes / 1024 / 4;   // DMA instructions per wave per stage
+  static constexpr bool kPair = false;           // one DMA unit = one step
+  static constexpr int kUnit = kBytes;
+  static constexpr int NJU = NJ;
   static constexpr int NR = kBytes / 16 / NT;    // 16-byte chunks per thread (register path)
   const bf16_t* base;
   int64_t ld;
@@ -327,6 +330,83 @@ struct Operand {
       const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       return __builtin_bit_cast(bf16x8, v);
     }
+  }
+};
+
+// A contraction-contiguous ("row") operand of BX rows loaded in units of two
+// steps: each DMA lane copies 16 bytes of a 128-byte row segment (two
+// steps of 32 elements), so every request is a whole 128-byte line instead
+// of half of one.  LDS unit layout [x][64]: row x at 128 x bytes, 16-byte
+// chunk c at (c ^ (x & 7)), so the 8 rows that one ds_read_b128 phase
+// serves hit distinct banks.  Substep sub (0..3) of a unit covers
+// contraction elements 16 sub .. 16 sub + 15.
+template <int BX>
+struct PairRow {
+  static constexpr int kBytes = BX * TK * 2;     // one step
+  static constexpr int NJ = kBytes / 1024 / 4;
+  static constexpr bool kPair = true;
+  static constexpr int kUnit = 2 * kBytes;
+  static constexpr int NJU = 2 * NJ;             // DMA instructions per wave per unit
+  static constexpr int NR = kBytes / 16 / NT;    // register path: 16-byte chunks per thread
+  const bf16_t* base;
+  int64_t ld;
+  int xv;
+  uint32_t voff[NJU];
+
+  __device__ __forceinline__ static int off(int x, int c) { return x * 128 + ((c ^ (x & 7)) << 4); }
+  __device__ __forceinline__ void setup(const bf16_t* b, int64_t ld_, int xv_) {
+    base = b;
+    ld = ld_;
+    xv = xv_;
+    const int tid = opaque_tid();
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int j = 0; j < NJU; ++j) {
+      const int byte = (w * NJU + j) * 1024 + lane * 16;
+      const int x = byte >> 7;
+      const int c = ((byte & 127) >> 4) ^ (x & 7);
+      const int xx = x < xv ? x : xv - 1;
+      voff[j] = static_cast<uint32_t>((xx * ld + c * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ const bf16_t* step_base(int kt) const {
+    return base + static_cast<int64_t>(kt) * TK;
+  }
+  // DMA instruction j (< NJU) of the unit starting at step kt (even);
+  // sb = uniform_ptr(step_base(kt)).
+  __device__ __forceinline__ void dma_one(const void* sb, int j, uint32_t lds) const {
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    dma16(sb, voff[j], lds + (w * NJU + j) * 1024);
+  }
+  // Ragged last step (kv < TK elements) into the first half of a unit.
+  __device__ __forceinline__ void tail_load(int kt, int kv, uint4 (&r)[NR]) const {
+    const bf16_t* b = step_base(kt);
+    const int tid = opaque_tid();
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int q = tid + i * NT;
+      const int x = q / kCPR, c = q % kCPR;
+      const bool ok = x < xv && c * 8 < kv;
+      r[i] = ok ? *reinterpret_cast<const uint4*>(b + x * ld + c * 8) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void tail_store(char* lds, const uint4 (&r)[NR]) const {
+    const int tid = opaque_tid();
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int q = tid + i * NT;
+      *reinterpret_cast<uint4*>(lds + off(q / kCPR, q % kCPR)) = r[i];
+    }
+  }
+  // Fragment (i, sub): x = xw + 32 i + lane % 32, chunk 2 sub + lane / 32;
+  // the swizzle term (x & 7) does not depend on i.
+  __device__ __forceinline__ static void frag_base(int xw, uint32_t (&fb)[4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) fb[t] = static_cast<uint32_t>(off(xw + (lane & 31), 2 * t + (lane >> 5)));
+  }
+  __device__ __forceinline__ static bf16x8 frag(const char* lds, const uint32_t (&fb)[4], int i, int sub) {
+    return *reinterpret_cast<const bf16x8*>(lds + fb[sub] + i * 32 * 128);
   }
 };
 
@@ -527,6 +607,195 @@ __device__ __forceinline__ void contract(char* lds, const OA& A, const OB& B, in
   __syncthreads();   // every wave is done with all stages before they are refilled
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n <= N (a chain of constant waits).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= N) wait_vmcnt<N>();
+    else wait_vmcnt_dyn<N - 1>(n);
+  }
+}
+
+// MFMAs of one substep (q = 0 .. NM-1) with NO other operations spread
+// between them in order, pinned there with scheduling barriers.
+template <int NM, int NO, class M, class O>
+__device__ __forceinline__ void interleave(M&& mma, O&& op) {
+#pragma unroll
+  for (int q = 0; q < NM; ++q) {
+    mma(q);
+#pragma unroll
+    for (int o = q * NO / NM; o < (q + 1) * NO / NM; ++o) op(o);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Contraction with a pair-loaded lhs (PairRow) and an rhs that is either
+// pair-loaded too or a per-step col operand, over a four-step LDS ring:
+// A holds two units of two steps, B two such units or four single steps.
+// The unit of a pair operand is free once both of its steps are consumed,
+// so the pair for steps t + 3, t + 4 is issued after the barrier of odd
+// steps t; a single-step B unit gets step t + 4 after every step t.  Every
+// block is issued, also past the last step (it then re-reads the last
+// valid unit into a unit that is no longer read), so each wait count is a
+// constant.  Requires an even number (>= 2) of full steps; a ragged rest
+// goes through registers into the first half of the next unit.
+template <class PA, class OB, class ACC>
+__device__ __forceinline__ void contract2(char* lds, const PA& A, const OB& B, int64_t Kc,
+                                          ACC& acc, const uint32_t (&fa)[4],
+                                          const uint32_t (&fb)[4]) {
+  constexpr bool BP = OB::kPair;
+  constexpr int UA = PA::kUnit, UB = OB::kUnit;
+  constexpr int JA = PA::NJU, JB = OB::NJU;
+  constexpr int NM = ACC::FM * ACC::FN;
+  // vmcnt entries a wave may leave in flight when it needs the next step:
+  // after an even step the pair issued with the last odd block plus the
+  // later single-step blocks; after an odd step only later blocks
+  constexpr int W_EVEN = BP ? JA + JB : JA + 2 * JB;
+  constexpr int W_ODD = BP ? 0 : 2 * JB;
+  constexpr int W_PRO = BP ? JA + JB : JA + 3 * JB;
+  static_assert(W_PRO < 64, "vmcnt range");
+  char* const la = lds;
+  char* const lb = lds + 2 * UA;
+  const int nfull = static_cast<int>(Kc / TK);
+  const int kv = static_cast<int>(Kc - static_cast<int64_t>(nfull) * TK);
+  auto aU = [&](int st) { return la + ((st >> 1) & 1) * UA; };
+  auto bU = [&](int st) { return BP ? lb + ((st >> 1) & 1) * UB : lb + (st & 3) * UB; };
+  // source step of a DMA unit, clamped to the last valid unit
+  auto pair_src = [&](int st) { return st < nfull ? st : nfull - 2; };
+  auto step_src = [&](int st) { return st < nfull ? st : nfull - 1; };
+  // the DMA block of (virtual) step t, all at once (prologue)
+  auto block = [&](int t) {
+    if (t & 1) {
+      const void* sa = uniform_ptr(A.step_base(pair_src(t + 3)));
+      const uint32_t l = lds_addr(aU(t + 3));
+#pragma unroll
+      for (int j = 0; j < JA; ++j) A.dma_one(sa, j, l);
+      if constexpr (BP) {
+        const void* sb = uniform_ptr(B.step_base(pair_src(t + 3)));
+        const uint32_t m = lds_addr(bU(t + 3));
+#pragma unroll
+        for (int j = 0; j < JB; ++j) B.dma_one(sb, j, m);
+      }
+    }
+    if constexpr (!BP) {
+      const void* sb = uniform_ptr(B.step_base(step_src(t + 4)));
+      const uint32_t m = lds_addr(bU(t + 4));
+#pragma unroll
+      for (int j = 0; j < JB; ++j) B.dma_one(sb, j, m);
+    }
+  };
+  typename ACC::Frags f0, f1;
+  acc.zero();
+  __builtin_amdgcn_s_waitcnt(0);            // nothing from the previous tile is in flight
+  if (nfull == 0) {
+    // only a ragged step: nothing to pipeline
+  } else {
+    for (int t = -4; t < 0; ++t) block(t);
+    wait_vmcnt<W_PRO>();                     // step 0 (A pair of block -3, B of block -4)
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ACC::FM; ++i) ACC::template load_a<PA>(f0, aU(0), fa, i, 0);
+#pragma unroll
+    for (int j = 0; j < ACC::FN; ++j) ACC::template load_b<OB>(f0, bU(0), fb, j, 0);
+    // MFMAs(s, 0) with the fragment reads of (s, 1); P is the parity of s
+    auto first_half = [&](auto par, int s) {
+      constexpr int P = decltype(par)::value;
+      constexpr int sa1 = 2 * P + 1, sb1 = BP ? 2 * P + 1 : 1;
+      char* const ua = aU(s);
+      char* const ub = bU(s);
+      interleave<NM, ACC::FM + ACC::FN>(
+          [&](int q) { acc.mma_one(f0, q); },
+          [&](int o) {
+            if (o < ACC::FM) ACC::template load_a<PA>(f1, ua, fa, o, sa1);
+            else ACC::template load_b<OB>(f1, ub, fb, o - ACC::FM, sb1);
+          });
+    };
+    // wait for step s + 1, barrier, then MFMAs(s, 1) with the fragment reads
+    // of (s + 1, 0) and the DMA block of step s (all waves are done with
+    // step s: its units may refill)
+    auto second_half = [&](auto par, int s) {
+      constexpr int P = decltype(par)::value;
+      constexpr int na0 = 2 * (1 - P), nb0 = BP ? 2 * (1 - P) : 0;
+      if constexpr (P == 1) wait_vmcnt<W_ODD>(); else wait_vmcnt<W_EVEN>();
+      __syncthreads();
+      char* const na = aU(s + 1);
+      char* const nb = bU(s + 1);
+      if constexpr (P == 1) {
+        const void* sa = uniform_ptr(A.step_base(pair_src(s + 3)));
+        const uint32_t da = lds_addr(aU(s + 3));
+        const void* sb = uniform_ptr(B.step_base(BP ? pair_src(s + 3) : step_src(s + 4)));
+        const uint32_t db = lds_addr(bU(BP ? s + 3 : s + 4));
+        constexpr int NO = ACC::FM + ACC::FN + JA + JB;
+        interleave<NM, NO>([&](int q) { acc.mma_one(f1, q); },
+                           [&](int o) {
+                             if (o < ACC::FM) ACC::template load_a<PA>(f0, na, fa, o, na0);
+                             else if (o < ACC::FM + ACC::FN)
+                               ACC::template load_b<OB>(f0, nb, fb, o - ACC::FM, nb0);
+                             else if (o < ACC::FM + ACC::FN + JA)
+                               A.dma_one(sa, o - ACC::FM - ACC::FN, da);
+                             else
+                               B.dma_one(sb, o - ACC::FM - ACC::FN - JA, db);
+                           });
+      } else {
+        const void* sb = uniform_ptr(B.step_base(BP ? 0 : step_src(s + 4)));
+        const uint32_t db = lds_addr(bU(s + 4));
+        constexpr int NO = ACC::FM + ACC::FN + (BP ? 0 : JB);
+        interleave<NM, NO>([&](int q) { acc.mma_one(f1, q); },
+                           [&](int o) {
+                             if (o < ACC::FM) ACC::template load_a<PA>(f0, na, fa, o, na0);
+                             else if (o < ACC::FM + ACC::FN)
+                               ACC::template load_b<OB>(f0, nb, fb, o - ACC::FM, nb0);
+                             else if constexpr (!BP) B.dma_one(sb, o - ACC::FM - ACC::FN, db);
+                           });
+      }
+    };
+    const std::integral_constant<int, 0> even;
+    const std::integral_constant<int, 1> odd;
+    for (int s = 0; s + 2 < nfull; s += 2) {
+      first_half(even, s);
+      second_half(even, s);
+      first_half(odd, s + 1);
+      second_half(odd, s + 1);
+    }
+    first_half(even, nfull - 2);
+    second_half(even, nfull - 2);
+    first_half(odd, nfull - 1);
+    acc.mma(f1);
+    wait_vmcnt<0>();   // the re-reads issued past the last step have landed
+  }
+  if (kv > 0) {
+    // the units of step nfull held steps nfull - 4 (.. nfull - 3), long
+    // consumed; nothing is in flight
+    {
+      uint4 t[PA::NR];
+      A.tail_load(nfull, kv, t);
+      A.tail_store(aU(nfull), t);
+    }
+    {
+      uint4 t[OB::NR];
+      B.tail_load(nfull, kv, t);
+      B.tail_store(bU(nfull), t);
+    }
+    __syncthreads();
+    // nfull is even: the tail sits at substeps 0 and 1 of its units
+#pragma unroll
+    for (int i = 0; i < ACC::FM; ++i) {
+      ACC::template load_a<PA>(f0, aU(nfull), fa, i, 0);
+      ACC::template load_a<PA>(f1, aU(nfull), fa, i, 1);
+    }
+#pragma unroll
+    for (int j = 0; j < ACC::FN; ++j) {
+      ACC::template load_b<OB>(f0, bU(nfull), fb, j, 0);
+      ACC::template load_b<OB>(f1, bU(nfull), fb, j, 1);
+    }
+    acc.mma(f0);
+    acc.mma(f1);
+  }
+  __syncthreads();   // every wave is done with all units before they are refilled
+}
+
 // Stages and LDS bytes of a TM x TN tile (128-row tiles keep three stages
 // so that two workgroups fit in one CU's LDS).
 template <int TM, int TN>
@@ -598,8 +867,11 @@ struct MaxG {
   static constexpr int value = TM <= 128 ? kMaxGShort : kMaxG;
 };
 
-template <bool B_COLK, int TM, int TN, typename TO>
+template <bool B_COLK, int TM, int TN, typename TO, bool PAIR>
 __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArgs a) {
+  static_assert(!PAIR || Stages<TM, TN>::NS == 4, "pair loading uses the four-step ring");
+  using OA = std::conditional_t<PAIR, PairRow<TM>, Operand<false, TM>>;
+  using OB = std::conditional_t<PAIR && !B_COLK, PairRow<TN>, Operand<B_COLK, TN>>;
   __shared__ __attribute__((aligned(1024))) char smem[Stages<TM, TN>::kBytes];
   __shared__ int row_base[MaxG<TM>::value + 1];
   __shared__ int tile_base[MaxG<TM>::value + 1];
@@ -608,12 +880,12 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
   __syncthreads();
   const int total = tile_base[a.G];
   TO* out = static_cast<TO*>(a.out);
-  Operand<false, TM> A;
-  Operand<B_COLK, TN> B;
+  OA A;
+  OB B;
   Acc<TM, TN> acc;
   uint32_t fa[4], fb[4];
-  Operand<false, TM>::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
-  Operand<B_COLK, TN>::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
+  OA::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
+  OB::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
   for (int it = 0;; ++it) {
     const int64_t tile = xcd_tile(it);
     if (tile >= total) break;
@@ -635,7 +907,8 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
     A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, rv);
     const bf16_t* bg = a.rhs + g * a.rhs_gs;
     B.setup(B_COLK ? bg + col0 : bg + col0 * a.ld_rhs, a.ld_rhs, cv);
-    contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
+    if constexpr (PAIR) contract2(smem, A, B, a.Kdim, acc, fa, fb);
+    else contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
     store_tile(acc, smem, out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate);
   }
   if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
@@ -861,27 +1134,37 @@ MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* 
     const int TNv = narrow ? 128 : 256;
     const int64_t upper = ((M_out + TMv - 1) / TMv + G) * ((N + TNv - 1) / TNv);
     const unsigned grid = persistent_grid(upper, short_m ? 2 : 1);
-#define GMM(BC, TMV, TNV, TO) \
-  hipLaunchKernelGGL((gmm_mfma_kernel<BC, TMV, TNV, TO>), dim3(grid), dim3(NT), 0, st, a)
+    // 256-row tiles load row operands as 128-byte segments (two steps per
+    // DMA unit) when the number of full contraction steps is even
+    const int64_t nsteps = Kdim / TK;
+    const bool pair = !short_m && nsteps >= 2 && nsteps % 2 == 0;
+#define GMM(BC, TMV, TNV, TO, P) \
+  hipLaunchKernelGGL((gmm_mfma_kernel<BC, TMV, TNV, TO, P>), dim3(grid), dim3(NT), 0, st, a)
+#define GMM2(BC, TMV, TNV, TO)          \
+  do {                                  \
+    if (pair) GMM(BC, TMV, TNV, TO, true); \
+    else GMM(BC, TMV, TNV, TO, false);  \
+  } while (0)
     if (narrow) {
       if (trans_rhs) {
-        if (out_dtype == MOE_BF16) GMM(false, 256, 128, bf16_t); else GMM(false, 256, 128, float);
+        if (out_dtype == MOE_BF16) GMM2(false, 256, 128, bf16_t); else GMM2(false, 256, 128, float);
       } else {
-        if (out_dtype == MOE_BF16) GMM(true, 256, 128, bf16_t); else GMM(true, 256, 128, float);
+        if (out_dtype == MOE_BF16) GMM2(true, 256, 128, bf16_t); else GMM2(true, 256, 128, float);
       }
     } else if (short_m) {
       if (trans_rhs) {
-        if (out_dtype == MOE_BF16) GMM(false, 128, 256, bf16_t); else GMM(false, 128, 256, float);
+        if (out_dtype == MOE_BF16) GMM(false, 128, 256, bf16_t, false); else GMM(false, 128, 256, float, false);
       } else {
-        if (out_dtype == MOE_BF16) GMM(true, 128, 256, bf16_t); else GMM(true, 128, 256, float);
+        if (out_dtype == MOE_BF16) GMM(true, 128, 256, bf16_t, false); else GMM(true, 128, 256, float, false);
       }
     } else {
       if (trans_rhs) {
-        if (out_dtype == MOE_BF16) GMM(false, 256, 256, bf16_t); else GMM(false, 256, 256, float);
+        if (out_dtype == MOE_BF16) GMM2(false, 256, 256, bf16_t); else GMM2(false, 256, 256, float);
       } else {
-        if (out_dtype == MOE_BF16) GMM(true, 256, 256, bf16_t); else GMM(true, 256, 256, float);
+        if (out_dtype == MOE_BF16) GMM2(true, 256, 256, bf16_t); else GMM2(true, 256, 256, float);
       }
     }
+#undef GMM2
 #undef GMM
   } else {
     const int64_t upper = ((M_out + FB - 1) / FB + G) * ((N + FB - 1) / FB);

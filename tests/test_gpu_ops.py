@@ -157,6 +157,7 @@ GS = {
     "ragged": [130, 0, 257, 1, 64, 0, 300],
     "empty_first": [0, 0, 128, 256],
     "one_group": [517],
+    "two_big": [800, 0, 900],      # >= 512 rows per group: 256-row tiles
     "all_empty": [0, 0, 0],
     "aligned": [128, 256, 0, 384],
     # more groups than the 128-row tile variant holds (1000): 256-row tiles
@@ -180,7 +181,13 @@ GMM_CASES = [
     ("ragged", 72, 40, 5, 0, True, "f32", "f32", True),
     ("one_group", 96, 8, 0, 0, False, "f32", "f32", False),
     ("aligned", 64, 24, 64, 30, True, "f32", "bf16", False),
-    ("one_group", 96, 264, 0, 0, False, "bf16", "bf16", False),  # 256 x 256 tiles
+    ("one_group", 96, 264, 0, 0, False, "bf16", "bf16", False),  # 256 x 256 tiles, odd steps
+    ("one_group", 200, 264, 0, 0, False, "bf16", "f32", False),  # 128-byte row segments + tail
+    ("one_group", 200, 264, 0, 0, True, "bf16", "bf16", True),
+    ("one_group", 1024, 264, 3, 0, False, "bf16", "bf16", False),  # long pipelined run
+    ("one_group", 1024, 136, 3, 0, True, "bf16", "f32", True),
+    ("two_big", 264, 520, 0, 0, True, "bf16", "bf16", False),
+    ("two_big", 136, 520, 5, 0, False, "bf16", "f32", True),
     ("one_group", 96, 264, 0, 0, True, "bf16", "f32", True),
     ("many", 64, 136, 3, 0, False, "bf16", "bf16", False),
     ("max_groups", 64, 136, 0, 0, True, "bf16", "f32", True),
