@@ -445,6 +445,16 @@ struct Acc {
                                                 int j, int sub) {
     f.b[j] = OB::frag(Bs, fb, j, sub);
   }
+  // Fragment read o (0 .. FM + FN - 1) of a substep, in the order the MFMAs
+  // q = i FN + j consume them: a0, b0 .. b(FN-1), a1 .. a(FM-1).
+  template <class OA, class OB>
+  __device__ __forceinline__ static void load_one(Frags& f, const char* As, const char* Bs,
+                                                  const uint32_t (&fa)[4], const uint32_t (&fb)[4],
+                                                  int o, int suba, int subb) {
+    if (o == 0) f.a[0] = OA::frag(As, fa, 0, suba);
+    else if (o <= FN) f.b[o - 1] = OB::frag(Bs, fb, o - 1, subb);
+    else f.a[o - FN] = OA::frag(As, fa, o - FN, suba);
+  }
   __device__ __forceinline__ void mma_one(const Frags& f, int q) {
     const int i = q / FN, j = q % FN;
     v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], v[i][j], 0, 0, 0);
@@ -490,6 +500,22 @@ struct MfmaArgs {
   int32_t* err;
 };
 
+// MFMAs of one substep (q = 0 .. NM-1) with NO other operations between
+// them in order, pinned there with scheduling barriers: the operations are
+// front-loaded, ceil(NO / NM) after each MFMA, so that fragment reads issued
+// first have the whole substep to land.
+template <int NM, int NO, class M, class O>
+__device__ __forceinline__ void interleave(M&& mma, O&& op) {
+  constexpr int K = (NO + NM - 1) / NM;
+#pragma unroll
+  for (int q = 0; q < NM; ++q) {
+    mma(q);
+#pragma unroll
+    for (int o = q * K; o < (q + 1) * K && o < NO; ++o) op(o);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Contraction over one tile: nfull DMA steps, then an optional ragged step.
 // LDS holds NS stages, each the A tile followed by the B tile.
 //
@@ -512,7 +538,6 @@ __device__ __forceinline__ void contract(char* lds, const OA& A, const OB& B, in
   constexpr int PER = OA::NJ + OB::NJ;      // DMA instructions per thread per stage
   typename ACC::Frags f0, f1;
   acc.zero();
-  __builtin_amdgcn_s_waitcnt(0);            // nothing from the previous tile is in flight
 #pragma unroll
   for (int p = 0; p < NS; ++p)
     if (p < nfull) {
@@ -533,19 +558,11 @@ __device__ __forceinline__ void contract(char* lds, const OA& A, const OB& B, in
     const int cur = s % NS;
     char* cs = lds + cur * SB;
     {
-      // MFMAs(s, 0) with the fragment reads of (s, 1) spread between them
+      // MFMAs(s, 0) with the fragment reads of (s, 1) between them
       constexpr int NM = ACC::FM * ACC::FN;
-      constexpr int NO = ACC::FM + ACC::FN;
-#pragma unroll
-      for (int q = 0; q < NM; ++q) {
-        acc.mma_one(f0, q);
-#pragma unroll
-        for (int o = q * NO / NM; o < (q + 1) * NO / NM; ++o) {
-          if (o < ACC::FM) ACC::template load_a<OA>(f1, cs, fa, o, 1);
-          else ACC::template load_b<OB>(f1, cs + OA::kBytes, fb, o - ACC::FM, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      interleave<NM, ACC::FM + ACC::FN>(
+          [&](int q) { acc.mma_one(f0, q); },
+          [&](int o) { ACC::template load_one<OA, OB>(f1, cs, cs + OA::kBytes, fa, fb, o, 1, 1); });
     }
     if (s + 1 < nfull) {
       // stages s + 2 .. s + NS - 1 may still be in flight; s + 1 must have landed
@@ -564,20 +581,14 @@ __device__ __forceinline__ void contract(char* lds, const OA& A, const OB& B, in
         const void* sb = uniform_ptr(B.step_base(s + NS));
         const uint32_t la = lds_addr(cs), lb = lds_addr(cs + OA::kBytes);
         constexpr int NM = ACC::FM * ACC::FN;
-        constexpr int NO = OA::NJ + OB::NJ + ACC::FM + ACC::FN;
-#pragma unroll
-        for (int q = 0; q < NM; ++q) {
-          acc.mma_one(f1, q);
-#pragma unroll
-          for (int o = q * NO / NM; o < (q + 1) * NO / NM; ++o) {
-            if (o < ACC::FM) ACC::template load_a<OA>(f0, ns, fa, o, 0);
-            else if (o < ACC::FM + ACC::FN)
-              ACC::template load_b<OB>(f0, ns + OA::kBytes, fb, o - ACC::FM, 0);
-            else if (o < ACC::FM + ACC::FN + OA::NJ) A.dma_one(sa, o - ACC::FM - ACC::FN, la);
-            else B.dma_one(sb, o - ACC::FM - ACC::FN - OA::NJ, lb);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        constexpr int NF = ACC::FM + ACC::FN;
+        interleave<NM, NF + OA::NJ + OB::NJ>(
+            [&](int q) { acc.mma_one(f1, q); },
+            [&](int o) {
+              if (o < NF) ACC::template load_one<OA, OB>(f0, ns, ns + OA::kBytes, fa, fb, o, 0, 0);
+              else if (o < NF + OA::NJ) A.dma_one(sa, o - NF, la);
+              else B.dma_one(sb, o - NF - OA::NJ, lb);
+            });
         continue;
       }
       ACC::template load<OA, OB>(f0, ns, ns + OA::kBytes, fa, fb, 0);
@@ -615,19 +626,6 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   } else {
     if (n >= N) wait_vmcnt<N>();
     else wait_vmcnt_dyn<N - 1>(n);
-  }
-}
-
-// MFMAs of one substep (q = 0 .. NM-1) with NO other operations spread
-// between them in order, pinned there with scheduling barriers.
-template <int NM, int NO, class M, class O>
-__device__ __forceinline__ void interleave(M&& mma, O&& op) {
-#pragma unroll
-  for (int q = 0; q < NM; ++q) {
-    mma(q);
-#pragma unroll
-    for (int o = q * NO / NM; o < (q + 1) * NO / NM; ++o) op(o);
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -688,7 +686,6 @@ __device__ __forceinline__ void contract2(char* lds, const PA& A, const OB& B, i
   };
   typename ACC::Frags f0, f1;
   acc.zero();
-  __builtin_amdgcn_s_waitcnt(0);            // nothing from the previous tile is in flight
   if (nfull == 0) {
     // only a ragged step: nothing to pipeline
   } else {
@@ -707,10 +704,7 @@ __device__ __forceinline__ void contract2(char* lds, const PA& A, const OB& B, i
       char* const ub = bU(s);
       interleave<NM, ACC::FM + ACC::FN>(
           [&](int q) { acc.mma_one(f0, q); },
-          [&](int o) {
-            if (o < ACC::FM) ACC::template load_a<PA>(f1, ua, fa, o, sa1);
-            else ACC::template load_b<OB>(f1, ub, fb, o - ACC::FM, sb1);
-          });
+          [&](int o) { ACC::template load_one<PA, OB>(f1, ua, ub, fa, fb, o, sa1, sb1); });
     };
     // wait for step s + 1, barrier, then MFMAs(s, 1) with the fragment reads
     // of (s + 1, 0) and the DMA block of step s (all waves are done with
@@ -728,26 +722,22 @@ __device__ __forceinline__ void contract2(char* lds, const PA& A, const OB& B, i
         const void* sb = uniform_ptr(B.step_base(BP ? pair_src(s + 3) : step_src(s + 4)));
         const uint32_t db = lds_addr(bU(BP ? s + 3 : s + 4));
         constexpr int NO = ACC::FM + ACC::FN + JA + JB;
+        constexpr int NF = ACC::FM + ACC::FN;
         interleave<NM, NO>([&](int q) { acc.mma_one(f1, q); },
                            [&](int o) {
-                             if (o < ACC::FM) ACC::template load_a<PA>(f0, na, fa, o, na0);
-                             else if (o < ACC::FM + ACC::FN)
-                               ACC::template load_b<OB>(f0, nb, fb, o - ACC::FM, nb0);
-                             else if (o < ACC::FM + ACC::FN + JA)
-                               A.dma_one(sa, o - ACC::FM - ACC::FN, da);
-                             else
-                               B.dma_one(sb, o - ACC::FM - ACC::FN - JA, db);
+                             if (o < NF) ACC::template load_one<PA, OB>(f0, na, nb, fa, fb, o, na0, nb0);
+                             else if (o < NF + JA) A.dma_one(sa, o - NF, da);
+                             else B.dma_one(sb, o - NF - JA, db);
                            });
       } else {
         const void* sb = uniform_ptr(B.step_base(BP ? 0 : step_src(s + 4)));
         const uint32_t db = lds_addr(bU(s + 4));
         constexpr int NO = ACC::FM + ACC::FN + (BP ? 0 : JB);
+        constexpr int NF = ACC::FM + ACC::FN;
         interleave<NM, NO>([&](int q) { acc.mma_one(f1, q); },
                            [&](int o) {
-                             if (o < ACC::FM) ACC::template load_a<PA>(f0, na, fa, o, na0);
-                             else if (o < ACC::FM + ACC::FN)
-                               ACC::template load_b<OB>(f0, nb, fb, o - ACC::FM, nb0);
-                             else if constexpr (!BP) B.dma_one(sb, o - ACC::FM - ACC::FN, db);
+                             if (o < NF) ACC::template load_one<PA, OB>(f0, na, nb, fa, fb, o, na0, nb0);
+                             else if constexpr (!BP) B.dma_one(sb, o - NF, db);
                            });
       }
     };
@@ -849,7 +839,8 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += old[e];
         }
-        store8(p, v);
+        if (accumulate) store8(p, v);
+        else store8_nt(p, v);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
