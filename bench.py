@@ -139,19 +139,23 @@ class LaunchRecorder:
 # (the rocprofv3 summary is matched on this name).
 # These are the 256 x 256 tile variants the Mixtral-8x7B shape runs on.
 KERNEL_NAME = {
-    "gmm_nn": "gmm_mfma_kernel<true, 256, 256, unsigned short>",
-    "gmm_nt": "gmm_mfma_kernel<false, 256, 256, unsigned short>",
-    "tgmm": "tgmm_mfma_kernel<256, unsigned short>",
-    "gmm_up_chunk": "gmm_mfma_kernel<true, 256, 256, float>",
+    "gmm_nn": "gmm_mfma_kernel<true, 256, 256, unsigned short, true>",
+    "gmm_nt": "gmm_mfma_kernel<false, 256, 256, unsigned short, true>",
+    "tgmm": "tgmm_mfma_kernel<256, 256, unsigned short>",
+    "gmm_up_chunk": "gmm_mfma_kernel<true, 128, 256, float, false>",
 }
 
 
 def kernel_source_digest() -> str:
-    h = hashlib.sha256()
+    """Digest of the grouped-GEMM source with comments and blank lines
+    removed, so that counters stay tied to the code they were taken on."""
+    import re
     src = os.path.join(ROOT, "mixture_experts_grouped_top_amd", "csrc", "gmm.hip")
-    with open(src, "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+    with open(src) as f:
+        text = f.read()
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_from_profiles(kind: str, workload: str):
@@ -173,13 +177,13 @@ def traffic_from_profiles(kind: str, workload: str):
 
 
 COPY_ROWS, COPY_COLS = 32768, 16384      # bf16 rows copied by the calibration run (1 GiB)
-COPY_KERNEL = "permute_gather_kernel"
+COPY_KERNEL = "permute_scatter_kernel"
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gmm_mixtral_traffic.json")
 
 
 def copy_calibration():
     """A plain copy of known size: moe_permute with one expert and top-1 is
-    the identity permutation, so its row-gather kernel reads and writes
+    the identity permutation, so its row-scatter kernel reads and writes
     COPY_ROWS x COPY_COLS bf16 once each (1 GiB each way)."""
     import torch
     import mixture_experts_grouped_top_amd as moe

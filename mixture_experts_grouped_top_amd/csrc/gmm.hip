@@ -6,17 +6,14 @@
 // shape (groups, in_size, out_size)) and the grouped_gemm calls of the
 // TransformerEngine MoE block.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, float32 accumulators.  A workgroup of
-// 4 waves (2 x 2) computes a BM x BN output tile; each wave a (BM/2) x (BN/2)
-// block of 32 x 32 MFMA tiles.  Both operands sit in LDS as [x][BK] rows of
-// the contraction index (128 B per row, 16-byte chunks XOR-swizzled by the
-// row so that the 32 rows one MFMA operand read touches spread over all
-// banks).  Operands whose contraction index is contiguous in memory (lhs
-// rows; a transposed rhs) are copied as 16-byte chunks; operands whose
-// contraction index is the row (a plain [K, N] rhs; both tgmm operands) are
-// loaded as 4 rows x 8 columns per thread and transposed in registers into
-// 8-byte LDS writes.  Global loads for step k+1 are issued before the MFMAs
-// of step k (two LDS buffers, one barrier per step).
+// bf16 path: v_mfma_f32_32x32x16_bf16, float32 accumulators in AGPRs.  A
+// workgroup of 4 waves (2 x 2) computes a TM x TN output tile (256 x 256,
+// 128 x 256 for small groups, 256 x 128 for narrow outputs); operands reach
+// LDS by direct global->LDS loads through a ring of contraction steps, and
+// the loads of later steps and the fragment reads of the next substep are
+// interleaved one by one with the MFMAs of the current one.  The LDS
+// layouts, the two-step (128-byte) loading of contraction-contiguous
+// operands and the pipelines are described where they are defined below.
 //
 // Tile schedule: the per-group row counts stay on the device.  Each
 // persistent workgroup scans group_sizes once into LDS (prefix of rows and of
@@ -138,8 +135,8 @@ __device__ void zero_rows(TO* out, int64_t ld, int64_t N, int64_t r0, int64_t r1
 // ---------------------------------------------------------------- bf16 MFMA
 //
 // Workgroup tile TM x TN (TN = 256, or 128 for narrow or single-step
-// problems), contraction step TK = 32, a ring of four LDS stages (up to
-// four steps of loads in flight).  Waves are arranged
+// problems), contraction step TK = 32, a ring of three or four LDS stages
+// (Stages below).  Waves are arranged
 // 2 x 2, each owning a (TM/2) x (TN/2) block of 32 x 32 accumulators.
 //
 // LDS layouts (per stage, per operand), 16-byte chunks XOR-swizzled:
