@@ -153,7 +153,7 @@ int moe_permute_bwd(const void* d_x_sorted, int dtype, int64_t T, int64_t D, int
  *   float32 accumulation; MOE_F32 runs in float32 FMA.  out_dtype is
  *   MOE_F32 or MOE_BF16 (rounded to nearest even).
  *   Requires Kdim, N, ld_* and strides to be multiples of 8 and 16-byte
- *   aligned pointers.  G <= 4096.  If sum(group_sizes) > M_out the groups are
+ *   aligned pointers.  G <= 1024.  If sum(group_sizes) > M_out the groups are
  *   clipped at M_out and MOE_DERR_GROUP_SIZES is raised.
  */
 int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
@@ -167,12 +167,18 @@ int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs, int
  *   lhs [M, Kdim] row stride ld_lhs; rhs [M, N] row stride ld_rhs; out[g]
  *   at out + g*out_group_stride with row stride ld_out.  An empty group's
  *   block is zero (accumulate == 0) or left unchanged (accumulate != 0).
+ *   valid_rows (device, [G], may be NULL): the caller asserts that rows
+ *   [valid_rows[g], group_sizes[g]) of group g are zero in lhs or in rhs;
+ *   the contraction then stops after the first valid_rows[g] rows of the
+ *   group (moe_permute's counts: the align_size / capacity padding rows
+ *   carry zeros).  NULL contracts over every row of each group.
  *   Same dtype and alignment rules as moe_gmm.
  */
 int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
-             const int32_t* group_sizes, int G, int64_t M, int64_t Kdim, int64_t N, int in_dtype,
-             void* out, int64_t ld_out, int64_t out_group_stride, int out_dtype, int accumulate,
-             int32_t* err, void* stream);
+             const int32_t* group_sizes, const int32_t* valid_rows, int G, int64_t M,
+             int64_t Kdim, int64_t N, int in_dtype, void* out, int64_t ld_out,
+             int64_t out_group_stride, int out_dtype, int accumulate, int32_t* err,
+             void* stream);
 
 /* -------------------------------------------------------------------- SwiGLU
  * moe_swiglu: act = silu(h0) * h1, silu(z) = z / (1 + e^-z), computed in

@@ -34,7 +34,7 @@ SIGNATURES = {
                          _P, _S, _P, _P]),
     "moe_permute_bwd": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _I, _P]),
     "moe_gmm": (_I, [_P, _L, _L, _P, _L, _L, _I, _P, _I, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
-    "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
+    "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
     "moe_swiglu": (_I, [_P, _P, _I, _L, _L, _P, _I, _P]),
     "moe_swiglu_bwd": (_I, [_P, _P, _I, _P, _L, _L, _P, _P, _I, _P]),
     "moe_combine": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _P, _P]),
@@ -245,8 +245,10 @@ def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: 
 
 
 def moe_tgmm(lhs, rhs, group_sizes, out=None, out_dtype=None, accumulate: bool = False, err=None,
-             stream=None):
-    """out[g] (+)= lhs[rows of g]^T . rhs[rows of g] -> [G, K, N]."""
+             stream=None, valid_rows=None):
+    """out[g] (+)= lhs[rows of g]^T . rhs[rows of g] -> [G, K, N].  valid_rows
+    ([G] int32, optional): rows past valid_rows[g] in each group are zero in
+    lhs or rhs and are skipped."""
     M, Kd = lhs.shape
     M2, N = rhs.shape
     if M2 != M:
@@ -257,8 +259,11 @@ def moe_tgmm(lhs, rhs, group_sizes, out=None, out_dtype=None, accumulate: bool =
         out = torch.empty((G, Kd, N), dtype=odt, device=lhs.device)
     if out.dim() != 3 or out.stride(2) != 1 or out.shape[0] != G:
         raise MoeError("out must be [G, K, N] with unit last stride")
+    if valid_rows is not None and valid_rows.numel() != G:
+        raise MoeError("valid_rows must have one entry per group")
     _check(load().moe_tgmm(_ptr(lhs), _rowmajor(lhs, "lhs"), _ptr(rhs), _rowmajor(rhs, "rhs"),
-                           _ptr(group_sizes), G, M, Kd, N, _dtype_code(lhs), _ptr(out),
+                           _ptr(group_sizes), _ptr(valid_rows), G, M, Kd, N, _dtype_code(lhs),
+                           _ptr(out),
                            out.stride(1), out.stride(0), _dtype_code(out), int(bool(accumulate)),
                            _ptr(err), _stream(stream)), "moe_tgmm")
     return out

@@ -194,7 +194,10 @@ class MoEPlan:
             B.moe_gmm(self.d_y_sorted, wo, gs, trans_rhs=True, out=self.d_act, err=self.err,
                       stream=stream)
         with self._rec("tgmm", 2.0 * R * s.D * s.F):
-            B.moe_tgmm(self.act, self.d_y_sorted, gs, out=self.d_wo, err=self.err, stream=stream)
+            # padding rows of each group (past its kept rows) are zero in
+            # d_y_sorted and x_sorted: the weight gradients stop at counts
+            B.moe_tgmm(self.act, self.d_y_sorted, gs, out=self.d_wo, err=self.err, stream=stream,
+                       valid_rows=self.idx["counts"])
         with self._rec("swiglu_bwd", nbytes=nb.get("swiglu_bwd", 0)):
             B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
                              stream=stream)
@@ -206,9 +209,11 @@ class MoEPlan:
                       accumulate=True, err=self.err, stream=stream)
         xs = self.x_sorted[:self.rows]
         with self._rec("tgmm", 2.0 * R * s.D * s.F):
-            B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream)
+            B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream,
+                       valid_rows=self.idx["counts"])
         with self._rec("tgmm", 2.0 * R * s.D * s.F):
-            B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream)
+            B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream,
+                       valid_rows=self.idx["counts"])
         with self._rec("permute_bwd", nbytes=nb.get("permute_bwd", 0)):
             B.moe_permute_bwd(self.d_x_sorted, ros, s.T, s.K, d_x=self.dx, stream=stream)
         B.moe_route_bwd(self.logits, self.ids, self.d_w, s.score, s.renorm, bias,

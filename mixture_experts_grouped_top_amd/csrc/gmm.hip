@@ -495,6 +495,7 @@ struct MfmaArgs {
   int64_t out_gs;        // tgmm: output group stride
   int accumulate;
   int32_t* err;
+  const int32_t* valid = nullptr;   // tgmm: leading rows of each group that may be non-zero
 };
 
 // MFMAs of one substep (q = 0 .. NM-1) with NO other operations between
@@ -927,7 +928,8 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void tgmm_mfma_kernel(MfmaAr
     int mt, nt;
     blocked_tile(local, mtn, ntn, mt, nt);
     const int64_t r0 = row_base[g];
-    const int rows_g = row_base[g + 1] - row_base[g];
+    int rows_g = row_base[g + 1] - row_base[g];
+    if (a.valid) rows_g = min(rows_g, max(a.valid[g], 0));   // the rest is zero
     if (rows_g == 0 && a.accumulate) continue;   // partial sum unchanged
     const int64_t m0 = static_cast<int64_t>(mt) * TM, n0 = static_cast<int64_t>(nt) * TN;
     const int mv = static_cast<int>(lmin(TM, a.Kdim - m0));
@@ -1019,9 +1021,9 @@ __global__ __launch_bounds__(NT) void gmm_f32_kernel(
 
 __global__ __launch_bounds__(NT) void tgmm_f32_kernel(
     const float* __restrict__ lhs, int64_t ld_lhs, const float* __restrict__ rhs, int64_t ld_rhs,
-    const int32_t* __restrict__ gsz, int G, int64_t M, int64_t Kdim, int64_t N,
-    float* __restrict__ out_f, bf16_t* __restrict__ out_h, int64_t ld_out, int64_t out_gs,
-    int accumulate, int32_t* err) {
+    const int32_t* __restrict__ gsz, const int32_t* __restrict__ valid, int G, int64_t M,
+    int64_t Kdim, int64_t N, float* __restrict__ out_f, bf16_t* __restrict__ out_h,
+    int64_t ld_out, int64_t out_gs, int accumulate, int32_t* err) {
   __shared__ float As[FK][FB + 4];
   __shared__ float Bs[FK][FB + 4];
   __shared__ int row_base[kMaxG + 1];
@@ -1037,7 +1039,8 @@ __global__ __launch_bounds__(NT) void tgmm_f32_kernel(
     const int local = static_cast<int>(tile - g * per_group);
     const int nt = local / mtn, mt = local % mtn;
     const int64_t r0 = row_base[g];
-    const int rows_g = row_base[g + 1] - row_base[g];
+    int rows_g = row_base[g + 1] - row_base[g];
+    if (valid) rows_g = min(rows_g, max(valid[g], 0));
     if (rows_g == 0 && accumulate) continue;
     const int64_t m0 = static_cast<int64_t>(mt) * FB, n0 = static_cast<int64_t>(nt) * FB;
     float acc[4][4] = {};
@@ -1174,9 +1177,10 @@ MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* 
 }
 
 MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
-                     const int32_t* group_sizes, int G, int64_t M, int64_t Kdim, int64_t N,
-                     int in_dtype, void* out, int64_t ld_out, int64_t out_group_stride,
-                     int out_dtype, int accumulate, int32_t* err, void* stream) {
+                     const int32_t* group_sizes, const int32_t* valid_rows, int G, int64_t M,
+                     int64_t Kdim, int64_t N, int in_dtype, void* out, int64_t ld_out,
+                     int64_t out_group_stride, int out_dtype, int accumulate, int32_t* err,
+                     void* stream) {
   if (G < 1 || G > kMaxG || M < 0 || Kdim < 0 || N < 0) return MOE_ERR_ARG;
   if (M > INT32_MAX) return MOE_ERR_ARG;
   if (in_dtype != MOE_BF16 && in_dtype != MOE_F32) return MOE_ERR_DTYPE;
@@ -1193,7 +1197,8 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == MOE_BF16) {
     MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
-               0, group_sizes, G, M, Kdim, N, out, ld_out, out_group_stride, accumulate, err};
+               0, group_sizes, G, M, Kdim, N, out, ld_out, out_group_stride, accumulate, err,
+               valid_rows};
     // short contractions (under 512 rows per group on average) leave each
     // tile's epilogue exposed: 128-row tiles let two workgroups share a CU
     const bool short_k = M < 512 * static_cast<int64_t>(G);
@@ -1214,8 +1219,8 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
     float* of = out_dtype == MOE_F32 ? static_cast<float*>(out) : nullptr;
     bf16_t* oh = out_dtype == MOE_BF16 ? static_cast<bf16_t*>(out) : nullptr;
     hipLaunchKernelGGL(tgmm_f32_kernel, dim3(grid), dim3(NT), 0, st, static_cast<const float*>(lhs),
-                       ld_lhs, static_cast<const float*>(rhs), ld_rhs, group_sizes, G, M, Kdim, N,
-                       of, oh, ld_out, out_group_stride, accumulate, err);
+                       ld_lhs, static_cast<const float*>(rhs), ld_rhs, group_sizes, valid_rows, G,
+                       M, Kdim, N, of, oh, ld_out, out_group_stride, accumulate, err);
   }
   return launch_status();
 }

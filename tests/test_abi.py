@@ -103,7 +103,7 @@ def test_argument_checks_return_before_launch(lib):
     assert gmm(ld=32) == -1
     assert gmm(G=5000) == -1
     # tgmm: output group stride too small
-    assert lib.moe_tgmm(P, 64, P, 64, P, 2, 10, 64, 64, 1, P, 64, 64, 1, 0, None, None) == -1
+    assert lib.moe_tgmm(P, 64, P, 64, P, None, 2, 10, 64, 64, 1, P, 64, 64, 1, 0, None, None) == -1
     # permute: rows below the static bound, missing workspace
     assert lib.moe_permute(P, 1, 16, 64, P, 2, 4, 0, 0, 0, P, 31, P, P, P, P, P, P, 1 << 20,
                            None, None) == -3

@@ -229,6 +229,32 @@ def test_gmm(gpu_lib, case):
     assert host(err)[0] == 0
 
 
+@pytest.mark.parametrize("it", ["bf16", "f32"])
+def test_tgmm_valid_rows(gpu_lib, it):
+    """With valid_rows the contraction stops after each group's first
+    valid_rows[g] rows: rows past them (garbage here) must not contribute,
+    and the result equals the oracle over the rows with the rest zeroed."""
+    gs = np.array([300, 0, 257, 128, 1000], dtype=np.int32)
+    valid = np.array([299, 0, 1, 0, 613], dtype=np.int32)
+    Kd, N = 264, 136
+    g = np.random.default_rng(11)
+    M = int(gs.sum())
+    lhs = _draw(g, (M, Kd), it)
+    rhs = _draw(g, (M, N), it)
+    lhs0, rhs0 = lhs.copy(), rhs.copy()
+    off = np.concatenate([[0], np.cumsum(gs)])
+    for e in range(len(gs)):
+        lhs0[off[e] + valid[e]:off[e + 1]] = 0
+        rhs0[off[e] + valid[e]:off[e + 1]] = 0
+    out = poison(torch.empty((len(gs), Kd, N), dtype=TD[it], device="cuda"))
+    gpu_lib.moe_tgmm(dev(lhs, TD[it]), dev(rhs, TD[it]), dev_i32(gs), out=out,
+                     valid_rows=dev_i32(valid))
+    want = oracle.tgmm(lhs0, rhs0, gs)
+    assert_close(host(out), want, TOL_F32 if it == "f32" else TOL_BF16, "tgmm valid_rows")
+    for e in np.where(valid == 0)[0]:
+        assert (host(out)[e] == 0).all()
+
+
 def test_gmm_strided_chunks(gpu_lib):
     """Contracting-dim chunks of a wider lhs and rhs (views with ld > K),
     accumulated in place into a float32 partial sum = the unchunked product."""
