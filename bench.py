@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--workload", default="mixtral")
     p.add_argument("--cpu-tokens", type=int, default=2048,
                    help="tokens of the workload the CPU oracle baseline runs on")
+    p.add_argument("--fused-wi", action="store_true",
+                   help="one [E, D, 2F] up-projection weight [wi_0 | wi_1]")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="do not bracket the expert GEMM launches with events")
@@ -293,15 +295,22 @@ def main():
     threads = min(16, len(os.sched_getaffinity(0)))
     inp = gen_inputs(w, threads)
     g = to_gpu(inp, dtype)
+    g["wi"] = None
+    if args.fused_wi:
+        g["wi"] = torch.cat([g.pop("wi_0"), g.pop("wi_1")], dim=2).contiguous()
+        g["wi_0"] = g["wi_1"] = None
+        torch.cuda.empty_cache()
     shape = moe.MoEShape(T=w.T, D=w.D, F=w.F, E=w.E, K=w.K, dtype=dtype, score=w.score,
                          renorm=w.renorm, align=w.align, capacity=w.capacity,
-                         n_chunks=w.n_chunks, pad_rows_to=w.pad_rows_to)
+                         n_chunks=w.n_chunks, pad_rows_to=w.pad_rows_to,
+                         fused_wi=args.fused_wi)
     plan = moe.MoEPlan(shape)
 
     def step():
         plan.forward(g["x"], g["wi_0"], g["wi_1"], g["wo"], Wg=g["Wg"], logits=g["logits"],
-                     bias=g["bias"])
-        plan.backward(g["dy"], g["x"], g["wi_0"], g["wi_1"], g["wo"], Wg=g["Wg"], bias=g["bias"])
+                     bias=g["bias"], wi=g["wi"])
+        plan.backward(g["dy"], g["x"], g["wi_0"], g["wi_1"], g["wo"], Wg=g["Wg"], bias=g["bias"],
+                      wi=g["wi"])
 
     # one untimed step to learn the kept row count (dropping) for the flop count
     step()
@@ -337,8 +346,8 @@ def main():
         kind = max(gemm, key=lambda k: gemm[k]["ms"])
         k = gemm[kind]
         ach = k["tflops"]
-        traffic = traffic_from_profiles(kind, args.workload)
-        label = KERNEL_NAME.get(kind, kind) if args.workload == "mixtral" else kind
+        traffic = None if args.fused_wi else traffic_from_profiles(kind, args.workload)
+        label = KERNEL_NAME.get(kind, kind) if args.workload == "mixtral" and not args.fused_wi else kind
         roofline = {"bound": "mfma", "kernel": label,
                     "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
@@ -363,7 +372,7 @@ def main():
         "config": {"workload": w.name, "tokens": w.T, "d_model": w.D, "d_ff": w.F,
                    "experts": w.E, "top_k": w.K, "score": w.score, "renorm": w.renorm,
                    "align_size": w.align, "capacity": w.capacity, "chunks": w.n_chunks,
-                   "routed_rows": R},
+                   "fused_wi": bool(args.fused_wi), "routed_rows": R},
         "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -183,16 +183,22 @@ int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
 /* -------------------------------------------------------------------- SwiGLU
  * moe_swiglu: act = silu(h0) * h1, silu(z) = z / (1 + e^-z), computed in
  * float32 (gate_proj_out / up_proj_out of the [TE-MoE] SwiGLU FFN).
- * h0, h1 [rows, F] in h_dtype; act [rows, F] in act_dtype.
+ * h0, h1 [rows, F] in h_dtype with row stride ld_h >= F (two column halves
+ * of one [rows, 2F] product of a fused [wi_0 | wi_1] weight: h1 = h0 + F,
+ * ld_h = 2F); act [rows, F] contiguous in act_dtype.  F and ld_h multiples
+ * of 8, rows * F / 8 < 2^31.
  */
-int moe_swiglu(const void* h0, const void* h1, int h_dtype, int64_t rows, int64_t F, void* act,
-               int act_dtype, void* stream);
+int moe_swiglu(const void* h0, const void* h1, int h_dtype, int64_t rows, int64_t F,
+               int64_t ld_h, void* act, int act_dtype, void* stream);
 
 /* moe_swiglu_bwd: d_h0 = d_act*h1*s*(1 + h0*(1 - s)), d_h1 = d_act*silu(h0),
- * s = sigmoid(h0).  h0, h1 in h_dtype; d_act in d_dtype; d_h0, d_h1 in d_dtype.
+ * s = sigmoid(h0).  h0, h1 in h_dtype with row stride ld_h; d_act [rows, F]
+ * contiguous in d_dtype; d_h0, d_h1 in d_dtype with row stride ld_dh (the
+ * halves of a [rows, 2F] gradient with ld_dh = 2F in the fused layout).
  */
-int moe_swiglu_bwd(const void* h0, const void* h1, int h_dtype, const void* d_act, int64_t rows,
-                   int64_t F, void* d_h0, void* d_h1, int d_dtype, void* stream);
+int moe_swiglu_bwd(const void* h0, const void* h1, int h_dtype, int64_t ld_h, const void* d_act,
+                   int64_t rows, int64_t F, void* d_h0, void* d_h1, int64_t ld_dh, int d_dtype,
+                   void* stream);
 
 /* ------------------------------------------------------------------ combine
  * moe_combine: y[t] = sum_j topk_w[t, j] * y_sorted[row_of_slot[t*K+j]] over

@@ -35,8 +35,8 @@ SIGNATURES = {
     "moe_permute_bwd": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _I, _P]),
     "moe_gmm": (_I, [_P, _L, _L, _P, _L, _L, _I, _P, _I, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
     "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
-    "moe_swiglu": (_I, [_P, _P, _I, _L, _L, _P, _I, _P]),
-    "moe_swiglu_bwd": (_I, [_P, _P, _I, _P, _L, _L, _P, _P, _I, _P]),
+    "moe_swiglu": (_I, [_P, _P, _I, _L, _L, _L, _P, _I, _P]),
+    "moe_swiglu_bwd": (_I, [_P, _P, _I, _L, _P, _L, _L, _P, _P, _L, _I, _P]),
     "moe_combine": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _P, _P]),
     "moe_combine_bwd": (_I, [_P, _P, _I, _L, _L, _I, _L, _P, _P, _P, _P, _P, _P]),
 }
@@ -271,28 +271,43 @@ def moe_tgmm(lhs, rhs, group_sizes, out=None, out_dtype=None, accumulate: bool =
 
 # ------------------------------------------------------------------ SwiGLU
 
+def _halves(h0, h1, name):
+    """h0, h1: [rows, F] views with unit column stride and one common row
+    stride (contiguous tensors, or the two halves of a [rows, 2F] tensor)."""
+    if h0.shape != h1.shape or h0.dim() != 2:
+        raise MoeError(f"{name}: both halves must be [rows, F]")
+    if h0.stride(1) != 1 or h1.stride(1) != 1 or h0.stride(0) != h1.stride(0):
+        raise MoeError(f"{name}: halves need unit column stride and a common row stride")
+    if h0.dtype != h1.dtype:
+        raise MoeError(f"{name}: halves differ in dtype")
+    return h0.stride(0) if h0.shape[0] > 1 else h0.shape[1]
+
+
 def moe_swiglu(h0, h1, act=None, act_dtype=None, stream=None):
-    _contig(h0, "h0")
-    _contig(h1, "h1")
+    ld = _halves(h0, h1, "h")
     rows, F = h0.shape
     if act is None:
         act = torch.empty((rows, F), dtype=h0.dtype if act_dtype is None else act_dtype,
                           device=h0.device)
-    _check(load().moe_swiglu(_ptr(h0), _ptr(h1), _dtype_code(h0), rows, F, _ptr(act),
+    _contig(act, "act")
+    _check(load().moe_swiglu(_ptr(h0), _ptr(h1), _dtype_code(h0), rows, F, ld, _ptr(act),
                              _dtype_code(act), _stream(stream)), "moe_swiglu")
     return act
 
 
 def moe_swiglu_bwd(h0, h1, d_act, d_h0=None, d_h1=None, stream=None):
+    ld = _halves(h0, h1, "h")
     rows, F = h0.shape
-    for t, n in ((h0, "h0"), (h1, "h1"), (d_act, "d_act")):
-        _contig(t, n)
+    _contig(d_act, "d_act")
     if d_h0 is None:
         d_h0 = torch.empty_like(d_act)
     if d_h1 is None:
         d_h1 = torch.empty_like(d_act)
-    _check(load().moe_swiglu_bwd(_ptr(h0), _ptr(h1), _dtype_code(h0), _ptr(d_act), rows, F,
-                                 _ptr(d_h0), _ptr(d_h1), _dtype_code(d_act), _stream(stream)),
+    ldd = _halves(d_h0, d_h1, "d_h")
+    if d_h0.dtype != d_act.dtype:
+        raise MoeError("d_h0/d_h1 must have the dtype of d_act")
+    _check(load().moe_swiglu_bwd(_ptr(h0), _ptr(h1), _dtype_code(h0), ld, _ptr(d_act), rows, F,
+                                 _ptr(d_h0), _ptr(d_h1), ldd, _dtype_code(d_act), _stream(stream)),
            "moe_swiglu_bwd")
     return d_h0, d_h1
 

@@ -40,6 +40,10 @@ class MoEShape:
     capacity_layout: bool = False
     n_chunks: int = 1
     pad_rows_to: int = 0
+    # one [E, D, 2F] up-projection weight wi = [wi_0 | wi_1] (the fused wi
+    # of the TransformerEngine MoE block): one up-projection gmm, one
+    # transposed-rhs gmm over 2F for d_x_sorted, one tgmm for d_wi
+    fused_wi: bool = False
 
 
 def _round_up(a: int, b: int) -> int:
@@ -74,8 +78,13 @@ class MoEPlan:
                               device=dev)
         self.err = torch.zeros(1, **i32)
         self.x_sorted = torch.empty((self.lhs_rows, s.D), **act)
-        self.h0 = torch.empty((self.rows, s.F), **part)
-        self.h1 = torch.empty((self.rows, s.F), **part)
+        if s.fused_wi:
+            # gate and up halves of one [rows, 2F] product
+            self.h = torch.empty((self.rows, 2 * s.F), **part)
+            self.h0, self.h1 = self.h[:, :s.F], self.h[:, s.F:]
+        else:
+            self.h0 = torch.empty((self.rows, s.F), **part)
+            self.h1 = torch.empty((self.rows, s.F), **part)
         self.act = torch.empty((self.rows, s.F), **act)
         self.y_sorted = torch.empty((self.rows, s.D), **act)
         self.y = torch.empty((s.T, s.D), **act)
@@ -83,13 +92,21 @@ class MoEPlan:
         self.d_y_sorted = torch.empty((self.rows, s.D), **act)
         self.d_w = torch.empty((s.T, s.K), **f32)
         self.d_act = torch.empty((self.rows, s.F), **act)
-        self.d_h0 = torch.empty((self.rows, s.F), **act)
-        self.d_h1 = torch.empty((self.rows, s.F), **act)
+        if s.fused_wi:
+            self.d_h = torch.empty((self.rows, 2 * s.F), **act)
+            self.d_h0, self.d_h1 = self.d_h[:, :s.F], self.d_h[:, s.F:]
+        else:
+            self.d_h0 = torch.empty((self.rows, s.F), **act)
+            self.d_h1 = torch.empty((self.rows, s.F), **act)
         self.d_x_sorted = torch.empty((self.rows, s.D), **act)
         self.dx = torch.empty((s.T, s.D), **act)
         self.d_logits = torch.empty((s.T, s.E), **act)
-        self.d_wi_0 = torch.empty((s.E, s.D, s.F), **act)
-        self.d_wi_1 = torch.empty((s.E, s.D, s.F), **act)
+        if s.fused_wi:
+            self.d_wi = torch.empty((s.E, s.D, 2 * s.F), **act)
+            self.d_wi_0, self.d_wi_1 = self.d_wi[:, :, :s.F], self.d_wi[:, :, s.F:]
+        else:
+            self.d_wi_0 = torch.empty((s.E, s.D, s.F), **act)
+            self.d_wi_1 = torch.empty((s.E, s.D, s.F), **act)
         self.d_wo = torch.empty((s.E, s.F, s.D), **act)
         # router weight gradient kept in float32 (a [D, E] reduction over all tokens)
         self.d_Wg = torch.empty((1, s.D, s.E), **f32) if router else None
@@ -138,9 +155,10 @@ class MoEPlan:
             swiglu_bwd=2 * Rp * F * bh + 3 * Rp * F * b,
             permute_bwd=R * D * b + T * D * b + T * K * 4)
 
-    def forward(self, x, wi_0, wi_1, wo, Wg=None, logits=None, bias=None, stream=None):
+    def forward(self, x, wi_0, wi_1, wo, Wg=None, logits=None, bias=None, stream=None, wi=None):
         """y = sum_j w[t,j] FFN_{e(t,j)}(x[t]).  Either Wg (router GEMM on the
-        device) or precomputed float32 logits."""
+        device) or precomputed float32 logits.  With fused_wi the
+        up-projection weight is wi [E, D, 2F] (wi_0, wi_1 unused)."""
         s = self.s
         if logits is None:
             B.moe_gmm(x, Wg.unsqueeze(0), self.gs_T, out=self.logits, err=self.err, stream=stream)
@@ -155,7 +173,9 @@ class MoEPlan:
                           workspace=self.ws, out=self.idx, stream=stream)
         gs = self.group_sizes
         R = self.kept_rows
-        if s.n_chunks > 1:
+        if s.fused_wi:
+            self._up_fused(wi, gs, R, stream)
+        elif s.n_chunks > 1:
             c = s.D // s.n_chunks
             for i in range(s.n_chunks):
                 xs = self.x_sorted[:, i * c:(i + 1) * c]
@@ -179,9 +199,21 @@ class MoEPlan:
                           stream=stream)
         return self.y
 
-    def backward(self, dy, x, wi_0, wi_1, wo, Wg=None, bias=None, stream=None):
-        """Gradients for upstream dy: fills dx, d_wi_0, d_wi_1, d_wo, d_logits
-        and (with the router) d_Wg."""
+    def _up_fused(self, wi, gs, R, stream):
+        s = self.s
+        if s.n_chunks > 1:
+            c = s.D // s.n_chunks
+            for i in range(s.n_chunks):
+                with self._rec("gmm_up_chunk", 4.0 * R * c * s.F):
+                    B.moe_gmm(self.x_sorted[:, i * c:(i + 1) * c], wi[:, i * c:(i + 1) * c, :],
+                              gs, out=self.h, accumulate=i > 0, err=self.err, stream=stream)
+        else:
+            with self._rec("gmm_nn", 4.0 * R * s.D * s.F):
+                B.moe_gmm(self.x_sorted, wi, gs, out=self.h, err=self.err, stream=stream)
+
+    def backward(self, dy, x, wi_0, wi_1, wo, Wg=None, bias=None, stream=None, wi=None):
+        """Gradients for upstream dy: fills dx, d_wi_0, d_wi_1 (halves of d_wi
+        with fused_wi), d_wo, d_logits and (with the router) d_Wg."""
         s = self.s
         gs = self.group_sizes
         R = self.kept_rows
@@ -201,19 +233,29 @@ class MoEPlan:
         with self._rec("swiglu_bwd", nbytes=nb.get("swiglu_bwd", 0)):
             B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
                              stream=stream)
-        with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
-            B.moe_gmm(self.d_h0, wi_0, gs, trans_rhs=True, out=self.d_x_sorted, err=self.err,
-                      stream=stream)
-        with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
-            B.moe_gmm(self.d_h1, wi_1, gs, trans_rhs=True, out=self.d_x_sorted,
-                      accumulate=True, err=self.err, stream=stream)
         xs = self.x_sorted[:self.rows]
-        with self._rec("tgmm", 2.0 * R * s.D * s.F):
-            B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream,
-                       valid_rows=self.idx["counts"])
-        with self._rec("tgmm", 2.0 * R * s.D * s.F):
-            B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream,
-                       valid_rows=self.idx["counts"])
+        if s.fused_wi:
+            # d_x_sorted = [d_h0 | d_h1] . [wi_0 | wi_1]^T in one contraction
+            # over 2F; d_wi = x_sorted^T [d_h0 | d_h1] in one tgmm
+            with self._rec("gmm_nt", 4.0 * R * s.D * s.F):
+                B.moe_gmm(self.d_h, wi, gs, trans_rhs=True, out=self.d_x_sorted, err=self.err,
+                          stream=stream)
+            with self._rec("tgmm", 4.0 * R * s.D * s.F):
+                B.moe_tgmm(xs, self.d_h, gs, out=self.d_wi, err=self.err, stream=stream,
+                           valid_rows=self.idx["counts"])
+        else:
+            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+                B.moe_gmm(self.d_h0, wi_0, gs, trans_rhs=True, out=self.d_x_sorted, err=self.err,
+                          stream=stream)
+            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+                B.moe_gmm(self.d_h1, wi_1, gs, trans_rhs=True, out=self.d_x_sorted,
+                          accumulate=True, err=self.err, stream=stream)
+            with self._rec("tgmm", 2.0 * R * s.D * s.F):
+                B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream,
+                           valid_rows=self.idx["counts"])
+            with self._rec("tgmm", 2.0 * R * s.D * s.F):
+                B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream,
+                           valid_rows=self.idx["counts"])
         with self._rec("permute_bwd", nbytes=nb.get("permute_bwd", 0)):
             B.moe_permute_bwd(self.d_x_sorted, ros, s.T, s.K, d_x=self.dx, stream=stream)
         B.moe_route_bwd(self.logits, self.ids, self.d_w, s.score, s.renorm, bias,

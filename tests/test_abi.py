@@ -111,4 +111,5 @@ def test_argument_checks_return_before_launch(lib):
                            None, None) == -5
     # combine: D not a multiple of 8
     assert lib.moe_combine(P, 1, 4, 12, 2, 8, P, P, P, None) == -1
-    assert lib.moe_swiglu(P, P, 3, 4, 8, P, 1, None) == -2
+    assert lib.moe_swiglu(P, P, 3, 4, 8, 8, P, 1, None) == -2
+    assert lib.moe_swiglu(P, P, 1, 4, 16, 8, P, 1, None) == -1      # row stride below F

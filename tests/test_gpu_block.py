@@ -13,6 +13,9 @@ from tests.gpu_util import TOL_BF16, TOL_F32, TOL_GRAD, assert_close, dev, host
 pytestmark = pytest.mark.gpu
 
 CHAIN = ["tiny", "mini_mixtral", "mini_deepseek", "mini_token_drop", "mini_chunked", "mini_align8"]
+# the same chain with the fused [wi_0 | wi_1] up-projection weight
+FUSED = ["tiny", "mini_mixtral", "mini_deepseek", "mini_chunked"]
+CASES = [(n, False) for n in CHAIN] + [(n, True) for n in FUSED]
 
 
 def workload_inputs(w: ms.Workload):
@@ -27,11 +30,12 @@ def workload_inputs(w: ms.Workload):
     return dict(x=x, wi_0=wi0, wi_1=wi1, wo=wo, dy=dy, Wg=Wg, logits=logits, bias=bias)
 
 
-def shape_of(w: ms.Workload) -> MoEShape:
+def shape_of(w: ms.Workload, fused_wi: bool = False) -> MoEShape:
     return MoEShape(T=w.T, D=w.D, F=w.F, E=w.E, K=w.K,
                     dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16,
                     score=w.score, renorm=w.renorm, align=w.align, capacity=w.capacity,
-                    capacity_layout=False, n_chunks=w.n_chunks, pad_rows_to=w.pad_rows_to)
+                    capacity_layout=False, n_chunks=w.n_chunks, pad_rows_to=w.pad_rows_to,
+                    fused_wi=fused_wi)
 
 
 def selection_margin(z32, K):
@@ -43,8 +47,8 @@ def selection_margin(z32, K):
     return gap.min() if gap.size else np.inf
 
 
-def run_gpu(w, inp, capacity_layout=False):
-    s = shape_of(w)
+def run_gpu(w, inp, capacity_layout=False, fused_wi=False):
+    s = shape_of(w, fused_wi)
     if capacity_layout:
         s = MoEShape(**{**s.__dict__, "capacity_layout": True})
     td = s.dtype
@@ -54,8 +58,9 @@ def run_gpu(w, inp, capacity_layout=False):
     Wg = dev(inp["Wg"], td) if inp["Wg"] is not None else None
     logits = dev(inp["logits"]) if inp["logits"] is not None else None
     bias = dev(inp["bias"]) if inp["bias"] is not None else None
-    plan.forward(x, W["wi_0"], W["wi_1"], W["wo"], Wg=Wg, logits=logits, bias=bias)
-    plan.backward(dev(inp["dy"], td), x, W["wi_0"], W["wi_1"], W["wo"], Wg=Wg, bias=bias)
+    wi = torch.cat([W["wi_0"], W["wi_1"]], dim=2).contiguous() if fused_wi else None
+    plan.forward(x, W["wi_0"], W["wi_1"], W["wo"], Wg=Wg, logits=logits, bias=bias, wi=wi)
+    plan.backward(dev(inp["dy"], td), x, W["wi_0"], W["wi_1"], W["wo"], Wg=Wg, bias=bias, wi=wi)
     torch.cuda.synchronize()
     return plan
 
@@ -70,11 +75,13 @@ def run_oracle(w, inp, lhs_rows):
     return f, b
 
 
-@pytest.fixture(scope="module", params=CHAIN)
+@pytest.fixture(scope="module", params=CASES,
+                ids=[f"{n}{'-fused_wi' if fz else ''}" for n, fz in CASES])
 def chain(request):
-    w = ms.get_workload(request.param)
+    name, fused = request.param
+    w = ms.get_workload(name)
     inp = workload_inputs(w)
-    plan = run_gpu(w, inp)
+    plan = run_gpu(w, inp, fused_wi=fused)
     f, b = run_oracle(w, inp, plan.lhs_rows)
     return w, inp, plan, f, b
 

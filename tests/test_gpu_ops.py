@@ -255,6 +255,25 @@ def test_tgmm_valid_rows(gpu_lib, it):
         assert (host(out)[e] == 0).all()
 
 
+@pytest.mark.parametrize("hd,ad", [("bf16", "bf16"), ("f32", "bf16"), ("f32", "f32")])
+def test_swiglu_fused_halves(gpu_lib, hd, ad):
+    """Gate and up halves of one [rows, 2F] product (row stride 2F), and the
+    gradient written into the halves of a [rows, 2F] buffer."""
+    g = np.random.default_rng(5)
+    rows, F = 37, 136
+    h = _draw(g, (rows, 2 * F), hd) * 3
+    da = _draw(g, (rows, F), ad)
+    hdev = dev(h, TD[hd])
+    act = gpu_lib.moe_swiglu(hdev[:, :F], hdev[:, F:], act_dtype=TD[ad])
+    tol = TOL_F32 if (hd, ad) == ("f32", "f32") else TOL_BF16
+    assert_close(host(act), oracle.swiglu(h[:, :F], h[:, F:]), tol, "swiglu halves")
+    dh = poison(torch.empty((rows, 2 * F), dtype=TD[ad], device="cuda"))
+    gpu_lib.moe_swiglu_bwd(hdev[:, :F], hdev[:, F:], dev(da, TD[ad]), d_h0=dh[:, :F], d_h1=dh[:, F:])
+    w0, w1 = oracle.swiglu_bwd(h[:, :F], h[:, F:], da)
+    assert_close(host(dh)[:, :F], w0, tol, "d_h0 half")
+    assert_close(host(dh)[:, F:], w1, tol, "d_h1 half")
+
+
 def test_gmm_strided_chunks(gpu_lib):
     """Contracting-dim chunks of a wider lhs and rhs (views with ld > K),
     accumulated in place into a float32 partial sum = the unchunked product."""
