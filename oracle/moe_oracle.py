@@ -14,6 +14,12 @@ expert FFNs, forward and backward, with every intermediate kept in float64
                 block pull request ("Add an MoE Block ... router,
                 permutation, groupedGEMM and communication"), Description /
                 Changes: fused top-K with optional sigmoid scoring.
+  route variants  a per-expert bias that moves only the selection (the
+                "pre_bias_logits" of the MaxText DeepSeek-V3 router), grouped
+                top-K ("n_routing_groups" / "topk_routing_group"), and the
+                optional auxiliary load-balancing loss of the TransformerEngine
+                MoE block (Description: "top-K with optional grouped/sigmoid
+                scoring ... and optional auxiliary load-balancing loss").
   permute       stable grouping of the routed (token, slot) pairs by expert,
                 per-expert group sizes, optional align_size padding and
                 capacity dropping.  Same pull request: the dispatch state
@@ -41,6 +47,8 @@ import numpy as np
 
 SOFTMAX = "softmax"
 SIGMOID = "sigmoid"
+LOGIT = "logit"      # a per-expert bias added to the logits (selection and weights)
+SELECT = "select"    # a per-expert bias added to the scores for the selection only
 
 
 def _f64(a) -> np.ndarray:
@@ -71,39 +79,70 @@ def biased_logits_f32(logits, bias=None) -> np.ndarray:
     return z
 
 
-def route(logits, K: int, score: str = SOFTMAX, renorm: bool = True, bias=None):
-    """Top-K routing.  Returns (ids int32 [T, K], weights float64 [T, K]).
-
-    Selection: experts ranked by their float32 (biased) logit, descending;
-    equal logits rank the lower expert id first; slot j holds the j-th
-    ranked expert.  Softmax and sigmoid are increasing, so ranking the
-    logits ranks the scores.
-    Weights: softmax p_e = exp(z_e - max z) / sum_e' exp(z_e' - max z) over
-    all E experts, or sigmoid s_e = 1 / (1 + exp(-z_e)); the K selected
-    scores, divided by their sum when renorm is set.
-    """
-    z32 = biased_logits_f32(logits, bias)
-    T, E = z32.shape
-    assert 1 <= K <= E
-    # stable sort of the negated logits: descending, ties keep ascending id
-    order = np.argsort(-z32, axis=1, kind="stable")
-    ids = order[:, :K]
-    z = z32.astype(np.float64)
+def _scores(z, score: str) -> np.ndarray:
+    """float64 scores of float64 logits z [T, E]: softmax over the E experts
+    or the logistic function per expert."""
     if score == SOFTMAX:
         m = z.max(axis=1, keepdims=True)
         ez = np.exp(z - m)
-        p = ez / ez.sum(axis=1, keepdims=True)
-    elif score == SIGMOID:
-        p = 1.0 / (1.0 + np.exp(-z))
+        return ez / ez.sum(axis=1, keepdims=True)
+    if score == SIGMOID:
+        return 1.0 / (1.0 + np.exp(-z))
+    raise ValueError(score)
+
+
+def route(logits, K: int, score: str = SOFTMAX, renorm: bool = True, bias=None,
+          bias_mode: str = LOGIT, n_groups: int = 0, topk_groups: int = 0):
+    """Top-K routing.  Returns (ids int32 [T, K], weights float64 [T, K]).
+
+    Selection: experts ranked by their selection key, descending; equal keys
+    rank the lower expert id first; slot j holds the j-th ranked expert.
+      bias_mode "logit": the key is the float32 logit plus bias (softmax and
+        sigmoid are increasing, so ranking the logits ranks the scores); the
+        weights are scores of the biased logits.
+      bias_mode "select": the key is score + bias with the scores of the
+        unbiased logits (a bias that only moves the selection); the weights
+        are the unbiased scores.
+    Weights: softmax p_e = exp(z_e - max z) / sum_e' exp(z_e' - max z) over
+    all E experts, or sigmoid s_e = 1 / (1 + exp(-z_e)); the K selected
+    scores, divided by their sum when renorm is set.
+    Grouped selection (n_groups > 1; E divisible by n_groups): the experts
+    form n_groups consecutive groups of E / n_groups; a group scores the sum
+    of its two largest keys (its one key for single-expert groups); the
+    topk_groups best groups (ties: lower group id) stay candidates and the K
+    experts are the top-K keys among them.
+    """
+    z32 = biased_logits_f32(logits, bias if bias_mode == LOGIT else None)
+    T, E = z32.shape
+    assert 1 <= K <= E
+    p = _scores(z32.astype(np.float64), score)
+    if bias_mode == LOGIT:
+        key = z32.astype(np.float64)
+    elif bias_mode == SELECT:
+        key = p + (0.0 if bias is None else _f64(bias)[None, :])
     else:
-        raise ValueError(score)
+        raise ValueError(bias_mode)
+    if n_groups > 1:
+        assert E % n_groups == 0 and 1 <= topk_groups <= n_groups
+        eg = E // n_groups
+        assert K <= topk_groups * eg
+        kg = key.reshape(T, n_groups, eg)
+        gscore = -np.sort(-kg, axis=2)[:, :, :min(2, eg)].sum(axis=2)
+        gbest = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_groups]
+        keep = np.zeros((T, n_groups), dtype=bool)
+        np.put_along_axis(keep, gbest, True, axis=1)
+        key = np.where(np.repeat(keep, eg, axis=1), key, -np.inf)
+    # stable sort of the negated keys: descending, ties keep ascending id
+    order = np.argsort(-key, axis=1, kind="stable")
+    ids = order[:, :K]
     w = np.take_along_axis(p, ids, axis=1)
     if renorm:
         w = w / w.sum(axis=1, keepdims=True)
     return ids.astype(np.int32), w
 
 
-def route_bwd(logits, ids, d_w, score: str = SOFTMAX, renorm: bool = True, bias=None):
+def route_bwd(logits, ids, d_w, score: str = SOFTMAX, renorm: bool = True, bias=None,
+              bias_mode: str = LOGIT):
     """Gradient of the routing weights with respect to the router logits,
     with the selection held fixed.  Returns d_logits float64 [T, E].
 
@@ -116,9 +155,11 @@ def route_bwd(logits, ids, d_w, score: str = SOFTMAX, renorm: bool = True, bias=
                          d s_j = (d w_j - sum_i w_i d w_i) / S and
                          d z_ej = d s_j s_j (1 - s_j).
       sigmoid, no renorm d z_ej = d w_j s_j (1 - s_j).
-    The additive prior has unit derivative, so d logits = d z.
+    The additive prior has unit derivative, so d logits = d z.  With
+    bias_mode "select" the weights are scores of the unbiased logits, so z
+    is the logits themselves (the bias only moved the selection).
     """
-    z = biased_logits_f32(logits, bias).astype(np.float64)
+    z = biased_logits_f32(logits, bias if bias_mode == LOGIT else None).astype(np.float64)
     ids = np.asarray(ids, dtype=np.int64)
     dw = _f64(d_w)
     T, E = z.shape
@@ -153,6 +194,52 @@ def route_bwd(logits, ids, d_w, score: str = SOFTMAX, renorm: bool = True, bias=
         raise ValueError(score)
     assert K == dw.shape[1]
     return dz
+
+
+def _aux_probs(logits, score: str):
+    """Per-token expert probabilities for the balancing loss: softmax over
+    the E pre-bias logits, or for sigmoid scoring the sigmoids normalised to
+    sum 1 over the E experts.  Returns (p [T, E], s or None)."""
+    z = _f64(logits)
+    if score == SOFTMAX:
+        return _scores(z, SOFTMAX), None
+    s = _scores(z, SIGMOID)
+    return s / s.sum(axis=1, keepdims=True), s
+
+
+def aux_loss(logits, ids, E: int, alpha: float, score: str = SOFTMAX):
+    """Auxiliary load-balancing loss (optional in the TransformerEngine MoE
+    block; its form is not written out on the pages, so this takes the
+    plainest one, the product of routed fraction and mean probability):
+      f_e  = (selected slots with expert e) / (T K), counted on the
+             selection before any capacity dropping;
+      P_e  = (1 / T) sum_t p_te with p from ``_aux_probs``;
+      loss = alpha * E * sum_e f_e P_e.
+    f is a count and carries no gradient.  Returns (loss, counts int64 [E],
+    P float64 [E])."""
+    ids = np.asarray(ids, dtype=np.int64)
+    T, K = ids.shape
+    counts = np.bincount(ids.reshape(-1), minlength=E)[:E]
+    p, _ = _aux_probs(logits, score)
+    P = p.mean(axis=0)
+    f = counts / float(T * K)
+    return float(alpha * E * np.dot(f, P)), counts, P
+
+
+def aux_loss_bwd(logits, counts, K: int, alpha: float, score: str = SOFTMAX):
+    """d loss / d logits [T, E] for ``aux_loss`` with the counts held fixed:
+      softmax:  d z_tk = (alpha E / T) p_tk (f_k - sum_e f_e p_te)
+      sigmoid:  p = s / S, d p_e / d z_k = s_k (1 - s_k) / S ([e = k] - p_e), so
+                d z_tk = (alpha E / T) s_k (1 - s_k) / S_t (f_k - sum_e f_e p_te)."""
+    p, s = _aux_probs(logits, score)
+    T, E = p.shape
+    f = np.asarray(counts, dtype=np.float64) / float(T * K)
+    inner = (p * f[None, :]).sum(axis=1, keepdims=True)
+    scale = alpha * E / T
+    if score == SOFTMAX:
+        return scale * p * (f[None, :] - inner)
+    S = s.sum(axis=1, keepdims=True)
+    return scale * s * (1.0 - s) / S * (f[None, :] - inner)
 
 
 # ---------------------------------------------------------------------------
@@ -377,21 +464,25 @@ def combine_bwd(dy, y_sorted, row_of_slot, w, rows: int):
 def moe_forward(x, wi_0, wi_1, wo, K: int, *, Wg=None, logits=None, bias=None,
                 score: str = SOFTMAX, renorm: bool = True, align: int = 0,
                 capacity: int = 0, capacity_layout: bool = False,
-                n_chunks: int = 1, lhs_rows: int | None = None):
+                n_chunks: int = 1, lhs_rows: int | None = None, bias_mode: str = LOGIT,
+                n_groups: int = 0, topk_groups: int = 0, aux_alpha: float = 0.0):
     """Forward pass.  Either ``Wg`` (router logits = x . Wg) or ``logits``.
 
     With n_chunks > 1 the up-projections are computed as the in-place
     partial-sum accumulation over n_chunks equal slices of d_model (the
     chunked loop of the "Overlap moe comms" pull request); lhs_rows is the
     row count of the (padded) sorted-token buffer, the output rows being the
-    routed rows.  Returns every residual the backward needs.
+    routed rows.  bias_mode / n_groups / topk_groups select the routing
+    variant of ``route``; aux_alpha > 0 adds ``aux_loss`` (returned as
+    "aux_loss", with its counts).  Returns every residual the backward needs.
     """
     x = np.asarray(x)
     T, D = x.shape
     E = wi_0.shape[0]
     if logits is None:
         logits = router_logits(x, Wg)
-    ids, w = route(logits, K, score, renorm, bias)
+    ids, w = route(logits, K, score, renorm, bias, bias_mode, n_groups, topk_groups)
+    aux = aux_loss(logits, ids, E, aux_alpha, score) if aux_alpha > 0 else None
     nrows = rows_bound(T, K, E, align, capacity, capacity_layout)
     P = permute(x, ids, E, align, capacity, capacity_layout,
                 rows=nrows if lhs_rows is None else lhs_rows)
@@ -410,8 +501,12 @@ def moe_forward(x, wi_0, wi_1, wo, K: int, *, Wg=None, logits=None, bias=None,
     act = swiglu(h0, h1)
     y_sorted = gmm(act, wo, gs)
     y = combine(y_sorted, P["row_of_slot"], w, T, K)
-    return dict(logits=_f64(logits), ids=ids, w=w, perm=P, x_sorted=xs, h0=h0, h1=h1,
-                act=act, y_sorted=y_sorted, y=y, rows=nrows)
+    out = dict(logits=_f64(logits), ids=ids, w=w, perm=P, x_sorted=xs, h0=h0, h1=h1,
+               act=act, y_sorted=y_sorted, y=y, rows=nrows, bias_mode=bias_mode,
+               aux_alpha=aux_alpha)
+    if aux is not None:
+        out["aux_loss"], out["aux_counts"], out["aux_probs"] = aux
+    return out
 
 
 def moe_backward(fwd, dy, x, wi_0, wi_1, wo, K: int, *, Wg=None, bias=None,
@@ -435,7 +530,12 @@ def moe_backward(fwd, dy, x, wi_0, wi_1, wo, K: int, *, Wg=None, bias=None,
     d_wi_0 = tgmm(xs, d_h0, gs)
     d_wi_1 = tgmm(xs, d_h1, gs)
     dx = permute_bwd(d_xs, ros, T, K)
-    d_logits = route_bwd(fwd["logits"], fwd["ids"], d_w, score, renorm, bias)
+    d_logits = route_bwd(fwd["logits"], fwd["ids"], d_w, score, renorm, bias,
+                         fwd.get("bias_mode", LOGIT))
+    if fwd.get("aux_alpha", 0.0) > 0:
+        # the balancing loss is added to the objective with weight one
+        d_logits = d_logits + aux_loss_bwd(fwd["logits"], fwd["aux_counts"], K,
+                                           fwd["aux_alpha"], score)
     out = dict(dx=dx, d_wi_0=d_wi_0, d_wi_1=d_wi_1, d_wo=d_wo, d_logits=d_logits, d_w=d_w,
                d_y_sorted=d_ys, d_act=d_act, d_h0=d_h0, d_h1=d_h1, d_x_sorted=d_xs)
     if Wg is not None:

@@ -112,6 +112,121 @@ def check_route_closed_forms():
     np.testing.assert_allclose(w, 1 / 3, rtol=1e-15)
 
 
+def _py_scores(z_row, score):
+    """Scores of one token's logits with the math module (no NumPy)."""
+    if score == "softmax":
+        m = max(z_row)
+        ex = [math.exp(v - m) for v in z_row]
+        tot = sum(ex)
+        return [v / tot for v in ex]
+    return [1.0 / (1.0 + math.exp(-v)) for v in z_row]
+
+
+def check_route_select_bias(seed=4):
+    """Selection-only bias: the key is score + bias, the weights the plain
+    scores of the selected experts.  Brute force per token, and with a zero
+    bias the plain routing."""
+    g = _rng(seed)
+    T, E, K = 24, 10, 3
+    z = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    bias = (g.standard_normal(E) * 0.3).astype(np.float32)
+    for score in ("softmax", "sigmoid"):
+        for renorm in (True, False):
+            ids, w = oracle.route(z, K, score, renorm, bias, "select")
+            for t in range(T):
+                p = _py_scores([float(v) for v in z[t]], score)
+                key = [p[e] + float(bias[e]) for e in range(E)]
+                sel = _select_by_scan(key, K)
+                assert list(ids[t]) == sel, (score, t)
+                ws = [p[e] for e in sel]
+                if renorm:
+                    tot = sum(ws)
+                    ws = [v / tot for v in ws]
+                np.testing.assert_allclose(w[t], ws, rtol=1e-12)
+            i0, w0 = oracle.route(z, K, score, renorm, np.zeros(E, np.float32), "select")
+            i1, w1 = oracle.route(z, K, score, renorm)
+            assert (i0 == i1).all()
+            np.testing.assert_allclose(w0, w1, rtol=1e-14)
+
+
+def _group_select_by_scan(key, K, n_groups, topk_groups):
+    E = len(key)
+    eg = E // n_groups
+    gscore = []
+    for gi in range(n_groups):
+        vals = sorted(key[gi * eg:(gi + 1) * eg], reverse=True)
+        gscore.append(sum(vals[:2]))
+    chosen = _select_by_scan(gscore, topk_groups)
+    masked = [key[e] if (e // eg) in chosen else -math.inf for e in range(E)]
+    return _select_by_scan(masked, K), chosen
+
+
+def check_route_groups(seed=5):
+    """Grouped selection against a loop version, the group invariant, and the
+    two settings that reduce to plain top-K."""
+    g = _rng(seed)
+    T, E, K = 30, 16, 4
+    z = (g.integers(-4, 5, size=(T, E)) * 0.25).astype(np.float32)   # many ties
+    bias = (g.integers(-2, 3, size=E) * 0.125).astype(np.float32)
+    for mode in ("logit", "select"):
+        for n_groups, topk_groups in ((4, 2), (8, 3), (16, 4), (2, 1)):
+            ids, _ = oracle.route(z, K, "sigmoid", True, bias, mode, n_groups, topk_groups)
+            for t in range(T):
+                if mode == "logit":
+                    key = [float(np.float32(z[t, e]) + np.float32(bias[e])) for e in range(E)]
+                else:
+                    p = _py_scores([float(v) for v in z[t]], "sigmoid")
+                    key = [p[e] + float(bias[e]) for e in range(E)]
+                sel, chosen = _group_select_by_scan(key, K, n_groups, topk_groups)
+                assert list(ids[t]) == sel, (mode, n_groups, t)
+                assert all((e // (E // n_groups)) in chosen for e in ids[t])
+        plain, _ = oracle.route(z, K, "sigmoid", True, bias, mode)
+        for n_groups, topk_groups in ((1, 1), (4, 4)):
+            ids, _ = oracle.route(z, K, "sigmoid", True, bias, mode, n_groups, topk_groups)
+            assert (ids == plain).all()
+
+
+def check_aux_loss_closed_forms():
+    alpha = 0.01
+    g = _rng(6)
+    T, E, K = 32, 8, 2
+    ids = np.stack([g.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    for score in ("softmax", "sigmoid"):
+        # equal logits: every probability is 1/E, so the loss is alpha whatever the routing
+        loss, _, P = oracle.aux_loss(np.zeros((T, E), np.float32), ids, E, alpha, score)
+        assert abs(loss - alpha) < 1e-15 and np.allclose(P, 1.0 / E, rtol=1e-15)
+        # perfectly balanced routing: every f_e = 1/E, so the loss is alpha whatever the logits
+        bal = np.array([[(t * K + j) % E for j in range(K)] for t in range(T)], dtype=np.int32)
+        z = g.standard_normal((T, E)).astype(np.float32)
+        loss, counts, _ = oracle.aux_loss(z, bal, E, alpha, score)
+        assert (counts == T * K // E).all() and abs(loss - alpha) < 1e-15
+    # one token, two experts, logits 0 and ln 3 (softmax 1/4, 3/4), expert 1 chosen:
+    # loss = alpha * 2 * (0 * 1/4 + 1 * 3/4)
+    loss, _, _ = oracle.aux_loss(np.array([[0.0, math.log(3)]]), np.array([[1]], np.int32), 2,
+                                 alpha, "softmax")
+    assert abs(loss - 1.5 * alpha) < 1e-15
+
+
+def check_aux_loss_bwd_fd(seed=7):
+    g = _rng(seed)
+    T, E, K = 6, 7, 2
+    alpha, eps = 0.3, 1e-6
+    z = g.standard_normal((T, E)) * 1.2
+    ids = np.stack([g.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    for score in ("softmax", "sigmoid"):
+        _, counts, _ = oracle.aux_loss(z, ids, E, alpha, score)
+        d = oracle.aux_loss_bwd(z, counts, K, alpha, score)
+        fd = np.zeros_like(z)
+        for t in range(T):
+            for e in range(E):
+                zp, zm = z.copy(), z.copy()
+                zp[t, e] += eps
+                zm[t, e] -= eps
+                fd[t, e] = (oracle.aux_loss(zp, ids, E, alpha, score)[0]
+                            - oracle.aux_loss(zm, ids, E, alpha, score)[0]) / (2 * eps)
+        np.testing.assert_allclose(d, fd, rtol=1e-5, atol=1e-9)
+
+
 def _margin(z32, K):
     """Smallest gap between the K-th and (K+1)-th largest value per row."""
     s = -np.sort(-z32.astype(np.float64), axis=1)

@@ -16,14 +16,28 @@ from tests import pins
 
 MUTATIONS = {
     "tie_break_higher_id": (
-        'order = np.argsort(-z32, axis=1, kind="stable")',
-        'order = z32.shape[1] - 1 - np.argsort(-z32[:, ::-1], axis=1, kind="stable")'),
+        'order = np.argsort(-key, axis=1, kind="stable")',
+        'order = key.shape[1] - 1 - np.argsort(-key[:, ::-1], axis=1, kind="stable")'),
     "renorm_dropped": (
         "    if renorm:\n        w = w / w.sum(axis=1, keepdims=True)\n    return ids",
         "    return ids"),
     "sigmoid_sign": (
-        "        p = 1.0 / (1.0 + np.exp(-z))\n    else:\n        raise ValueError(score)\n    w = np.take",
-        "        p = 1.0 / (1.0 + np.exp(z))\n    else:\n        raise ValueError(score)\n    w = np.take"),
+        "        return 1.0 / (1.0 + np.exp(-z))\n    raise ValueError(score)",
+        "        return 1.0 / (1.0 + np.exp(z))\n    raise ValueError(score)"),
+    "select_bias_ignored": (
+        "key = p + (0.0 if bias is None else _f64(bias)[None, :])", "key = p"),
+    "select_bias_in_weights": (
+        "z32 = biased_logits_f32(logits, bias if bias_mode == LOGIT else None)\n    T, E = z32.shape",
+        "z32 = biased_logits_f32(logits, bias)\n    T, E = z32.shape"),
+    "group_score_top1": ("[:, :, :min(2, eg)].sum(axis=2)", "[:, :, :1].sum(axis=2)"),
+    "group_ties_higher_id": (
+        'gbest = np.argsort(-gscore, axis=1, kind="stable")[:, :topk_groups]',
+        'gbest = n_groups - 1 - np.argsort(-gscore[:, ::-1], axis=1, kind="stable")[:, :topk_groups]'),
+    "aux_probs_unnormalised": ("return s / s.sum(axis=1, keepdims=True), s", "return s, s"),
+    "aux_bwd_sign": ("return scale * p * (f[None, :] - inner)", "return scale * p * (f[None, :] + inner)"),
+    "aux_bwd_sigmoid_missing_S": (
+        "return scale * s * (1.0 - s) / S * (f[None, :] - inner)",
+        "return scale * s * (1.0 - s) * (f[None, :] - inner)"),
     "route_bwd_sign": ("dz[rows, ids] = w * (dw - inner)", "dz[rows, ids] = w * (dw + inner)"),
     "route_bwd_sigmoid_renorm_missing_S": ("ds = (dw - inner) / S", "ds = (dw - inner)"),
     "route_bwd_softmax_only_selected": ("dz = -p * inner", "dz = np.zeros_like(p)"),
