@@ -56,6 +56,9 @@ enum {
 
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
+/* How a per-expert routing bias enters: added to the logits (selection and
+ * weights), or added to the scores for the selection only. */
+enum { MOE_BIAS_LOGIT = 0, MOE_BIAS_SELECT = 1 };
 
 /* bits OR-ed into the device error word */
 enum {
@@ -67,34 +70,73 @@ enum {
 const char* moe_status_string(int status);
 int moe_abi_version(void);  /* bumped on any signature change */
 
-/* ---------------------------------------------------------------- routing
+/* -------------------------------------------------------------- routing
  * moe_route: top-K routing [TE-MoE, Description/Changes: fused top-K with
- * optional sigmoid scoring].
- *   z[t,e] = logits[t,e] + bias[e] in float32 (bias may be NULL; -inf
- *   switches an expert off).  Experts are ranked by z descending; equal z
- *   ranks the lower id first; topk_ids[t, j] is the j-th ranked expert.
- *   score MOE_SOFTMAX: p = softmax over all E of z; MOE_SIGMOID: p = 1/(1+e^-z).
+ * optional grouped/sigmoid scoring; MaxText DeepSeek-V3 router:
+ * pre_bias_logits, n_routing_groups / topk_routing_group].
+ *   Scores: MOE_SOFTMAX p = softmax over all E of z; MOE_SIGMOID
+ *   p = 1/(1+e^-z); z = logits + bias (bias_mode MOE_BIAS_LOGIT; -inf
+ *   switches an expert off) or z = logits (MOE_BIAS_SELECT).
+ *   Selection key, float32: z (MOE_BIAS_LOGIT) or p + bias (MOE_BIAS_SELECT:
+ *   the bias moves only the selection).  Experts are ranked by key
+ *   descending; an equal key ranks the lower id first; topk_ids[t, j] is the
+ *   j-th ranked expert.
+ *   Grouped selection (n_groups > 1, E % n_groups == 0, n_groups <= 64,
+ *   1 <= topk_groups <= n_groups, K <= topk_groups * E / n_groups): experts
+ *   [g E/n_groups, (g+1) E/n_groups) form group g, scored by the sum of its
+ *   two largest keys (float32; its only key if groups have one expert); the
+ *   topk_groups best groups (ties: lower g) keep their experts as
+ *   candidates.  n_groups <= 1: no grouping (topk_groups ignored).
  *   topk_w[t, j] = p of the j-th expert, divided by the sum over the K
  *   selected when renorm != 0.
  *   logits [T, E] f32, bias [E] f32 or NULL, topk_ids [T, K] i32,
- *   topk_w [T, K] f32.  Requires 1 <= K <= E <= 1024.
+ *   topk_w [T, K] f32.  Requires 1 <= K <= E <= 1024, K <= 64.
  */
-int moe_route(const float* logits, const float* bias, int64_t T, int E, int K, int score,
-              int renorm, int32_t* topk_ids, float* topk_w, void* stream);
+int moe_route(const float* logits, const float* bias, int bias_mode, int n_groups,
+              int topk_groups, int64_t T, int E, int K, int score, int renorm, int32_t* topk_ids,
+              float* topk_w, void* stream);
 
 /* moe_route_bwd: d_logits [T, E] (fully written) from d_topk_w [T, K], with
  * the selection topk_ids held fixed (the gate-kernel gradient path of the
- * [TE-MoE] block backward).  Same logits/bias/score/renorm as the forward.
- * d_logits is stored in dlogits_dtype (MOE_F32, or MOE_BF16 to feed a bf16
- * router-GEMM backward); the arithmetic is float32.
+ * [TE-MoE] block backward).  Same logits/bias/bias_mode/score/renorm as the
+ * forward (a MOE_BIAS_SELECT bias does not enter the weights, so it has no
+ * gradient path).  d_logits is stored in dlogits_dtype (MOE_F32, or
+ * MOE_BF16 to feed a bf16 router-GEMM backward); the arithmetic is float32.
  *   softmax+renorm: dz_ej = w_j (dw_j - sum_i w_i dw_i), others 0
  *   softmax:        dz_e  = p_e ([e = e_j] dw_j - sum_i p_ei dw_i), all e
  *   sigmoid+renorm: dz_ej = s_j(1-s_j)(dw_j - sum_i w_i dw_i) / sum_i s_i
  *   sigmoid:        dz_ej = dw_j s_j (1 - s_j)
  */
-int moe_route_bwd(const float* logits, const float* bias, const int32_t* topk_ids,
+int moe_route_bwd(const float* logits, const float* bias, int bias_mode, const int32_t* topk_ids,
                   const float* d_topk_w, int64_t T, int E, int K, int score, int renorm,
                   void* d_logits, int dlogits_dtype, void* stream);
+
+/* Workspace bytes moe_aux_loss needs (256-byte aligned device memory). */
+size_t moe_aux_loss_workspace(int64_t T, int E);
+
+/* moe_aux_loss: the auxiliary load-balancing loss [TE-MoE, Description:
+ * optional auxiliary load-balancing loss]:
+ *   f_e = (selected slots of expert e in topk_ids) / (T K)
+ *   P_e = (1/T) sum_t p_te,  p = softmax of the logits over the E experts,
+ *         or for MOE_SIGMOID the sigmoids of the logits normalised to sum 1
+ *   loss = alpha * E * sum_e f_e P_e   (one float32, device)
+ * expert_counts [E] (T K f_e) and expert_probs [E] (P_e) are written when
+ * not NULL; the backward needs the counts.  Sums are taken in a fixed order
+ * (deterministic).  T >= 1.
+ */
+int moe_aux_loss(const float* logits, const int32_t* topk_ids, int64_t T, int E, int K, int score,
+                 float alpha, float* loss, int32_t* expert_counts, float* expert_probs,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/* moe_aux_loss_bwd: d_logits (+)= d loss / d logits with the counts held
+ * fixed (f carries no gradient):
+ *   softmax: (alpha E / T) p_tk (f_k - sum_e f_e p_te)
+ *   sigmoid: (alpha E / T) s_tk (1 - s_tk) / S_t (f_k - sum_e f_e p_te)
+ * accumulate != 0 adds into d_logits (e.g. after moe_route_bwd).
+ */
+int moe_aux_loss_bwd(const float* logits, const int32_t* expert_counts, int64_t T, int E, int K,
+                     int score, float alpha, void* d_logits, int dlogits_dtype, int accumulate,
+                     void* stream);
 
 /* -------------------------------------------------------------- permutation
  * moe_rows_bound: the static row count of the expert-sorted buffers:

@@ -19,15 +19,20 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
 
 # Entry points (name -> (restype, argtypes)); must match include/moe.h.
 _P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+_F = ctypes.c_float
 SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_abi_version": (_I, []),
-    "moe_route": (_I, [_P, _P, _L, _I, _I, _I, _I, _P, _P, _P]),
-    "moe_route_bwd": (_I, [_P, _P, _P, _P, _L, _I, _I, _I, _I, _P, _I, _P]),
+    "moe_route": (_I, [_P, _P, _I, _I, _I, _L, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_route_bwd": (_I, [_P, _P, _I, _P, _P, _L, _I, _I, _I, _I, _P, _I, _P]),
+    "moe_aux_loss_workspace": (_S, [_L, _I]),
+    "moe_aux_loss": (_I, [_P, _P, _L, _I, _I, _I, _F, _P, _P, _P, _P, _S, _P]),
+    "moe_aux_loss_bwd": (_I, [_P, _P, _L, _I, _I, _I, _F, _P, _I, _I, _P]),
     "moe_rows_bound": (_L, [_L, _I, _I, _I, _I, _I]),
     "moe_permute_workspace": (_S, [_L, _I, _I]),
     "moe_permute": (_I, [_P, _I, _L, _L, _P, _I, _I, _I, _I, _I, _P, _L, _P, _P, _P, _P, _P,
@@ -117,8 +122,17 @@ def _contig(t: torch.Tensor, name: str):
 
 # ----------------------------------------------------------------- routing
 
+def _bias_mode(mode) -> int:
+    if mode in ("logit", MOE_BIAS_LOGIT):
+        return MOE_BIAS_LOGIT
+    if mode in ("select", MOE_BIAS_SELECT):
+        return MOE_BIAS_SELECT
+    raise MoeError(f"unknown bias mode {mode!r}")
+
+
 def moe_route(logits, K: int, score="softmax", renorm: bool = True, bias=None,
-              topk_ids=None, topk_w=None, stream=None):
+              topk_ids=None, topk_w=None, stream=None, bias_mode="logit", n_groups: int = 0,
+              topk_groups: int = 0):
     T, E = logits.shape
     _contig(logits, "logits")
     dev = logits.device
@@ -126,20 +140,60 @@ def moe_route(logits, K: int, score="softmax", renorm: bool = True, bias=None,
         topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
     if topk_w is None:
         topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
-    _check(load().moe_route(_ptr(logits), _ptr(bias), T, E, K, _score(score), int(bool(renorm)),
+    _check(load().moe_route(_ptr(logits), _ptr(bias), _bias_mode(bias_mode), int(n_groups),
+                            int(topk_groups), T, E, K, _score(score), int(bool(renorm)),
                             _ptr(topk_ids), _ptr(topk_w), _stream(stream)), "moe_route")
     return topk_ids, topk_w
 
 
 def moe_route_bwd(logits, topk_ids, d_topk_w, score="softmax", renorm: bool = True, bias=None,
-                  d_logits=None, dtype=torch.float32, stream=None):
+                  d_logits=None, dtype=torch.float32, stream=None, bias_mode="logit"):
     T, E = logits.shape
     K = topk_ids.shape[1]
     if d_logits is None:
         d_logits = torch.empty((T, E), dtype=dtype, device=logits.device)
-    _check(load().moe_route_bwd(_ptr(logits), _ptr(bias), _ptr(topk_ids), _ptr(d_topk_w), T, E, K,
-                                _score(score), int(bool(renorm)), _ptr(d_logits),
-                                _dtype_code(d_logits), _stream(stream)), "moe_route_bwd")
+    _check(load().moe_route_bwd(_ptr(logits), _ptr(bias), _bias_mode(bias_mode), _ptr(topk_ids),
+                                _ptr(d_topk_w), T, E, K, _score(score), int(bool(renorm)),
+                                _ptr(d_logits), _dtype_code(d_logits), _stream(stream)),
+           "moe_route_bwd")
+    return d_logits
+
+
+def moe_aux_loss_workspace(T: int, E: int) -> int:
+    return load().moe_aux_loss_workspace(T, E)
+
+
+def moe_aux_loss(logits, topk_ids, alpha: float, score="softmax", loss=None, counts=None,
+                 probs=None, workspace=None, stream=None):
+    """Returns (loss [1] float32, counts [E] int32, probs [E] float32)."""
+    T, E = logits.shape
+    K = topk_ids.shape[1]
+    _contig(logits, "logits")
+    dev = logits.device
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+    if probs is None:
+        probs = torch.empty(E, dtype=torch.float32, device=dev)
+    ws_bytes = moe_aux_loss_workspace(T, E)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    _check(load().moe_aux_loss(_ptr(logits), _ptr(topk_ids), T, E, K, _score(score), float(alpha),
+                               _ptr(loss), _ptr(counts), _ptr(probs), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_aux_loss")
+    return loss, counts, probs
+
+
+def moe_aux_loss_bwd(logits, counts, K: int, alpha: float, score="softmax", d_logits=None,
+                     dtype=torch.float32, accumulate: bool = False, stream=None):
+    T, E = logits.shape
+    if d_logits is None:
+        d_logits = torch.empty((T, E), dtype=dtype, device=logits.device)
+    _check(load().moe_aux_loss_bwd(_ptr(logits), _ptr(counts), T, E, K, _score(score),
+                                   float(alpha), _ptr(d_logits), _dtype_code(d_logits),
+                                   int(bool(accumulate)), _stream(stream)), "moe_aux_loss_bwd")
     return d_logits
 
 

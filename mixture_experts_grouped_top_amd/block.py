@@ -44,6 +44,12 @@ class MoEShape:
     # of the TransformerEngine MoE block): one up-projection gmm, one
     # transposed-rhs gmm over 2F for d_x_sorted, one tgmm for d_wi
     fused_wi: bool = False
+    # routing variants: how the bias enters ("logit" or "select"), grouped
+    # top-K (n_groups > 1), and the load-balancing loss weight (0 = off)
+    bias_mode: str = "logit"
+    n_groups: int = 0
+    topk_groups: int = 0
+    aux_alpha: float = 0.0
 
 
 def _round_up(a: int, b: int) -> int:
@@ -68,6 +74,12 @@ class MoEPlan:
         self.gs_T = torch.tensor([s.T], **i32)
         # forward
         self.logits = torch.empty((s.T, s.E), **f32)
+        if s.aux_alpha > 0:
+            self.aux_loss = torch.empty(1, **f32)
+            self.aux_counts = torch.empty(s.E, **i32)
+            self.aux_probs = torch.empty(s.E, **f32)
+            self.aux_ws = torch.empty(max(B.moe_aux_loss_workspace(s.T, s.E), 256),
+                                      dtype=torch.uint8, device=dev)
         self.ids = torch.empty((s.T, s.K), **i32)
         self.w = torch.empty((s.T, s.K), **f32)
         self.idx = dict(counts=torch.empty(s.E, **i32), group_sizes=torch.empty(s.E, **i32),
@@ -165,7 +177,12 @@ class MoEPlan:
         else:
             self.logits.copy_(logits)
         B.moe_route(self.logits, s.K, s.score, s.renorm, bias, topk_ids=self.ids, topk_w=self.w,
-                    stream=stream)
+                    stream=stream, bias_mode=s.bias_mode, n_groups=s.n_groups,
+                    topk_groups=s.topk_groups)
+        if s.aux_alpha > 0:
+            B.moe_aux_loss(self.logits, self.ids, s.aux_alpha, s.score, loss=self.aux_loss,
+                           counts=self.aux_counts, probs=self.aux_probs, workspace=self.aux_ws,
+                           stream=stream)
         nb = self._bytes() if self.recorder is not None else {}
         with self._rec("permute", nbytes=nb.get("permute", 0)):
             B.moe_permute(x, self.ids, s.E, s.align, s.capacity, s.capacity_layout,
@@ -259,7 +276,11 @@ class MoEPlan:
         with self._rec("permute_bwd", nbytes=nb.get("permute_bwd", 0)):
             B.moe_permute_bwd(self.d_x_sorted, ros, s.T, s.K, d_x=self.dx, stream=stream)
         B.moe_route_bwd(self.logits, self.ids, self.d_w, s.score, s.renorm, bias,
-                        d_logits=self.d_logits, stream=stream)
+                        d_logits=self.d_logits, stream=stream, bias_mode=s.bias_mode)
+        if s.aux_alpha > 0:
+            # the balancing loss enters the objective with weight one
+            B.moe_aux_loss_bwd(self.logits, self.aux_counts, s.K, s.aux_alpha, s.score,
+                               d_logits=self.d_logits, accumulate=True, stream=stream)
         if Wg is not None and self.router:
             B.moe_tgmm(x, self.d_logits, self.gs_T, out=self.d_Wg, err=self.err, stream=stream)
             B.moe_gmm(self.d_logits, Wg.unsqueeze(0), self.gs_T, trans_rhs=True, out=self.dx,

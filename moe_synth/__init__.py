@@ -61,6 +61,11 @@ class Workload:
     pad_rows_to: int = 0             # lhs row count rounded up to this (0 = none)
     w_std: float = 0.02              # std of Wg, wi_0, wi_1, wo
     seed: int = 0
+    bias_mode: str = "logit"         # "select": the bias moves only the selection
+    select_bias_std: float = 0.0     # std of the per-expert selection bias ("select")
+    n_groups: int = 0                # expert groups of grouped top-K (0 = none)
+    topk_groups: int = 0             # groups kept per token
+    aux_alpha: float = 0.0           # weight of the load-balancing loss (0 = off)
 
     @property
     def R(self) -> int:
@@ -91,6 +96,15 @@ WORKLOADS = {
                  zipf_s=1.5, n_forced_empty=3, n_chunks=4, pad_rows_to=128),
         Workload("mini_align8", 257, 128, 96, 16, 3, "bf16", "softmax", True,
                  align=8, zipf_s=1.2, n_forced_empty=2),
+        # router variants: a selection-only expert bias with grouped top-K and
+        # the load-balancing loss (sigmoid scores), and the loss with softmax
+        Workload("mini_dsv3_router", 320, 256, 192, 32, 4, "bf16", "sigmoid", True,
+                 align=16, bias_mode="select", select_bias_std=0.05, n_groups=8,
+                 topk_groups=3, aux_alpha=0.01),
+        Workload("mini_mixtral_aux", 600, 256, 384, 8, 2, "bf16", "softmax", True,
+                 aux_alpha=0.02),
+        Workload("tiny_grouped", 512, 64, 128, 8, 2, "f32", "softmax", True,
+                 n_groups=4, topk_groups=2, aux_alpha=0.01),
     ]
 }
 
@@ -191,12 +205,20 @@ def forced_empty_experts(w: Workload, seed: Optional[int] = None) -> np.ndarray:
 
 
 def gen_logit_bias(w: Workload, seed: Optional[int] = None) -> Optional[np.ndarray]:
-    """Per-expert prior added to the router logits, float32 [E], or None.
+    """Per-expert prior added to the router logits, float32 [E], or None
+    (for bias_mode "select": the selection-only bias).
 
     Zipf(s) popularity: expert e gets rank r(e) from a seeded permutation of
     1..E and prior p_r = r^-s (p_1 = 1), contributing ln p_r = -s ln r to its
     logit.  The forced-empty experts get -inf so they are never selected.
     """
+    if w.bias_mode == "select":
+        # selection-only expert bias: N(0, select_bias_std^2) per expert
+        s = w.seed if seed is None else seed
+        bias = (stream(s, w.name, "select_bias").standard_normal(w.E) * w.select_bias_std)
+        bias = bias.astype(np.float32)
+        bias[forced_empty_experts(w, seed)] = -np.inf
+        return bias
     if w.zipf_s is None and w.n_forced_empty == 0:
         return None
     s = w.seed if seed is None else seed

@@ -38,7 +38,8 @@ def test_header_declares_the_abi():
     for name in ["moe_route", "moe_route_bwd", "moe_permute", "moe_permute_bwd", "moe_gmm",
                  "moe_tgmm", "moe_swiglu", "moe_swiglu_bwd", "moe_combine", "moe_combine_bwd",
                  "moe_rows_bound", "moe_permute_workspace", "moe_status_string",
-                 "moe_abi_version"]:
+                 "moe_abi_version", "moe_aux_loss_workspace", "moe_aux_loss",
+                 "moe_aux_loss_bwd"]:
         assert name in d, name
 
 
@@ -79,11 +80,19 @@ def test_argument_checks_return_before_launch(lib):
     """Invalid arguments are rejected on the host (no device pointer is touched)."""
     P = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
     # K > E
-    assert lib.moe_route(P, None, 8, 4, 5, 0, 1, P, P, None) == -1
-    # unknown score
-    assert lib.moe_route(P, None, 8, 4, 2, 7, 1, P, P, None) == -1
+    assert lib.moe_route(P, None, 0, 0, 0, 8, 4, 5, 0, 1, P, P, None) == -1
+    # unknown score, unknown bias mode
+    assert lib.moe_route(P, None, 0, 0, 0, 8, 4, 2, 7, 1, P, P, None) == -1
+    assert lib.moe_route(P, None, 5, 0, 0, 8, 4, 2, 0, 1, P, P, None) == -1
+    # groups: E not divisible, too few candidates, topk_groups out of range
+    assert lib.moe_route(P, None, 0, 3, 1, 8, 16, 2, 0, 1, P, P, None) == -1
+    assert lib.moe_route(P, None, 1, 8, 1, 8, 16, 3, 1, 1, P, P, None) == -1
+    assert lib.moe_route(P, None, 1, 4, 5, 8, 16, 2, 1, 1, P, P, None) == -1
     # E too large
-    assert lib.moe_route_bwd(P, None, P, P, 8, 2048, 2, 0, 1, P, 0, None) == -1
+    assert lib.moe_route_bwd(P, None, 0, P, P, 8, 2048, 2, 0, 1, P, 0, None) == -1
+    # aux loss: no tokens, missing workspace
+    assert lib.moe_aux_loss(P, P, 0, 8, 2, 0, 0.1, P, None, None, P, 1 << 20, None) == -1
+    assert lib.moe_aux_loss(P, P, 16, 8, 2, 0, 0.1, P, None, None, None, 0, None) == -5
     # bad d_logits dtype is caught after the size checks
     # gmm: G = 0, M_out > M_lhs, K not a multiple of 8, bad dtype, ld < K
     args = lambda **kw: dict(dict(lhs=P, M_lhs=64, ld=64, rhs=P, ldr=64, gst=64 * 64, tr=0, gs=P,

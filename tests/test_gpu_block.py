@@ -1,6 +1,8 @@
 """The whole forward + backward chain on the GPU against the float64 oracle,
 on the seeded workloads of moe_synth (the fp32 tiny workload and scaled-down
-copies of the Mixtral, DeepSeek-V3, token-dropping and chunked workloads)."""
+copies of the Mixtral, DeepSeek-V3, token-dropping and chunked workloads,
+and the routing variants: selection-only bias, grouped top-K, balancing
+loss)."""
 import numpy as np
 import pytest
 import torch
@@ -9,10 +11,12 @@ import moe_synth as ms
 import oracle
 from mixture_experts_grouped_top_amd import MoEPlan, MoEShape
 from tests.gpu_util import TOL_BF16, TOL_F32, TOL_GRAD, assert_close, dev, host
+from tests.margins import decision_margins, selection_keys
 
 pytestmark = pytest.mark.gpu
 
-CHAIN = ["tiny", "mini_mixtral", "mini_deepseek", "mini_token_drop", "mini_chunked", "mini_align8"]
+CHAIN = ["tiny", "mini_mixtral", "mini_deepseek", "mini_token_drop", "mini_chunked", "mini_align8",
+         "mini_dsv3_router", "mini_mixtral_aux", "tiny_grouped"]
 # the same chain with the fused [wi_0 | wi_1] up-projection weight
 FUSED = ["tiny", "mini_mixtral", "mini_deepseek", "mini_chunked"]
 CASES = [(n, False) for n in CHAIN] + [(n, True) for n in FUSED]
@@ -35,16 +39,8 @@ def shape_of(w: ms.Workload, fused_wi: bool = False) -> MoEShape:
                     dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16,
                     score=w.score, renorm=w.renorm, align=w.align, capacity=w.capacity,
                     capacity_layout=False, n_chunks=w.n_chunks, pad_rows_to=w.pad_rows_to,
-                    fused_wi=fused_wi)
-
-
-def selection_margin(z32, K):
-    s = -np.sort(-z32.astype(np.float64), axis=1)
-    if K >= z32.shape[1]:
-        return np.inf
-    gap = s[:, K - 1] - s[:, K]
-    gap = gap[np.isfinite(gap)]
-    return gap.min() if gap.size else np.inf
+                    fused_wi=fused_wi, bias_mode=w.bias_mode, n_groups=w.n_groups,
+                    topk_groups=w.topk_groups, aux_alpha=w.aux_alpha)
 
 
 def run_gpu(w, inp, capacity_layout=False, fused_wi=False):
@@ -69,7 +65,9 @@ def run_oracle(w, inp, lhs_rows):
     kw = dict(score=w.score, renorm=w.renorm, bias=inp["bias"])
     f = oracle.moe_forward(inp["x"], inp["wi_0"], inp["wi_1"], inp["wo"], w.K, Wg=inp["Wg"],
                            logits=inp["logits"], align=w.align, capacity=w.capacity,
-                           n_chunks=w.n_chunks, lhs_rows=lhs_rows, **kw)
+                           n_chunks=w.n_chunks, lhs_rows=lhs_rows, bias_mode=w.bias_mode,
+                           n_groups=w.n_groups, topk_groups=w.topk_groups,
+                           aux_alpha=w.aux_alpha, **kw)
     b = oracle.moe_backward(f, inp["dy"], inp["x"], inp["wi_0"], inp["wi_1"], inp["wo"], w.K,
                             Wg=inp["Wg"], **kw)
     return f, b
@@ -91,14 +89,17 @@ def test_chain_routing_and_permutation(chain):
     if inp["Wg"] is not None:
         # the GPU router GEMM agrees with the float64 logits ...
         assert_close(host(plan.logits), f["logits"], TOL_F32, "logits")
-        # ... and every token's selection margin exceeds twice the measured
-        # difference of the biased float32 logits the two sides rank, so
-        # the selection cannot differ (a seed with a near-tie fails here)
-        z_o = oracle.biased_logits_f32(f["logits"], inp["bias"])
-        z_g = oracle.biased_logits_f32(host(plan.logits), inp["bias"])
-        fin = np.isfinite(z_o)
-        eps = float(np.max(np.abs(z_g[fin].astype(np.float64) - z_o[fin])))
-        assert selection_margin(z_o, w.K) > 2 * eps, "seeded input has a near-tie selection"
+        # ... and every decision of the selection has a margin above twice
+        # the measured difference of the keys the two sides rank (plus a few
+        # float32 ulps for score keys and group sums), so the selection
+        # cannot differ (a seed with a near-tie fails here)
+        k_o = selection_keys(f["logits"], inp["bias"], w.score, w.bias_mode)
+        k_g = selection_keys(host(plan.logits), inp["bias"], w.score, w.bias_mode)
+        fin = np.isfinite(k_o)
+        eps = float(np.max(np.abs(k_g[fin] - k_o[fin])))
+        slack = 0.0 if (w.bias_mode == "logit" and w.n_groups <= 1) else 1e-6
+        margin = decision_margins(k_o, w.K, w.n_groups, w.topk_groups).min()
+        assert margin > 2 * eps + slack, "seeded input has a near-tie selection"
     assert (host(plan.ids) == f["ids"]).all()
     for k in ("counts", "group_sizes", "group_offsets", "row_of_slot", "slot_of_row"):
         assert (host(plan.idx[k]) == f["perm"][k]).all(), k
@@ -106,6 +107,10 @@ def test_chain_routing_and_permutation(chain):
     assert_close(host(plan.w), f["w"], TOL_F32, "topk_w")
     if w.n_forced_empty:
         assert (f["perm"]["counts"][ms.forced_empty_experts(w)] == 0).all()
+    if w.aux_alpha > 0:
+        assert (host(plan.aux_counts) == f["aux_counts"]).all()
+        assert_close(host(plan.aux_probs), f["aux_probs"], TOL_F32, "aux probs")
+        assert_close(host(plan.aux_loss), np.array([f["aux_loss"]]), TOL_F32, "aux loss")
 
 
 def test_chain_forward(chain):

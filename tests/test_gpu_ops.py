@@ -8,6 +8,7 @@ import torch
 import moe_synth as ms
 import oracle
 from tests.gpu_util import (TOL_BF16, TOL_F32, assert_close, dev, dev_i32, host, max_rel, poison)
+from tests.margins import decision_margins, selection_keys
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +59,109 @@ def test_route_bwd(gpu_lib, E, K, score, renorm, dtype):
                               dtype=dtype)
     want = oracle.route_bwd(z, oi, dw, score, renorm, bias)
     assert_close(host(d), want, TOL_F32 if dtype == torch.float32 else TOL_BF16, "d_logits")
+
+
+VARIANTS = [
+    # E, K, n_groups, topk_groups, bias_mode, score, renorm
+    (256, 8, 8, 4, "select", "sigmoid", True),    # DeepSeek-V3 routing
+    (256, 8, 8, 4, "logit", "softmax", True),
+    (64, 6, 8, 3, "select", "softmax", False),
+    (160, 6, 8, 3, "select", "sigmoid", False),
+    (64, 4, 64, 4, "select", "sigmoid", True),    # one expert per group
+    (32, 2, 0, 0, "select", "sigmoid", False),    # selection bias, no groups
+    (8, 8, 4, 4, "logit", "softmax", True),       # every group and expert kept
+    (1024, 4, 32, 2, "select", "sigmoid", True),
+    (128, 3, 64, 2, "logit", "sigmoid", True),    # most groups, two experts each
+]
+
+
+@pytest.mark.parametrize("case", VARIANTS, ids=[str(c) for c in VARIANTS])
+def test_route_variants(gpu_lib, case):
+    E, K, G, TG, mode, score, renorm = case
+    g = np.random.default_rng(E * 31 + K * 7 + G)
+    T = 301
+    z = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    z[::7] = np.round(z[::7])                 # exact ties in the logits
+    if mode == "select":
+        bias = (g.standard_normal(E) * 0.05).astype(np.float32)
+    else:
+        bias = (-0.5 * np.log(g.permutation(E) + 1.0)).astype(np.float32)
+    if E >= 32:
+        bias[[1, E - 2]] = -np.inf            # never selected
+    ids, w = gpu_lib.moe_route(dev(z), K, score, renorm, bias=dev(bias), bias_mode=mode,
+                               n_groups=G, topk_groups=TG)
+    oi, ow = oracle.route(z, K, score, renorm, bias, bias_mode=mode, n_groups=G, topk_groups=TG)
+    gi = host(ids)
+    # float32 keys on the GPU, float64 in the oracle: a selection may differ
+    # only at a token whose decision margin is a few float32 ulps of the key
+    margin = decision_margins(selection_keys(z, bias, score, mode), K, G, TG)
+    same = (gi == oi).all(axis=1)
+    tie_ok = margin < (0.0 if mode == "logit" and G <= 1 else 1e-6)
+    assert (same | tie_ok).all(), np.nonzero(~(same | tie_ok))[0][:8]
+    assert same.mean() > 0.95
+    for t in np.nonzero(~same)[0]:
+        assert len(set(gi[t].tolist())) == K and ((gi[t] >= 0) & (gi[t] < E)).all()
+    assert_close(host(w)[same], ow[same], TOL_F32, "topk_w")
+
+
+@pytest.mark.parametrize("score,renorm", MODES)
+def test_route_bwd_select_bias(gpu_lib, score, renorm):
+    """With a selection-only bias the weights are scores of the logits
+    themselves, so the gradient ignores the bias."""
+    g = np.random.default_rng(5)
+    T, E, K = 263, 64, 6
+    z = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    bias = (g.standard_normal(E) * 0.05).astype(np.float32)
+    dw = g.standard_normal((T, K)).astype(np.float32)
+    oi, _ = oracle.route(z, K, score, renorm, bias, bias_mode="select", n_groups=8, topk_groups=3)
+    d = gpu_lib.moe_route_bwd(dev(z), dev_i32(oi), dev(dw), score, renorm, bias=dev(bias),
+                              bias_mode="select")
+    want = oracle.route_bwd(z, oi, dw, score, renorm, bias, bias_mode="select")
+    assert_close(host(d), want, TOL_F32, "d_logits")
+
+
+AUX = [
+    # T, E, K, score
+    (301, 8, 2, "softmax"),
+    (1000, 256, 8, "sigmoid"),
+    (700, 64, 6, "softmax"),
+    (257, 1024, 4, "sigmoid"),          # the largest expert count, several blocks
+    (1, 5, 5, "softmax"),
+]
+
+
+@pytest.mark.parametrize("case", AUX, ids=[str(c) for c in AUX])
+def test_aux_loss(gpu_lib, case):
+    T, E, K, score = case
+    g = np.random.default_rng(T + E)
+    z = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    ids = _topk_ids(g, T, E, K)
+    alpha = 0.01
+    loss, counts, probs = gpu_lib.moe_aux_loss(dev(z), dev_i32(ids), alpha, score)
+    o_loss, o_counts, o_P = oracle.aux_loss(z, ids, E, alpha, score)
+    assert (host(counts) == o_counts).all()
+    assert_close(host(probs), o_P, TOL_F32, "aux probs")
+    assert abs(float(host(loss)[0]) - o_loss) <= TOL_F32 * abs(o_loss)
+    want = oracle.aux_loss_bwd(z, o_counts, K, alpha, score)
+    d = gpu_lib.moe_aux_loss_bwd(dev(z), counts, K, alpha, score)
+    assert_close(host(d), want, TOL_F32, "aux d_logits")
+    # accumulate onto an existing gradient, in bf16
+    base = g.standard_normal((T, E)).astype(np.float32) * 1e-3
+    acc = dev(base, torch.bfloat16)
+    start = host(acc).astype(np.float64)
+    gpu_lib.moe_aux_loss_bwd(dev(z), counts, K, alpha, score, d_logits=acc, accumulate=True)
+    assert_close(host(acc), start + want, TOL_BF16, "aux d_logits accumulated")
+
+
+def test_aux_loss_no_tokens(gpu_lib):
+    """The loss divides by T: no tokens is an argument error, while the
+    gradient of no tokens is empty and succeeds."""
+    z = torch.empty((0, 16), dtype=torch.float32, device="cuda")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(gpu_lib.MoeError):
+        gpu_lib.moe_aux_loss(z, ids, 0.01, "sigmoid")
+    counts = torch.zeros(16, dtype=torch.int32, device="cuda")
+    assert gpu_lib.moe_aux_loss_bwd(z, counts, 2, 0.01, "sigmoid").shape == (0, 16)
 
 
 # ------------------------------------------------------------- permutation
