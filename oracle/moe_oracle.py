@@ -18,8 +18,8 @@ expert FFNs, forward and backward, with every intermediate kept in float64
                 "pre_bias_logits" of the MaxText DeepSeek-V3 router), grouped
                 top-K ("n_routing_groups" / "topk_routing_group"), and the
                 optional auxiliary load-balancing loss of the TransformerEngine
-                MoE block (Description: "top-K with optional grouped/sigmoid
-                scoring ... and optional auxiliary load-balancing loss").
+                MoE block (its Description lists grouped and sigmoid scoring
+                and the balancing loss as options of the fused router).
   permute       stable grouping of the routed (token, slot) pairs by expert,
                 per-expert group sizes, optional align_size padding and
                 capacity dropping.  Same pull request: the dispatch state
@@ -30,6 +30,10 @@ expert FFNs, forward and backward, with every intermediate kept in float64
                 partial sums.  MaxText "Overlap moe comms with collective
                 matmul", Description and the review of the gmm backward
                 rule and of the partial_sum shape assertion.
+  MLP biases    optional per-expert biases on the up- and down-projection
+                outputs and their gradients (per-group row sums); MaxText
+                "Overlap moe comms" pull request, Testing (MLP bias with the
+                chunked layer) and the chunked layer's w0/w1/wo bias arguments.
   swiglu        silu(gate_proj_out) * up_proj_out (TransformerEngine pull
                 request commit notes naming the two SwiGLU projection outputs).
   combine       weighted sum of each token's K expert outputs, and its
@@ -342,14 +346,17 @@ def permute_bwd(d_x_sorted, row_of_slot, T: int, K: int) -> np.ndarray:
 # Grouped GEMMs
 # ---------------------------------------------------------------------------
 
-def gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, partial=None, rows_out: int | None = None):
+def gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, partial=None, rows_out: int | None = None,
+        bias=None):
     """Grouped GEMM: for each group g, rows [o_g, o_g + n_g) of the output are
     lhs[those rows] . rhs[g] (rhs[g] is [K, N]; with trans_rhs it is stored
     [N, K] and used transposed).  With ``partial`` the result is added to a
     copy of it (in-place partial-sum accumulation).  The output may have
     fewer rows than lhs (lhs padded to a row tile, partial sum not).
     Rows at or beyond sum(group_sizes) are zero without ``partial`` and
-    equal to ``partial`` with it.
+    equal to ``partial`` with it.  ``bias`` [G, N] (the per-expert MLP bias
+    of the MaxText "Overlap moe comms" pull request's chunked layer,
+    w0_bias / w1_bias / wo_bias) adds bias[g] to every row of group g.
     """
     gs = np.asarray(group_sizes, dtype=np.int64)
     lhs = np.asarray(lhs)
@@ -370,6 +377,22 @@ def gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, partial=None, rows_out: 
             if trans_rhs:
                 W = W.T
             out[start:start + n] += _f64(lhs[start:start + n]) @ W
+            if bias is not None:
+                out[start:start + n] += _f64(bias[g])[None, :]
+        start += n
+    return out
+
+
+def group_sum(rows, group_sizes) -> np.ndarray:
+    """out[g] = sum of the rows of group g, [G, N]: the gradient of a
+    per-group bias added to those rows (zero for an empty group)."""
+    gs = np.asarray(group_sizes, dtype=np.int64)
+    rows = _f64(rows)
+    out = np.zeros((len(gs), rows.shape[1]), dtype=np.float64)
+    start = 0
+    for g in range(len(gs)):
+        n = int(gs[g])
+        out[g] = rows[start:start + n].sum(axis=0)
         start += n
     return out
 
@@ -465,7 +488,8 @@ def moe_forward(x, wi_0, wi_1, wo, K: int, *, Wg=None, logits=None, bias=None,
                 score: str = SOFTMAX, renorm: bool = True, align: int = 0,
                 capacity: int = 0, capacity_layout: bool = False,
                 n_chunks: int = 1, lhs_rows: int | None = None, bias_mode: str = LOGIT,
-                n_groups: int = 0, topk_groups: int = 0, aux_alpha: float = 0.0):
+                n_groups: int = 0, topk_groups: int = 0, aux_alpha: float = 0.0,
+                b_wi_0=None, b_wi_1=None, b_wo=None):
     """Forward pass.  Either ``Wg`` (router logits = x . Wg) or ``logits``.
 
     With n_chunks > 1 the up-projections are computed as the in-place
@@ -474,7 +498,10 @@ def moe_forward(x, wi_0, wi_1, wo, K: int, *, Wg=None, logits=None, bias=None,
     row count of the (padded) sorted-token buffer, the output rows being the
     routed rows.  bias_mode / n_groups / topk_groups select the routing
     variant of ``route``; aux_alpha > 0 adds ``aux_loss`` (returned as
-    "aux_loss", with its counts).  Returns every residual the backward needs.
+    "aux_loss", with its counts).  b_wi_0, b_wi_1 [E, F] and b_wo [E, D] are
+    optional per-expert MLP biases; under partial sums the up-projection
+    biases are added once, with the last chunk.  Returns every residual the
+    backward needs.
     """
     x = np.asarray(x)
     T, D = x.shape
@@ -493,17 +520,21 @@ def moe_forward(x, wi_0, wi_1, wo, K: int, *, Wg=None, logits=None, bias=None,
         h0 = h1 = None
         for i in range(n_chunks):
             sl = slice(i * c, (i + 1) * c)
-            h0 = gmm(xs[:, sl], wi_0[:, sl, :], gs, partial=h0, rows_out=nrows)
-            h1 = gmm(xs[:, sl], wi_1[:, sl, :], gs, partial=h1, rows_out=nrows)
+            last = i == n_chunks - 1
+            h0 = gmm(xs[:, sl], wi_0[:, sl, :], gs, partial=h0, rows_out=nrows,
+                     bias=b_wi_0 if last else None)
+            h1 = gmm(xs[:, sl], wi_1[:, sl, :], gs, partial=h1, rows_out=nrows,
+                     bias=b_wi_1 if last else None)
     else:
-        h0 = gmm(xs, wi_0, gs, rows_out=nrows)
-        h1 = gmm(xs, wi_1, gs, rows_out=nrows)
+        h0 = gmm(xs, wi_0, gs, rows_out=nrows, bias=b_wi_0)
+        h1 = gmm(xs, wi_1, gs, rows_out=nrows, bias=b_wi_1)
     act = swiglu(h0, h1)
-    y_sorted = gmm(act, wo, gs)
+    y_sorted = gmm(act, wo, gs, bias=b_wo)
     y = combine(y_sorted, P["row_of_slot"], w, T, K)
     out = dict(logits=_f64(logits), ids=ids, w=w, perm=P, x_sorted=xs, h0=h0, h1=h1,
                act=act, y_sorted=y_sorted, y=y, rows=nrows, bias_mode=bias_mode,
-               aux_alpha=aux_alpha)
+               aux_alpha=aux_alpha,
+               mlp_bias=any(b is not None for b in (b_wi_0, b_wi_1, b_wo)))
     if aux is not None:
         out["aux_loss"], out["aux_counts"], out["aux_probs"] = aux
     return out
@@ -513,7 +544,9 @@ def moe_backward(fwd, dy, x, wi_0, wi_1, wo, K: int, *, Wg=None, bias=None,
                  score: str = SOFTMAX, renorm: bool = True):
     """Backward pass for upstream dy (hand-derived, mirroring the forward as
     the TransformerEngine block's single custom VJP does).  Returns dict with
-    dx, d_wi_0, d_wi_1, d_wo, d_logits, d_w and (if Wg given) d_Wg."""
+    dx, d_wi_0, d_wi_1, d_wo, d_logits, d_w, (if Wg given) d_Wg and (with MLP
+    biases) d_b_wi_0, d_b_wi_1, d_b_wo: each bias gradient is the per-group
+    sum of the gradient rows of the output it was added to."""
     x = np.asarray(x)
     T = x.shape[0]
     P = fwd["perm"]
@@ -538,6 +571,10 @@ def moe_backward(fwd, dy, x, wi_0, wi_1, wo, K: int, *, Wg=None, bias=None,
                                            fwd["aux_alpha"], score)
     out = dict(dx=dx, d_wi_0=d_wi_0, d_wi_1=d_wi_1, d_wo=d_wo, d_logits=d_logits, d_w=d_w,
                d_y_sorted=d_ys, d_act=d_act, d_h0=d_h0, d_h1=d_h1, d_x_sorted=d_xs)
+    if fwd.get("mlp_bias", False):
+        out["d_b_wi_0"] = group_sum(d_h0, gs)
+        out["d_b_wi_1"] = group_sum(d_h1, gs)
+        out["d_b_wo"] = group_sum(d_ys, gs)
     if Wg is not None:
         out["d_Wg"] = _f64(x).T @ d_logits
         out["dx"] = dx + d_logits @ _f64(Wg).T

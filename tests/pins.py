@@ -414,7 +414,7 @@ def check_adjoints(seed=8):
 # gmm / tgmm
 # ---------------------------------------------------------------------------
 
-def _brute_gmm(lhs, rhs, gs, trans, partial, rows_out):
+def _brute_gmm(lhs, rhs, gs, trans, partial, rows_out, bias=None):
     N = len(rhs[0]) if trans else len(rhs[0][0])
     Kd = len(lhs[0])
     out = [[0.0] * N for _ in range(rows_out)] if partial is None else partial.tolist()
@@ -425,7 +425,7 @@ def _brute_gmm(lhs, rhs, gs, trans, partial, rows_out):
                 acc = 0.0
                 for k in range(Kd):
                     acc += lhs[r][k] * (rhs[g][c][k] if trans else rhs[g][k][c])
-                out[r][c] += acc
+                out[r][c] += acc + (0.0 if bias is None else bias[g][c])
             r += 1
     return np.array(out)
 
@@ -448,6 +448,41 @@ def check_gmm_bruteforce(seed=9):
             want = _brute_gmm(lhs.tolist(), rhs.tolist(), gs, trans, P, sum(gs) + 1)
             np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
             assert (got[sum(gs):] == P[sum(gs):]).all()
+            # a per-group bias on every row of its group, with and without a partial sum
+            B = g.standard_normal((G, N))
+            got = oracle.gmm(lhs, rhs, gs, trans_rhs=trans, bias=B)
+            want = _brute_gmm(lhs.tolist(), rhs.tolist(), gs, trans, None, M_lhs, B.tolist())
+            np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+            assert (got[sum(gs):] == 0).all()
+            got = oracle.gmm(lhs, rhs, gs, trans_rhs=trans, partial=P, bias=B)
+            want = _brute_gmm(lhs.tolist(), rhs.tolist(), gs, trans, P, sum(gs) + 1, B.tolist())
+            np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
+def check_group_sum(seed=17):
+    """Per-group row sums by scalar loops, zero for empty groups, and the
+    adjoint of the bias: <gmm(X, W, bias=B) - gmm(X, W), Y> = <B, group_sum(Y)>."""
+    g = _rng(seed)
+    for gs in ([3, 0, 4, 1], [0, 0, 5], [6, 0]):
+        G, M, N = len(gs), sum(gs) + 2, 4
+        Y = g.standard_normal((M, N))
+        got = oracle.group_sum(Y, gs)
+        r0 = 0
+        for gg, n in enumerate(gs):
+            for c in range(N):
+                acc = 0.0
+                for r in range(r0, r0 + n):
+                    acc += Y[r, c]
+                assert abs(got[gg, c] - acc) < 1e-13
+                if n == 0:
+                    assert got[gg, c] == 0.0
+            r0 += n
+        X = g.standard_normal((M, 3))
+        W = g.standard_normal((G, 3, N))
+        B = g.standard_normal((G, N))
+        lhs = float(((oracle.gmm(X, W, gs, bias=B) - oracle.gmm(X, W, gs)) * Y).sum())
+        rhs = float((B * got).sum())
+        assert abs(lhs - rhs) < 1e-12 * max(1.0, abs(lhs))
 
 
 def check_tgmm_bruteforce(seed=10):
@@ -542,8 +577,9 @@ def _tiny_block(g, T=24, D=6, F=5, E=5):
     return x, Wg, wi0, wi1, wo
 
 
-def _dense_token_ffn(x, ids, w, wi0, wi1, wo, kept=None):
-    """Per-token sum of its experts' SwiGLU FFNs, no grouping at all."""
+def _dense_token_ffn(x, ids, w, wi0, wi1, wo, kept=None, biases=None):
+    """Per-token sum of its experts' SwiGLU FFNs, no grouping at all
+    (biases: optional per-expert b0 [E, F], b1 [E, F], bo [E, D])."""
     T, D = x.shape
     y = np.zeros((T, D))
     for t in range(T):
@@ -552,11 +588,15 @@ def _dense_token_ffn(x, ids, w, wi0, wi1, wo, kept=None):
                 continue
             e = ids[t, j]
             F = wi0.shape[2]
-            h0 = [sum(x[t, d] * wi0[e, d, f] for d in range(D)) for f in range(F)]
-            h1 = [sum(x[t, d] * wi1[e, d, f] for d in range(D)) for f in range(F)]
+            b0, b1, bo = biases if biases is not None else (None, None, None)
+            h0 = [sum(x[t, d] * wi0[e, d, f] for d in range(D)) + (b0[e, f] if b0 is not None else 0)
+                  for f in range(F)]
+            h1 = [sum(x[t, d] * wi1[e, d, f] for d in range(D)) + (b1[e, f] if b1 is not None else 0)
+                  for f in range(F)]
             a = [h0[f] / (1 + math.exp(-h0[f])) * h1[f] for f in range(F)]
             for d in range(D):
-                y[t, d] += w[t, j] * sum(a[f] * wo[e, f, d] for f in range(F))
+                yo = sum(a[f] * wo[e, f, d] for f in range(F)) + (bo[e, d] if bo is not None else 0)
+                y[t, d] += w[t, j] * yo
     return y
 
 
@@ -580,6 +620,17 @@ def check_block_dense(seed=14):
             f2 = oracle.moe_forward(x, wi0, wi1, wo, K, Wg=Wg, score=score, renorm=renorm,
                                     capacity=C, capacity_layout=True)
             np.testing.assert_allclose(f2["y"], f["y"], rtol=1e-13, atol=1e-14)
+    # per-expert MLP biases, with align padding and with dropping
+    F = wi0.shape[2]
+    b0 = g.standard_normal((E, F))
+    b1 = g.standard_normal((E, F))
+    bo = g.standard_normal((E, x.shape[1]))
+    for (K, a, C) in [(2, 4, 0), (1, 0, 3)]:
+        f = oracle.moe_forward(x, wi0, wi1, wo, K, Wg=Wg, align=a, capacity=C,
+                               b_wi_0=b0, b_wi_1=b1, b_wo=bo)
+        kept = (f["perm"]["row_of_slot"] >= 0).reshape(-1, K)
+        want = _dense_token_ffn(x, f["ids"], f["w"], wi0, wi1, wo, kept, (b0, b1, bo))
+        np.testing.assert_allclose(f["y"], want, rtol=1e-12, atol=1e-13)
 
 
 def check_block_chunked(seed=15):
@@ -587,6 +638,14 @@ def check_block_chunked(seed=15):
     x, Wg, wi0, wi1, wo = _tiny_block(g, D=8)
     f1 = oracle.moe_forward(x, wi0, wi1, wo, 2, Wg=Wg)
     f4 = oracle.moe_forward(x, wi0, wi1, wo, 2, Wg=Wg, n_chunks=4, lhs_rows=64)
+    for k in ("h0", "h1", "y"):
+        np.testing.assert_allclose(f4[k], f1[k], rtol=1e-13, atol=1e-14)
+    # MLP biases enter once, whatever the number of chunks
+    E, F = wi0.shape[0], wi0.shape[2]
+    bk = dict(b_wi_0=g.standard_normal((E, F)), b_wi_1=g.standard_normal((E, F)),
+              b_wo=g.standard_normal((E, x.shape[1])))
+    f1 = oracle.moe_forward(x, wi0, wi1, wo, 2, Wg=Wg, **bk)
+    f4 = oracle.moe_forward(x, wi0, wi1, wo, 2, Wg=Wg, n_chunks=4, lhs_rows=64, **bk)
     for k in ("h0", "h1", "y"):
         np.testing.assert_allclose(f4[k], f1[k], rtol=1e-13, atol=1e-14)
 
@@ -602,14 +661,20 @@ def check_block_grad_fd(seed=16):
             (1, "softmax", False, 0, 4, None), (2, "sigmoid", False, 0, 0, None)]:
         b32 = None if bias is None else bias.astype(np.float32)
         kw = dict(score=score, renorm=renorm, align=a, capacity=C, bias=b32)
-        f = oracle.moe_forward(x, wi0, wi1, wo, K, Wg=Wg, **kw)
+        E, F = wi0.shape[0], wi0.shape[2]
+        # per-expert MLP biases in the cases with align padding or dropping
+        mlp = a > 0 or C > 0
+        b0, b1, bo = (g.standard_normal((E, F)), g.standard_normal((E, F)),
+                      g.standard_normal((E, x.shape[1])))
+        bk = dict(b_wi_0=b0, b_wi_1=b1, b_wo=bo) if mlp else {}
+        f = oracle.moe_forward(x, wi0, wi1, wo, K, Wg=Wg, **kw, **bk)
         z = oracle.biased_logits_f32(f["logits"], b32)
         assert _margin(z, K) > 1e-4, "selection too close to a tie for finite differences"
         grads = oracle.moe_backward(f, dy, x, wi0, wi1, wo, K, Wg=Wg, score=score, renorm=renorm,
                                     bias=b32)
         ids0 = f["ids"]
 
-        def L(xx, Wgg, a0, a1, oo):
+        def L(xx, Wgg, a0, a1, oo, c0, c1, co):
             # the selection must not move; weights are recomputed in float64
             lg = xx @ Wgg
             if b32 is not None:
@@ -617,17 +682,22 @@ def check_block_grad_fd(seed=16):
             ids, w = _route_f64(lg, K, score, renorm)
             assert (ids == ids0).all()
             P = oracle.permute(xx, ids, wi0.shape[0], align=a, capacity=C)
-            h0 = oracle.gmm(P["x_sorted"], a0, P["group_sizes"])
-            h1 = oracle.gmm(P["x_sorted"], a1, P["group_sizes"])
-            ys = oracle.gmm(oracle.swiglu(h0, h1), oo, P["group_sizes"])
+            h0 = oracle.gmm(P["x_sorted"], a0, P["group_sizes"], bias=c0)
+            h1 = oracle.gmm(P["x_sorted"], a1, P["group_sizes"], bias=c1)
+            ys = oracle.gmm(oracle.swiglu(h0, h1), oo, P["group_sizes"], bias=co)
             return float((oracle.combine(ys, P["row_of_slot"], w, xx.shape[0], K) * dy).sum())
 
         params = [x, Wg, wi0, wi1, wo]
         names = ["dx", "d_Wg", "d_wi_0", "d_wi_1", "d_wo"]
+        if mlp:
+            params += [b0, b1, bo]
+            names += ["d_b_wi_0", "d_b_wi_1", "d_b_wo"]
+        else:
+            params += [None, None, None]
         for i, name in enumerate(names):
             d = g.standard_normal(params[i].shape)
-            pp = [p.copy() for p in params]
-            pm = [p.copy() for p in params]
+            pp = [None if p is None else p.copy() for p in params]
+            pm = [None if p is None else p.copy() for p in params]
             pp[i] = params[i] + eps * d
             pm[i] = params[i] - eps * d
             fd = (L(*pp) - L(*pm)) / (2 * eps)

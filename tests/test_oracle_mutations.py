@@ -57,6 +57,12 @@ MUTATIONS = {
     "swiglu_bwd_dropped_term": ("(1.0 + h0 * (1.0 - sg))", "(1.0 + h0 * sg)"),
     "combine_bwd_missing_weight": ("d_ys[r] = w[t, j] * dy[t]", "d_ys[r] = dy[t]"),
     "permute_bwd_overwrites": ("                dx[t] += d[r]", "                dx[t] = d[r]"),
+    "mlp_bias_every_chunk": ("bias=b_wi_0 if last else None", "bias=b_wi_0"),
+    "mlp_bias_wrong_group": ("out[start:start + n] += _f64(bias[g])[None, :]",
+                             "out[start:start + n] += _f64(bias[max(g - 1, 0)])[None, :]"),
+    "group_sum_skips_first_row": ("out[g] = rows[start:start + n].sum(axis=0)",
+                                  "out[g] = rows[start + 1:start + n].sum(axis=0)"),
+    "bias_grad_wrong_operand": ('out["d_b_wo"] = group_sum(d_ys, gs)', 'out["d_b_wo"] = group_sum(d_act, gs)'),
     "backward_d_wo_wrong_operand": ('d_wo = tgmm(fwd["act"], d_ys, gs)', 'd_wo = tgmm(fwd["h1"], d_ys, gs)'),
     "backward_dx_second_gmm_not_accumulated": (
         "d_xs = gmm(d_h1, wi_1, gs, trans_rhs=True, partial=d_xs)",
