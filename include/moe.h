@@ -194,14 +194,19 @@ int moe_permute_bwd(const void* d_x_sorted, int dtype, int64_t T, int64_t D, int
  *   in_dtype is the dtype of lhs and rhs; MOE_BF16 runs on bf16 MFMA with
  *   float32 accumulation; MOE_F32 runs in float32 FMA.  out_dtype is
  *   MOE_F32 or MOE_BF16 (rounded to nearest even).
+ *   bias (device, may be NULL): [G, N] row-major in in_dtype, the per-expert
+ *   MLP bias of the [MT-Chunk] chunked layer (its w0/w1/wo bias arguments;
+ *   Testing: MLP bias with the chunked layer).  bias[g] is added to every
+ *   output row of group g, after the product and any partial sum; under
+ *   partial sums pass it with one of the calls only.
  *   Requires Kdim, N, ld_* and strides to be multiples of 8 and 16-byte
  *   aligned pointers.  G <= 1024.  If sum(group_sizes) > M_out the groups are
  *   clipped at M_out and MOE_DERR_GROUP_SIZES is raised.
  */
 int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
             int64_t rhs_group_stride, int trans_rhs, const int32_t* group_sizes, int G,
-            int64_t Kdim, int64_t N, int in_dtype, void* out, int64_t M_out, int64_t ld_out,
-            int out_dtype, int accumulate, int32_t* err, void* stream);
+            int64_t Kdim, int64_t N, int in_dtype, const void* bias, void* out, int64_t M_out,
+            int64_t ld_out, int out_dtype, int accumulate, int32_t* err, void* stream);
 
 /* moe_tgmm: transposed grouped GEMM [MT-Chunk: tgmm, output
  * (num_local_groups, in_size, out_size), zero-initialised empty groups].
@@ -221,6 +226,25 @@ int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
              int64_t Kdim, int64_t N, int in_dtype, void* out, int64_t ld_out,
              int64_t out_group_stride, int out_dtype, int accumulate, int32_t* err,
              void* stream);
+
+/* Workspace bytes moe_group_sum needs: (ceil(M / 256) + G) * N float32
+ * partial rows (16-byte aligned device memory). */
+size_t moe_group_sum_workspace(int64_t M, int G, int64_t N);
+
+/* moe_group_sum: per-group column sums, the gradient of a per-expert MLP
+ * bias [MT-Chunk chunked layer with MLP bias]:
+ *   out[g, :] (+)= sum of rows [o_g, o_g + n_g) of in,  o_g = sum_{g'<g} n_g'
+ *   in [M, N] with row stride ld_in, in in_dtype; out [G, N] row-major in
+ *   out_dtype (MOE_F32 or MOE_BF16).  Sums are float32 in a fixed order
+ *   (deterministic).  An empty group gives zero (accumulate == 0) or leaves
+ *   out[g] unchanged (accumulate != 0).  valid_rows (device, [G], may be
+ *   NULL): rows past valid_rows[g] in group g are zero and are skipped (as
+ *   in moe_tgmm).  N and ld_in multiples of 8, 16-byte aligned pointers,
+ *   G <= 1024; sum(group_sizes) > M raises MOE_DERR_GROUP_SIZES.
+ */
+int moe_group_sum(const void* in, int64_t ld_in, int in_dtype, const int32_t* group_sizes,
+                  const int32_t* valid_rows, int G, int64_t M, int64_t N, void* out, int out_dtype,
+                  int accumulate, void* workspace, size_t ws_bytes, int32_t* err, void* stream);
 
 /* -------------------------------------------------------------------- SwiGLU
  * moe_swiglu: act = silu(h0) * h1, silu(z) = z / (1 + e^-z), computed in

@@ -11,6 +11,7 @@ from ._binding import (MOE_BF16, MOE_BIAS_LOGIT, MOE_BIAS_SELECT, MOE_DERR_EXPER
                        MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS, MOE_F32, MOE_SIGMOID, MOE_SOFTMAX,
                        SIGNATURES, MoeError, load, moe_aux_loss, moe_aux_loss_bwd,
                        moe_aux_loss_workspace, moe_combine, moe_combine_bwd, moe_gmm,
+                       moe_group_sum, moe_group_sum_workspace, ABI_VERSION,
                        moe_permute, moe_permute_bwd, moe_permute_workspace, moe_route,
                        moe_route_bwd, moe_rows_bound, moe_swiglu, moe_swiglu_bwd, moe_tgmm,
                        LIB_PATH)
@@ -21,6 +22,7 @@ __all__ = [
     "moe_aux_loss_workspace", "moe_aux_loss", "moe_aux_loss_bwd", "MOE_BIAS_LOGIT",
     "MOE_BIAS_SELECT",
     "moe_permute_workspace", "moe_permute", "moe_permute_bwd", "moe_gmm", "moe_tgmm",
+    "moe_group_sum_workspace", "moe_group_sum", "ABI_VERSION",
     "moe_swiglu", "moe_swiglu_bwd", "moe_combine", "moe_combine_bwd", "MoEPlan", "MoEShape",
     "MOE_F32", "MOE_BF16", "MOE_SOFTMAX", "MOE_SIGMOID", "MOE_DERR_EXPERT_ID",
     "MOE_DERR_GROUP_SIZES", "MOE_DERR_ROWS",

@@ -21,6 +21,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
+ABI_VERSION = 5   # moe_abi_version() of the library these signatures describe
 
 # Entry points (name -> (restype, argtypes)); must match include/moe.h.
 _P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -38,8 +39,11 @@ SIGNATURES = {
     "moe_permute": (_I, [_P, _I, _L, _L, _P, _I, _I, _I, _I, _I, _P, _L, _P, _P, _P, _P, _P,
                          _P, _S, _P, _P]),
     "moe_permute_bwd": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _I, _P]),
-    "moe_gmm": (_I, [_P, _L, _L, _P, _L, _L, _I, _P, _I, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
+    "moe_gmm": (_I, [_P, _L, _L, _P, _L, _L, _I, _P, _I, _L, _L, _I, _P, _P, _L, _L, _I, _I, _P,
+                     _P]),
     "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
+    "moe_group_sum_workspace": (_S, [_L, _I, _L]),
+    "moe_group_sum": (_I, [_P, _L, _I, _P, _P, _I, _L, _L, _P, _I, _I, _P, _S, _P, _P]),
     "moe_swiglu": (_I, [_P, _P, _I, _L, _L, _L, _P, _I, _P]),
     "moe_swiglu_bwd": (_I, [_P, _P, _I, _L, _P, _L, _L, _P, _P, _L, _I, _P]),
     "moe_combine": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _P, _P]),
@@ -65,6 +69,9 @@ def load():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
+        if lib.moe_abi_version() != ABI_VERSION:
+            raise MoeError(f"{LIB_PATH} reports ABI version {lib.moe_abi_version()}, the binding "
+                           f"expects {ABI_VERSION}: rebuild it")
         _lib = lib
     return _lib
 
@@ -269,10 +276,11 @@ def moe_permute_bwd(d_x_sorted, row_of_slot, T: int, K: int, d_x=None, accumulat
 # ----------------------------------------------------------- grouped GEMMs
 
 def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: Optional[int] = None,
-            out_dtype=None, accumulate: bool = False, err=None, stream=None):
-    """out[rows of g] (+)= lhs[rows of g] . rhs[g] (rhs[g]: [K, N], or [N, K]
-    used transposed).  lhs and out may be strided 2-D views (unit column
-    stride); rhs a 3-D view with unit last stride."""
+            out_dtype=None, accumulate: bool = False, err=None, stream=None, bias=None):
+    """out[rows of g] (+)= lhs[rows of g] . rhs[g] (+ bias[g]) (rhs[g]: [K, N],
+    or [N, K] used transposed; bias: optional contiguous [G, N] in lhs's
+    dtype).  lhs and out may be strided 2-D views (unit column stride); rhs
+    a 3-D view with unit last stride."""
     M_lhs, Kd = lhs.shape
     ld_lhs = _rowmajor(lhs, "lhs")
     if rhs.dim() != 3 or rhs.stride(2) != 1:
@@ -285,6 +293,10 @@ def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: 
         raise MoeError("group_sizes must have one entry per rhs group")
     if lhs.dtype != rhs.dtype:
         raise MoeError("lhs and rhs dtypes differ")
+    if bias is not None:
+        _contig(bias, "bias")
+        if tuple(bias.shape) != (G, N) or bias.dtype != lhs.dtype:
+            raise MoeError("bias must be [G, N] in the dtype of lhs")
     if out is None:
         M_out = M_lhs if rows_out is None else rows_out
         odt = lhs.dtype if out_dtype is None else out_dtype
@@ -293,7 +305,7 @@ def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: 
     ld_out = _rowmajor(out, "out")
     _check(load().moe_gmm(_ptr(lhs), M_lhs, ld_lhs, _ptr(rhs), rhs.stride(1), rhs.stride(0),
                           int(bool(trans_rhs)), _ptr(group_sizes), G, Kd, N, _dtype_code(lhs),
-                          _ptr(out), M_out, ld_out, _dtype_code(out), int(bool(accumulate)),
+                          _ptr(bias), _ptr(out), M_out, ld_out, _dtype_code(out), int(bool(accumulate)),
                           _ptr(err), _stream(stream)), "moe_gmm")
     return out
 
@@ -320,6 +332,34 @@ def moe_tgmm(lhs, rhs, group_sizes, out=None, out_dtype=None, accumulate: bool =
                            _ptr(out),
                            out.stride(1), out.stride(0), _dtype_code(out), int(bool(accumulate)),
                            _ptr(err), _stream(stream)), "moe_tgmm")
+    return out
+
+
+def moe_group_sum_workspace(M: int, G: int, N: int) -> int:
+    return load().moe_group_sum_workspace(M, G, N)
+
+
+def moe_group_sum(x, group_sizes, out=None, out_dtype=torch.float32, accumulate: bool = False,
+                  valid_rows=None, workspace=None, err=None, stream=None):
+    """out[g] (+)= sum of the rows of group g of x [M, N] -> [G, N] (the
+    gradient of a per-group bias).  x may be a strided 2-D view."""
+    M, N = x.shape
+    G = group_sizes.numel()
+    if out is None:
+        out = torch.empty((G, N), dtype=out_dtype, device=x.device)
+    _contig(out, "out")
+    if tuple(out.shape) != (G, N):
+        raise MoeError("out must be [G, N]")
+    if valid_rows is not None and valid_rows.numel() != G:
+        raise MoeError("valid_rows must have one entry per group")
+    ws_bytes = moe_group_sum_workspace(M, G, N)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+    _check(load().moe_group_sum(_ptr(x), _rowmajor(x, "x"), _dtype_code(x), _ptr(group_sizes),
+                                _ptr(valid_rows), G, M, N, _ptr(out), _dtype_code(out),
+                                int(bool(accumulate)), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _ptr(err),
+                                _stream(stream)), "moe_group_sum")
     return out
 
 

@@ -50,6 +50,10 @@ class MoEShape:
     n_groups: int = 0
     topk_groups: int = 0
     aux_alpha: float = 0.0
+    # per-expert MLP biases on the up- and down-projection outputs (added in
+    # the GEMM epilogues; under partial sums with the last chunk) and their
+    # gradients as per-group row sums
+    mlp_bias: bool = False
 
 
 def _round_up(a: int, b: int) -> int:
@@ -120,6 +124,17 @@ class MoEPlan:
             self.d_wi_0 = torch.empty((s.E, s.D, s.F), **act)
             self.d_wi_1 = torch.empty((s.E, s.D, s.F), **act)
         self.d_wo = torch.empty((s.E, s.F, s.D), **act)
+        if s.mlp_bias:
+            if s.fused_wi:
+                self.d_b_wi = torch.empty((s.E, 2 * s.F), **act)
+                self.d_b_wi_0, self.d_b_wi_1 = self.d_b_wi[:, :s.F], self.d_b_wi[:, s.F:]
+            else:
+                self.d_b_wi_0 = torch.empty((s.E, s.F), **act)
+                self.d_b_wi_1 = torch.empty((s.E, s.F), **act)
+            self.d_b_wo = torch.empty((s.E, s.D), **act)
+            self.gsum_ws = torch.empty(
+                max(B.moe_group_sum_workspace(self.rows, s.E, max(2 * s.F, s.D)), 256),
+                dtype=torch.uint8, device=dev)
         # router weight gradient kept in float32 (a [D, E] reduction over all tokens)
         self.d_Wg = torch.empty((1, s.D, s.E), **f32) if router else None
         self.recorder = None   # optional callable(kind, flops, bytes) -> context manager
@@ -167,11 +182,17 @@ class MoEPlan:
             swiglu_bwd=2 * Rp * F * bh + 3 * Rp * F * b,
             permute_bwd=R * D * b + T * D * b + T * K * 4)
 
-    def forward(self, x, wi_0, wi_1, wo, Wg=None, logits=None, bias=None, stream=None, wi=None):
+    def forward(self, x, wi_0, wi_1, wo, Wg=None, logits=None, bias=None, stream=None, wi=None,
+                mlp_bias=None):
         """y = sum_j w[t,j] FFN_{e(t,j)}(x[t]).  Either Wg (router GEMM on the
         device) or precomputed float32 logits.  With fused_wi the
-        up-projection weight is wi [E, D, 2F] (wi_0, wi_1 unused)."""
+        up-projection weight is wi [E, D, 2F] (wi_0, wi_1 unused).  With
+        mlp_bias set in the shape, mlp_bias is a dict of the per-expert biases
+        "wi_0", "wi_1" [E, F] ("wi" [E, 2F] with fused_wi) and "wo" [E, D]."""
         s = self.s
+        mb = mlp_bias if s.mlp_bias else {}
+        if s.mlp_bias and (not mb or mb.get("wo") is None):
+            raise B.MoeError("the shape has MLP biases: pass mlp_bias")
         if logits is None:
             B.moe_gmm(x, Wg.unsqueeze(0), self.gs_T, out=self.logits, err=self.err, stream=stream)
         else:
@@ -191,46 +212,55 @@ class MoEPlan:
         gs = self.group_sizes
         R = self.kept_rows
         if s.fused_wi:
-            self._up_fused(wi, gs, R, stream)
+            self._up_fused(wi, gs, R, stream, mb.get("wi"))
         elif s.n_chunks > 1:
             c = s.D // s.n_chunks
             for i in range(s.n_chunks):
                 xs = self.x_sorted[:, i * c:(i + 1) * c]
+                last = i == s.n_chunks - 1   # the biases enter once, with the last chunk
                 with self._rec("gmm_up_chunk", 2.0 * R * c * s.F):
                     B.moe_gmm(xs, wi_0[:, i * c:(i + 1) * c, :], gs, out=self.h0,
-                              accumulate=i > 0, err=self.err, stream=stream)
+                              accumulate=i > 0, err=self.err, stream=stream,
+                              bias=mb.get("wi_0") if last else None)
                 with self._rec("gmm_up_chunk", 2.0 * R * c * s.F):
                     B.moe_gmm(xs, wi_1[:, i * c:(i + 1) * c, :], gs, out=self.h1,
-                              accumulate=i > 0, err=self.err, stream=stream)
+                              accumulate=i > 0, err=self.err, stream=stream,
+                              bias=mb.get("wi_1") if last else None)
         else:
             with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
-                B.moe_gmm(self.x_sorted, wi_0, gs, out=self.h0, err=self.err, stream=stream)
+                B.moe_gmm(self.x_sorted, wi_0, gs, out=self.h0, err=self.err, stream=stream,
+                          bias=mb.get("wi_0"))
             with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
-                B.moe_gmm(self.x_sorted, wi_1, gs, out=self.h1, err=self.err, stream=stream)
+                B.moe_gmm(self.x_sorted, wi_1, gs, out=self.h1, err=self.err, stream=stream,
+                          bias=mb.get("wi_1"))
         with self._rec("swiglu", nbytes=nb.get("swiglu", 0)):
             B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
         with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
-            B.moe_gmm(self.act, wo, gs, out=self.y_sorted, err=self.err, stream=stream)
+            B.moe_gmm(self.act, wo, gs, out=self.y_sorted, err=self.err, stream=stream,
+                      bias=mb.get("wo"))
         with self._rec("combine", nbytes=nb.get("combine", 0)):
             B.moe_combine(self.y_sorted, self.idx["row_of_slot"], self.w, y=self.y,
                           stream=stream)
         return self.y
 
-    def _up_fused(self, wi, gs, R, stream):
+    def _up_fused(self, wi, gs, R, stream, b_wi=None):
         s = self.s
         if s.n_chunks > 1:
             c = s.D // s.n_chunks
             for i in range(s.n_chunks):
                 with self._rec("gmm_up_chunk", 4.0 * R * c * s.F):
                     B.moe_gmm(self.x_sorted[:, i * c:(i + 1) * c], wi[:, i * c:(i + 1) * c, :],
-                              gs, out=self.h, accumulate=i > 0, err=self.err, stream=stream)
+                              gs, out=self.h, accumulate=i > 0, err=self.err, stream=stream,
+                              bias=b_wi if i == s.n_chunks - 1 else None)
         else:
             with self._rec("gmm_nn", 4.0 * R * s.D * s.F):
-                B.moe_gmm(self.x_sorted, wi, gs, out=self.h, err=self.err, stream=stream)
+                B.moe_gmm(self.x_sorted, wi, gs, out=self.h, err=self.err, stream=stream,
+                          bias=b_wi)
 
     def backward(self, dy, x, wi_0, wi_1, wo, Wg=None, bias=None, stream=None, wi=None):
         """Gradients for upstream dy: fills dx, d_wi_0, d_wi_1 (halves of d_wi
-        with fused_wi), d_wo, d_logits and (with the router) d_Wg."""
+        with fused_wi), d_wo, d_logits, (with the router) d_Wg and (with MLP
+        biases) d_b_wi_0, d_b_wi_1 (halves of d_b_wi with fused_wi), d_b_wo."""
         s = self.s
         gs = self.group_sizes
         R = self.kept_rows
@@ -273,6 +303,22 @@ class MoEPlan:
             with self._rec("tgmm", 2.0 * R * s.D * s.F):
                 B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream,
                            valid_rows=self.idx["counts"])
+        if s.mlp_bias:
+            # bias gradients: per-group sums of the rows of the gradient of
+            # the output each bias was added to (padding rows are zero)
+            cnt = self.idx["counts"]
+            with self._rec("group_sum"):
+                B.moe_group_sum(self.d_y_sorted, gs, out=self.d_b_wo, valid_rows=cnt,
+                                workspace=self.gsum_ws, err=self.err, stream=stream)
+            if s.fused_wi:
+                with self._rec("group_sum"):
+                    B.moe_group_sum(self.d_h, gs, out=self.d_b_wi, valid_rows=cnt,
+                                    workspace=self.gsum_ws, err=self.err, stream=stream)
+            else:
+                for dh, db in ((self.d_h0, self.d_b_wi_0), (self.d_h1, self.d_b_wi_1)):
+                    with self._rec("group_sum"):
+                        B.moe_group_sum(dh, gs, out=db, valid_rows=cnt, workspace=self.gsum_ws,
+                                        err=self.err, stream=stream)
         with self._rec("permute_bwd", nbytes=nb.get("permute_bwd", 0)):
             B.moe_permute_bwd(self.d_x_sorted, ros, s.T, s.K, d_x=self.dx, stream=stream)
         B.moe_route_bwd(self.logits, self.ids, self.d_w, s.score, s.renorm, bias,

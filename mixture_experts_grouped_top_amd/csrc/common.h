@@ -28,6 +28,53 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
+// Wave 0 scans the group sizes: row_base[g] (rows clipped to max_rows) and,
+// if tile_base != nullptr, tile_base[g] = tiles of groups < g, where a group
+// of n rows owns ceil(n / BM) * ntn tiles.
+__device__ inline void scan_groups(const int32_t* __restrict__ gsz, int G, int64_t max_rows, int BMv,
+                            int ntn, int* row_base, int* tile_base, int32_t* err) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int64_t rows_run = 0;
+  int tiles_run = 0;
+  bool bad = false;
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    int n = (g < G) ? gsz[g] : 0;
+    if (n < 0) { n = 0; bad = true; }
+    int64_t incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    int64_t start = rows_run + incl - n;
+    int64_t end = rows_run + incl;
+    if (end > max_rows) bad = true;
+    if (start > max_rows) start = max_rows;
+    if (end > max_rows) end = max_rows;
+    const int neff = static_cast<int>(end - start);
+    int t = tile_base ? ((neff + BMv - 1) / BMv) * ntn : 0;
+    int tincl = t;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(tincl, o, 64);
+      if (lane >= o) tincl += u;
+    }
+    if (g < G) {
+      row_base[g] = static_cast<int>(start);
+      if (tile_base) tile_base[g] = tiles_run + tincl - t;
+    }
+    rows_run += __shfl(incl, 63, 64);
+    tiles_run += __shfl(tincl, 63, 64);
+  }
+  if (lane == 0) {
+    row_base[G] = static_cast<int>(rows_run > max_rows ? max_rows : rows_run);
+    if (tile_base) tile_base[G] = tiles_run;
+  }
+  if (bad && lane == 0 && err) atomicOr(err, MOE_DERR_GROUP_SIZES);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static __forceinline__ float load(const float* p) { return *p; }

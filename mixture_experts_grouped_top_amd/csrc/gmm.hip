@@ -52,53 +52,6 @@ constexpr int kMaxG = 1024;
 
 __device__ __forceinline__ int64_t lmin(int64_t a, int64_t b) { return a < b ? a : b; }
 
-// Wave 0 scans the group sizes: row_base[g] (rows clipped to max_rows) and,
-// if tile_base != nullptr, tile_base[g] = tiles of groups < g, where a group
-// of n rows owns ceil(n / BM) * ntn tiles.
-__device__ void scan_groups(const int32_t* __restrict__ gsz, int G, int64_t max_rows, int BMv,
-                            int ntn, int* row_base, int* tile_base, int32_t* err) {
-  if (threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
-  int64_t rows_run = 0;
-  int tiles_run = 0;
-  bool bad = false;
-  for (int g0 = 0; g0 < G; g0 += 64) {
-    const int g = g0 + lane;
-    int n = (g < G) ? gsz[g] : 0;
-    if (n < 0) { n = 0; bad = true; }
-    int64_t incl = n;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t u = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += u;
-    }
-    int64_t start = rows_run + incl - n;
-    int64_t end = rows_run + incl;
-    if (end > max_rows) bad = true;
-    if (start > max_rows) start = max_rows;
-    if (end > max_rows) end = max_rows;
-    const int neff = static_cast<int>(end - start);
-    int t = tile_base ? ((neff + BMv - 1) / BMv) * ntn : 0;
-    int tincl = t;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(tincl, o, 64);
-      if (lane >= o) tincl += u;
-    }
-    if (g < G) {
-      row_base[g] = static_cast<int>(start);
-      if (tile_base) tile_base[g] = tiles_run + tincl - t;
-    }
-    rows_run += __shfl(incl, 63, 64);
-    tiles_run += __shfl(tincl, 63, 64);
-  }
-  if (lane == 0) {
-    row_base[G] = static_cast<int>(rows_run > max_rows ? max_rows : rows_run);
-    if (tile_base) tile_base[G] = tiles_run;
-  }
-  if (bad && lane == 0 && err) atomicOr(err, MOE_DERR_GROUP_SIZES);
-}
-
 // Position of a group's local tile l among mt x nt tiles: column blocks of
 // kNB tiles, row-major inside a block (consecutive indices cover about
 // 32 / kNB row tiles x kNB column tiles, so the tiles that run together on
@@ -496,6 +449,7 @@ struct MfmaArgs {
   int accumulate;
   int32_t* err;
   const int32_t* valid = nullptr;   // tgmm: leading rows of each group that may be non-zero
+  const bf16_t* bias = nullptr;      // gmm: per-group bias rows [G, N], added to the output
 };
 
 // MFMAs of one substep (q = 0 .. NM-1) with NO other operations between
@@ -799,7 +753,8 @@ struct Stages {
 // operand stages, free once the contraction has ended with a barrier.
 template <int TM, int TN, typename TO>
 __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO* o, int64_t ldo,
-                                           int rv, int cv, int accumulate) {
+                                           int rv, int cv, int accumulate,
+                                           const bf16_t* bias = nullptr) {
   constexpr int WC = TN / 2;
   constexpr int SROW = WC * 4 + 16;
   constexpr int CPR = WC / 8;                 // 8-column chunks per slab row
@@ -836,6 +791,12 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
           load8(p, old);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += old[e];
+        }
+        if (bias) {
+          float b[8];
+          load8(bias + gcol, b);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += b[e];
         }
         if (accumulate) store8(p, v);
         else store8_nt(p, v);
@@ -898,7 +859,8 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
     B.setup(B_COLK ? bg + col0 : bg + col0 * a.ld_rhs, a.ld_rhs, cv);
     if constexpr (PAIR) contract2(smem, A, B, a.Kdim, acc, fa, fb);
     else contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
-    store_tile(acc, smem, out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate);
+    store_tile(acc, smem, out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate,
+               a.bias ? a.bias + g * a.N + col0 : nullptr);
   }
   if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
 }
@@ -952,7 +914,7 @@ __global__ __launch_bounds__(NT) void gmm_f32_kernel(
     const float* __restrict__ lhs, int64_t ld_lhs, const float* __restrict__ rhs, int64_t ld_rhs,
     int64_t rhs_gs, const int32_t* __restrict__ gsz, int G, int64_t Kdim, int64_t N,
     float* __restrict__ out_f, bf16_t* __restrict__ out_h, int64_t M_out, int64_t ld_out,
-    int accumulate, int32_t* err) {
+    int accumulate, int32_t* err, const float* __restrict__ bias) {
   __shared__ float As[FK][FB + 4];
   __shared__ float Bs[FK][FB + 4];
   __shared__ int row_base[kMaxG + 1];
@@ -1008,8 +970,9 @@ __global__ __launch_bounds__(NT) void gmm_f32_kernel(
         const int64_t c = col0 + tx * 4 + j;
         if (r < rv && c < N) {
           const int64_t off = (row0 + r) * ld_out + c;
-          if (out_f) store_out(out_f + off, acc[i][j], accumulate);
-          else store_out(out_h + off, acc[i][j], accumulate);
+          const float v = bias ? acc[i][j] + bias[g * N + c] : acc[i][j];
+          if (out_f) store_out(out_f + off, v, accumulate);
+          else store_out(out_h + off, v, accumulate);
         }
       }
   }
@@ -1097,8 +1060,8 @@ using namespace moe;
 MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs,
                     int64_t ld_rhs, int64_t rhs_group_stride, int trans_rhs,
                     const int32_t* group_sizes, int G, int64_t Kdim, int64_t N, int in_dtype,
-                    void* out, int64_t M_out, int64_t ld_out, int out_dtype, int accumulate,
-                    int32_t* err, void* stream) {
+                    const void* bias, void* out, int64_t M_out, int64_t ld_out, int out_dtype,
+                    int accumulate, int32_t* err, void* stream) {
   if (G < 1 || G > kMaxG || M_lhs < 0 || M_out < 0 || M_out > M_lhs || Kdim < 0 || N < 0)
     return MOE_ERR_ARG;
   if (M_out > INT32_MAX) return MOE_ERR_ARG;
@@ -1112,10 +1075,12 @@ MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* 
   if (M_out == 0 || N == 0) return MOE_OK;
   if (!lhs || !rhs || !group_sizes || !out || !aligned16(lhs) || !aligned16(rhs) || !aligned16(out))
     return MOE_ERR_ARG;
+  if (bias && !aligned16(bias)) return MOE_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == MOE_BF16) {
     MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
                rhs_group_stride, group_sizes, G, M_out, Kdim, N, out, ld_out, 0, accumulate, err};
+    a.bias = static_cast<const bf16_t*>(bias);
     // narrow outputs and single-step contractions use a 256 x 128 tile;
     // small groups (fewer than 512 rows per group on average) use 128-row
     // tiles, two workgroups per CU
@@ -1166,12 +1131,12 @@ MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* 
       hipLaunchKernelGGL(gmm_f32_kernel<true>, dim3(grid), dim3(NT), 0, st,
                          static_cast<const float*>(lhs), ld_lhs, static_cast<const float*>(rhs),
                          ld_rhs, rhs_group_stride, group_sizes, G, Kdim, N, of, oh, M_out, ld_out,
-                         accumulate, err);
+                         accumulate, err, static_cast<const float*>(bias));
     else
       hipLaunchKernelGGL(gmm_f32_kernel<false>, dim3(grid), dim3(NT), 0, st,
                          static_cast<const float*>(lhs), ld_lhs, static_cast<const float*>(rhs),
                          ld_rhs, rhs_group_stride, group_sizes, G, Kdim, N, of, oh, M_out, ld_out,
-                         accumulate, err);
+                         accumulate, err, static_cast<const float*>(bias));
   }
   return launch_status();
 }

@@ -37,7 +37,7 @@ __all__ = [
     "Workload", "WORKLOADS", "get_workload", "stream", "bf16_round",
     "bf16_bits", "bf16_from_bits", "gen_x", "gen_gate", "gen_expert_weight",
     "gen_expert_weights", "gen_logit_bias", "gen_uniform_logits", "gen_dy",
-    "gen_logits_normal", "forced_empty_experts",
+    "gen_logits_normal", "forced_empty_experts", "gen_mlp_bias",
 ]
 
 
@@ -66,6 +66,7 @@ class Workload:
     n_groups: int = 0                # expert groups of grouped top-K (0 = none)
     topk_groups: int = 0             # groups kept per token
     aux_alpha: float = 0.0           # weight of the load-balancing loss (0 = off)
+    mlp_bias_std: float = 0.0        # std of the per-expert MLP biases (0 = no biases)
 
     @property
     def R(self) -> int:
@@ -105,6 +106,13 @@ WORKLOADS = {
                  aux_alpha=0.02),
         Workload("tiny_grouped", 512, 64, 128, 8, 2, "f32", "softmax", True,
                  n_groups=4, topk_groups=2, aux_alpha=0.01),
+        # per-expert MLP biases on wi_0, wi_1 and wo: fp32, with align_size
+        # padding, and under the chunked partial sums
+        Workload("tiny_bias", 512, 64, 128, 8, 2, "f32", "softmax", True, mlp_bias_std=0.1),
+        Workload("mini_bias_align", 300, 256, 192, 32, 8, "bf16", "sigmoid", True,
+                 align=128, zipf_s=1.2, n_forced_empty=4, mlp_bias_std=0.1),
+        Workload("mini_bias_chunked", 333, 512, 160, 16, 4, "bf16", "softmax", True,
+                 zipf_s=1.5, n_forced_empty=3, n_chunks=4, pad_rows_to=128, mlp_bias_std=0.1),
     ]
 }
 
@@ -187,6 +195,17 @@ def gen_expert_weight(w: Workload, name: str, e: int, seed: Optional[int] = None
 def gen_expert_weights(w: Workload, name: str, seed: Optional[int] = None) -> np.ndarray:
     """All experts' weights stacked: [E, D, F] (wi_0, wi_1) or [E, F, D] (wo)."""
     return np.stack([gen_expert_weight(w, name, e, seed) for e in range(w.E)])
+
+
+def gen_mlp_bias(w: Workload, name: str, seed: Optional[int] = None) -> Optional[np.ndarray]:
+    """Per-expert MLP bias of projection `name`: wi_0/wi_1 -> [E, F], wo ->
+    [E, D]; ~ N(0, mlp_bias_std^2) in the workload dtype, or None."""
+    if w.mlp_bias_std <= 0:
+        return None
+    s = w.seed if seed is None else seed
+    g = stream(s, w.name, "bias_" + name)
+    shape = (w.E, w.D) if name == "wo" else (w.E, w.F)
+    return _store(w, g.standard_normal(shape, dtype=np.float32), w.mlp_bias_std)
 
 
 def forced_empty_experts(w: Workload, seed: Optional[int] = None) -> np.ndarray:

@@ -39,7 +39,7 @@ def test_header_declares_the_abi():
                  "moe_tgmm", "moe_swiglu", "moe_swiglu_bwd", "moe_combine", "moe_combine_bwd",
                  "moe_rows_bound", "moe_permute_workspace", "moe_status_string",
                  "moe_abi_version", "moe_aux_loss_workspace", "moe_aux_loss",
-                 "moe_aux_loss_bwd"]:
+                 "moe_aux_loss_bwd", "moe_group_sum_workspace", "moe_group_sum"]:
         assert name in d, name
 
 
@@ -73,7 +73,10 @@ def test_workspace_and_status(lib):
     assert moe.moe_permute_workspace(4096, 8, 256) % 256 == 0
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.moe_status_string(code)
-    assert lib.moe_abi_version() >= 1
+    assert lib.moe_abi_version() == moe.ABI_VERSION
+    # group-sum partial rows: (ceil(M / 256) + G) * N float32
+    assert moe.moe_group_sum_workspace(1000, 8, 64) == (4 + 8) * 64 * 4
+    assert moe.moe_group_sum_workspace(0, 3, 16) == 3 * 16 * 4
 
 
 def test_argument_checks_return_before_launch(lib):
@@ -102,8 +105,8 @@ def test_argument_checks_return_before_launch(lib):
     def gmm(**kw):
         a = args(**kw)
         return lib.moe_gmm(a["lhs"], a["M_lhs"], a["ld"], a["rhs"], a["ldr"], a["gst"], a["tr"],
-                           a["gs"], a["G"], a["Kd"], a["N"], a["it"], a["out"], a["M_out"],
-                           a["ldo"], a["ot"], a["acc"], None, None)
+                           a["gs"], a["G"], a["Kd"], a["N"], a["it"], a.get("bias"), a["out"],
+                           a["M_out"], a["ldo"], a["ot"], a["acc"], None, None)
     assert gmm(G=0) == -1
     assert gmm(M_out=65) == -1
     assert gmm(Kd=60, ld=60) == -1
@@ -111,6 +114,14 @@ def test_argument_checks_return_before_launch(lib):
     assert gmm(ot=9) == -2
     assert gmm(ld=32) == -1
     assert gmm(G=5000) == -1
+    assert gmm(bias=ctypes.c_void_p(18)) == -1      # misaligned bias
+    # group sum: N not a multiple of 8, G too large, missing or short workspace, bad dtype
+    W = ctypes.c_void_p(256)
+    assert lib.moe_group_sum(P, 12, 1, P, None, 2, 10, 12, P, 0, 0, W, 1 << 20, None, None) == -1
+    assert lib.moe_group_sum(P, 64, 1, P, None, 1025, 10, 64, P, 0, 0, W, 1 << 20, None, None) == -1
+    assert lib.moe_group_sum(P, 64, 1, P, None, 2, 10, 64, P, 0, 0, None, 0, None, None) == -5
+    assert lib.moe_group_sum(P, 64, 1, P, None, 2, 10, 64, P, 0, 0, W, 64, None, None) == -5
+    assert lib.moe_group_sum(P, 64, 4, P, None, 2, 10, 64, P, 0, 0, W, 1 << 20, None, None) == -2
     # tgmm: output group stride too small
     assert lib.moe_tgmm(P, 64, P, 64, P, None, 2, 10, 64, 64, 1, P, 64, 64, 1, 0, None, None) == -1
     # permute: rows below the static bound, missing workspace

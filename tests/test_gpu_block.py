@@ -16,9 +16,11 @@ from tests.margins import decision_margins, selection_keys
 pytestmark = pytest.mark.gpu
 
 CHAIN = ["tiny", "mini_mixtral", "mini_deepseek", "mini_token_drop", "mini_chunked", "mini_align8",
-         "mini_dsv3_router", "mini_mixtral_aux", "tiny_grouped"]
+         "mini_dsv3_router", "mini_mixtral_aux", "tiny_grouped", "tiny_bias", "mini_bias_align",
+         "mini_bias_chunked"]
 # the same chain with the fused [wi_0 | wi_1] up-projection weight
-FUSED = ["tiny", "mini_mixtral", "mini_deepseek", "mini_chunked"]
+FUSED = ["tiny", "mini_mixtral", "mini_deepseek", "mini_chunked", "mini_bias_align",
+         "mini_bias_chunked"]
 CASES = [(n, False) for n in CHAIN] + [(n, True) for n in FUSED]
 
 
@@ -31,7 +33,9 @@ def workload_inputs(w: ms.Workload):
     Wg = ms.gen_gate(w) if w.logits == "gemm" else None
     logits = ms.gen_uniform_logits(w) if w.logits == "uniform" else None
     bias = ms.gen_logit_bias(w)
-    return dict(x=x, wi_0=wi0, wi_1=wi1, wo=wo, dy=dy, Wg=Wg, logits=logits, bias=bias)
+    mlp = {k: ms.gen_mlp_bias(w, k) for k in ("wi_0", "wi_1", "wo")}
+    return dict(x=x, wi_0=wi0, wi_1=wi1, wo=wo, dy=dy, Wg=Wg, logits=logits, bias=bias,
+                mlp=mlp if w.mlp_bias_std > 0 else None)
 
 
 def shape_of(w: ms.Workload, fused_wi: bool = False) -> MoEShape:
@@ -40,7 +44,8 @@ def shape_of(w: ms.Workload, fused_wi: bool = False) -> MoEShape:
                     score=w.score, renorm=w.renorm, align=w.align, capacity=w.capacity,
                     capacity_layout=False, n_chunks=w.n_chunks, pad_rows_to=w.pad_rows_to,
                     fused_wi=fused_wi, bias_mode=w.bias_mode, n_groups=w.n_groups,
-                    topk_groups=w.topk_groups, aux_alpha=w.aux_alpha)
+                    topk_groups=w.topk_groups, aux_alpha=w.aux_alpha,
+                    mlp_bias=w.mlp_bias_std > 0)
 
 
 def run_gpu(w, inp, capacity_layout=False, fused_wi=False):
@@ -55,7 +60,13 @@ def run_gpu(w, inp, capacity_layout=False, fused_wi=False):
     logits = dev(inp["logits"]) if inp["logits"] is not None else None
     bias = dev(inp["bias"]) if inp["bias"] is not None else None
     wi = torch.cat([W["wi_0"], W["wi_1"]], dim=2).contiguous() if fused_wi else None
-    plan.forward(x, W["wi_0"], W["wi_1"], W["wo"], Wg=Wg, logits=logits, bias=bias, wi=wi)
+    mb = None
+    if inp["mlp"] is not None:
+        mb = {k: dev(v, td) for k, v in inp["mlp"].items()}
+        if fused_wi:
+            mb["wi"] = torch.cat([mb["wi_0"], mb["wi_1"]], dim=1).contiguous()
+    plan.forward(x, W["wi_0"], W["wi_1"], W["wo"], Wg=Wg, logits=logits, bias=bias, wi=wi,
+                 mlp_bias=mb)
     plan.backward(dev(inp["dy"], td), x, W["wi_0"], W["wi_1"], W["wo"], Wg=Wg, bias=bias, wi=wi)
     torch.cuda.synchronize()
     return plan
@@ -63,11 +74,13 @@ def run_gpu(w, inp, capacity_layout=False, fused_wi=False):
 
 def run_oracle(w, inp, lhs_rows):
     kw = dict(score=w.score, renorm=w.renorm, bias=inp["bias"])
+    mlp = inp["mlp"] or {}
     f = oracle.moe_forward(inp["x"], inp["wi_0"], inp["wi_1"], inp["wo"], w.K, Wg=inp["Wg"],
                            logits=inp["logits"], align=w.align, capacity=w.capacity,
                            n_chunks=w.n_chunks, lhs_rows=lhs_rows, bias_mode=w.bias_mode,
                            n_groups=w.n_groups, topk_groups=w.topk_groups,
-                           aux_alpha=w.aux_alpha, **kw)
+                           aux_alpha=w.aux_alpha, b_wi_0=mlp.get("wi_0"),
+                           b_wi_1=mlp.get("wi_1"), b_wo=mlp.get("wo"), **kw)
     b = oracle.moe_backward(f, inp["dy"], inp["x"], inp["wi_0"], inp["wi_1"], inp["wo"], w.K,
                             Wg=inp["Wg"], **kw)
     return f, b
@@ -135,9 +148,12 @@ def test_chain_backward(chain):
     assert_close(host(plan.dx), b["dx"], tol, "dx")
     if inp["Wg"] is not None:
         assert_close(host(plan.d_Wg)[0], b["d_Wg"], tol, "d_Wg")
-    # empty experts get exactly zero weight gradients
+    bias_grads = ("d_b_wo", "d_b_wi_0", "d_b_wi_1") if inp["mlp"] is not None else ()
+    for k in bias_grads:
+        assert_close(host(getattr(plan, k)), b[k], tol, k)
+    # empty experts get exactly zero weight (and bias) gradients
     empty = np.where(f["perm"]["group_sizes"] == 0)[0]
-    for k in ("d_wo", "d_wi_0", "d_wi_1"):
+    for k in ("d_wo", "d_wi_0", "d_wi_1") + bias_grads:
         assert (host(getattr(plan, k))[empty] == 0).all()
 
 

@@ -306,8 +306,9 @@ def _draw(g, shape, dt):
 TD = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
+@pytest.mark.parametrize("with_bias", [False, True], ids=["", "bias"])
 @pytest.mark.parametrize("case", GMM_CASES, ids=[f"{c[0]}-{c[1]}x{c[2]}-t{int(c[5])}-{c[6]}{c[7]}-a{int(c[8])}" for c in GMM_CASES])
-def test_gmm(gpu_lib, case):
+def test_gmm(gpu_lib, case, with_bias):
     name, Kd, N, extra, short, trans, it, ot, acc = case
     gs = np.array(GS[name], dtype=np.int32)
     G = len(gs)
@@ -319,9 +320,10 @@ def test_gmm(gpu_lib, case):
     P = _draw(g, (M_out, N), ot) if acc else None
     out = dev(P, TD[ot]) if acc else poison(torch.empty((M_out, N), dtype=TD[ot], device="cuda"))
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bias = _draw(g, (G, N), it) if with_bias else None
     gpu_lib.moe_gmm(dev(lhs, TD[it]), dev(rhs, TD[it]), dev_i32(gs), trans_rhs=trans, out=out,
-                    accumulate=acc, err=err)
-    want = oracle.gmm(lhs, rhs, gs, trans_rhs=trans, partial=P, rows_out=M_out)
+                    accumulate=acc, err=err, bias=None if bias is None else dev(bias, TD[it]))
+    want = oracle.gmm(lhs, rhs, gs, trans_rhs=trans, partial=P, rows_out=M_out, bias=bias)
     got = host(out)
     tol = TOL_F32 if ot == "f32" else TOL_BF16
     assert_close(got, want, tol, "gmm")
@@ -395,6 +397,60 @@ def test_gmm_strided_chunks(gpu_lib):
                         accumulate=i > 0)
     want = oracle.gmm(x, w, gs, rows_out=int(gs.sum()))
     assert_close(host(out), want, TOL_F32, "chunked gmm")
+
+
+GROUP_SUM_CASES = [
+    # groups, N, in, out, accumulate, valid rows, strided input
+    ("ragged", 136, "bf16", "f32", False, False, False),
+    ("ragged", 520, "f32", "f32", True, False, False),
+    ("empty_first", 264, "bf16", "bf16", False, True, False),
+    ("two_big", 1032, "bf16", "f32", False, True, True),    # several 256-row tiles per group
+    ("one_group", 8, "bf16", "bf16", True, False, False),
+    ("all_empty", 64, "bf16", "f32", False, False, False),
+    ("all_empty", 64, "f32", "bf16", True, False, False),
+    ("many", 136, "bf16", "f32", False, True, False),
+    ("max_groups", 72, "f32", "f32", False, False, True),
+]
+
+
+@pytest.mark.parametrize("case", GROUP_SUM_CASES, ids=[str(c) for c in GROUP_SUM_CASES])
+def test_group_sum(gpu_lib, case):
+    name, N, it, ot, acc, use_valid, strided = case
+    gs = np.array(GS[name], dtype=np.int32)
+    G = len(gs)
+    g = np.random.default_rng(N * 3 + G)
+    M = int(gs.sum()) + 9                      # rows past the groups are ignored
+    x = _draw(g, (M, N), it)
+    valid = None
+    if use_valid:
+        valid = np.minimum(gs, g.integers(0, 300, G)).astype(np.int32)
+        off = np.concatenate([[0], np.cumsum(gs)])
+        for e in range(G):
+            x[off[e] + valid[e]:off[e + 1]] = 0    # what valid_rows asserts
+    if strided:
+        wide = dev(np.concatenate([x, _draw(g, (M, 8), it)], axis=1), TD[it])
+        xd = wide[:, :N]
+    else:
+        xd = dev(x, TD[it])
+    P = _draw(g, (G, N), ot) if acc else None
+    out = dev(P, TD[ot]) if acc else poison(torch.empty((G, N), dtype=TD[ot], device="cuda"))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gpu_lib.moe_group_sum(xd, dev_i32(gs), out=out, accumulate=acc, err=err,
+                          valid_rows=None if valid is None else dev_i32(valid))
+    want = oracle.group_sum(x, gs) + (P if acc else 0)
+    got = host(out)
+    assert_close(got, want, TOL_F32 if ot == "f32" else TOL_BF16, "group_sum")
+    for e in np.where(gs == 0)[0]:
+        assert (got[e] == (P[e] if acc else 0)).all()
+    assert host(err)[0] == 0
+
+
+def test_group_sum_deterministic(gpu_lib):
+    gs = np.array(GS["two_big"], dtype=np.int32)
+    x = dev(np.random.default_rng(2).standard_normal((int(gs.sum()), 264)).astype(np.float32))
+    a = gpu_lib.moe_group_sum(x, dev_i32(gs))
+    b = gpu_lib.moe_group_sum(x, dev_i32(gs))
+    assert torch.equal(a, b)
 
 
 TGMM_CASES = [
