@@ -49,6 +49,8 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import fp8_oracle as F8
+
 SOFTMAX = "softmax"
 SIGMOID = "sigmoid"
 LOGIT = "logit"      # a per-expert bias added to the logits (selection and weights)
@@ -489,7 +491,7 @@ def moe_forward(x, wi_0, wi_1, wo, K: int, *, Wg=None, logits=None, bias=None,
                 capacity: int = 0, capacity_layout: bool = False,
                 n_chunks: int = 1, lhs_rows: int | None = None, bias_mode: str = LOGIT,
                 n_groups: int = 0, topk_groups: int = 0, aux_alpha: float = 0.0,
-                b_wi_0=None, b_wi_1=None, b_wo=None):
+                b_wi_0=None, b_wi_1=None, b_wo=None, fp8: bool = False):
     """Forward pass.  Either ``Wg`` (router logits = x . Wg) or ``logits``.
 
     With n_chunks > 1 the up-projections are computed as the in-place
@@ -500,8 +502,10 @@ def moe_forward(x, wi_0, wi_1, wo, K: int, *, Wg=None, logits=None, bias=None,
     variant of ``route``; aux_alpha > 0 adds ``aux_loss`` (returned as
     "aux_loss", with its counts).  b_wi_0, b_wi_1 [E, F] and b_wo [E, D] are
     optional per-expert MLP biases; under partial sums the up-projection
-    biases are added once, with the last chunk.  Returns every residual the
-    backward needs.
+    biases are added once, with the last chunk.  fp8: the expert GEMMs take
+    FP8 operands with current scaling (``fp8_oracle``): x_sorted and act
+    e4m3 per tensor, the expert weights e4m3 per expert (no chunking).
+    Returns every residual the backward needs.
     """
     x = np.asarray(x)
     T, D = x.shape
@@ -515,7 +519,15 @@ def moe_forward(x, wi_0, wi_1, wo, K: int, *, Wg=None, logits=None, bias=None,
                 rows=nrows if lhs_rows is None else lhs_rows)
     xs = P["x_sorted"]
     gs = P["group_sizes"]
-    if n_chunks > 1:
+    q8 = {}
+    if fp8:
+        assert n_chunks == 1, "the FP8 variant is unchunked"
+        q8["x"] = F8.quantize_tensor(xs, F8.E4M3)
+        for name, wt in (("wi_0", wi_0), ("wi_1", wi_1), ("wo", wo)):
+            q8[name] = F8.quantize_experts(wt, F8.E4M3)
+        h0 = gmm(q8["x"][2], q8["wi_0"][2], gs, rows_out=nrows, bias=b_wi_0)
+        h1 = gmm(q8["x"][2], q8["wi_1"][2], gs, rows_out=nrows, bias=b_wi_1)
+    elif n_chunks > 1:
         c = D // n_chunks
         h0 = h1 = None
         for i in range(n_chunks):
@@ -529,12 +541,16 @@ def moe_forward(x, wi_0, wi_1, wo, K: int, *, Wg=None, logits=None, bias=None,
         h0 = gmm(xs, wi_0, gs, rows_out=nrows, bias=b_wi_0)
         h1 = gmm(xs, wi_1, gs, rows_out=nrows, bias=b_wi_1)
     act = swiglu(h0, h1)
-    y_sorted = gmm(act, wo, gs, bias=b_wo)
+    if fp8:
+        q8["act"] = F8.quantize_tensor(act, F8.E4M3)
+        y_sorted = gmm(q8["act"][2], q8["wo"][2], gs, bias=b_wo)
+    else:
+        y_sorted = gmm(act, wo, gs, bias=b_wo)
     y = combine(y_sorted, P["row_of_slot"], w, T, K)
     out = dict(logits=_f64(logits), ids=ids, w=w, perm=P, x_sorted=xs, h0=h0, h1=h1,
                act=act, y_sorted=y_sorted, y=y, rows=nrows, bias_mode=bias_mode,
                aux_alpha=aux_alpha,
-               mlp_bias=any(b is not None for b in (b_wi_0, b_wi_1, b_wo)))
+               mlp_bias=any(b is not None for b in (b_wi_0, b_wi_1, b_wo)), fp8=q8 or None)
     if aux is not None:
         out["aux_loss"], out["aux_counts"], out["aux_probs"] = aux
     return out
@@ -554,14 +570,31 @@ def moe_backward(fwd, dy, x, wi_0, wi_1, wo, K: int, *, Wg=None, bias=None,
     ros = P["row_of_slot"]
     nrows = fwd["rows"]
     d_ys, d_w = combine_bwd(dy, fwd["y_sorted"], ros, fwd["w"], nrows)
-    d_act = gmm(d_ys, wo, gs, trans_rhs=True)
-    d_wo = tgmm(fwd["act"], d_ys, gs)
+    q8 = fwd.get("fp8")
+    if q8:
+        # backward GEMMs: gradients e5m2 per tensor, the forward's e4m3
+        # operands reused (the second quantized copy of each)
+        g8 = {"d_y_sorted": F8.quantize_tensor(d_ys, F8.E5M2)}
+        d_act = gmm(g8["d_y_sorted"][2], q8["wo"][2], gs, trans_rhs=True)
+        d_wo = tgmm(q8["act"][2], g8["d_y_sorted"][2], gs)
+    else:
+        d_act = gmm(d_ys, wo, gs, trans_rhs=True)
+        d_wo = tgmm(fwd["act"], d_ys, gs)
     d_h0, d_h1 = swiglu_bwd(fwd["h0"], fwd["h1"], d_act)
     xs = fwd["x_sorted"][:nrows]
-    d_xs = gmm(d_h0, wi_0, gs, trans_rhs=True)
-    d_xs = gmm(d_h1, wi_1, gs, trans_rhs=True, partial=d_xs)
-    d_wi_0 = tgmm(xs, d_h0, gs)
-    d_wi_1 = tgmm(xs, d_h1, gs)
+    if q8:
+        g8["d_h0"] = F8.quantize_tensor(d_h0, F8.E5M2)
+        g8["d_h1"] = F8.quantize_tensor(d_h1, F8.E5M2)
+        xd = q8["x"][2][:nrows]
+        d_xs = gmm(g8["d_h0"][2], q8["wi_0"][2], gs, trans_rhs=True)
+        d_xs = gmm(g8["d_h1"][2], q8["wi_1"][2], gs, trans_rhs=True, partial=d_xs)
+        d_wi_0 = tgmm(xd, g8["d_h0"][2], gs)
+        d_wi_1 = tgmm(xd, g8["d_h1"][2], gs)
+    else:
+        d_xs = gmm(d_h0, wi_0, gs, trans_rhs=True)
+        d_xs = gmm(d_h1, wi_1, gs, trans_rhs=True, partial=d_xs)
+        d_wi_0 = tgmm(xs, d_h0, gs)
+        d_wi_1 = tgmm(xs, d_h1, gs)
     dx = permute_bwd(d_xs, ros, T, K)
     d_logits = route_bwd(fwd["logits"], fwd["ids"], d_w, score, renorm, bias,
                          fwd.get("bias_mode", LOGIT))
@@ -571,6 +604,8 @@ def moe_backward(fwd, dy, x, wi_0, wi_1, wo, K: int, *, Wg=None, bias=None,
                                            fwd["aux_alpha"], score)
     out = dict(dx=dx, d_wi_0=d_wi_0, d_wi_1=d_wi_1, d_wo=d_wo, d_logits=d_logits, d_w=d_w,
                d_y_sorted=d_ys, d_act=d_act, d_h0=d_h0, d_h1=d_h1, d_x_sorted=d_xs)
+    if q8:
+        out["fp8"] = g8
     if fwd.get("mlp_bias", False):
         out["d_b_wi_0"] = group_sum(d_h0, gs)
         out["d_b_wi_1"] = group_sum(d_h1, gs)

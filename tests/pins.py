@@ -703,3 +703,140 @@ def check_block_grad_fd(seed=16):
             fd = (L(*pp) - L(*pm)) / (2 * eps)
             an = float((grads[name] * d).sum())
             assert abs(fd - an) < 1e-6 * max(1.0, abs(fd)), (name, score, renorm, fd, an)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (current scaling, e4m3 forward / e5m2 backward)
+# ---------------------------------------------------------------------------
+
+def check_fp8_codes_vs_torch(seed=18):
+    """Decoding every code, and encoding in-range values (random, exact ties,
+    subnormals), agree with torch's float8 conversions, an independent
+    implementation of the same OCP formats."""
+    import torch
+    F8 = oracle.fp8
+    g = _rng(seed)
+    for fmt, dt in ((F8.E4M3, torch.float8_e4m3fn), (F8.E5M2, torch.float8_e5m2)):
+        codes = np.arange(256, dtype=np.uint8)
+        mine = F8.decode(codes, fmt)
+        th = torch.from_numpy(codes).view(dt).float().numpy().astype(np.float64)
+        assert ((mine == th) | (np.isnan(mine) & np.isnan(th))).all(), fmt
+        v = (g.standard_normal(20000) * np.exp(g.uniform(-14, 12, 20000))).astype(np.float32)
+        # midpoints between neighbouring finite values (ties) and their negatives
+        fin = np.sort(mine[np.isfinite(mine) & (mine >= 0)])
+        mids = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+        v = np.concatenate([v, mids, -mids, np.float32([0.0, -0.0])])
+        v = v[np.abs(v) <= F8.fmax(fmt)]
+        got = F8.encode(v.astype(np.float64), fmt)
+        want = torch.from_numpy(v).to(dt).view(torch.uint8).numpy()
+        assert (got == want).all(), (fmt, v[got != want][:5])
+
+
+def check_fp8_saturation_and_scaling():
+    F8 = oracle.fp8
+    # beyond the largest finite value: saturate, keep the sign
+    assert list(F8.encode([449.0, 1e9, -1e9, 464.0], F8.E4M3)) == [0x7E, 0x7E, 0xFE, 0x7E]
+    assert list(F8.encode([57345.0, 1e30, -61440.0], F8.E5M2)) == [0x7B, 0x7B, 0xFB]
+    # ties to even: 1 + 1/16 -> 1 (mantissa 0), 1 + 3/16 -> 1.25 (mantissa 2)
+    assert list(F8.encode([1.0625, 1.1875], F8.E4M3)) == [0x38, 0x3A]
+    # smallest subnormals: 2^-9 (e4m3) and 2^-16 (e5m2); half of them rounds to 0
+    assert list(F8.encode([2.0 ** -9, 2.0 ** -10, 2.0 ** -16], F8.E4M3)) == [0x01, 0x00, 0x00]
+    assert list(F8.encode([2.0 ** -16, 3 * 2.0 ** -17], F8.E5M2)) == [0x01, 0x02]
+    # scale = fmax / amax in float32; amax 0 -> 1; the amax element maps to fmax
+    s, si = F8.scales(np.float32([2.0, 0.0, 3.0]), F8.E4M3)
+    assert s[0] == 224.0 and s[1] == 1.0 and si[0] == np.float32(1 / 224.0)
+    assert s[2] == np.float32(np.float32(448.0) / np.float32(3.0))
+    x = np.array([[3.0, -1.0, 0.001]], np.float32)
+    q, si, d = F8.quantize_tensor(x, F8.E4M3)
+    assert q[0, 0] == 0x7E and d[0, 0] == 448.0 * float(si)
+    # per-expert scaling: each expert's amax maps to fmax
+    w = np.stack([np.full((2, 3), 0.5, np.float32), np.full((2, 3), -8.0, np.float32)])
+    q, si, d = F8.quantize_experts(w, F8.E5M2)
+    assert (q[0] == 0x7B).all() and (q[1] == 0xFB).all()
+    # 57344 * float32(1 / scale) is the amax up to the rounding of 1 / scale
+    np.testing.assert_allclose(d, w.astype(np.float64), rtol=1e-7)
+
+
+def _fp8_deq_loop(x, fmt, per_expert=False):
+    """Current scaling written out with scalar loops over the pinned
+    encode/decode: amax, float32 scale, float32 product, code, value."""
+    F8 = oracle.fp8
+    x = np.asarray(x, dtype=np.float32)
+    units = [x[e] for e in range(x.shape[0])] if per_expert else [x]
+    out = []
+    for u in units:
+        am = np.float32(0.0)
+        for val in u.reshape(-1):
+            am = max(am, np.float32(abs(val)))
+        s = np.float32(1.0) if am == 0 else np.float32(np.float32(F8.fmax(fmt)) / am)
+        si = np.float32(np.float32(1.0) / s)
+        flat = [float(F8.decode(F8.encode([float(np.float32(val * s))], fmt), fmt)[0]) * float(si)
+                for val in u.reshape(-1)]
+        out.append(np.array(flat).reshape(u.shape))
+    return np.stack(out) if per_expert else out[0]
+
+
+def check_fp8_block_bruteforce(seed=19):
+    """The FP8 forward and backward of a tiny block against per-token scalar
+    loops over operands quantized by ``_fp8_deq_loop``: x, act e4m3 per
+    tensor, weights e4m3 per expert, the gradients d_y_sorted, d_h0, d_h1
+    e5m2 per tensor."""
+    g = _rng(seed)
+    x, Wg, wi0, wi1, wo = _tiny_block(g, T=12, D=4, F=3, E=3)
+    x, Wg = x.astype(np.float32), Wg.astype(np.float32)
+    wi0, wi1, wo = (w.astype(np.float32) for w in (wi0, wi1, wo))
+    dy = g.standard_normal(x.shape).astype(np.float32)
+    K = 2
+    f = oracle.moe_forward(x, wi0, wi1, wo, K, Wg=Wg, align=2, fp8=True)
+    b = oracle.moe_backward(f, dy, x, wi0, wi1, wo, K, Wg=Wg)
+    P = f["perm"]
+    gs, rows = P["group_sizes"], f["rows"]
+    xs = P["x_sorted"].astype(np.float32)
+    xd = _fp8_deq_loop(xs, "e4m3")
+    w0d, w1d, wod = (_fp8_deq_loop(w, "e4m3", per_expert=True) for w in (wi0, wi1, wo))
+    grp = np.repeat(np.arange(len(gs)), gs)            # group of each routed row
+    R = len(grp)
+    F, D = wi0.shape[2], wi0.shape[1]
+    h0 = np.zeros((rows, F))
+    h1 = np.zeros((rows, F))
+    for r in range(R):
+        for c in range(F):
+            h0[r, c] = sum(xd[r, k] * w0d[grp[r], k, c] for k in range(D))
+            h1[r, c] = sum(xd[r, k] * w1d[grp[r], k, c] for k in range(D))
+    np.testing.assert_allclose(f["h0"], h0, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(f["h1"], h1, rtol=1e-12, atol=1e-13)
+    act = h0 / (1 + np.exp(-h0)) * h1
+    ad = _fp8_deq_loop(act, "e4m3")
+    ys = np.zeros((rows, D))
+    for r in range(R):
+        for c in range(D):
+            ys[r, c] = sum(ad[r, k] * wod[grp[r], k, c] for k in range(F))
+    np.testing.assert_allclose(f["y_sorted"], ys, rtol=1e-12, atol=1e-13)
+    # backward: d_y_sorted rows are w * dy of their token (pinned elsewhere)
+    dysd = _fp8_deq_loop(b["d_y_sorted"], "e5m2")
+    d_act = np.zeros((rows, F))
+    d_wo = np.zeros_like(wo, dtype=np.float64)
+    for r in range(R):
+        for c in range(F):
+            d_act[r, c] = sum(dysd[r, k] * wod[grp[r], c, k] for k in range(D))
+            for k in range(D):
+                d_wo[grp[r], c, k] += ad[r, c] * dysd[r, k]
+    np.testing.assert_allclose(b["d_act"], d_act, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(b["d_wo"], d_wo, rtol=1e-12, atol=1e-13)
+    sg = 1 / (1 + np.exp(-h0))
+    dh0 = d_act * h1 * sg * (1 + h0 * (1 - sg))
+    dh1 = d_act * h0 * sg
+    dh0d, dh1d = _fp8_deq_loop(dh0, "e5m2"), _fp8_deq_loop(dh1, "e5m2")
+    d_xs = np.zeros((rows, D))
+    d_wi0 = np.zeros_like(wi0, dtype=np.float64)
+    for r in range(R):
+        for k in range(D):
+            d_xs[r, k] = sum(dh0d[r, c] * w0d[grp[r], k, c] + dh1d[r, c] * w1d[grp[r], k, c]
+                             for c in range(F))
+            for c in range(F):
+                d_wi0[grp[r], k, c] += xd[r, k] * dh0d[r, c]
+    np.testing.assert_allclose(b["d_x_sorted"], d_xs, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(b["d_wi_0"], d_wi0, rtol=1e-12, atol=1e-13)
+    # and the FP8 block stays within the formats' rounding of the exact block
+    e = oracle.moe_forward(x, wi0, wi1, wo, K, Wg=Wg, align=2)
+    assert np.abs(f["y"] - e["y"]).max() <= 0.15 * np.abs(e["y"]).max()

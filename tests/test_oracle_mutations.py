@@ -63,6 +63,15 @@ MUTATIONS = {
     "group_sum_skips_first_row": ("out[g] = rows[start:start + n].sum(axis=0)",
                                   "out[g] = rows[start + 1:start + n].sum(axis=0)"),
     "bias_grad_wrong_operand": ('out["d_b_wo"] = group_sum(d_ys, gs)', 'out["d_b_wo"] = group_sum(d_act, gs)'),
+    "fp8_ties_away": ("r = np.round(a / quantum) * quantum", "r = np.floor(a / quantum + 0.5) * quantum",
+                      "fp8"),
+    "fp8_no_saturation": ("r = np.minimum(r, top)", "r = r", "fp8"),
+    "fp8_scale_inverted": ("f / np.where(am > 0, am, np.float32(1))",
+                           "np.where(am > 0, am, np.float32(1)) / f", "fp8"),
+    "fp8_backward_in_e4m3": ('g8 = {"d_y_sorted": F8.quantize_tensor(d_ys, F8.E5M2)}',
+                             'g8 = {"d_y_sorted": F8.quantize_tensor(d_ys, F8.E4M3)}'),
+    "fp8_weights_per_tensor": ("q8[name] = F8.quantize_experts(wt, F8.E4M3)",
+                               "q8[name] = (None, None, F8.quantize_tensor(wt.reshape(wt.shape[0] * wt.shape[1], -1), F8.E4M3)[2].reshape(wt.shape))"),
     "backward_d_wo_wrong_operand": ('d_wo = tgmm(fwd["act"], d_ys, gs)', 'd_wo = tgmm(fwd["h1"], d_ys, gs)'),
     "backward_dx_second_gmm_not_accumulated": (
         "d_xs = gmm(d_h1, wi_1, gs, trans_rhs=True, partial=d_xs)",
@@ -73,10 +82,11 @@ MUTATIONS = {
 }
 
 
-def _mutant_module(old, new):
-    src = inspect.getsource(om)
+def _mutant_module(old, new, base=om):
+    src = inspect.getsource(base)
     assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
     mod = types.ModuleType("oracle_mutant")
+    mod.__package__ = "oracle"          # its relative imports resolve in the oracle package
     exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
     return mod
 
@@ -94,7 +104,14 @@ def _run_all_pins():
 
 @pytest.mark.parametrize("mutation", sorted(MUTATIONS))
 def test_mutation_is_caught(mutation, monkeypatch):
-    old, new = MUTATIONS[mutation]
+    old, new, *where = MUTATIONS[mutation]
+    if where == ["fp8"]:
+        # the FP8 module: every user (the pins and the block) sees the mutant
+        mod = _mutant_module(old, new, oracle.fp8)
+        monkeypatch.setattr(oracle, "fp8", mod)
+        monkeypatch.setattr(om, "F8", mod)
+        assert _run_all_pins(), f"no pin caught mutation {mutation}"
+        return
     mod = _mutant_module(old, new)
     for fname in dir(om):
         obj = getattr(om, fname)
