@@ -59,6 +59,8 @@ enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
 /* How a per-expert routing bias enters: added to the logits (selection and
  * weights), or added to the scores for the selection only. */
 enum { MOE_BIAS_LOGIT = 0, MOE_BIAS_SELECT = 1 };
+/* FP8 formats (OCP): E4M3FN (bias 7, fmax 448) and E5M2 (bias 15, fmax 57344) */
+enum { MOE_FP8_E4M3 = 0, MOE_FP8_E5M2 = 1 };
 
 /* bits OR-ed into the device error word */
 enum {
@@ -245,6 +247,91 @@ size_t moe_group_sum_workspace(int64_t M, int G, int64_t N);
 int moe_group_sum(const void* in, int64_t ld_in, int in_dtype, const int32_t* group_sizes,
                   const int32_t* valid_rows, int G, int64_t M, int64_t N, void* out, int out_dtype,
                   int accumulate, void* workspace, size_t ws_bytes, int32_t* err, void* stream);
+
+/* ------------------------------------------------------------------- FP8
+ * The quantization=fp8 recipe of [MT-GG] (current-tensor scaling, e4m3 in
+ * the forward, e5m2 in the backward, two quantized copies of each operand)
+ * with the per-expert weight amax of [TE-MoE] commit notes.  Every FP8 GEMM
+ * below takes both operands contraction-contiguous; the quantizer writes the
+ * transposed copy a GEMM needs.  FP8 buffers are bytes; strides in bytes
+ * (= elements).
+ */
+
+/* Workspace bytes of moe_fp8_amax_scale (16-byte aligned device memory). */
+size_t moe_fp8_scale_workspace(int64_t rows, int64_t cols, int G);
+
+/* moe_fp8_amax_scale: current scaling of x [rows, cols] (row stride ld,
+ * dtype MOE_BF16 or MOE_F32) split into G equal blocks of rows / G rows (G = 1:
+ * the whole tensor; G = E over a weight viewed as [E * a, b]: per expert).
+ * Writes scales [3 G] float32: amax[g] = max |x| of block g, scale[g] =
+ * fmax / amax[g] (1 if amax is 0), scale_inv[g] = 1 / scale[g] (correctly
+ * rounded float32 divisions).  Requires rows % G == 0, cols and ld
+ * multiples of 8.  Deterministic.
+ */
+int moe_fp8_amax_scale(const void* x, int64_t ld, int dtype, int64_t rows, int64_t cols, int G,
+                       int fmt, float* scales, void* workspace, size_t ws_bytes, void* stream);
+
+/* Column count P of a transposed copy in the padded layout: 64 * (ceil(rows /
+ * 64) + G - 1) bounds the sum over groups of their rows rounded up to 64. */
+int64_t moe_fp8_padded_rows(int64_t rows, int G);
+
+/* moe_fp8_quantize: q = fp8(float32(x) * scale), the float32 product rounded
+ * to the nearest FP8 value (ties to even), magnitudes above fmax saturated to
+ * fmax, the sign kept.  x [rows, cols] (row stride ld) is split into groups
+ * of group_sizes[g] consecutive rows (device, [G], G <= 1024); scale is
+ * scale[g] (per_group != 0) or scale[0].
+ *   q (may be NULL): row-wise copy [rows, cols], row stride ld_q; only rows
+ *     inside groups are written.
+ *   qt (may be NULL): transposed copy.  qt_group_stride == 0: one [cols, P]
+ *     matrix (row stride ld_qt >= moe_fp8_padded_rows(rows, G)); group g's
+ *     rows start at column 64 * sum_{g'<g} ceil(n_g' / 64) and the columns up
+ *     to the group's next multiple of 64 are zero (the layout moe_tgmm_fp8
+ *     reads).  qt_group_stride > 0: group g at qt + g * qt_group_stride as
+ *     [cols, n_g] with row stride ld_qt (>= n_g); only the group's rows are
+ *     written (the per-expert weight copy moe_gmm_fp8 reads).
+ *   cols, ld, ld_q multiples of 8; ld_qt, qt_group_stride multiples of 16;
+ *   16-byte aligned pointers.
+ */
+int moe_fp8_quantize(const void* x, int64_t ld, int dtype, int64_t rows, int64_t cols,
+                     const int32_t* group_sizes, int G, const float* scale, int per_group, int fmt,
+                     void* q, int64_t ld_q, void* qt, int64_t ld_qt, int64_t qt_group_stride,
+                     int32_t* err, void* stream);
+
+/* moe_gmm_fp8: grouped GEMM on FP8 operands (bf16 MFMA semantics of moe_gmm
+ * with trans_rhs = 1):
+ *   out[o_g + i, :] (+)= sa * sb[g] * lhs[o_g + i, :Kdim] . B_g^T (+ bias[g])
+ *   lhs [M_lhs, Kdim] FP8 (lhs_fmt, row stride ld_lhs), sa = lhs_scale_inv[0];
+ *   B_g = rhs + g * rhs_group_stride as [N, Kdim] (row stride ld_rhs, rhs_fmt),
+ *   sb = rhs_scale_inv (device, [G]: per expert).  Products are exact and
+ *   accumulated in float32 by v_mfma_f32_32x32x64_f8f6f4; the scales are
+ *   applied to the float32 sums.  bias: as in moe_gmm (bf16).  Output rows
+ *   and accumulate as in moe_gmm.  Kdim, ld_lhs, ld_rhs, rhs_group_stride
+ *   multiples of 16; N, ld_out multiples of 8; G <= 1000.
+ */
+int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_fmt,
+                const float* lhs_scale_inv, const void* rhs, int64_t ld_rhs,
+                int64_t rhs_group_stride, int rhs_fmt, const float* rhs_scale_inv,
+                const int32_t* group_sizes, int G, int64_t Kdim, int64_t N, const void* bias,
+                void* out, int64_t M_out, int64_t ld_out, int out_dtype, int accumulate,
+                int32_t* err, void* stream);
+
+/* moe_tgmm_fp8: transposed grouped GEMM on transposed FP8 copies in the
+ * padded layout of moe_fp8_quantize (qt_group_stride == 0), for groups
+ * group_sizes [G] of the M grouped rows:
+ *   out[g] (+)= sa * sb * lhs_t[:Kdim, cols of g] . rhs_t[:N, cols of g]^T
+ *   -> [Kdim, N] at out + g * out_group_stride (row stride ld_out).
+ *   sa = lhs_scale_inv[0], sb = rhs_scale_inv[0].  The contraction covers
+ *   each group's rows rounded up to 64 (zeros past its end), or valid_rows[g]
+ *   rounded up to 64 when valid_rows (device, [G]) is given (rows past it are
+ *   zero, as in moe_tgmm).  Empty groups: zero, or unchanged when
+ *   accumulating.  ld_lhs, ld_rhs >= moe_fp8_padded_rows(M, G), multiples of
+ *   16; G <= 1000.
+ */
+int moe_tgmm_fp8(const void* lhs_t, int64_t ld_lhs, int lhs_fmt, const float* lhs_scale_inv,
+                 const void* rhs_t, int64_t ld_rhs, int rhs_fmt, const float* rhs_scale_inv,
+                 const int32_t* group_sizes, const int32_t* valid_rows, int G, int64_t M,
+                 int64_t Kdim, int64_t N, void* out, int64_t ld_out, int64_t out_group_stride,
+                 int out_dtype, int accumulate, int32_t* err, void* stream);
 
 /* -------------------------------------------------------------------- SwiGLU
  * moe_swiglu: act = silu(h0) * h1, silu(z) = z / (1 + e^-z), computed in

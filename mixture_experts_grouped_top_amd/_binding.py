@@ -21,7 +21,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
-ABI_VERSION = 5   # moe_abi_version() of the library these signatures describe
+MOE_FP8_E4M3, MOE_FP8_E5M2 = 0, 1
+ABI_VERSION = 6   # moe_abi_version() of the library these signatures describe
 
 # Entry points (name -> (restype, argtypes)); must match include/moe.h.
 _P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -44,6 +45,14 @@ SIGNATURES = {
     "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
     "moe_group_sum_workspace": (_S, [_L, _I, _L]),
     "moe_group_sum": (_I, [_P, _L, _I, _P, _P, _I, _L, _L, _P, _I, _I, _P, _S, _P, _P]),
+    "moe_fp8_scale_workspace": (_S, [_L, _L, _I]),
+    "moe_fp8_amax_scale": (_I, [_P, _L, _I, _L, _L, _I, _I, _P, _P, _S, _P]),
+    "moe_fp8_padded_rows": (_L, [_L, _I]),
+    "moe_fp8_quantize": (_I, [_P, _L, _I, _L, _L, _P, _I, _P, _I, _I, _P, _L, _P, _L, _L, _P, _P]),
+    "moe_gmm_fp8": (_I, [_P, _L, _L, _I, _P, _P, _L, _L, _I, _P, _P, _I, _L, _L, _P, _P, _L, _L,
+                         _I, _I, _P, _P]),
+    "moe_tgmm_fp8": (_I, [_P, _L, _I, _P, _P, _L, _I, _P, _P, _P, _I, _L, _L, _L, _P, _L, _L, _I,
+                          _I, _P, _P]),
     "moe_swiglu": (_I, [_P, _P, _I, _L, _L, _L, _P, _I, _P]),
     "moe_swiglu_bwd": (_I, [_P, _P, _I, _L, _P, _L, _L, _P, _P, _L, _I, _P]),
     "moe_combine": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _P, _P]),
@@ -360,6 +369,105 @@ def moe_group_sum(x, group_sizes, out=None, out_dtype=torch.float32, accumulate:
                                 int(bool(accumulate)), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _ptr(err),
                                 _stream(stream)), "moe_group_sum")
+    return out
+
+
+# --------------------------------------------------------------------- FP8
+
+def _fmt(f) -> int:
+    if f in ("e4m3", MOE_FP8_E4M3):
+        return MOE_FP8_E4M3
+    if f in ("e5m2", MOE_FP8_E5M2):
+        return MOE_FP8_E5M2
+    raise MoeError(f"unknown FP8 format {f!r}")
+
+
+def moe_fp8_scale_workspace(rows: int, cols: int, G: int = 1) -> int:
+    return load().moe_fp8_scale_workspace(rows, cols, G)
+
+
+def moe_fp8_padded_rows(rows: int, G: int) -> int:
+    return load().moe_fp8_padded_rows(rows, G)
+
+
+def moe_fp8_amax_scale(x, fmt, G: int = 1, scales=None, workspace=None, stream=None):
+    """Current scaling of x [rows, cols] (G equal row blocks): returns the
+    float32 [3, G] tensor (amax, scale, scale_inv)."""
+    rows, cols = x.shape
+    if scales is None:
+        scales = torch.empty((3, G), dtype=torch.float32, device=x.device)
+    _contig(scales, "scales")
+    ws_bytes = moe_fp8_scale_workspace(rows, cols, G)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+    _check(load().moe_fp8_amax_scale(_ptr(x), _rowmajor(x, "x"), _dtype_code(x), rows, cols, G,
+                                     _fmt(fmt), _ptr(scales), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream)), "moe_fp8_amax_scale")
+    return scales
+
+
+def moe_fp8_quantize(x, group_sizes, scale, fmt, per_group: bool = False, q=None, qt=None,
+                     qt_group_stride: int = 0, ld_qt: Optional[int] = None, err=None, stream=None):
+    """FP8 codes of x [rows, cols] times scale (device float32: scale[g] per
+    group, or scale[0]).  q: row-wise uint8 copy [rows, cols] (2-D view) or
+    None; qt: transposed copy (uint8 buffer; padded [cols, P] layout when
+    qt_group_stride is 0, else per group [cols, n_g] blocks) or None."""
+    rows, cols = x.shape
+    G = group_sizes.numel()
+    ld_q = _rowmajor(q, "q") if q is not None else 0
+    if qt is not None and ld_qt is None:
+        ld_qt = qt.stride(0) if qt.dim() == 2 else qt.stride(-2)
+    _check(load().moe_fp8_quantize(_ptr(x), _rowmajor(x, "x"), _dtype_code(x), rows, cols,
+                                   _ptr(group_sizes), G, _ptr(scale), int(bool(per_group)),
+                                   _fmt(fmt), _ptr(q), ld_q, _ptr(qt), int(ld_qt or 0),
+                                   int(qt_group_stride), _ptr(err), _stream(stream)),
+           "moe_fp8_quantize")
+    return q, qt
+
+
+def moe_gmm_fp8(lhs, lhs_fmt, lhs_scale_inv, rhs, rhs_fmt, rhs_scale_inv, group_sizes, out=None,
+                rows_out: Optional[int] = None, out_dtype=torch.bfloat16, accumulate: bool = False,
+                bias=None, err=None, stream=None):
+    """out[rows of g] (+)= sa sb[g] lhs[rows of g] . rhs[g]^T (+ bias[g]);
+    lhs uint8 [M, K] (2-D view), rhs uint8 [G, N, K] (3-D view, unit last
+    stride), scale_inv tensors float32 on the device."""
+    M_lhs, Kd = lhs.shape
+    if rhs.dim() != 3 or rhs.stride(2) != 1 or rhs.shape[2] != Kd:
+        raise MoeError("rhs must be a [G, N, K] view with unit last stride")
+    G, N = rhs.shape[0], rhs.shape[1]
+    if out is None:
+        out = torch.empty((M_lhs if rows_out is None else rows_out, N), dtype=out_dtype,
+                          device=lhs.device)
+    if bias is not None:
+        _contig(bias, "bias")
+    _check(load().moe_gmm_fp8(_ptr(lhs), M_lhs, _rowmajor(lhs, "lhs"), _fmt(lhs_fmt),
+                              _ptr(lhs_scale_inv), _ptr(rhs), rhs.stride(1), rhs.stride(0),
+                              _fmt(rhs_fmt), _ptr(rhs_scale_inv), _ptr(group_sizes), G, Kd, N,
+                              _ptr(bias), _ptr(out), out.shape[0], _rowmajor(out, "out"),
+                              _dtype_code(out), int(bool(accumulate)), _ptr(err),
+                              _stream(stream)), "moe_gmm_fp8")
+    return out
+
+
+def moe_tgmm_fp8(lhs_t, lhs_fmt, lhs_scale_inv, rhs_t, rhs_fmt, rhs_scale_inv, group_sizes,
+                 M: int, out=None, out_dtype=torch.bfloat16, accumulate: bool = False,
+                 valid_rows=None, err=None, stream=None):
+    """out[g] (+)= sa sb lhs_t[:, cols of g] . rhs_t[:, cols of g]^T ->
+    [G, Kd, N]; lhs_t [Kd, P], rhs_t [N, P] uint8 in the padded transposed
+    layout of moe_fp8_quantize for M grouped rows."""
+    Kd, N = lhs_t.shape[0], rhs_t.shape[0]
+    G = group_sizes.numel()
+    if out is None:
+        out = torch.empty((G, Kd, N), dtype=out_dtype, device=lhs_t.device)
+    if out.dim() != 3 or out.stride(2) != 1:
+        raise MoeError("out must be [G, K, N] with unit last stride")
+    _check(load().moe_tgmm_fp8(_ptr(lhs_t), _rowmajor(lhs_t, "lhs_t"), _fmt(lhs_fmt),
+                               _ptr(lhs_scale_inv), _ptr(rhs_t), _rowmajor(rhs_t, "rhs_t"),
+                               _fmt(rhs_fmt), _ptr(rhs_scale_inv), _ptr(group_sizes),
+                               _ptr(valid_rows), G, M, Kd, N, _ptr(out), out.stride(1),
+                               out.stride(0), _dtype_code(out), int(bool(accumulate)), _ptr(err),
+                               _stream(stream)), "moe_tgmm_fp8")
     return out
 
 

@@ -754,7 +754,7 @@ struct Stages {
 template <int TM, int TN, typename TO>
 __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO* o, int64_t ldo,
                                            int rv, int cv, int accumulate,
-                                           const bf16_t* bias = nullptr) {
+                                           const bf16_t* bias = nullptr, float scale = 1.f) {
   constexpr int WC = TN / 2;
   constexpr int SROW = WC * 4 + 16;
   constexpr int CPR = WC / 8;                 // 8-column chunks per slab row
@@ -784,6 +784,8 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
       const float4 lo = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32);
       const float4 hi = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= scale;
       if (grow < rv && gcol < cv) {
         TO* p = o + static_cast<int64_t>(grow) * ldo + gcol;
         if (accumulate) {
@@ -901,6 +903,232 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void tgmm_mfma_kernel(MfmaAr
     contract<Stages<TM, TN>::NS>(smem, A, B, rows_g, acc, fa, fb);
     store_tile(acc, smem, out + g * a.out_gs + m0 * a.ld_out + n0, a.ld_out, mv, nv,
                a.accumulate);
+  }
+}
+
+// ---------------------------------------------------------------- fp8 MFMA
+//
+// FP8 operands (the quantization=fp8 run of the MaxText grouped-GEMM pull
+// request: e4m3 forward, e5m2 backward, current scaling) on
+// v_mfma_f32_32x32x64_f8f6f4: both operands contraction-contiguous (the
+// quantizer writes the transposed copy each GEMM needs), so both are "row"
+// tiles.  A contraction step is the same 64-byte row segment as a bf16 step
+// and reuses its LDS layout, DMA and fragment reads: the 64 FP8 values of a
+// step are viewed as 32 two-byte units.  One MFMA consumes both 16-byte
+// fragments (substeps 0 and 1) of a step; A and B use the same byte-to-k
+// assignment, so the products pair up correctly.  Tiles are 128 x 256 with
+// a three-step ring and two workgroups per CU; each step waits for its data,
+// reads all fragments, then runs its MFMAs with the DMA of a later step
+// spread between them.  The epilogue multiplies by the two operands'
+// scale_inv (per tensor, or per expert for the weights).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+
+template <int TM, int TN, int FA, int FB>
+struct Acc8 : Acc<TM, TN> {
+  using Base = Acc<TM, TN>;
+  struct Frags8 {
+    i32x8 a[Base::FM], b[Base::FN];
+  };
+  template <class O>
+  __device__ __forceinline__ static i32x8 frag8(const char* lds, const uint32_t (&fb)[4], int i) {
+    const i32x4v lo = __builtin_bit_cast(i32x4v, O::frag(lds, fb, i, 0));
+    const i32x4v hi = __builtin_bit_cast(i32x4v, O::frag(lds, fb, i, 1));
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ __forceinline__ void mma8(const Frags8& f, int q) {
+    const int i = q / Base::FN, j = q % Base::FN;
+    this->v[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], this->v[i][j],
+                                                                     FA, FB, 0, 0, 0, 0);
+  }
+};
+
+struct Fp8Args {
+  const bf16_t* lhs;     // FP8 bytes viewed as two-byte units
+  int64_t ld_lhs;        // in units
+  const bf16_t* rhs;
+  int64_t ld_rhs;
+  int64_t rhs_gs;        // gmm: rhs group stride (units)
+  const int32_t* gsz;
+  const int32_t* valid;  // tgmm: rows of each group that may be non-zero (or null)
+  int G;
+  int64_t M;             // gmm: output rows; tgmm: rows of the grouped buffers
+  int64_t Kdim;          // gmm: contraction (units); tgmm: output rows per group
+  int64_t N;
+  void* out;
+  int64_t ld_out;
+  int64_t out_gs;
+  int accumulate;
+  int32_t* err;
+  const float* sinv_a;   // [1]
+  const float* sinv_b;   // gmm: [G] (per expert); tgmm: [1]
+  const bf16_t* bias;    // gmm: [G, N] or null
+};
+
+// Contraction over nfull full steps and kv trailing units (< TK) of A and B
+// (both row operands), NS-stage ring.  Every step issues one DMA block, the
+// source clamped to the last full step past the end, so the wait before
+// each step is a constant.
+template <int NS, class OA, class OB, class ACC>
+__device__ __forceinline__ void contract_f8(char* lds, const OA& A, const OB& B, int64_t Kc,
+                                            ACC& acc, const uint32_t (&fa)[4],
+                                            const uint32_t (&fb)[4]) {
+  constexpr int SB = OA::kBytes + OB::kBytes;
+  constexpr int PER = OA::NJ + OB::NJ;
+  constexpr int NM = ACC::FM * ACC::FN;
+  static_assert((NS - 2) * PER < 64, "vmcnt range");
+  const int nfull = static_cast<int>(Kc / TK);
+  const int kv = static_cast<int>(Kc - static_cast<int64_t>(nfull) * TK);
+  typename ACC::Frags8 f;
+  acc.zero();
+  if (nfull > 0) {
+    auto src = [&](int st) { return st < nfull ? st : nfull - 1; };
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) {
+      A.dma(src(p), lds_addr(lds + p * SB));
+      B.dma(src(p), lds_addr(lds + p * SB + OA::kBytes));
+    }
+    for (int s = 0; s < nfull; ++s) {
+      wait_vmcnt<(NS - 2) * PER>();          // step s has landed
+      __syncthreads();                        // ... for every wave; step s - 1 is consumed
+      const char* cs = lds + (s % NS) * SB;
+#pragma unroll
+      for (int i = 0; i < ACC::FM; ++i) f.a[i] = ACC::template frag8<OA>(cs, fa, i);
+#pragma unroll
+      for (int j = 0; j < ACC::FN; ++j) f.b[j] = ACC::template frag8<OB>(cs + OA::kBytes, fb, j);
+      // step s + NS - 1 into the stage of step s - 1
+      const int nx = src(s + NS - 1);
+      const void* sa = uniform_ptr(A.step_base(nx));
+      const void* sb = uniform_ptr(B.step_base(nx));
+      char* ds = lds + ((s + NS - 1) % NS) * SB;
+      const uint32_t la = lds_addr(ds), lb = lds_addr(ds + OA::kBytes);
+      interleave<NM, PER>([&](int q) { acc.mma8(f, q); },
+                          [&](int o) {
+                            if (o < OA::NJ) A.dma_one(sa, o, la);
+                            else B.dma_one(sb, o - OA::NJ, lb);
+                          });
+    }
+    wait_vmcnt<0>();
+  }
+  if (kv > 0) {
+    __syncthreads();   // every wave's DMA has landed and no wave reads the stages
+    char* ts = lds + (nfull % NS) * SB;
+    {
+      uint4 t[OA::NR];
+      A.tail_load(nfull, kv, t);
+      A.tail_store(ts, t);
+    }
+    {
+      uint4 t[OB::NR];
+      B.tail_load(nfull, kv, t);
+      B.tail_store(ts + OA::kBytes, t);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ACC::FM; ++i) f.a[i] = ACC::template frag8<OA>(ts, fa, i);
+#pragma unroll
+    for (int j = 0; j < ACC::FN; ++j) f.b[j] = ACC::template frag8<OB>(ts + OA::kBytes, fb, j);
+#pragma unroll
+    for (int q = 0; q < NM; ++q) acc.mma8(f, q);
+  }
+  __syncthreads();   // every wave is done with all stages before they are refilled
+}
+
+constexpr int kF8TM = 128, kF8TN = 256, kF8NS = 3;
+constexpr int kF8Bytes = kF8NS * (kF8TM + kF8TN) * TK * 2;
+
+// Grouped GEMM, ragged rows: out[rows of g] (+)= sa sb[g] A[rows of g] B_g^T
+// (+ bias[g]), B_g = rhs + g rhs_gs as [N, K].
+template <int FA, int FB, typename TO>
+__global__ __launch_bounds__(NT, 2) void gmm_fp8_kernel(Fp8Args a) {
+  constexpr int TM = kF8TM, TN = kF8TN;
+  __shared__ __attribute__((aligned(1024))) char smem[kF8Bytes];
+  __shared__ int row_base[kMaxGShort + 1];
+  __shared__ int tile_base[kMaxGShort + 1];
+  const int ntn = static_cast<int>((a.N + TN - 1) / TN);
+  scan_groups(a.gsz, a.G, a.M, TM, ntn, row_base, tile_base, blockIdx.x == 0 ? a.err : nullptr);
+  __syncthreads();
+  const int total = tile_base[a.G];
+  TO* out = static_cast<TO*>(a.out);
+  Operand<false, TM> A;
+  Operand<false, TN> B;
+  Acc8<TM, TN, FA, FB> acc;
+  uint32_t fa[4], fb[4];
+  Operand<false, TM>::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
+  Operand<false, TN>::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
+  const float sa = a.sinv_a[0];
+  for (int it = 0;; ++it) {
+    const int64_t tile = xcd_tile(it);
+    if (tile >= total) break;
+    int lo = 0, hi = a.G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_base[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int rows_g = row_base[g + 1] - row_base[g];
+    const int mtiles = (rows_g + TM - 1) / TM;
+    const int local = static_cast<int>(tile - tile_base[g]);
+    int mt, nt;
+    blocked_tile(local, mtiles, ntn, mt, nt);
+    const int64_t row0 = row_base[g] + static_cast<int64_t>(mt) * TM;
+    const int rv = min(TM, rows_g - mt * TM);
+    const int64_t col0 = static_cast<int64_t>(nt) * TN;
+    const int cv = static_cast<int>(lmin(TN, a.N - col0));
+    A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, rv);
+    B.setup(a.rhs + g * a.rhs_gs + col0 * a.ld_rhs, a.ld_rhs, cv);
+    contract_f8<kF8NS>(smem, A, B, a.Kdim, acc, fa, fb);
+    store_tile(static_cast<const Acc<TM, TN>&>(acc), smem, out + row0 * a.ld_out + col0, a.ld_out,
+               rv, cv, a.accumulate, a.bias ? a.bias + g * a.N + col0 : nullptr, sa * a.sinv_b[g]);
+  }
+  if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
+}
+
+// Transposed grouped GEMM over transposed copies: lhs_t [Kdim, P] and
+// rhs_t [N, P], group g at columns 64 * (64-row tiles of the groups before
+// g); out[g] (+)= sa sb lhs_t[:, cols of g] rhs_t[:, cols of g]^T.  The
+// contraction covers the group's rows rounded up to 64 (the quantizer wrote
+// zeros there), or its valid rows rounded up.
+template <int FA, int FB, typename TO>
+__global__ __launch_bounds__(NT, 2) void tgmm_fp8_kernel(Fp8Args a) {
+  constexpr int TM = kF8TM, TN = kF8TN;
+  __shared__ __attribute__((aligned(1024))) char smem[kF8Bytes];
+  __shared__ int row_base[kMaxGShort + 1];
+  __shared__ int tile_base[kMaxGShort + 1];
+  scan_groups(a.gsz, a.G, a.M, 64, 1, row_base, tile_base, blockIdx.x == 0 ? a.err : nullptr);
+  __syncthreads();
+  const int mtn = static_cast<int>((a.Kdim + TM - 1) / TM);
+  const int ntn = static_cast<int>((a.N + TN - 1) / TN);
+  const int64_t per_group = static_cast<int64_t>(mtn) * ntn;
+  const int64_t total = per_group * a.G;
+  TO* out = static_cast<TO*>(a.out);
+  Operand<false, TM> A;
+  Operand<false, TN> B;
+  Acc8<TM, TN, FA, FB> acc;
+  uint32_t fa[4], fb[4];
+  Operand<false, TM>::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
+  Operand<false, TN>::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
+  const float scale = a.sinv_a[0] * a.sinv_b[0];
+  for (int it = 0;; ++it) {
+    const int64_t tile = xcd_tile(it);
+    if (tile >= total) break;
+    const int g = static_cast<int>(tile / per_group);
+    const int local = static_cast<int>(tile - g * per_group);
+    int mt, nt;
+    blocked_tile(local, mtn, ntn, mt, nt);
+    int rows_g = row_base[g + 1] - row_base[g];
+    if (a.valid) rows_g = min(rows_g, max(a.valid[g], 0));
+    if (rows_g == 0 && a.accumulate) continue;
+    const int64_t kc = static_cast<int64_t>((rows_g + 63) / 64) * 32;    // units
+    const int64_t c0 = static_cast<int64_t>(tile_base[g]) * 32;           // units
+    const int64_t m0 = static_cast<int64_t>(mt) * TM, n0 = static_cast<int64_t>(nt) * TN;
+    const int mv = static_cast<int>(lmin(TM, a.Kdim - m0));
+    const int nv = static_cast<int>(lmin(TN, a.N - n0));
+    A.setup(a.lhs + m0 * a.ld_lhs + c0, a.ld_lhs, mv);
+    B.setup(a.rhs + n0 * a.ld_rhs + c0, a.ld_rhs, nv);
+    contract_f8<kF8NS>(smem, A, B, kc, acc, fa, fb);
+    store_tile(static_cast<const Acc<TM, TN>&>(acc), smem, out + g * a.out_gs + m0 * a.ld_out + n0,
+               a.ld_out, mv, nv, a.accumulate, nullptr, scale);
   }
 }
 
@@ -1187,5 +1415,89 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
                        ld_lhs, static_cast<const float*>(rhs), ld_rhs, group_sizes, valid_rows, G,
                        M, Kdim, N, of, oh, ld_out, out_group_stride, accumulate, err);
   }
+  return launch_status();
+}
+
+MOE_API int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_fmt,
+                        const float* lhs_scale_inv, const void* rhs, int64_t ld_rhs,
+                        int64_t rhs_group_stride, int rhs_fmt, const float* rhs_scale_inv,
+                        const int32_t* group_sizes, int G, int64_t Kdim, int64_t N,
+                        const void* bias, void* out, int64_t M_out, int64_t ld_out, int out_dtype,
+                        int accumulate, int32_t* err, void* stream) {
+  if (G < 1 || G > kMaxGShort || M_lhs < 0 || M_out < 0 || M_out > M_lhs || Kdim < 0 || N < 0)
+    return MOE_ERR_ARG;
+  if (M_out > INT32_MAX) return MOE_ERR_ARG;
+  if ((lhs_fmt != MOE_FP8_E4M3 && lhs_fmt != MOE_FP8_E5M2) ||
+      (rhs_fmt != MOE_FP8_E4M3 && rhs_fmt != MOE_FP8_E5M2))
+    return MOE_ERR_ARG;
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_DTYPE;
+  if (Kdim % 16 || ld_lhs % 16 || ld_rhs % 16 || rhs_group_stride % 16 || !mult8(N) ||
+      !mult8(ld_out))
+    return MOE_ERR_ARG;
+  if (ld_lhs < Kdim || ld_rhs < Kdim || ld_out < N) return MOE_ERR_ARG;
+  if (ld_lhs / 2 > kMaxLd || ld_rhs / 2 > kMaxLd) return MOE_ERR_ARG;
+  if (M_out == 0 || N == 0) return MOE_OK;
+  if (!lhs || !rhs || !group_sizes || !out || !lhs_scale_inv || !rhs_scale_inv ||
+      !aligned16(lhs) || !aligned16(rhs) || !aligned16(out) || (bias && !aligned16(bias)))
+    return MOE_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Fp8Args a{static_cast<const bf16_t*>(lhs), ld_lhs / 2, static_cast<const bf16_t*>(rhs),
+            ld_rhs / 2, rhs_group_stride / 2, group_sizes, nullptr, G, M_out, Kdim / 2, N, out,
+            ld_out, 0, accumulate, err, lhs_scale_inv, rhs_scale_inv,
+            static_cast<const bf16_t*>(bias)};
+  const int64_t upper = ((M_out + kF8TM - 1) / kF8TM + G) * ((N + kF8TN - 1) / kF8TN);
+  const unsigned grid = persistent_grid(upper, 2);
+#define G8(FA, FB, TO) hipLaunchKernelGGL((gmm_fp8_kernel<FA, FB, TO>), dim3(grid), dim3(NT), 0, st, a)
+#define G8O(FA, FB) \
+  do { if (out_dtype == MOE_BF16) G8(FA, FB, bf16_t); else G8(FA, FB, float); } while (0)
+  if (lhs_fmt == MOE_FP8_E4M3 && rhs_fmt == MOE_FP8_E4M3) G8O(MOE_FP8_E4M3, MOE_FP8_E4M3);
+  else if (lhs_fmt == MOE_FP8_E5M2 && rhs_fmt == MOE_FP8_E4M3) G8O(MOE_FP8_E5M2, MOE_FP8_E4M3);
+  else if (lhs_fmt == MOE_FP8_E4M3) G8O(MOE_FP8_E4M3, MOE_FP8_E5M2);
+  else G8O(MOE_FP8_E5M2, MOE_FP8_E5M2);
+#undef G8O
+#undef G8
+  return launch_status();
+}
+
+MOE_API int64_t moe_fp8_padded_rows(int64_t rows, int G) {
+  if (rows < 0 || G < 1) return -1;
+  return 64 * ((rows + 63) / 64 + G - 1);
+}
+
+MOE_API int moe_tgmm_fp8(const void* lhs_t, int64_t ld_lhs, int lhs_fmt, const float* lhs_scale_inv,
+                         const void* rhs_t, int64_t ld_rhs, int rhs_fmt,
+                         const float* rhs_scale_inv, const int32_t* group_sizes,
+                         const int32_t* valid_rows, int G, int64_t M, int64_t Kdim, int64_t N,
+                         void* out, int64_t ld_out, int64_t out_group_stride, int out_dtype,
+                         int accumulate, int32_t* err, void* stream) {
+  if (G < 1 || G > kMaxGShort || M < 0 || M > INT32_MAX || Kdim < 0 || N < 0) return MOE_ERR_ARG;
+  if ((lhs_fmt != MOE_FP8_E4M3 && lhs_fmt != MOE_FP8_E5M2) ||
+      (rhs_fmt != MOE_FP8_E4M3 && rhs_fmt != MOE_FP8_E5M2))
+    return MOE_ERR_ARG;
+  if (out_dtype != MOE_BF16 && out_dtype != MOE_F32) return MOE_ERR_DTYPE;
+  const int64_t P = moe_fp8_padded_rows(M, G);
+  if (ld_lhs % 16 || ld_rhs % 16 || ld_lhs < P || ld_rhs < P || !mult8(N) || !mult8(ld_out) ||
+      ld_out < N || out_group_stride < Kdim * ld_out)
+    return MOE_ERR_ARG;
+  if (ld_lhs / 2 > kMaxLd || ld_rhs / 2 > kMaxLd) return MOE_ERR_ARG;
+  if (Kdim == 0 || N == 0) return MOE_OK;
+  if (!lhs_t || !rhs_t || !group_sizes || !out || !lhs_scale_inv || !rhs_scale_inv ||
+      !aligned16(lhs_t) || !aligned16(rhs_t) || !aligned16(out))
+    return MOE_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Fp8Args a{static_cast<const bf16_t*>(lhs_t), ld_lhs / 2, static_cast<const bf16_t*>(rhs_t),
+            ld_rhs / 2, 0, group_sizes, valid_rows, G, M, Kdim, N, out, ld_out, out_group_stride,
+            accumulate, err, lhs_scale_inv, rhs_scale_inv, nullptr};
+  const int64_t upper = ((Kdim + kF8TM - 1) / kF8TM) * ((N + kF8TN - 1) / kF8TN) * G;
+  const unsigned grid = persistent_grid(upper, 2);
+#define T8(FA, FB, TO) hipLaunchKernelGGL((tgmm_fp8_kernel<FA, FB, TO>), dim3(grid), dim3(NT), 0, st, a)
+#define T8O(FA, FB) \
+  do { if (out_dtype == MOE_BF16) T8(FA, FB, bf16_t); else T8(FA, FB, float); } while (0)
+  if (lhs_fmt == MOE_FP8_E4M3 && rhs_fmt == MOE_FP8_E5M2) T8O(MOE_FP8_E4M3, MOE_FP8_E5M2);
+  else if (lhs_fmt == MOE_FP8_E4M3) T8O(MOE_FP8_E4M3, MOE_FP8_E4M3);
+  else if (rhs_fmt == MOE_FP8_E5M2) T8O(MOE_FP8_E5M2, MOE_FP8_E5M2);
+  else T8O(MOE_FP8_E5M2, MOE_FP8_E4M3);
+#undef T8O
+#undef T8
   return launch_status();
 }

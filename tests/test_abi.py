@@ -39,7 +39,9 @@ def test_header_declares_the_abi():
                  "moe_tgmm", "moe_swiglu", "moe_swiglu_bwd", "moe_combine", "moe_combine_bwd",
                  "moe_rows_bound", "moe_permute_workspace", "moe_status_string",
                  "moe_abi_version", "moe_aux_loss_workspace", "moe_aux_loss",
-                 "moe_aux_loss_bwd", "moe_group_sum_workspace", "moe_group_sum"]:
+                 "moe_aux_loss_bwd", "moe_group_sum_workspace", "moe_group_sum",
+                 "moe_fp8_scale_workspace", "moe_fp8_amax_scale", "moe_fp8_padded_rows",
+                 "moe_fp8_quantize", "moe_gmm_fp8", "moe_tgmm_fp8"]:
         assert name in d, name
 
 
@@ -122,6 +124,20 @@ def test_argument_checks_return_before_launch(lib):
     assert lib.moe_group_sum(P, 64, 1, P, None, 2, 10, 64, P, 0, 0, None, 0, None, None) == -5
     assert lib.moe_group_sum(P, 64, 1, P, None, 2, 10, 64, P, 0, 0, W, 64, None, None) == -5
     assert lib.moe_group_sum(P, 64, 4, P, None, 2, 10, 64, P, 0, 0, W, 1 << 20, None, None) == -2
+    # fp8: unknown format, rows not divisible by G, K not a multiple of 16, G > 1000,
+    # transposed copy narrower than the padded layout
+    assert lib.moe_fp8_amax_scale(P, 64, 1, 64, 64, 1, 7, P, W, 1 << 20, None) == -1
+    assert lib.moe_fp8_amax_scale(P, 64, 1, 65, 64, 2, 0, P, W, 1 << 20, None) == -1
+    assert lib.moe_fp8_amax_scale(P, 64, 1, 64, 64, 1, 0, P, None, 0, None) == -5
+    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 40, 40 * 64, 0, P, P, 2, 40, 64, None, P, 64, 64,
+                           1, 0, None, None) == -1
+    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 64, 64 * 64, 0, P, P, 1001, 64, 64, None, P, 64,
+                           64, 1, 0, None, None) == -1
+    assert lib.moe_fp8_padded_rows(100, 3) == 64 * (2 + 2)
+    assert lib.moe_fp8_quantize(P, 64, 1, 100, 64, P, 3, P, 0, 0, None, 0, P, 128, 0, None,
+                                None) == -1
+    assert lib.moe_tgmm_fp8(P, 128, 0, P, P, 256, 1, P, P, None, 3, 100, 64, 64, P, 64, 64 * 64,
+                            1, 0, None, None) == -1
     # tgmm: output group stride too small
     assert lib.moe_tgmm(P, 64, P, 64, P, None, 2, 10, 64, 64, 1, P, 64, 64, 1, 0, None, None) == -1
     # permute: rows below the static bound, missing workspace
