@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE FFN fwd+bwd grouped-GEMM TFLOP/s and % of bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
@@ -49,6 +50,8 @@ def parse():
                    help="tokens of the workload the CPU oracle baseline runs on")
     p.add_argument("--fused-wi", action="store_true",
                    help="one [E, D, 2F] up-projection weight [wi_0 | wi_1]")
+    p.add_argument("--fp8", action="store_true",
+                   help="FP8 expert GEMMs (e4m3 forward, e5m2 backward, current scaling)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="do not bracket the expert GEMM launches with events")
@@ -303,8 +306,9 @@ def main():
     shape = moe.MoEShape(T=w.T, D=w.D, F=w.F, E=w.E, K=w.K, dtype=dtype, score=w.score,
                          renorm=w.renorm, align=w.align, capacity=w.capacity,
                          n_chunks=w.n_chunks, pad_rows_to=w.pad_rows_to,
-                         fused_wi=args.fused_wi)
+                         fused_wi=args.fused_wi, fp8=args.fp8)
     plan = moe.MoEPlan(shape)
+    peak = PEAK_FP8_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
 
     def step():
         plan.forward(g["x"], g["wi_0"], g["wi_1"], g["wo"], Wg=g["Wg"], logits=g["logits"],
@@ -346,11 +350,12 @@ def main():
         kind = max(gemm, key=lambda k: gemm[k]["ms"])
         k = gemm[kind]
         ach = k["tflops"]
-        traffic = None if args.fused_wi else traffic_from_profiles(kind, args.workload)
-        label = KERNEL_NAME.get(kind, kind) if args.workload == "mixtral" and not args.fused_wi else kind
+        plain = not (args.fused_wi or args.fp8)
+        traffic = traffic_from_profiles(kind, args.workload) if plain else None
+        label = KERNEL_NAME.get(kind, kind) if args.workload == "mixtral" and plain else kind
         roofline = {"bound": "mfma", "kernel": label,
-                    "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                    "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": traffic,
                     "avg_launch_ms": round(k["avg_ms"], 4),
                     "flops_per_launch": k["flops"] / k["launches"]}
     for kk, v in kernels.items():
@@ -367,13 +372,14 @@ def main():
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if dtype == torch.bfloat16 else "f32",
+        "dtype": ("fp8 e4m3/e5m2 GEMM operands, bf16 activations" if args.fp8 else
+                  "bf16" if dtype == torch.bfloat16 else "f32"),
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights; no dataset)",
         "config": {"workload": w.name, "tokens": w.T, "d_model": w.D, "d_ff": w.F,
                    "experts": w.E, "top_k": w.K, "score": w.score, "renorm": w.renorm,
                    "align_size": w.align, "capacity": w.capacity, "chunks": w.n_chunks,
-                   "fused_wi": bool(args.fused_wi), "routed_rows": R},
-        "mfma_peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                   "fused_wi": bool(args.fused_wi), "fp8": bool(args.fp8), "routed_rows": R},
+        "mfma_peak_frac": round(tflops / peak, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "device_error_flags": err,

@@ -54,6 +54,11 @@ class MoEShape:
     # the GEMM epilogues; under partial sums with the last chunk) and their
     # gradients as per-group row sums
     mlp_bias: bool = False
+    # FP8 expert GEMMs with current scaling: x_sorted and act e4m3 per
+    # tensor, the expert weights e4m3 per expert, the gradients d_y_sorted,
+    # d_h0, d_h1 e5m2 per tensor; each operand quantized once into the
+    # row-wise and transposed copies its GEMMs read (unchunked, two weights)
+    fp8: bool = False
 
 
 def _round_up(a: int, b: int) -> int:
@@ -135,9 +140,106 @@ class MoEPlan:
             self.gsum_ws = torch.empty(
                 max(B.moe_group_sum_workspace(self.rows, s.E, max(2 * s.F, s.D)), 256),
                 dtype=torch.uint8, device=dev)
+        if s.fp8:
+            self._init_fp8(dev)
         # router weight gradient kept in float32 (a [D, E] reduction over all tokens)
         self.d_Wg = torch.empty((1, s.D, s.E), **f32) if router else None
         self.recorder = None   # optional callable(kind, flops, bytes) -> context manager
+
+    def _init_fp8(self, dev):
+        s = self.s
+        if s.n_chunks > 1 or s.fused_wi:
+            raise B.MoeError("the FP8 plan is unchunked with two up-projection weights")
+        u8 = dict(dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        E, D, F = s.E, s.D, s.F
+        self.P8 = B.moe_fp8_padded_rows(self.lhs_rows, E)   # columns of the transposed copies
+        q = self.q8 = {}
+        # activations / gradients: (rows, cols) -> row-wise [rows, cols], transposed [cols, P]
+        for name, rows, cols in (("x", self.lhs_rows, D), ("act", self.rows, F),
+                                 ("d_y_sorted", self.rows, D), ("d_h0", self.rows, F),
+                                 ("d_h1", self.rows, F)):
+            q[name] = (torch.empty((rows, cols), **u8), torch.empty((cols, self.P8), **u8),
+                       torch.empty((3, 1), **f32))
+        # weights [E, a, b]: row-wise [E, a, b] and per-expert transposed [E, b, a]
+        for name, a, b in (("wi_0", D, F), ("wi_1", D, F), ("wo", F, D)):
+            q[name] = (torch.empty((E, a, b), **u8), torch.empty((E, b, a), **u8),
+                       torch.empty((3, E), **f32))
+        self.w_rows = {D: torch.full((E,), D, dtype=torch.int32, device=dev),
+                       F: torch.full((E,), F, dtype=torch.int32, device=dev)}
+        ws = max(B.moe_fp8_scale_workspace(self.lhs_rows, max(D, F), 1),
+                 B.moe_fp8_scale_workspace(E * max(D, F), max(D, F), E))
+        self.f8_ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+
+    def _quant(self, name, x, fmt, stream):
+        """Current scaling of an activation or gradient tensor into both copies."""
+        qr, qt, sc = self.q8[name]
+        # algorithmic bytes: x read twice (amax, quantize), two FP8 copies written
+        nbytes = x.numel() * (2 * x.element_size() + 2)
+        with self._rec("fp8_quantize", nbytes=nbytes):
+            B.moe_fp8_amax_scale(x, fmt, scales=sc, workspace=self.f8_ws, stream=stream)
+            B.moe_fp8_quantize(x, self.group_sizes, sc[1], fmt, q=qr, qt=qt, err=self.err,
+                               stream=stream)
+
+    def _quant_weight(self, name, w, stream):
+        qr, qt, sc = self.q8[name]
+        E, a, b = w.shape
+        w2 = w.reshape(E * a, b)
+        with self._rec("fp8_quantize", nbytes=w.numel() * (2 * w.element_size() + 2)):
+            B.moe_fp8_amax_scale(w2, "e4m3", G=E, scales=sc, workspace=self.f8_ws, stream=stream)
+            B.moe_fp8_quantize(w2, self.w_rows[a], sc[1], "e4m3", per_group=True,
+                               q=qr.view(E * a, b), qt=qt, qt_group_stride=a * b, ld_qt=a,
+                               err=self.err, stream=stream)
+
+    def _forward_fp8(self, wi_0, wi_1, wo, mb, stream):
+        s, q = self.s, self.q8
+        gs, R = self.group_sizes, self.kept_rows
+        self._quant("x", self.x_sorted, "e4m3", stream)
+        for name, w in (("wi_0", wi_0), ("wi_1", wi_1), ("wo", wo)):
+            self._quant_weight(name, w, stream)
+        xq, _, sx = q["x"]
+        for name, h in (("wi_0", self.h0), ("wi_1", self.h1)):
+            _, wt, sw = q[name]
+            with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+                B.moe_gmm_fp8(xq, "e4m3", sx[2], wt, "e4m3", sw[2], gs, out=h, bias=mb.get(name),
+                              err=self.err, stream=stream)
+        with self._rec("swiglu", nbytes=self._bytes().get("swiglu", 0) if self.recorder else 0):
+            B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
+        self._quant("act", self.act, "e4m3", stream)
+        aq, _, sa = q["act"]
+        _, wt, sw = q["wo"]
+        with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+            B.moe_gmm_fp8(aq, "e4m3", sa[2], wt, "e4m3", sw[2], gs, out=self.y_sorted,
+                          bias=mb.get("wo"), err=self.err, stream=stream)
+
+    def _backward_fp8(self, stream):
+        s, q = self.s, self.q8
+        gs, R, cnt = self.group_sizes, self.kept_rows, self.idx["counts"]
+        self._quant("d_y_sorted", self.d_y_sorted, "e5m2", stream)
+        dq, dqt, sd = q["d_y_sorted"]
+        wor, _, swo = q["wo"]
+        with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+            B.moe_gmm_fp8(dq, "e5m2", sd[2], wor, "e4m3", swo[2], gs, out=self.d_act, err=self.err,
+                          stream=stream)
+        _, aqt, sa = q["act"]
+        with self._rec("tgmm", 2.0 * R * s.D * s.F):
+            B.moe_tgmm_fp8(aqt, "e4m3", sa[2], dqt, "e5m2", sd[2], gs, self.rows, out=self.d_wo,
+                           valid_rows=cnt, err=self.err, stream=stream)
+        with self._rec("swiglu_bwd", nbytes=self._bytes().get("swiglu_bwd", 0) if self.recorder else 0):
+            B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
+                             stream=stream)
+        _, xqt, sx = q["x"]
+        for i, (gname, wname, dh, dw) in enumerate((("d_h0", "wi_0", self.d_h0, self.d_wi_0),
+                                                    ("d_h1", "wi_1", self.d_h1, self.d_wi_1))):
+            self._quant(gname, dh, "e5m2", stream)
+            hq, hqt, sh = q[gname]
+            wr, _, sw = q[wname]
+            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+                B.moe_gmm_fp8(hq, "e5m2", sh[2], wr, "e4m3", sw[2], gs, out=self.d_x_sorted,
+                              accumulate=i > 0, err=self.err, stream=stream)
+            with self._rec("tgmm", 2.0 * R * s.D * s.F):
+                B.moe_tgmm_fp8(xqt, "e4m3", sx[2], hqt, "e5m2", sh[2], gs, self.rows, out=dw,
+                               valid_rows=cnt, err=self.err, stream=stream)
 
     def _rec(self, kind: str, flops: float = 0.0, nbytes: float = 0.0):
         if self.recorder is None:
@@ -211,6 +313,12 @@ class MoEPlan:
                           workspace=self.ws, out=self.idx, stream=stream)
         gs = self.group_sizes
         R = self.kept_rows
+        if s.fp8:
+            self._forward_fp8(wi_0, wi_1, wo, mb, stream)
+            with self._rec("combine", nbytes=nb.get("combine", 0)):
+                B.moe_combine(self.y_sorted, self.idx["row_of_slot"], self.w, y=self.y,
+                              stream=stream)
+            return self.y
         if s.fused_wi:
             self._up_fused(wi, gs, R, stream, mb.get("wi"))
         elif s.n_chunks > 1:
@@ -262,13 +370,24 @@ class MoEPlan:
         with fused_wi), d_wo, d_logits, (with the router) d_Wg and (with MLP
         biases) d_b_wi_0, d_b_wi_1 (halves of d_b_wi with fused_wi), d_b_wo."""
         s = self.s
-        gs = self.group_sizes
-        R = self.kept_rows
         ros, sor = self.idx["row_of_slot"], self.idx["slot_of_row"]
         nb = self._bytes() if self.recorder is not None else {}
         with self._rec("combine_bwd", nbytes=nb.get("combine_bwd", 0)):
             B.moe_combine_bwd(dy, self.y_sorted, ros, sor, self.w, d_y_sorted=self.d_y_sorted,
                               d_topk_w=self.d_w, stream=stream)
+        xs = self.x_sorted[:self.rows]
+        if s.fp8:
+            self._backward_fp8(stream)
+        else:
+            self._backward_gemms(wi_0, wi_1, wo, wi, xs, stream)
+        self._backward_tail(dy, x, Wg, bias, stream)
+        return self.dx
+
+    def _backward_gemms(self, wi_0, wi_1, wo, wi, xs, stream):
+        s = self.s
+        gs = self.group_sizes
+        R = self.kept_rows
+        nb = self._bytes() if self.recorder is not None else {}
         with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
             B.moe_gmm(self.d_y_sorted, wo, gs, trans_rhs=True, out=self.d_act, err=self.err,
                       stream=stream)
@@ -280,7 +399,6 @@ class MoEPlan:
         with self._rec("swiglu_bwd", nbytes=nb.get("swiglu_bwd", 0)):
             B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
                              stream=stream)
-        xs = self.x_sorted[:self.rows]
         if s.fused_wi:
             # d_x_sorted = [d_h0 | d_h1] . [wi_0 | wi_1]^T in one contraction
             # over 2F; d_wi = x_sorted^T [d_h0 | d_h1] in one tgmm
@@ -303,6 +421,12 @@ class MoEPlan:
             with self._rec("tgmm", 2.0 * R * s.D * s.F):
                 B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream,
                            valid_rows=self.idx["counts"])
+
+    def _backward_tail(self, dy, x, Wg, bias, stream):
+        s = self.s
+        gs = self.group_sizes
+        ros = self.idx["row_of_slot"]
+        nb = self._bytes() if self.recorder is not None else {}
         if s.mlp_bias:
             # bias gradients: per-group sums of the rows of the gradient of
             # the output each bias was added to (padding rows are zero)
