@@ -94,9 +94,13 @@ __device__ void zero_rows(TO* out, int64_t ld, int64_t N, int64_t r0, int64_t r1
 //
 // LDS layouts (per stage, per operand), 16-byte chunks XOR-swizzled:
 //   contraction-contiguous operand ("row" tile): [x][TK], 64-byte rows;
-//     chunk c of row x sits at c ^ ((x >> 1) & 3), so any 8 consecutive
-//     rows of one MFMA operand read (ds_read_b128) hit distinct banks, and
-//     the swizzle repeats every 8 rows (fragment i of a wave is fragment 0
+//     chunk c of row x sits at c ^ ((x >> 2) & 3).  A ds_read_b128 is
+//     served 16 lanes (256 bytes, all 64 banks) per cycle; a fragment read
+//     gives those lanes 16 consecutive rows, whose 64-byte rows start on 4
+//     bank offsets, and the swizzle spreads the 4 rows of each offset over
+//     the 4 chunk positions, so the read is conflict-free (measured with
+//     the LDS bank-conflict counter; the (x >> 1) swizzle conflicts 2-way).
+//     The swizzle repeats every 16 rows (fragment i of a wave is fragment 0
 //     plus a constant offset).
 //   contraction-major operand ("col" tile): [TK][BX], BX*2-byte rows;
 //     chunk c of row k sits at c ^ 4 (k & 3), so the four rows x four chunks
@@ -120,7 +124,7 @@ __device__ void zero_rows(TO* out, int64_t ld, int64_t N, int64_t r0, int64_t r1
 constexpr int TK = 32;
 constexpr int kCPR = TK / 8;                // 16-byte chunks per row of a row tile
 
-__device__ __forceinline__ int row_swz(int x) { return (x >> 1) & 3; }
+__device__ __forceinline__ int row_swz(int x) { return (x >> 2) & 3; }
 __device__ __forceinline__ int row_off(int x, int c) { return x * (TK * 2) + ((c ^ row_swz(x)) << 4); }
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maximum)
@@ -287,8 +291,9 @@ struct Operand {
 // steps: each DMA lane copies 16 bytes of a 128-byte row segment (two
 // steps of 32 elements), so every request is a whole 128-byte line instead
 // of half of one.  LDS unit layout [x][64]: row x at 128 x bytes, 16-byte
-// chunk c at (c ^ (x & 7)), so the 8 rows that one ds_read_b128 phase
-// serves hit distinct banks.  Substep sub (0..3) of a unit covers
+// chunk c at (c ^ ((x >> 1) & 7)): the 16 rows that one ds_read_b128 cycle
+// serves start on 2 bank offsets and the swizzle gives the 8 rows of each
+// offset 8 distinct chunk positions, so all 64 banks are hit once.  Substep sub (0..3) of a unit covers
 // contraction elements 16 sub .. 16 sub + 15.
 template <int BX>
 struct PairRow {
@@ -303,7 +308,7 @@ struct PairRow {
   int xv;
   uint32_t voff[NJU];
 
-  __device__ __forceinline__ static int off(int x, int c) { return x * 128 + ((c ^ (x & 7)) << 4); }
+  __device__ __forceinline__ static int off(int x, int c) { return x * 128 + ((c ^ ((x >> 1) & 7)) << 4); }
   __device__ __forceinline__ void setup(const bf16_t* b, int64_t ld_, int xv_) {
     base = b;
     ld = ld_;
@@ -314,7 +319,7 @@ struct PairRow {
     for (int j = 0; j < NJU; ++j) {
       const int byte = (w * NJU + j) * 1024 + lane * 16;
       const int x = byte >> 7;
-      const int c = ((byte & 127) >> 4) ^ (x & 7);
+      const int c = ((byte & 127) >> 4) ^ ((x >> 1) & 7);
       const int xx = x < xv ? x : xv - 1;
       voff[j] = static_cast<uint32_t>((xx * ld + c * 8) * 2);
     }
@@ -349,7 +354,7 @@ struct PairRow {
     }
   }
   // Fragment (i, sub): x = xw + 32 i + lane % 32, chunk 2 sub + lane / 32;
-  // the swizzle term (x & 7) does not depend on i.
+  // the swizzle term ((x >> 1) & 7) does not depend on i.
   __device__ __forceinline__ static void frag_base(int xw, uint32_t (&fb)[4]) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
