@@ -233,6 +233,61 @@ __global__ __launch_bounds__(kThreads) void gather_sum_kernel(
   if (t >= T_) return;
   const int rl = slot_rows(ros + t * K, K);
   const float wl = WEIGHTED ? (lane < K ? wts[t * K + lane] : 0.f) : 1.f;
+  if (K <= kJB && rows > 0 && !accumulate) {
+    // One batch holds every slot: software-pipelined over the lane's
+    // chunks, the loads of chunk i + 1 are issued before chunk i is summed
+    // and stored.  Every issue is unconditional (past the last chunk a lane
+    // re-reads the first 16 bytes of row 0, an L2-resident line), so the
+    // wait before each sum leaves the next chunk's loads in flight.
+    const T* pr[kJB];
+    float wv[kJB];
+#pragma unroll
+    for (int q = 0; q < kJB; ++q) {
+      const int r = q < K ? lane_value(rl, q) : -1;
+      wv[q] = r < 0 ? 0.f : (WEIGHTED ? lane_value(wl, q) : 1.f);
+      pr[q] = src + static_cast<int64_t>(r < 0 ? 0 : r) * D;
+    }
+    T* out = dst + t * D;
+    const int64_t c0 = static_cast<int64_t>(lane) * 8;
+    const int nch = c0 < D ? static_cast<int>((D - c0 + 511) / 512) : 0;
+    Raw8<T> ra[kJB], rb[kJB];
+    auto issue = [&](Raw8<T>(&raw)[kJB], int i) {
+      const bool real = i < nch;
+      const int64_t c = c0 + 512 * static_cast<int64_t>(i);
+#pragma unroll
+      for (int q = 0; q < kJB; ++q) raw[q].load(real ? pr[q] + c : src + c0 % 512);
+    };
+    auto finish = [&](Raw8<T>(&raw)[kJB], int i) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int q = 0; q < kJB; ++q) {
+        float v[8];
+        raw[q].get(v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = fmaf(wv[q], v[e], acc[e]);
+      }
+      store8_nt(out + c0 + 512 * static_cast<int64_t>(i), acc);
+    };
+    if (nch == 0) return;
+    issue(ra, 0);
+    int i = 0;
+    // scheduling barriers keep the issue order (the compiler would
+    // otherwise move the next loads behind the sums)
+    for (; i + 2 <= nch; i += 2) {
+      issue(rb, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      finish(ra, i);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ra, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      finish(rb, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (i < nch) finish(ra, i);
+    return;
+  }
   for (int64_t c = static_cast<int64_t>(lane) * 8; c < D; c += 64 * 8) {
     float acc[8];
 #pragma unroll
