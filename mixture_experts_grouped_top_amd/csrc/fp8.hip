@@ -73,15 +73,27 @@ __global__ __launch_bounds__(256) void amax_partial_kernel(const T* __restrict__
   const int64_t n = rows_per_unit * cpr;
   const T* base = x + static_cast<int64_t>(g) * rows_per_unit * ld;
   float m = 0.f;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(nb) * 256) {
-    const int64_t r = i / cpr, c = (i - r * cpr) * 8;
-    Raw8<T> raw;
-    raw.load(base + r * ld + c);
-    float v[8];
-    raw.get(v);
+  // four chunks per thread in flight per iteration
+  constexpr int U = 4;
+  const int64_t stride = static_cast<int64_t>(nb) * 256;
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i0 < n; i0 += U * stride) {
+    Raw8<T> raw[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n) {
+        const int64_t r = i / cpr, c = (i - r * cpr) * 8;
+        raw[u].load(base + r * ld + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u * stride >= n) break;
+      float v[8];
+      raw[u].get(v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    }
   }
   __shared__ float red[4];
   m = wave_max(m);
@@ -119,15 +131,18 @@ int amax_blocks(int64_t elems, int G) {
   return static_cast<int>(nb < 1 ? 1 : nb);
 }
 
-// Quantize tiles of 64 rows x 64 columns of a row-grouped matrix.  The tile
-// schedule follows the 64-row tiles of each group (tile_base from the group
-// sizes), times the column tiles.  Each thread converts 16 elements of one
-// row (two 16-byte loads); the row-wise copy gets them as one 16-byte store,
-// the transposed copy through an LDS transpose as 16-byte runs of rows.
+// Quantize tiles of 128 rows x 128 columns of a row-grouped matrix.  The
+// rows of a tile are two 64-row tiles of the groups' 64-row tiling (which
+// may belong to two groups), so every row segment of both copies a tile
+// writes is a whole 128-byte line, written by one workgroup at one time.
+// Each thread converts 4 consecutive rows x 16 columns (eight 16-byte
+// loads in flight), stores them row-wise, and writes one dword per column
+// (its 4 rows) into an LDS tile that is read back along columns for the
+// transposed copy.
 // Transposed layouts:
-//   qt_gs == 0: one [cols, P] matrix, group g's rows at columns
-//               64 * (64-row tiles of the groups before g), the rows between
-//               a group's end and its next multiple of 64 written as zero;
+//   qt_gs == 0: one [cols, P] matrix, the 64-row tile rt of the groups'
+//               tiling at columns 64 rt (a group's rows, then zeros up to
+//               its next multiple of 64);
 //   qt_gs > 0:  group g at qt + g * qt_gs as [cols, n_g] (row stride ld_qt),
 //               only the group's own rows written.
 template <typename T, int FMT>
@@ -138,72 +153,103 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     int32_t* err) {
   __shared__ int row_base[kMaxGroups + 1];
   __shared__ int tile_base[kMaxGroups + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t tr[64][64 + 16];
-  const int ntc = static_cast<int>((cols + 63) / 64);
+  __shared__ __attribute__((aligned(16))) uint32_t tr[128][32 + 4];   // [column][rows / 4]
+  const int ntc = static_cast<int>((cols + 127) / 128);
   scan_groups(gsz, G, rows, 64, 1, row_base, tile_base, blockIdx.x == 0 ? err : nullptr);
   __syncthreads();
-  const int64_t total = static_cast<int64_t>(tile_base[G]) * ntc;
+  const int nrt = tile_base[G];                       // 64-row tiles
+  const int64_t total = static_cast<int64_t>((nrt + 1) / 2) * ntc;
   const int tid = threadIdx.x;
-  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
-    const int rt = static_cast<int>(t / ntc), ct = static_cast<int>(t - static_cast<int64_t>(rt) * ntc);
+  const int rg = tid >> 3, cg = tid & 7;               // rows 4 rg .. + 3, columns 16 cg .. + 15
+  const int half = rg >> 4;                            // which 64-row tile of the pair
+  auto group_of = [&](int rt) {
     int lo = 0, hi = G - 1;   // largest g with tile_base[g] <= rt
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (tile_base[mid] <= rt) lo = mid; else hi = mid - 1;
     }
-    const int g = lo;
-    const int lr = rt - tile_base[g];                 // row tile inside the group
-    const int n_g = row_base[g + 1] - row_base[g];
-    const int r_in = 64 * lr;                         // first group row of the tile
-    const int rv = min(64, n_g - r_in);
+    return lo;
+  };
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    const int pr = static_cast<int>(t / ntc), ct = static_cast<int>(t - static_cast<int64_t>(pr) * ntc);
+    // this thread's 64-row tile
+    const int rt = 2 * pr + half;
+    const bool tile_ok = rt < nrt;
+    const int g = tile_ok ? group_of(rt) : 0;
+    const int r_in = tile_ok ? 64 * (rt - tile_base[g]) : 0;     // first group row of the tile
+    const int rv = tile_ok ? min(64, row_base[g + 1] - row_base[g] - r_in) : 0;
+    const int lr = 4 * (rg & 15);                      // first of the thread's rows in its tile
+    const int64_t col = static_cast<int64_t>(ct) * 128 + 16 * cg;
+    const bool col_ok = col < cols, two = col + 8 < cols;
     const float s = scale[per_group ? g : 0];
-    // thread: row tid / 4, columns 16 (tid % 4) .. + 15 of the tile
-    const int r = tid >> 2, c16 = (tid & 3) * 16;
-    const int64_t col = static_cast<int64_t>(ct) * 64 + c16;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (r < rv && col < cols) {
-      const T* p = x + (static_cast<int64_t>(row_base[g]) + r_in + r) * ld + col;
+    // eight loads (two per row), a lane with nothing to load reads x[0..7]
+    Raw8<T> raw[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = col_ok && lr + i < rv;
+      const T* p = x + (static_cast<int64_t>(row_base[g]) + r_in + lr + i) * ld + col;
+      raw[i][0].load(ok ? p : x);
+      raw[i][1].load(ok && two ? p + 8 : x);
+    }
+    uint32_t w[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = col_ok && lr + i < rv;
       float v[16];
-      Raw8<T> a, b;
-      a.load(p);
-      const bool two = col + 8 < cols;
-      if (two) b.load(p + 8);
-      a.get(v);
-      if (two) b.get(v + 8);
-      else
+      raw[i][0].get(v);
+      raw[i][1].get(v + 8);
 #pragma unroll
-        for (int e = 8; e < 16; ++e) v[e] = 0.f;
+      for (int k = 0; k < 4; ++k) w[i][k] = 0u;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) w[e >> 2] |= f32_to_fp8<FMT>(__fmul_rn(v[e], s)) << (8 * (e & 3));
-      if (q) {
-        uint8_t* d = q + (static_cast<int64_t>(row_base[g]) + r_in + r) * ld_q + col;
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t c = f32_to_fp8<FMT>(__fmul_rn(v[e], s));
+        w[i][e >> 2] |= (ok && (e < 8 || two) ? c : 0u) << (8 * (e & 3));
+      }
+      if (q && ok) {
+        uint8_t* d = q + (static_cast<int64_t>(row_base[g]) + r_in + lr + i) * ld_q + col;
         // rows are 16-byte aligned when ld_q is a multiple of 16, else 8-byte
         if (two && !(ld_q & 15)) {
-          *reinterpret_cast<uint4*>(d) = make_uint4(w[0], w[1], w[2], w[3]);
+          *reinterpret_cast<uint4*>(d) = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
         } else {
-          *reinterpret_cast<uint2*>(d) = make_uint2(w[0], w[1]);
-          if (two) *reinterpret_cast<uint2*>(d + 8) = make_uint2(w[2], w[3]);
+          *reinterpret_cast<uint2*>(d) = make_uint2(w[i][0], w[i][1]);
+          if (two) *reinterpret_cast<uint2*>(d + 8) = make_uint2(w[i][2], w[i][3]);
         }
       }
     }
     if (qt) {
-      // rows past rv (group end, zero padding) carry zeros
+      // column 16 cg + e, rows 4 rg .. + 3 as one dword (row 4 rg in the low byte)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) tr[c16 + e][r] = static_cast<uint8_t>(w[e >> 2] >> (8 * (e & 3)));
+      for (int e = 0; e < 16; ++e) {
+        const int sh = 8 * (e & 3);
+        const uint32_t b0 = (w[0][e >> 2] >> sh) & 0xFFu, b1 = (w[1][e >> 2] >> sh) & 0xFFu;
+        const uint32_t b2 = (w[2][e >> 2] >> sh) & 0xFFu, b3 = (w[3][e >> 2] >> sh) & 0xFFu;
+        tr[16 * cg + e][rg] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      }
       __syncthreads();
-      // thread: tile column tid / 4, rows 16 (tid % 4) .. + 15
-      const int cc = tid >> 2, r16 = (tid & 3) * 16;
-      const int64_t gc = static_cast<int64_t>(ct) * 64 + cc;
-      const int rows_out = qt_gs ? rv : 64;           // the global layout pads to 64
-      if (gc < cols && r16 < rows_out) {
-        uint8_t* d;
-        if (qt_gs) d = qt + static_cast<int64_t>(g) * qt_gs + gc * ld_qt + r_in + r16;
-        else d = qt + gc * ld_qt + static_cast<int64_t>(rt) * 64 + r16;
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(&tr[cc][r16]);
-        if (r16 + 16 <= rows_out) {
-          *reinterpret_cast<uint4*>(d) = make_uint4(src[0], src[1], src[2], src[3]);
+      // thread: tile column tid / 2, the 64 rows of tile 2 pr + (tid & 1)
+      const int cc = tid >> 1, h = tid & 1;
+      const int rt2 = 2 * pr + h;
+      const int64_t gc = static_cast<int64_t>(ct) * 128 + cc;
+      if (rt2 < nrt && gc < cols) {
+        const uint32_t* sv = &tr[cc][16 * h];
+        if (qt_gs == 0) {
+          uint8_t* d = qt + gc * ld_qt + static_cast<int64_t>(rt2) * 64;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<uint4*>(d + 16 * k) = make_uint4(sv[4 * k], sv[4 * k + 1], sv[4 * k + 2], sv[4 * k + 3]);
         } else {
-          for (int e = 0; e < rows_out - r16; ++e) d[e] = tr[cc][r16 + e];
+          const int g2 = group_of(rt2);
+          const int r2 = 64 * (rt2 - tile_base[g2]);
+          const int rv2 = min(64, row_base[g2 + 1] - row_base[g2] - r2);
+          uint8_t* d = qt + static_cast<int64_t>(g2) * qt_gs + gc * ld_qt + r2;
+          if (rv2 == 64) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              *reinterpret_cast<uint4*>(d + 16 * k) = make_uint4(sv[4 * k], sv[4 * k + 1], sv[4 * k + 2], sv[4 * k + 3]);
+          } else {
+            const uint8_t* sb = reinterpret_cast<const uint8_t*>(sv);
+            for (int e = 0; e < rv2; ++e) d[e] = sb[e];
+          }
         }
       }
       __syncthreads();
@@ -266,7 +312,7 @@ MOE_API int moe_fp8_quantize(const void* x, int64_t ld, int dtype, int64_t rows,
   if (rows == 0 || cols == 0) return MOE_OK;
   if (!x || !aligned16(x)) return MOE_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t tiles = ((rows + 63) / 64 + G) * ((cols + 63) / 64);
+  const int64_t tiles = ((rows + 63) / 128 + G) * ((cols + 127) / 128);
   int64_t grid = static_cast<int64_t>(device_cu_count()) * 8;
   if (tiles < grid) grid = tiles;
   if (grid < 1) grid = 1;
