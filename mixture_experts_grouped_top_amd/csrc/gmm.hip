@@ -921,11 +921,14 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void tgmm_mfma_kernel(MfmaAr
 // and reuses its LDS layout, DMA and fragment reads: the 64 FP8 values of a
 // step are viewed as 32 two-byte units.  One MFMA consumes both 16-byte
 // fragments (substeps 0 and 1) of a step; A and B use the same byte-to-k
-// assignment, so the products pair up correctly.  Tiles are 128 x 256 with
-// a three-step ring and two workgroups per CU; each step waits for its data,
-// reads all fragments, then runs its MFMAs with the DMA of a later step
-// spread between them.  The epilogue multiplies by the two operands'
-// scale_inv (per tensor, or per expert for the weights).
+// assignment, so the products pair up correctly.  Each step waits for its
+// data, reads all fragments, then runs its MFMAs with the DMA of a later
+// step spread between them.  Two tile shapes, chosen per launch like the
+// bf16 ones: 256 x 256 with a four-step ring and one workgroup per CU when groups
+// hold 512 rows or more on average (contraction rows for the tgmm), else
+// 128 x 256 with a three-step ring and two workgroups per CU.  The epilogue
+// multiplies by the two operands' scale_inv (per tensor, or per expert for
+// the weights).
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4v __attribute__((ext_vector_type(4)));
 
@@ -1039,15 +1042,19 @@ __device__ __forceinline__ void contract_f8(char* lds, const OA& A, const OB& B,
   __syncthreads();   // every wave is done with all stages before they are refilled
 }
 
-constexpr int kF8TM = 128, kF8TN = 256, kF8NS = 3;
-constexpr int kF8Bytes = kF8NS * (kF8TM + kF8TN) * TK * 2;
+constexpr int kF8TN = 256;
+template <int TM>
+struct F8Tile {
+  static constexpr int NS = TM >= 256 ? 4 : 3;
+  static constexpr int kBytes = NS * (TM + kF8TN) * TK * 2;
+};
 
 // Grouped GEMM, ragged rows: out[rows of g] (+)= sa sb[g] A[rows of g] B_g^T
 // (+ bias[g]), B_g = rhs + g rhs_gs as [N, K].
-template <int FA, int FB, typename TO>
-__global__ __launch_bounds__(NT, 2) void gmm_fp8_kernel(Fp8Args a) {
-  constexpr int TM = kF8TM, TN = kF8TN;
-  __shared__ __attribute__((aligned(1024))) char smem[kF8Bytes];
+template <int FA, int FB, typename TO, int TM>
+__global__ __launch_bounds__(NT, TM >= 256 ? 1 : 2) void gmm_fp8_kernel(Fp8Args a) {
+  constexpr int TN = kF8TN;
+  __shared__ __attribute__((aligned(1024))) char smem[F8Tile<TM>::kBytes];
   __shared__ int row_base[kMaxGShort + 1];
   __shared__ int tile_base[kMaxGShort + 1];
   const int ntn = static_cast<int>((a.N + TN - 1) / TN);
@@ -1082,7 +1089,7 @@ __global__ __launch_bounds__(NT, 2) void gmm_fp8_kernel(Fp8Args a) {
     const int cv = static_cast<int>(lmin(TN, a.N - col0));
     A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, rv);
     B.setup(a.rhs + g * a.rhs_gs + col0 * a.ld_rhs, a.ld_rhs, cv);
-    contract_f8<kF8NS>(smem, A, B, a.Kdim, acc, fa, fb);
+    contract_f8<F8Tile<TM>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
     store_tile(static_cast<const Acc<TM, TN>&>(acc), smem, out + row0 * a.ld_out + col0, a.ld_out,
                rv, cv, a.accumulate, a.bias ? a.bias + g * a.N + col0 : nullptr, sa * a.sinv_b[g]);
   }
@@ -1094,10 +1101,10 @@ __global__ __launch_bounds__(NT, 2) void gmm_fp8_kernel(Fp8Args a) {
 // g); out[g] (+)= sa sb lhs_t[:, cols of g] rhs_t[:, cols of g]^T.  The
 // contraction covers the group's rows rounded up to 64 (the quantizer wrote
 // zeros there), or its valid rows rounded up.
-template <int FA, int FB, typename TO>
-__global__ __launch_bounds__(NT, 2) void tgmm_fp8_kernel(Fp8Args a) {
-  constexpr int TM = kF8TM, TN = kF8TN;
-  __shared__ __attribute__((aligned(1024))) char smem[kF8Bytes];
+template <int FA, int FB, typename TO, int TM>
+__global__ __launch_bounds__(NT, TM >= 256 ? 1 : 2) void tgmm_fp8_kernel(Fp8Args a) {
+  constexpr int TN = kF8TN;
+  __shared__ __attribute__((aligned(1024))) char smem[F8Tile<TM>::kBytes];
   __shared__ int row_base[kMaxGShort + 1];
   __shared__ int tile_base[kMaxGShort + 1];
   scan_groups(a.gsz, a.G, a.M, 64, 1, row_base, tile_base, blockIdx.x == 0 ? a.err : nullptr);
@@ -1131,7 +1138,7 @@ __global__ __launch_bounds__(NT, 2) void tgmm_fp8_kernel(Fp8Args a) {
     const int nv = static_cast<int>(lmin(TN, a.N - n0));
     A.setup(a.lhs + m0 * a.ld_lhs + c0, a.ld_lhs, mv);
     B.setup(a.rhs + n0 * a.ld_rhs + c0, a.ld_rhs, nv);
-    contract_f8<kF8NS>(smem, A, B, kc, acc, fa, fb);
+    contract_f8<F8Tile<TM>::NS>(smem, A, B, kc, acc, fa, fb);
     store_tile(static_cast<const Acc<TM, TN>&>(acc), smem, out + g * a.out_gs + m0 * a.ld_out + n0,
                a.ld_out, mv, nv, a.accumulate, nullptr, scale);
   }
@@ -1450,9 +1457,14 @@ MOE_API int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_
             ld_rhs / 2, rhs_group_stride / 2, group_sizes, nullptr, G, M_out, Kdim / 2, N, out,
             ld_out, 0, accumulate, err, lhs_scale_inv, rhs_scale_inv,
             static_cast<const bf16_t*>(bias)};
-  const int64_t upper = ((M_out + kF8TM - 1) / kF8TM + G) * ((N + kF8TN - 1) / kF8TN);
-  const unsigned grid = persistent_grid(upper, 2);
-#define G8(FA, FB, TO) hipLaunchKernelGGL((gmm_fp8_kernel<FA, FB, TO>), dim3(grid), dim3(NT), 0, st, a)
+  // 256-row tiles when groups hold 512 rows or more on average
+  const bool big = M_out >= 512 * static_cast<int64_t>(G);
+  const int TMv = big ? 256 : 128;
+  const int64_t upper = ((M_out + TMv - 1) / TMv + G) * ((N + kF8TN - 1) / kF8TN);
+  const unsigned grid = persistent_grid(upper, big ? 1 : 2);
+#define G8T(FA, FB, TO, TMV) \
+  hipLaunchKernelGGL((gmm_fp8_kernel<FA, FB, TO, TMV>), dim3(grid), dim3(NT), 0, st, a)
+#define G8(FA, FB, TO) do { if (big) G8T(FA, FB, TO, 256); else G8T(FA, FB, TO, 128); } while (0)
 #define G8O(FA, FB) \
   do { if (out_dtype == MOE_BF16) G8(FA, FB, bf16_t); else G8(FA, FB, float); } while (0)
   if (lhs_fmt == MOE_FP8_E4M3 && rhs_fmt == MOE_FP8_E4M3) G8O(MOE_FP8_E4M3, MOE_FP8_E4M3);
@@ -1461,6 +1473,7 @@ MOE_API int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_
   else G8O(MOE_FP8_E5M2, MOE_FP8_E5M2);
 #undef G8O
 #undef G8
+#undef G8T
   return launch_status();
 }
 
@@ -1493,9 +1506,14 @@ MOE_API int moe_tgmm_fp8(const void* lhs_t, int64_t ld_lhs, int lhs_fmt, const f
   Fp8Args a{static_cast<const bf16_t*>(lhs_t), ld_lhs / 2, static_cast<const bf16_t*>(rhs_t),
             ld_rhs / 2, 0, group_sizes, valid_rows, G, M, Kdim, N, out, ld_out, out_group_stride,
             accumulate, err, lhs_scale_inv, rhs_scale_inv, nullptr};
-  const int64_t upper = ((Kdim + kF8TM - 1) / kF8TM) * ((N + kF8TN - 1) / kF8TN) * G;
-  const unsigned grid = persistent_grid(upper, 2);
-#define T8(FA, FB, TO) hipLaunchKernelGGL((tgmm_fp8_kernel<FA, FB, TO>), dim3(grid), dim3(NT), 0, st, a)
+  // 256-row tiles when groups contract over 512 rows or more on average
+  const bool big = M >= 512 * static_cast<int64_t>(G);
+  const int TMv = big ? 256 : 128;
+  const int64_t upper = ((Kdim + TMv - 1) / TMv) * ((N + kF8TN - 1) / kF8TN) * G;
+  const unsigned grid = persistent_grid(upper, big ? 1 : 2);
+#define T8T(FA, FB, TO, TMV) \
+  hipLaunchKernelGGL((tgmm_fp8_kernel<FA, FB, TO, TMV>), dim3(grid), dim3(NT), 0, st, a)
+#define T8(FA, FB, TO) do { if (big) T8T(FA, FB, TO, 256); else T8T(FA, FB, TO, 128); } while (0)
 #define T8O(FA, FB) \
   do { if (out_dtype == MOE_BF16) T8(FA, FB, bf16_t); else T8(FA, FB, float); } while (0)
   if (lhs_fmt == MOE_FP8_E4M3 && rhs_fmt == MOE_FP8_E5M2) T8O(MOE_FP8_E4M3, MOE_FP8_E5M2);
@@ -1504,5 +1522,6 @@ MOE_API int moe_tgmm_fp8(const void* lhs_t, int64_t ld_lhs, int lhs_fmt, const f
   else T8O(MOE_FP8_E5M2, MOE_FP8_E4M3);
 #undef T8O
 #undef T8
+#undef T8T
   return launch_status();
 }
