@@ -464,6 +464,12 @@ TGMM_CASES = [
     ("aligned", 16, 48, "f32", "f32", True),
     ("max_groups", 16, 136, "bf16", "f32", False),
     ("one_group", 264, 136, "bf16", "bf16", True),   # long contraction: 256-row tiles
+    # bf16 out, no partial sum, short contractions (128-row tiles)
+    ("ragged", 136, 264, "bf16", "bf16", False),
+    ("empty_first", 200, 264, "bf16", "bf16", False),
+    ("all_empty", 64, 64, "bf16", "bf16", False),
+    ("max_groups", 16, 136, "bf16", "bf16", False),
+    ("many", 264, 520, "bf16", "bf16", False),
 ]
 
 
