@@ -196,6 +196,10 @@ int moe_permute_bwd(const void* d_x_sorted, int dtype, int64_t T, int64_t D, int
  *   in_dtype is the dtype of lhs and rhs; MOE_BF16 runs on bf16 MFMA with
  *   float32 accumulation; MOE_F32 runs in float32 FMA.  out_dtype is
  *   MOE_F32 or MOE_BF16 (rounded to nearest even).
+ *   valid_rows (device, [G], may be NULL): the caller asserts that lhs rows
+ *   [valid_rows[g], group_sizes[g]) of group g are zero (moe_permute's
+ *   counts: align_size / capacity padding rows); those rows are not read and
+ *   their products are written as zero.  NULL reads every row.
  *   bias (device, may be NULL): [G, N] row-major in in_dtype, the per-expert
  *   MLP bias of the [MT-Chunk] chunked layer (its w0/w1/wo bias arguments;
  *   Testing: MLP bias with the chunked layer).  bias[g] is added to every
@@ -206,9 +210,10 @@ int moe_permute_bwd(const void* d_x_sorted, int dtype, int64_t T, int64_t D, int
  *   clipped at M_out and MOE_DERR_GROUP_SIZES is raised.
  */
 int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
-            int64_t rhs_group_stride, int trans_rhs, const int32_t* group_sizes, int G,
-            int64_t Kdim, int64_t N, int in_dtype, const void* bias, void* out, int64_t M_out,
-            int64_t ld_out, int out_dtype, int accumulate, int32_t* err, void* stream);
+            int64_t rhs_group_stride, int trans_rhs, const int32_t* group_sizes,
+            const int32_t* valid_rows, int G, int64_t Kdim, int64_t N, int in_dtype,
+            const void* bias, void* out, int64_t M_out, int64_t ld_out, int out_dtype,
+            int accumulate, int32_t* err, void* stream);
 
 /* moe_tgmm: transposed grouped GEMM [MT-Chunk: tgmm, output
  * (num_local_groups, in_size, out_size), zero-initialised empty groups].
@@ -304,14 +309,15 @@ int moe_fp8_quantize(const void* x, int64_t ld, int dtype, int64_t rows, int64_t
  *   B_g = rhs + g * rhs_group_stride as [N, Kdim] (row stride ld_rhs, rhs_fmt),
  *   sb = rhs_scale_inv (device, [G]: per expert).  Products are exact and
  *   accumulated in float32 by v_mfma_f32_32x32x64_f8f6f4; the scales are
- *   applied to the float32 sums.  bias: as in moe_gmm (bf16).  Output rows
+ *   applied to the float32 sums.  valid_rows, bias: as in moe_gmm.  Output rows
  *   and accumulate as in moe_gmm.  Kdim, ld_lhs, ld_rhs, rhs_group_stride
  *   multiples of 16; N, ld_out multiples of 8; G <= 1000.
  */
 int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_fmt,
                 const float* lhs_scale_inv, const void* rhs, int64_t ld_rhs,
                 int64_t rhs_group_stride, int rhs_fmt, const float* rhs_scale_inv,
-                const int32_t* group_sizes, int G, int64_t Kdim, int64_t N, const void* bias,
+                const int32_t* group_sizes, const int32_t* valid_rows, int G, int64_t Kdim,
+                int64_t N, const void* bias,
                 void* out, int64_t M_out, int64_t ld_out, int out_dtype, int accumulate,
                 int32_t* err, void* stream);
 

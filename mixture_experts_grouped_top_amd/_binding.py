@@ -22,7 +22,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
 MOE_FP8_E4M3, MOE_FP8_E5M2 = 0, 1
-ABI_VERSION = 6   # moe_abi_version() of the library these signatures describe
+ABI_VERSION = 7   # moe_abi_version() of the library these signatures describe
 
 # Entry points (name -> (restype, argtypes)); must match include/moe.h.
 _P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -40,8 +40,8 @@ SIGNATURES = {
     "moe_permute": (_I, [_P, _I, _L, _L, _P, _I, _I, _I, _I, _I, _P, _L, _P, _P, _P, _P, _P,
                          _P, _S, _P, _P]),
     "moe_permute_bwd": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _I, _P]),
-    "moe_gmm": (_I, [_P, _L, _L, _P, _L, _L, _I, _P, _I, _L, _L, _I, _P, _P, _L, _L, _I, _I, _P,
-                     _P]),
+    "moe_gmm": (_I, [_P, _L, _L, _P, _L, _L, _I, _P, _P, _I, _L, _L, _I, _P, _P, _L, _L, _I, _I,
+                     _P, _P]),
     "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
     "moe_group_sum_workspace": (_S, [_L, _I, _L]),
     "moe_group_sum": (_I, [_P, _L, _I, _P, _P, _I, _L, _L, _P, _I, _I, _P, _S, _P, _P]),
@@ -49,8 +49,8 @@ SIGNATURES = {
     "moe_fp8_amax_scale": (_I, [_P, _L, _I, _L, _L, _I, _I, _P, _P, _S, _P]),
     "moe_fp8_padded_rows": (_L, [_L, _I]),
     "moe_fp8_quantize": (_I, [_P, _L, _I, _L, _L, _P, _I, _P, _I, _I, _P, _L, _P, _L, _L, _P, _P]),
-    "moe_gmm_fp8": (_I, [_P, _L, _L, _I, _P, _P, _L, _L, _I, _P, _P, _I, _L, _L, _P, _P, _L, _L,
-                         _I, _I, _P, _P]),
+    "moe_gmm_fp8": (_I, [_P, _L, _L, _I, _P, _P, _L, _L, _I, _P, _P, _P, _I, _L, _L, _P, _P, _L,
+                         _L, _I, _I, _P, _P]),
     "moe_tgmm_fp8": (_I, [_P, _L, _I, _P, _P, _L, _I, _P, _P, _P, _I, _L, _L, _L, _P, _L, _L, _I,
                           _I, _P, _P]),
     "moe_swiglu": (_I, [_P, _P, _I, _L, _L, _L, _P, _I, _P]),
@@ -285,11 +285,13 @@ def moe_permute_bwd(d_x_sorted, row_of_slot, T: int, K: int, d_x=None, accumulat
 # ----------------------------------------------------------- grouped GEMMs
 
 def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: Optional[int] = None,
-            out_dtype=None, accumulate: bool = False, err=None, stream=None, bias=None):
+            out_dtype=None, accumulate: bool = False, err=None, stream=None, bias=None,
+            valid_rows=None):
     """out[rows of g] (+)= lhs[rows of g] . rhs[g] (+ bias[g]) (rhs[g]: [K, N],
     or [N, K] used transposed; bias: optional contiguous [G, N] in lhs's
     dtype).  lhs and out may be strided 2-D views (unit column stride); rhs
-    a 3-D view with unit last stride."""
+    a 3-D view with unit last stride.  valid_rows ([G] int32, optional): lhs
+    rows past valid_rows[g] in each group are zero and are not read."""
     M_lhs, Kd = lhs.shape
     ld_lhs = _rowmajor(lhs, "lhs")
     if rhs.dim() != 3 or rhs.stride(2) != 1:
@@ -313,7 +315,8 @@ def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: 
     M_out = out.shape[0]
     ld_out = _rowmajor(out, "out")
     _check(load().moe_gmm(_ptr(lhs), M_lhs, ld_lhs, _ptr(rhs), rhs.stride(1), rhs.stride(0),
-                          int(bool(trans_rhs)), _ptr(group_sizes), G, Kd, N, _dtype_code(lhs),
+                          int(bool(trans_rhs)), _ptr(group_sizes), _ptr(valid_rows), G, Kd, N,
+                          _dtype_code(lhs),
                           _ptr(bias), _ptr(out), M_out, ld_out, _dtype_code(out), int(bool(accumulate)),
                           _ptr(err), _stream(stream)), "moe_gmm")
     return out
@@ -428,7 +431,7 @@ def moe_fp8_quantize(x, group_sizes, scale, fmt, per_group: bool = False, q=None
 
 def moe_gmm_fp8(lhs, lhs_fmt, lhs_scale_inv, rhs, rhs_fmt, rhs_scale_inv, group_sizes, out=None,
                 rows_out: Optional[int] = None, out_dtype=torch.bfloat16, accumulate: bool = False,
-                bias=None, err=None, stream=None):
+                bias=None, err=None, stream=None, valid_rows=None):
     """out[rows of g] (+)= sa sb[g] lhs[rows of g] . rhs[g]^T (+ bias[g]);
     lhs uint8 [M, K] (2-D view), rhs uint8 [G, N, K] (3-D view, unit last
     stride), scale_inv tensors float32 on the device."""
@@ -443,7 +446,8 @@ def moe_gmm_fp8(lhs, lhs_fmt, lhs_scale_inv, rhs, rhs_fmt, rhs_scale_inv, group_
         _contig(bias, "bias")
     _check(load().moe_gmm_fp8(_ptr(lhs), M_lhs, _rowmajor(lhs, "lhs"), _fmt(lhs_fmt),
                               _ptr(lhs_scale_inv), _ptr(rhs), rhs.stride(1), rhs.stride(0),
-                              _fmt(rhs_fmt), _ptr(rhs_scale_inv), _ptr(group_sizes), G, Kd, N,
+                              _fmt(rhs_fmt), _ptr(rhs_scale_inv), _ptr(group_sizes),
+                              _ptr(valid_rows), G, Kd, N,
                               _ptr(bias), _ptr(out), out.shape[0], _rowmajor(out, "out"),
                               _dtype_code(out), int(bool(accumulate)), _ptr(err),
                               _stream(stream)), "moe_gmm_fp8")

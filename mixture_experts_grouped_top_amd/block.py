@@ -201,7 +201,7 @@ class MoEPlan:
         for name, h in (("wi_0", self.h0), ("wi_1", self.h1)):
             _, wt, sw = q[name]
             with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
-                B.moe_gmm_fp8(xq, "e4m3", sx[2], wt, "e4m3", sw[2], gs, out=h, bias=mb.get(name),
+                B.moe_gmm_fp8(xq, "e4m3", sx[2], wt, "e4m3", sw[2], gs, valid_rows=self.vrows, out=h, bias=mb.get(name),
                               err=self.err, stream=stream)
         with self._rec("swiglu", nbytes=self._bytes().get("swiglu", 0) if self.recorder else 0):
             B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
@@ -209,7 +209,7 @@ class MoEPlan:
         aq, _, sa = q["act"]
         _, wt, sw = q["wo"]
         with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
-            B.moe_gmm_fp8(aq, "e4m3", sa[2], wt, "e4m3", sw[2], gs, out=self.y_sorted,
+            B.moe_gmm_fp8(aq, "e4m3", sa[2], wt, "e4m3", sw[2], gs, valid_rows=self.vact, out=self.y_sorted,
                           bias=mb.get("wo"), err=self.err, stream=stream)
 
     def _backward_fp8(self, stream):
@@ -219,7 +219,7 @@ class MoEPlan:
         dq, dqt, sd = q["d_y_sorted"]
         wor, _, swo = q["wo"]
         with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
-            B.moe_gmm_fp8(dq, "e5m2", sd[2], wor, "e4m3", swo[2], gs, out=self.d_act, err=self.err,
+            B.moe_gmm_fp8(dq, "e5m2", sd[2], wor, "e4m3", swo[2], gs, valid_rows=self.vrows, out=self.d_act, err=self.err,
                           stream=stream)
         _, aqt, sa = q["act"]
         with self._rec("tgmm", 2.0 * R * s.D * s.F):
@@ -235,7 +235,7 @@ class MoEPlan:
             hq, hqt, sh = q[gname]
             wr, _, sw = q[wname]
             with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
-                B.moe_gmm_fp8(hq, "e5m2", sh[2], wr, "e4m3", sw[2], gs, out=self.d_x_sorted,
+                B.moe_gmm_fp8(hq, "e5m2", sh[2], wr, "e4m3", sw[2], gs, valid_rows=self.vrows, out=self.d_x_sorted,
                               accumulate=i > 0, err=self.err, stream=stream)
             with self._rec("tgmm", 2.0 * R * s.D * s.F):
                 B.moe_tgmm_fp8(xqt, "e4m3", sx[2], hqt, "e5m2", sh[2], gs, self.rows, out=dw,
@@ -249,6 +249,17 @@ class MoEPlan:
     @property
     def group_sizes(self):
         return self.idx["group_sizes"]
+
+    # Rows past each group's kept rows (align / capacity padding) are zero in
+    # x_sorted, d_y_sorted and d_h, so the GEMMs reading them as lhs skip
+    # them; act has zero padding rows only without MLP biases.
+    @property
+    def vrows(self):
+        return self.idx["counts"]
+
+    @property
+    def vact(self):
+        return None if self.s.mlp_bias else self.idx["counts"]
 
     # Routed rows the expert GEMMs must process (the algorithmic work); set
     # by the caller when dropping makes it smaller than T*K (it is only used
@@ -327,24 +338,24 @@ class MoEPlan:
                 xs = self.x_sorted[:, i * c:(i + 1) * c]
                 last = i == s.n_chunks - 1   # the biases enter once, with the last chunk
                 with self._rec("gmm_up_chunk", 2.0 * R * c * s.F):
-                    B.moe_gmm(xs, wi_0[:, i * c:(i + 1) * c, :], gs, out=self.h0,
+                    B.moe_gmm(xs, wi_0[:, i * c:(i + 1) * c, :], gs, valid_rows=self.vrows, out=self.h0,
                               accumulate=i > 0, err=self.err, stream=stream,
                               bias=mb.get("wi_0") if last else None)
                 with self._rec("gmm_up_chunk", 2.0 * R * c * s.F):
-                    B.moe_gmm(xs, wi_1[:, i * c:(i + 1) * c, :], gs, out=self.h1,
+                    B.moe_gmm(xs, wi_1[:, i * c:(i + 1) * c, :], gs, valid_rows=self.vrows, out=self.h1,
                               accumulate=i > 0, err=self.err, stream=stream,
                               bias=mb.get("wi_1") if last else None)
         else:
             with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
-                B.moe_gmm(self.x_sorted, wi_0, gs, out=self.h0, err=self.err, stream=stream,
+                B.moe_gmm(self.x_sorted, wi_0, gs, valid_rows=self.vrows, out=self.h0, err=self.err, stream=stream,
                           bias=mb.get("wi_0"))
             with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
-                B.moe_gmm(self.x_sorted, wi_1, gs, out=self.h1, err=self.err, stream=stream,
+                B.moe_gmm(self.x_sorted, wi_1, gs, valid_rows=self.vrows, out=self.h1, err=self.err, stream=stream,
                           bias=mb.get("wi_1"))
         with self._rec("swiglu", nbytes=nb.get("swiglu", 0)):
             B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
         with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
-            B.moe_gmm(self.act, wo, gs, out=self.y_sorted, err=self.err, stream=stream,
+            B.moe_gmm(self.act, wo, gs, valid_rows=self.vact, out=self.y_sorted, err=self.err, stream=stream,
                       bias=mb.get("wo"))
         with self._rec("combine", nbytes=nb.get("combine", 0)):
             B.moe_combine(self.y_sorted, self.idx["row_of_slot"], self.w, y=self.y,
@@ -358,11 +369,11 @@ class MoEPlan:
             for i in range(s.n_chunks):
                 with self._rec("gmm_up_chunk", 4.0 * R * c * s.F):
                     B.moe_gmm(self.x_sorted[:, i * c:(i + 1) * c], wi[:, i * c:(i + 1) * c, :],
-                              gs, out=self.h, accumulate=i > 0, err=self.err, stream=stream,
+                              gs, valid_rows=self.vrows, out=self.h, accumulate=i > 0, err=self.err, stream=stream,
                               bias=b_wi if i == s.n_chunks - 1 else None)
         else:
             with self._rec("gmm_nn", 4.0 * R * s.D * s.F):
-                B.moe_gmm(self.x_sorted, wi, gs, out=self.h, err=self.err, stream=stream,
+                B.moe_gmm(self.x_sorted, wi, gs, valid_rows=self.vrows, out=self.h, err=self.err, stream=stream,
                           bias=b_wi)
 
     def backward(self, dy, x, wi_0, wi_1, wo, Wg=None, bias=None, stream=None, wi=None):
@@ -389,7 +400,7 @@ class MoEPlan:
         R = self.kept_rows
         nb = self._bytes() if self.recorder is not None else {}
         with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
-            B.moe_gmm(self.d_y_sorted, wo, gs, trans_rhs=True, out=self.d_act, err=self.err,
+            B.moe_gmm(self.d_y_sorted, wo, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_act, err=self.err,
                       stream=stream)
         with self._rec("tgmm", 2.0 * R * s.D * s.F):
             # padding rows of each group (past its kept rows) are zero in
@@ -403,17 +414,17 @@ class MoEPlan:
             # d_x_sorted = [d_h0 | d_h1] . [wi_0 | wi_1]^T in one contraction
             # over 2F; d_wi = x_sorted^T [d_h0 | d_h1] in one tgmm
             with self._rec("gmm_nt", 4.0 * R * s.D * s.F):
-                B.moe_gmm(self.d_h, wi, gs, trans_rhs=True, out=self.d_x_sorted, err=self.err,
+                B.moe_gmm(self.d_h, wi, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_x_sorted, err=self.err,
                           stream=stream)
             with self._rec("tgmm", 4.0 * R * s.D * s.F):
                 B.moe_tgmm(xs, self.d_h, gs, out=self.d_wi, err=self.err, stream=stream,
                            valid_rows=self.idx["counts"])
         else:
             with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
-                B.moe_gmm(self.d_h0, wi_0, gs, trans_rhs=True, out=self.d_x_sorted, err=self.err,
+                B.moe_gmm(self.d_h0, wi_0, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_x_sorted, err=self.err,
                           stream=stream)
             with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
-                B.moe_gmm(self.d_h1, wi_1, gs, trans_rhs=True, out=self.d_x_sorted,
+                B.moe_gmm(self.d_h1, wi_1, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_x_sorted,
                           accumulate=True, err=self.err, stream=stream)
             with self._rec("tgmm", 2.0 * R * s.D * s.F):
                 B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream,

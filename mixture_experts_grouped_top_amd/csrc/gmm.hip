@@ -759,7 +759,8 @@ struct Stages {
 template <int TM, int TN, typename TO>
 __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO* o, int64_t ldo,
                                            int rv, int cv, int accumulate,
-                                           const bf16_t* bias = nullptr, float scale = 1.f) {
+                                           const bf16_t* bias = nullptr, float scale = 1.f,
+                                           int rz = 1 << 30) {
   constexpr int WC = TN / 2;
   constexpr int SROW = WC * 4 + 16;
   constexpr int CPR = WC / 8;                 // 8-column chunks per slab row
@@ -790,7 +791,7 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
       const float4 hi = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] *= scale;
+      for (int e = 0; e < 8; ++e) v[e] = grow < rz ? v[e] * scale : 0.f;   // rows >= rz: zero lhs rows
       if (grow < rv && gcol < cv) {
         TO* p = o + static_cast<int64_t>(grow) * ldo + gcol;
         if (accumulate) {
@@ -861,13 +862,16 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
     const int rv = min(TM, rows_g - mt * TM);
     const int64_t col0 = static_cast<int64_t>(nt) * TN;
     const int cv = static_cast<int>(lmin(TN, a.N - col0));
-    A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, rv);
+    // rows past the group's valid rows are zero in lhs: not loaded (the
+    // DMA re-reads the last loaded row), and their products written as zero
+    const int vr = a.valid ? max(0, min(rv, min(rows_g, max(a.valid[g], 0)) - mt * TM)) : rv;
+    A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, max(vr, 1));
     const bf16_t* bg = a.rhs + g * a.rhs_gs;
     B.setup(B_COLK ? bg + col0 : bg + col0 * a.ld_rhs, a.ld_rhs, cv);
     if constexpr (PAIR) contract2(smem, A, B, a.Kdim, acc, fa, fb);
     else contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
     store_tile(acc, smem, out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate,
-               a.bias ? a.bias + g * a.N + col0 : nullptr);
+               a.bias ? a.bias + g * a.N + col0 : nullptr, 1.f, vr);
   }
   if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
 }
@@ -1087,11 +1091,13 @@ __global__ __launch_bounds__(NT, TM >= 256 ? 1 : 2) void gmm_fp8_kernel(Fp8Args 
     const int rv = min(TM, rows_g - mt * TM);
     const int64_t col0 = static_cast<int64_t>(nt) * TN;
     const int cv = static_cast<int>(lmin(TN, a.N - col0));
-    A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, rv);
+    const int vr = a.valid ? max(0, min(rv, min(rows_g, max(a.valid[g], 0)) - mt * TM)) : rv;
+    A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, max(vr, 1));
     B.setup(a.rhs + g * a.rhs_gs + col0 * a.ld_rhs, a.ld_rhs, cv);
     contract_f8<F8Tile<TM>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
     store_tile(static_cast<const Acc<TM, TN>&>(acc), smem, out + row0 * a.ld_out + col0, a.ld_out,
-               rv, cv, a.accumulate, a.bias ? a.bias + g * a.N + col0 : nullptr, sa * a.sinv_b[g]);
+               rv, cv, a.accumulate, a.bias ? a.bias + g * a.N + col0 : nullptr, sa * a.sinv_b[g],
+               vr);
   }
   if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
 }
@@ -1299,7 +1305,8 @@ using namespace moe;
 
 MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs,
                     int64_t ld_rhs, int64_t rhs_group_stride, int trans_rhs,
-                    const int32_t* group_sizes, int G, int64_t Kdim, int64_t N, int in_dtype,
+                    const int32_t* group_sizes, const int32_t* valid_rows, int G, int64_t Kdim,
+                    int64_t N, int in_dtype,
                     const void* bias, void* out, int64_t M_out, int64_t ld_out, int out_dtype,
                     int accumulate, int32_t* err, void* stream) {
   if (G < 1 || G > kMaxG || M_lhs < 0 || M_out < 0 || M_out > M_lhs || Kdim < 0 || N < 0)
@@ -1319,7 +1326,8 @@ MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == MOE_BF16) {
     MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
-               rhs_group_stride, group_sizes, G, M_out, Kdim, N, out, ld_out, 0, accumulate, err};
+               rhs_group_stride, group_sizes, G, M_out, Kdim, N, out, ld_out, 0, accumulate, err,
+               valid_rows};
     a.bias = static_cast<const bf16_t*>(bias);
     // narrow outputs and single-step contractions use a 256 x 128 tile;
     // small groups (fewer than 512 rows per group on average) use 128-row
@@ -1433,7 +1441,8 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
 MOE_API int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_fmt,
                         const float* lhs_scale_inv, const void* rhs, int64_t ld_rhs,
                         int64_t rhs_group_stride, int rhs_fmt, const float* rhs_scale_inv,
-                        const int32_t* group_sizes, int G, int64_t Kdim, int64_t N,
+                        const int32_t* group_sizes, const int32_t* valid_rows, int G, int64_t Kdim,
+                        int64_t N,
                         const void* bias, void* out, int64_t M_out, int64_t ld_out, int out_dtype,
                         int accumulate, int32_t* err, void* stream) {
   if (G < 1 || G > kMaxGShort || M_lhs < 0 || M_out < 0 || M_out > M_lhs || Kdim < 0 || N < 0)
@@ -1454,7 +1463,7 @@ MOE_API int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_
     return MOE_ERR_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Fp8Args a{static_cast<const bf16_t*>(lhs), ld_lhs / 2, static_cast<const bf16_t*>(rhs),
-            ld_rhs / 2, rhs_group_stride / 2, group_sizes, nullptr, G, M_out, Kdim / 2, N, out,
+            ld_rhs / 2, rhs_group_stride / 2, group_sizes, valid_rows, G, M_out, Kdim / 2, N, out,
             ld_out, 0, accumulate, err, lhs_scale_inv, rhs_scale_inv,
             static_cast<const bf16_t*>(bias)};
   // 256-row tiles when groups hold 512 rows or more on average

@@ -107,8 +107,8 @@ def test_argument_checks_return_before_launch(lib):
     def gmm(**kw):
         a = args(**kw)
         return lib.moe_gmm(a["lhs"], a["M_lhs"], a["ld"], a["rhs"], a["ldr"], a["gst"], a["tr"],
-                           a["gs"], a["G"], a["Kd"], a["N"], a["it"], a.get("bias"), a["out"],
-                           a["M_out"], a["ldo"], a["ot"], a["acc"], None, None)
+                           a["gs"], None, a["G"], a["Kd"], a["N"], a["it"], a.get("bias"),
+                           a["out"], a["M_out"], a["ldo"], a["ot"], a["acc"], None, None)
     assert gmm(G=0) == -1
     assert gmm(M_out=65) == -1
     assert gmm(Kd=60, ld=60) == -1
@@ -129,10 +129,10 @@ def test_argument_checks_return_before_launch(lib):
     assert lib.moe_fp8_amax_scale(P, 64, 1, 64, 64, 1, 7, P, W, 1 << 20, None) == -1
     assert lib.moe_fp8_amax_scale(P, 64, 1, 65, 64, 2, 0, P, W, 1 << 20, None) == -1
     assert lib.moe_fp8_amax_scale(P, 64, 1, 64, 64, 1, 0, P, None, 0, None) == -5
-    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 40, 40 * 64, 0, P, P, 2, 40, 64, None, P, 64, 64,
-                           1, 0, None, None) == -1
-    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 64, 64 * 64, 0, P, P, 1001, 64, 64, None, P, 64,
+    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 40, 40 * 64, 0, P, P, None, 2, 40, 64, None, P, 64,
                            64, 1, 0, None, None) == -1
+    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 64, 64 * 64, 0, P, P, None, 1001, 64, 64, None, P,
+                           64, 64, 1, 0, None, None) == -1
     assert lib.moe_fp8_padded_rows(100, 3) == 64 * (2 + 2)
     assert lib.moe_fp8_quantize(P, 64, 1, 100, 64, P, 3, P, 0, 0, None, 0, P, 128, 0, None,
                                 None) == -1

@@ -163,6 +163,27 @@ def test_gmm_fp8(gpu_lib, case):
     assert host(err)[0] == 0
 
 
+@pytest.mark.parametrize("big", [False, True])
+def test_gmm_fp8_valid_rows(gpu_lib, big):
+    """FP8 gmm skips lhs rows past valid_rows (garbage codes here)."""
+    gs = np.array([1024, 1024] if big else [300, 0, 257, 128], dtype=np.int32)
+    valid = np.array([1000, 3] if big else [299, 0, 1, 0], dtype=np.int32)
+    G, M, K, N = len(gs), int(gs.sum()), 256, 264
+    g = np.random.default_rng(4 + big)
+    qa = _codes(g, (M, K), "e4m3")
+    qb = _codes(g, (G, N, K), "e4m3")
+    qa0 = qa.copy()
+    off = np.concatenate([[0], np.cumsum(gs)])
+    for e in range(G):
+        qa0[off[e] + valid[e]:off[e + 1]] = 0
+    sa, sb = np.float32([0.03]), np.full(G, 0.5, np.float32)
+    out = gpu_lib.moe_gmm_fp8(_u8(qa), "e4m3", dev(sa), _u8(qb), "e4m3", dev(sb), dev_i32(gs),
+                              out_dtype=torch.float32, valid_rows=dev_i32(valid))
+    want = oracle.gmm(F8.dequantize(qa0, "e4m3", sa[0]), F8.dequantize(qb, "e4m3", sb), gs,
+                      trans_rhs=True)
+    assert_close(host(out), want, TOL_F32, "gmm_fp8 valid_rows")
+
+
 TGMM8_CASES = [
     # group sizes, valid rows, Kd, N, formats, out, accumulate
     ([130, 0, 257, 1, 64, 0, 300], None, 136, 264, "e4m3", "e5m2", "f32", False),

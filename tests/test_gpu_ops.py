@@ -335,6 +335,43 @@ def test_gmm(gpu_lib, case, with_bias):
     assert host(err)[0] == 0
 
 
+GMM_VALID = [
+    # group sizes, valid rows, K, N, trans, accumulate
+    ([300, 0, 257, 128, 1000], [299, 0, 1, 0, 613], 264, 136, False, False),   # 128-row tiles
+    ([300, 0, 257, 128, 1000], [299, 0, 1, 0, 613], 136, 264, True, True),
+    ([1024, 1024], [1000, 3], 512, 264, False, False),                         # 256-row pair tiles
+    ([1024, 1024], [1000, 3], 512, 264, True, False),
+    ([517], [0], 64, 8, False, True),                                         # no valid row at all
+]
+
+
+@pytest.mark.parametrize("case", GMM_VALID, ids=[str(i) for i in range(len(GMM_VALID))])
+def test_gmm_valid_rows(gpu_lib, case):
+    """Rows past valid_rows[g] of each group are not read (garbage here) and
+    give zero products: the result equals the oracle with those rows zeroed,
+    plus the bias and the partial sum on every row of the group."""
+    gs, valid, K, N, trans, acc = case
+    gs = np.array(gs, dtype=np.int32)
+    valid = np.array(valid, dtype=np.int32)
+    G = len(gs)
+    g = np.random.default_rng(K + N)
+    M = int(gs.sum())
+    lhs = _draw(g, (M, K), "bf16")
+    rhs = _draw(g, (G, N, K) if trans else (G, K, N), "bf16")
+    bias = _draw(g, (G, N), "bf16")
+    lhs0 = lhs.copy()
+    off = np.concatenate([[0], np.cumsum(gs)])
+    for e in range(G):
+        lhs0[off[e] + valid[e]:off[e + 1]] = 0
+    P = _draw(g, (M, N), "f32") if acc else None
+    out = dev(P) if acc else poison(torch.empty((M, N), dtype=torch.float32, device="cuda"))
+    gpu_lib.moe_gmm(dev(lhs, torch.bfloat16), dev(rhs, torch.bfloat16), dev_i32(gs), trans_rhs=trans,
+                    out=out, accumulate=acc, bias=dev(bias, torch.bfloat16),
+                    valid_rows=dev_i32(valid))
+    want = oracle.gmm(lhs0, rhs, gs, trans_rhs=trans, partial=P, bias=bias)
+    assert_close(host(out), want, TOL_F32, "gmm valid_rows")
+
+
 @pytest.mark.parametrize("it", ["bf16", "f32"])
 def test_tgmm_valid_rows(gpu_lib, it):
     """With valid_rows the contraction stops after each group's first
