@@ -16,16 +16,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// float32 -> bf16, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two packed bf16 in one dword (lo = a, hi = b): round to
+// nearest, ties to even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
-// Two floats -> two packed bf16 in one dword (lo = a, hi = b).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+// float32 -> bf16, round to nearest, ties to even.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return static_cast<bf16_t>(pack_bf16x2(f, 0.f));
 }
 
 // Wave 0 scans the group sizes: row_base[g] (rows clipped to max_rows) and,

@@ -369,6 +369,19 @@ template <int TM, int TN>
 struct Acc {
   static constexpr int FM = TM / 64, FN = TN / 64;
   f32x16 v[FM][FN];
+  // Fragment rows i < live take MFMAs; the rest hold only zero rows of lhs
+  // (rows past a group's valid rows, or past its last row), so their
+  // products are zero and are skipped.  Wave-uniform; FM unless a gmm tile
+  // sets it.  Only 128-row tiles skip (they serve small, padded groups; in
+  // the 256-row kernels the branches cost registers).
+  static constexpr bool kSkip = TM <= 128;
+  int live = FM;
+  // live for a tile whose first vrows rows (of TM) may be non-zero, for
+  // this wave's row block
+  __device__ __forceinline__ void set_live_rows(int vrows) {
+    const int wr = static_cast<int>(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 1) * (TM / 2);
+    live = __builtin_amdgcn_readfirstlane(min(FM, max(0, (vrows - wr + 31) >> 5)));
+  }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -412,14 +425,15 @@ struct Acc {
   }
   __device__ __forceinline__ void mma_one(const Frags& f, int q) {
     const int i = q / FN, j = q % FN;
-    v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], v[i][j], 0, 0, 0);
+    if (!kSkip || i < live) v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], v[i][j], 0, 0, 0);
   }
   __device__ __forceinline__ void mma(const Frags& f) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
+      if (!kSkip || i < live)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], v[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j)
+          v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], v[i][j], 0, 0, 0);
   }
   // f(row, col, value) for every accumulator element (row/col inside the tile)
   template <typename F>
@@ -753,9 +767,12 @@ struct Stages {
 
 // Write the accumulator tile: for each of its FM 32-row slabs a wave stages
 // the slab (32 x TN/2 float32) in its own LDS region, then reads it back as
-// 8-column row chunks and stores them with 16-byte (bf16) or 32-byte (fp32)
-// accesses; rows >= rv and columns >= cv are skipped.  The LDS is the
-// operand stages, free once the contraction has ended with a barrier.
+// 8-column row chunks (all of a lane's chunks at once, so the reads overlap)
+// and stores them with 16-byte (bf16) or 32-byte (fp32) accesses; rows >= rv
+// and columns >= cv are skipped.  A wave whose whole block is stored plainly
+// (in bounds, no partial sum, bias or scale) takes a path without per-chunk
+// tests.  The LDS is the operand stages, free once the contraction has ended
+// with a barrier.
 template <int TM, int TN, typename TO>
 __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO* o, int64_t ldo,
                                            int rv, int cv, int accumulate,
@@ -764,11 +781,15 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
   constexpr int WC = TN / 2;
   constexpr int SROW = WC * 4 + 16;
   constexpr int CPR = WC / 8;                 // 8-column chunks per slab row
+  constexpr int NQ = 32 * CPR / 64;           // chunks per lane per slab
   const int tid = opaque_tid();
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   static_assert(4 * 32 * SROW <= Stages<TM, TN>::kBytes, "epilogue slabs fit in the stage buffers");
   char* slab = lds + w * 32 * SROW;
   const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * WC;
+  const bool plain = !accumulate && !bias && scale == 1.f && wr + TM / 2 <= min(rv, rz) &&
+                     wc + WC <= cv;
 #pragma unroll
   for (int i = 0; i < Acc<TM, TN>::FM; ++i) {
 #pragma unroll
@@ -782,18 +803,28 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float4 lo[NQ], hi[NQ];
 #pragma unroll
-    for (int q = 0; q < 32 * CPR / 64; ++q) {
+    for (int q = 0; q < NQ; ++q) {
+      const int chunk = lane + 64 * q;
+      const int row = chunk / CPR, c8 = chunk % CPR;
+      lo[q] = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32);
+      hi[q] = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
       const int chunk = lane + 64 * q;
       const int row = chunk / CPR, c8 = chunk % CPR;
       const int grow = wr + 32 * i + row, gcol = wc + 8 * c8;
-      const float4 lo = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32);
-      const float4 hi = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
-      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      float v[8] = {lo[q].x, lo[q].y, lo[q].z, lo[q].w, hi[q].x, hi[q].y, hi[q].z, hi[q].w};
+      TO* p = o + static_cast<int64_t>(grow) * ldo + gcol;
+      if (plain) {
+        store8_nt(p, v);
+        continue;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = grow < rz ? v[e] * scale : 0.f;   // rows >= rz: zero lhs rows
       if (grow < rv && gcol < cv) {
-        TO* p = o + static_cast<int64_t>(grow) * ldo + gcol;
         if (accumulate) {
           float old[8];
           load8(p, old);
@@ -865,6 +896,7 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
     // rows past the group's valid rows are zero in lhs: not loaded (the
     // DMA re-reads the last loaded row), and their products written as zero
     const int vr = a.valid ? max(0, min(rv, min(rows_g, max(a.valid[g], 0)) - mt * TM)) : rv;
+    acc.set_live_rows(vr);
     A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, max(vr, 1));
     const bf16_t* bg = a.rhs + g * a.rhs_gs;
     B.setup(B_COLK ? bg + col0 : bg + col0 * a.ld_rhs, a.ld_rhs, cv);
@@ -950,7 +982,8 @@ struct Acc8 : Acc<TM, TN> {
   }
   __device__ __forceinline__ void mma8(const Frags8& f, int q) {
     const int i = q / Base::FN, j = q % Base::FN;
-    this->v[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], this->v[i][j],
+    if (!Base::kSkip || i < this->live)
+      this->v[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], this->v[i][j],
                                                                      FA, FB, 0, 0, 0, 0);
   }
 };
@@ -1092,6 +1125,7 @@ __global__ __launch_bounds__(NT, TM >= 256 ? 1 : 2) void gmm_fp8_kernel(Fp8Args 
     const int64_t col0 = static_cast<int64_t>(nt) * TN;
     const int cv = static_cast<int>(lmin(TN, a.N - col0));
     const int vr = a.valid ? max(0, min(rv, min(rows_g, max(a.valid[g], 0)) - mt * TM)) : rv;
+    acc.set_live_rows(vr);
     A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, max(vr, 1));
     B.setup(a.rhs + g * a.rhs_gs + col0 * a.ld_rhs, a.ld_rhs, cv);
     contract_f8<F8Tile<TM>::NS>(smem, A, B, a.Kdim, acc, fa, fb);

@@ -163,11 +163,20 @@ def test_gmm_fp8(gpu_lib, case):
     assert host(err)[0] == 0
 
 
-@pytest.mark.parametrize("big", [False, True])
-def test_gmm_fp8_valid_rows(gpu_lib, big):
+FP8_VALID = {
+    "small": ([300, 0, 257, 128], [299, 0, 1, 0]),
+    "big": ([1024, 1024], [1000, 3]),
+    # valid rows ending at and around the waves' 32-row fragment boundaries
+    "frag": ([128] * 10 + [384], [1, 31, 32, 33, 63, 64, 65, 96, 97, 128, 300]),
+}
+
+
+@pytest.mark.parametrize("case", list(FP8_VALID))
+def test_gmm_fp8_valid_rows(gpu_lib, case):
     """FP8 gmm skips lhs rows past valid_rows (garbage codes here)."""
-    gs = np.array([1024, 1024] if big else [300, 0, 257, 128], dtype=np.int32)
-    valid = np.array([1000, 3] if big else [299, 0, 1, 0], dtype=np.int32)
+    gs = np.array(FP8_VALID[case][0], dtype=np.int32)
+    valid = np.array(FP8_VALID[case][1], dtype=np.int32)
+    big = case == "big"
     G, M, K, N = len(gs), int(gs.sum()), 256, 264
     g = np.random.default_rng(4 + big)
     qa = _codes(g, (M, K), "e4m3")

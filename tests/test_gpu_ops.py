@@ -342,6 +342,10 @@ GMM_VALID = [
     ([1024, 1024], [1000, 3], 512, 264, False, False),                         # 256-row pair tiles
     ([1024, 1024], [1000, 3], 512, 264, True, False),
     ([517], [0], 64, 8, False, True),                                         # no valid row at all
+    # 128-row tiles whose valid rows end at and around the 32-row fragment
+    # boundaries of its waves (fragments past them take no MFMAs)
+    ([128] * 10 + [384], [1, 31, 32, 33, 63, 64, 65, 96, 97, 128, 300], 264, 264, False, False),
+    ([128] * 10 + [384], [1, 31, 32, 33, 63, 64, 65, 96, 97, 128, 300], 264, 264, True, True),
 ]
 
 
