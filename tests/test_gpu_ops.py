@@ -267,6 +267,8 @@ GS = {
     # more groups than the 128-row tile variant holds (1000): 256-row tiles
     "many": [(i * 7) % 3 for i in range(1010)],
     "max_groups": [(i * 5) % 4 for i in range(1024)],
+    # skewed short contractions over many tiles per workgroup
+    "skewed": [(i * 37) % 300 for i in range(64)],
 }
 
 GMM_CASES = [
@@ -511,6 +513,7 @@ TGMM_CASES = [
     ("all_empty", 64, 64, "bf16", "bf16", False),
     ("max_groups", 16, 136, "bf16", "bf16", False),
     ("many", 264, 520, "bf16", "bf16", False),
+    ("skewed", 520, 1032, "bf16", "bf16", False),   # full and ragged tiles, several per workgroup
 ]
 
 
