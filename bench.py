@@ -152,12 +152,15 @@ KERNEL_NAME = {
 
 
 def kernel_source_digest() -> str:
-    """Digest of the grouped-GEMM source with comments and blank lines
-    removed, so that counters stay tied to the code they were taken on."""
+    """Digest of the grouped-GEMM source and the helpers it includes, with
+    comments and blank lines removed, so that counters stay tied to the code
+    they were taken on."""
     import re
-    src = os.path.join(ROOT, "mixture_experts_grouped_top_amd", "csrc", "gmm.hip")
-    with open(src) as f:
-        text = f.read()
+    csrc = os.path.join(ROOT, "mixture_experts_grouped_top_amd", "csrc")
+    text = ""
+    for name in ("gmm.hip", "common.h"):
+        with open(os.path.join(csrc, name)) as f:
+            text += f.read()
     text = re.sub(r"//[^\n]*", "", text)
     code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
