@@ -23,37 +23,28 @@ namespace {
 constexpr int kAmaxPerBlock = 16384;   // elements per amax block (target)
 constexpr int kMaxGroups = 1024;
 
-// Code of the FP8 value nearest to v (ties to even), saturating; sign kept.
+// Codes of the FP8 values nearest to a, b, c, d (ties to even), saturating,
+// sign kept, packed a in the low byte: each value is clamped to +-fmax
+// (v_med3_f32) and converted by v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32, two per
+// instruction.  The clamp makes the hardware rounding saturate; for every
+// finite float32 this gives the same code as rounding the exact value to
+// nearest-even and saturating (compared over all 2^32 bit patterns).
 template <int FMT>
-__device__ __forceinline__ uint32_t f32_to_fp8(float v) {
-  constexpr int MB = FMT == MOE_FP8_E4M3 ? 3 : 2;
-  constexpr int BIAS = FMT == MOE_FP8_E4M3 ? 7 : 15;
-  constexpr uint32_t MAXC = FMT == MOE_FP8_E4M3 ? 0x7Eu : 0x7Bu;
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
   constexpr float FMAX = FMT == MOE_FP8_E4M3 ? 448.f : 57344.f;
-  // smallest normal 2^(1 - BIAS); subnormal spacing 2^(1 - BIAS - MB)
-  constexpr float MIN_NORMAL = FMT == MOE_FP8_E4M3 ? 0x1p-6f : 0x1p-14f;
-  constexpr float INV_SUB_STEP = FMT == MOE_FP8_E4M3 ? 0x1p9f : 0x1p16f;
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t ua = u & 0x7FFFFFFFu;
-  const float a = __uint_as_float(ua);
-  uint32_t code;
-  if (!(a < FMAX)) {
-    code = MAXC;
-  } else if (a < MIN_NORMAL) {
-    // exact power-of-two scaling, then round half to even (v_rndne_f32)
-    code = static_cast<uint32_t>(__builtin_rintf(a * INV_SUB_STEP));
+  a = __builtin_amdgcn_fmed3f(a, -FMAX, FMAX);
+  b = __builtin_amdgcn_fmed3f(b, -FMAX, FMAX);
+  c = __builtin_amdgcn_fmed3f(c, -FMAX, FMAX);
+  d = __builtin_amdgcn_fmed3f(d, -FMAX, FMAX);
+  int r;
+  if constexpr (FMT == MOE_FP8_E4M3) {
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
   } else {
-    const int e = static_cast<int>(ua >> 23) - 127;
-    const uint32_t m = ua & 0x7FFFFFu;
-    uint32_t q = m >> (23 - MB);
-    const uint32_t rem = m & ((1u << (23 - MB)) - 1u);
-    const uint32_t half = 1u << (22 - MB);
-    if (rem > half || (rem == half && (q & 1u))) ++q;
-    code = (static_cast<uint32_t>(e + BIAS) << MB) + q;   // a carry moves to the exponent
-    if (code > MAXC) code = MAXC;
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, r, true);
   }
-  return sign | code;
+  return static_cast<uint32_t>(r);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -199,11 +190,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(
       raw[i][0].get(v);
       raw[i][1].get(v + 8);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w[i][k] = 0u;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t c = f32_to_fp8<FMT>(__fmul_rn(v[e], s));
-        w[i][e >> 2] |= (ok && (e < 8 || two) ? c : 0u) << (8 * (e & 3));
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t c = pack4_fp8<FMT>(__fmul_rn(v[4 * k], s), __fmul_rn(v[4 * k + 1], s),
+                                          __fmul_rn(v[4 * k + 2], s), __fmul_rn(v[4 * k + 3], s));
+        w[i][k] = ok && (k < 2 || two) ? c : 0u;
       }
       if (q && ok) {
         uint8_t* d = q + (static_cast<int64_t>(row_base[g]) + r_in + lr + i) * ld_q + col;

@@ -767,7 +767,7 @@ struct Stages {
 
 // Write the accumulator tile: for each of its FM 32-row slabs a wave stages
 // the slab (32 x TN/2 float32) in its own LDS region, then reads it back as
-// 8-column row chunks (all of a lane's chunks at once, so the reads overlap)
+// 8-column row chunks (four of a lane's chunks at once, so the reads overlap)
 // and stores them with 16-byte (bf16) or 32-byte (fp32) accesses; rows >= rv
 // and columns >= cv are skipped.  A wave whose whole block is stored plainly
 // (in bounds, no partial sum, bias or scale) takes a path without per-chunk
@@ -782,6 +782,7 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
   constexpr int SROW = WC * 4 + 16;
   constexpr int CPR = WC / 8;                 // 8-column chunks per slab row
   constexpr int NQ = 32 * CPR / 64;           // chunks per lane per slab
+  constexpr int QB = NQ < 4 ? NQ : 4;         // chunks whose reads are in flight together
   const int tid = opaque_tid();
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -803,20 +804,23 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float4 lo[NQ], hi[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int chunk = lane + 64 * q;
+    for (int q0 = 0; q0 < NQ; q0 += QB) {
+    float4 lo[QB], hi[QB];
+#pragma unroll
+    for (int u = 0; u < QB; ++u) {
+      const int chunk = lane + 64 * (q0 + u);
       const int row = chunk / CPR, c8 = chunk % CPR;
-      lo[q] = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32);
-      hi[q] = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
+      lo[u] = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32);
+      hi[u] = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
     }
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int u = 0; u < QB; ++u) {
+      const int q = q0 + u;
       const int chunk = lane + 64 * q;
       const int row = chunk / CPR, c8 = chunk % CPR;
       const int grow = wr + 32 * i + row, gcol = wc + 8 * c8;
-      float v[8] = {lo[q].x, lo[q].y, lo[q].z, lo[q].w, hi[q].x, hi[q].y, hi[q].z, hi[q].w};
+      float v[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w, hi[u].x, hi[u].y, hi[u].z, hi[u].w};
       TO* p = o + static_cast<int64_t>(grow) * ldo + gcol;
       if (plain) {
         store8_nt(p, v);
@@ -840,6 +844,7 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
         if (accumulate) store8(p, v);
         else store8_nt(p, v);
       }
+    }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

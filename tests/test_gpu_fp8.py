@@ -95,6 +95,56 @@ def test_fp8_quantize(gpu_lib, case):
     assert (got_t[:, used:] == 0xAA).all()
 
 
+def _all_bf16():
+    """Every finite bf16 value below 1e30 in magnitude (as float32; the
+    float32 products with the test scales stay finite)."""
+    v = ms.bf16_from_bits(np.arange(1 << 16, dtype=np.uint16))
+    return v[np.isfinite(v) & (np.abs(v) < 1e30)]
+
+
+def _f32_sweep(fmt):
+    """float32 values around every FP8 code: the codes, the midpoints between
+    neighbours (ties), one float32 ulp either side of them, and random bit
+    patterns over the format's exponent range and beyond."""
+    codes = np.arange(256, dtype=np.uint8)
+    d = F8.decode(codes, fmt)
+    d = np.sort(d[np.isfinite(d) & (d >= 0)])
+    mids = (d[1:] + d[:-1]) / 2
+    base = np.concatenate([d, mids]).astype(np.float32)
+    near = np.concatenate([base, np.nextafter(base, np.float32(np.inf)),
+                           np.nextafter(base, np.float32(-np.inf))])
+    g = np.random.default_rng(99)
+    e = g.integers(-40 if fmt == "e4m3" else -50, 30 if fmt == "e5m2" else 20, 200000)
+    rnd = (g.uniform(1, 2, e.size) * np.exp2(e.astype(np.float64))).astype(np.float32)
+    v = np.concatenate([near, rnd, [0.0, 1e-45, 1e30]]).astype(np.float32)
+    return np.concatenate([v, -v])
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("src", ["bf16-all", "f32-sweep"])
+def test_fp8_quantize_codes_exhaustive(gpu_lib, fmt, src):
+    """The quantizer's codes equal the oracle's (round to nearest even of the
+    float32 product, saturating, sign kept) for every finite bf16 input and
+    for float32 inputs at, between and next to every FP8 value, under scales
+    that keep, round and saturate them."""
+    v = _all_bf16() if src == "bf16-all" else _f32_sweep(fmt)
+    dt = "bf16" if src == "bf16-all" else "f32"
+    cols = 128
+    rows = (v.size + cols - 1) // cols
+    x = np.zeros(rows * cols, dtype=np.float32)
+    x[:v.size] = v
+    x = x.reshape(rows, cols)
+    gs = np.array([rows], dtype=np.int32)
+    for scale in (1.0, 0.8125, 3.0 if fmt == "e4m3" else 1000.0):
+        q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+        gpu_lib.moe_fp8_quantize(dev(x, TD[dt]), dev_i32(gs),
+                                 torch.tensor([scale], dtype=torch.float32, device="cuda"), fmt, q=q)
+        want = F8.quantize(x, fmt, np.float32(scale))
+        got = host(q)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, (scale, x.ravel()[bad[:5]], got.ravel()[bad[:5]], want.ravel()[bad[:5]])
+
+
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 def test_fp8_quantize_weights(gpu_lib, fmt):
     """Per-expert scaling of a weight stack [E, a, b]: row-wise copy and the
