@@ -215,6 +215,30 @@ int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs, int
             const void* bias, void* out, int64_t M_out, int64_t ld_out, int out_dtype,
             int accumulate, int32_t* err, void* stream);
 
+/* moe_gmm_swiglu: the up-projection with a fused weight and the SwiGLU
+ * activation in its epilogue (the fused gate/up weight of [TE-MoE]; the
+ * gate_proj_out / up_proj_out pair its commit notes name; SwiGLU as in
+ * moe_swiglu).  rhs + g*rhs_group_stride is wi[g] = [wi_0[g] | wi_1[g]]
+ * viewed as [Kdim, 2F] with row stride ld_rhs (gate columns 0..F-1, up
+ * columns F..2F-1).  For each group (rows as moe_gmm's):
+ *     h[o_g + i, :]   = lhs[o_g + i, :Kdim] . wi[g] (+ bias[g])   [rows, 2F]
+ *     act[o_g + i, :] = silu(h[.., :F]) * h[.., F:]                [rows, F]
+ *   with act computed from the bf16-rounded h, so the result equals
+ *   moe_gmm into h followed by moe_swiglu on its halves, bit for bit.
+ *   h (may be NULL: not written) keeps the pre-activation values the
+ *   backward needs; row stride ld_h >= 2F.  act has row stride ld_act >= F.
+ *   Rows in [sum(group_sizes), M_out) of h and act are zero-filled.
+ *   valid_rows and bias as in moe_gmm (bias [G, 2F]).  bf16 only; F a
+ *   multiple of 128; Kdim, ld_* and strides multiples of 8; 16-byte aligned
+ *   pointers; G <= 1024.  No partial sums (chunked up-projections use
+ *   moe_gmm, then moe_swiglu).
+ */
+int moe_gmm_swiglu(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
+                   int64_t rhs_group_stride, const int32_t* group_sizes, const int32_t* valid_rows,
+                   int G, int64_t Kdim, int64_t F, int in_dtype, const void* bias, void* h,
+                   int64_t ld_h, void* act, int64_t ld_act, int64_t M_out, int32_t* err,
+                   void* stream);
+
 /* moe_tgmm: transposed grouped GEMM [MT-Chunk: tgmm, output
  * (num_local_groups, in_size, out_size), zero-initialised empty groups].
  *   out[g] (+)= lhs[rows of g, :Kdim]^T . rhs[rows of g, :N]   -> [Kdim, N]

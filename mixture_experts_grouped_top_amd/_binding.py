@@ -22,7 +22,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
 MOE_FP8_E4M3, MOE_FP8_E5M2 = 0, 1
-ABI_VERSION = 7   # moe_abi_version() of the library these signatures describe
+ABI_VERSION = 8   # moe_abi_version() of the library these signatures describe
 
 # Entry points (name -> (restype, argtypes)); must match include/moe.h.
 _P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -42,6 +42,8 @@ SIGNATURES = {
     "moe_permute_bwd": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _I, _P]),
     "moe_gmm": (_I, [_P, _L, _L, _P, _L, _L, _I, _P, _P, _I, _L, _L, _I, _P, _P, _L, _L, _I, _I,
                      _P, _P]),
+    "moe_gmm_swiglu": (_I, [_P, _L, _L, _P, _L, _L, _P, _P, _I, _L, _L, _I, _P, _P, _L, _P, _L, _L,
+                            _P, _P]),
     "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
     "moe_group_sum_workspace": (_S, [_L, _I, _L]),
     "moe_group_sum": (_I, [_P, _L, _I, _P, _P, _I, _L, _L, _P, _I, _I, _P, _S, _P, _P]),
@@ -320,6 +322,46 @@ def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: 
                           _ptr(bias), _ptr(out), M_out, ld_out, _dtype_code(out), int(bool(accumulate)),
                           _ptr(err), _stream(stream)), "moe_gmm")
     return out
+
+
+def moe_gmm_swiglu(lhs, wi, group_sizes, act=None, h=None, rows_out: Optional[int] = None,
+                   bias=None, valid_rows=None, write_h: bool = True, err=None, stream=None):
+    """Fused up-projection with SwiGLU: h[rows of g] = lhs[rows of g] . wi[g]
+    (+ bias[g]) with wi [G, K, 2F] = [wi_0 | wi_1] (3-D view, unit last
+    stride), and act = silu(h[:, :F]) * h[:, F:] from the bf16-rounded h.
+    Returns (h, act); h is allocated only when write_h and h is None."""
+    M_lhs, Kd = lhs.shape
+    ld_lhs = _rowmajor(lhs, "lhs")
+    if wi.dim() != 3 or wi.stride(2) != 1:
+        raise MoeError("wi must be a 3-D view with unit last stride")
+    G, K2, F2 = wi.shape
+    if K2 != Kd:
+        raise MoeError("contracting dimensions differ")
+    if F2 % 2:
+        raise MoeError("wi must have 2F columns")
+    F = F2 // 2
+    if group_sizes.numel() != G:
+        raise MoeError("group_sizes must have one entry per rhs group")
+    if lhs.dtype != wi.dtype:
+        raise MoeError("lhs and wi dtypes differ")
+    if bias is not None:
+        _contig(bias, "bias")
+        if tuple(bias.shape) != (G, F2) or bias.dtype != lhs.dtype:
+            raise MoeError("bias must be [G, 2F] in the dtype of lhs")
+    M_out = M_lhs if rows_out is None else rows_out
+    if act is None:
+        act = torch.empty((M_out, F), dtype=lhs.dtype, device=lhs.device)
+    if h is None and write_h:
+        h = torch.empty((M_out, F2), dtype=lhs.dtype, device=lhs.device)
+    if act.shape[0] != M_out or (h is not None and h.shape[0] != M_out):
+        raise MoeError("h and act must have rows_out rows")
+    ld_act = _rowmajor(act, "act")
+    ld_h = _rowmajor(h, "h") if h is not None else 0
+    _check(load().moe_gmm_swiglu(_ptr(lhs), M_lhs, ld_lhs, _ptr(wi), wi.stride(1), wi.stride(0),
+                                 _ptr(group_sizes), _ptr(valid_rows), G, Kd, F, _dtype_code(lhs),
+                                 _ptr(bias), _ptr(h), ld_h, _ptr(act), ld_act, M_out, _ptr(err),
+                                 _stream(stream)), "moe_gmm_swiglu")
+    return h, act
 
 
 def moe_tgmm(lhs, rhs, group_sizes, out=None, out_dtype=None, accumulate: bool = False, err=None,

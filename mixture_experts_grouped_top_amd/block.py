@@ -352,8 +352,9 @@ class MoEPlan:
             with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
                 B.moe_gmm(self.x_sorted, wi_1, gs, valid_rows=self.vrows, out=self.h1, err=self.err, stream=stream,
                           bias=mb.get("wi_1"))
-        with self._rec("swiglu", nbytes=nb.get("swiglu", 0)):
-            B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
+        if not self.swiglu_epilogue:   # else the up-projection's epilogue wrote act
+            with self._rec("swiglu", nbytes=nb.get("swiglu", 0)):
+                B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
         with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
             B.moe_gmm(self.act, wo, gs, valid_rows=self.vact, out=self.y_sorted, err=self.err, stream=stream,
                       bias=mb.get("wo"))
@@ -361,6 +362,13 @@ class MoEPlan:
             B.moe_combine(self.y_sorted, self.idx["row_of_slot"], self.w, y=self.y,
                           stream=stream)
         return self.y
+
+    @property
+    def swiglu_epilogue(self) -> bool:
+        """The fused up-projection computes act in its epilogue (one launch,
+        bf16, d_ff a multiple of 128, no contraction chunks)."""
+        s = self.s
+        return s.fused_wi and s.n_chunks == 1 and s.dtype == torch.bfloat16 and s.F % 128 == 0
 
     def _up_fused(self, wi, gs, R, stream, b_wi=None):
         s = self.s
@@ -371,6 +379,11 @@ class MoEPlan:
                     B.moe_gmm(self.x_sorted[:, i * c:(i + 1) * c], wi[:, i * c:(i + 1) * c, :],
                               gs, valid_rows=self.vrows, out=self.h, accumulate=i > 0, err=self.err, stream=stream,
                               bias=b_wi if i == s.n_chunks - 1 else None)
+        elif self.swiglu_epilogue:
+            # one launch: h (kept for the backward) and act = SwiGLU(h) from its epilogue
+            with self._rec("gmm_nn", 4.0 * R * s.D * s.F):
+                B.moe_gmm_swiglu(self.x_sorted, wi, gs, act=self.act, h=self.h, valid_rows=self.vrows,
+                                 bias=b_wi, err=self.err, stream=stream)
         else:
             with self._rec("gmm_nn", 4.0 * R * s.D * s.F):
                 B.moe_gmm(self.x_sorted, wi, gs, valid_rows=self.vrows, out=self.h, err=self.err, stream=stream,

@@ -30,6 +30,13 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(pack_bf16x2(f, 0.f));
 }
 
+// SwiGLU of one element, float32: silu(g) * u with silu(g) = g / (1 + e^-g).
+// One definition for the SwiGLU pass and the fused up-projection epilogue,
+// so that both give the same bits.
+__device__ __forceinline__ float swiglu_f32(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
 // Wave 0 scans the group sizes: row_base[g] (rows clipped to max_rows) and,
 // if tile_base != nullptr, tile_base[g] = tiles of groups < g, where a group
 // of n rows owns ceil(n / BM) * ntn tiles.

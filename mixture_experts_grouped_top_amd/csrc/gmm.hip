@@ -179,12 +179,14 @@ struct Operand {
   const bf16_t* base;
   int64_t ld;
   int xv;                 // valid x extent (>= 1)
+  int64_t split;          // col tile: elements added to the columns of its second half
   uint32_t voff[NJ];      // byte offsets of this lane's DMA chunks
 
-  __device__ __forceinline__ void setup(const bf16_t* b, int64_t ld_, int xv_) {
+  __device__ __forceinline__ void setup(const bf16_t* b, int64_t ld_, int xv_, int64_t split_ = 0) {
     base = b;
     ld = ld_;
     xv = xv_;
+    split = split_;
     const int tid = opaque_tid();
     const int lane = tid & 63, w = tid >> 6;
 #pragma unroll
@@ -200,7 +202,7 @@ struct Operand {
         int c = ((byte % (BX * 2)) >> 4) ^ col_swz(k);
         const int cmax = (xv - 1) >> 3;
         if (c > cmax) c = cmax;
-        voff[j] = static_cast<uint32_t>((k * ld + c * 8) * 2);
+        voff[j] = static_cast<uint32_t>((k * ld + c * 8 + (c >= BX / 16 ? split : 0)) * 2);
       }
     }
   }
@@ -234,7 +236,7 @@ struct Operand {
       } else {
         const int k = q / (BX / 8), c = q % (BX / 8);
         ok = k < kv && c * 8 < xv;
-        p = b + k * ld + c * 8;
+        p = b + k * ld + c * 8 + (c >= BX / 16 ? split : 0);
       }
       r[i] = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
     }
@@ -469,6 +471,8 @@ struct MfmaArgs {
   int32_t* err;
   const int32_t* valid = nullptr;   // tgmm: leading rows of each group that may be non-zero
   const bf16_t* bias = nullptr;      // gmm: per-group bias rows [G, N], added to the output
+  bf16_t* act = nullptr;             // gmm with the SwiGLU epilogue: act [M, F]
+  int64_t ld_act = 0;
 };
 
 // MFMAs of one substep (q = 0 .. NM-1) with NO other operations between
@@ -853,6 +857,90 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
   __syncthreads();   // the stages are refilled by the next tile
 }
 
+// Epilogue of the fused up-projection with SwiGLU: tile columns [0, TN/2)
+// are gate columns, [TN/2, TN) the up columns of the same d_ff range, so
+// waves 2p and 2p + 1 hold the two halves of the same rows.  Per 32-row
+// slab all four waves stage their float32 block in LDS; each wave writes its
+// own half to h (h0: gate rows, h1: up rows; bias added, rows >= rz zero)
+// and the pair computes act = silu(g) * u on the bf16-rounded h values (as
+// the SwiGLU pass over h does), each wave half of the slab's chunks.
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile_swiglu(const Acc<TM, TN>& acc, char* lds, bf16_t* h0,
+                                                  bf16_t* h1, int64_t ld_h, bf16_t* act,
+                                                  int64_t ld_act, int rv, const bf16_t* b0,
+                                                  const bf16_t* b1, int rz) {
+  constexpr int WC = TN / 2;
+  constexpr int SROW = WC * 4 + 16;
+  constexpr int CPR = WC / 8;                 // 8-column chunks per slab row
+  constexpr int NQ = 32 * CPR / 64;           // h chunks per lane per slab
+  constexpr int NA = NQ / 2;                  // act chunks per lane per slab
+  static_assert(4 * 32 * SROW <= Stages<TM, TN>::kBytes, "epilogue slabs fit in the stage buffers");
+  const int tid = opaque_tid();
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int up = w & 1;
+  char* slab = lds + w * 32 * SROW;
+  const char* sg = lds + (w & ~1) * 32 * SROW;   // the pair's gate slab
+  const char* su = sg + 32 * SROW;               // and its up slab
+  const int wr = (w >> 1) * (TM / 2);
+  bf16_t* hw = up ? h1 : h0;
+  const bf16_t* bw = up ? b1 : b0;
+  auto value = [&](const char* sl, int row, int c8, int grow, const bf16_t* bias, float v[8]) {
+    const float4 lo = *reinterpret_cast<const float4*>(sl + row * SROW + c8 * 32);
+    const float4 hi = *reinterpret_cast<const float4*>(sl + row * SROW + c8 * 32 + 16);
+    v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = grow < rz ? v[e] : 0.f;
+    if (bias) {
+      float b[8];
+      load8(bias + 8 * c8, b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += b[e];
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < Acc<TM, TN>::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < Acc<TM, TN>::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = 32 * j + (lane & 31);
+        *reinterpret_cast<float*>(slab + row * SROW + col * 4) = acc.v[i][j][r];
+      }
+    __syncthreads();   // both halves of these rows are staged
+    if (hw) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int chunk = lane + 64 * q;
+        const int row = chunk / CPR, c8 = chunk % CPR;
+        const int grow = wr + 32 * i + row;
+        if (grow < rv) {
+          float v[8];
+          value(slab, row, c8, grow, bw, v);
+          store8_nt(hw + static_cast<int64_t>(grow) * ld_h + 8 * c8, v);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      const int chunk = up * (32 * CPR / 2) + lane + 64 * q;
+      const int row = chunk / CPR, c8 = chunk % CPR;
+      const int grow = wr + 32 * i + row;
+      if (grow < rv) {
+        float g[8], u[8], o[8];
+        value(sg, row, c8, grow, b0, g);
+        value(su, row, c8, grow, b1, u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o[e] = swiglu_f32(bf16_to_f32(f32_to_bf16(g[e])), bf16_to_f32(f32_to_bf16(u[e])));
+        store8_nt(act + static_cast<int64_t>(grow) * ld_act + 8 * c8, o);
+      }
+    }
+    __syncthreads();   // the slabs are rewritten (and, after the last, refilled by the next tile)
+  }
+}
+
 // Largest group count a gmm tile variant supports: the 128-row variant
 // keeps its LDS (three stages + two group prefixes) within half a CU.
 constexpr int kMaxGShort = 1000;
@@ -861,8 +949,10 @@ struct MaxG {
   static constexpr int value = TM <= 128 ? kMaxGShort : kMaxG;
 };
 
-template <bool B_COLK, int TM, int TN, typename TO, bool PAIR>
+template <bool B_COLK, int TM, int TN, typename TO, bool PAIR, bool SWI = false>
 __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArgs a) {
+  static_assert(!SWI || (B_COLK && TN == 256 && std::is_same<TO, bf16_t>::value),
+                "the SwiGLU epilogue takes a [K, 2F] rhs and bf16 outputs");
   static_assert(!PAIR || Stages<TM, TN>::NS == 4, "pair loading uses the four-step ring");
   using OA = std::conditional_t<PAIR, PairRow<TM>, Operand<false, TM>>;
   using OB = std::conditional_t<PAIR && !B_COLK, PairRow<TN>, Operand<B_COLK, TN>>;
@@ -904,13 +994,32 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
     acc.set_live_rows(vr);
     A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, max(vr, 1));
     const bf16_t* bg = a.rhs + g * a.rhs_gs;
-    B.setup(B_COLK ? bg + col0 : bg + col0 * a.ld_rhs, a.ld_rhs, cv);
-    if constexpr (PAIR) contract2(smem, A, B, a.Kdim, acc, fa, fb);
-    else contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
-    store_tile(acc, smem, out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate,
-               a.bias ? a.bias + g * a.N + col0 : nullptr, 1.f, vr);
+    if constexpr (SWI) {
+      // gate columns F0 .. F0 + TN/2 of wi and the up columns F + F0 ..
+      const int64_t F = a.N / 2, f0 = static_cast<int64_t>(nt) * (TN / 2);
+      B.setup(bg + f0, a.ld_rhs, TN, F - TN / 2);
+      if constexpr (PAIR) contract2(smem, A, B, a.Kdim, acc, fa, fb);
+      else contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
+      bf16_t* h = static_cast<bf16_t*>(a.out);
+      const bf16_t* bb = a.bias ? a.bias + g * a.N : nullptr;
+      store_tile_swiglu(acc, smem, h ? h + row0 * a.ld_out + f0 : nullptr,
+                        h ? h + row0 * a.ld_out + F + f0 : nullptr, a.ld_out,
+                        a.act + row0 * a.ld_act + f0, a.ld_act, rv, bb ? bb + f0 : nullptr,
+                        bb ? bb + F + f0 : nullptr, vr);
+    } else {
+      B.setup(B_COLK ? bg + col0 : bg + col0 * a.ld_rhs, a.ld_rhs, cv);
+      if constexpr (PAIR) contract2(smem, A, B, a.Kdim, acc, fa, fb);
+      else contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
+      store_tile(acc, smem, out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate,
+                 a.bias ? a.bias + g * a.N + col0 : nullptr, 1.f, vr);
+    }
   }
-  if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
+  if constexpr (SWI) {
+    if (out) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
+    zero_rows(a.act, a.ld_act, a.N / 2, row_base[a.G], a.M);
+  } else {
+    if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
+  }
 }
 
 template <int TM, int TN, typename TO>
@@ -1425,6 +1534,47 @@ MOE_API int moe_gmm(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* 
                          ld_rhs, rhs_group_stride, group_sizes, G, Kdim, N, of, oh, M_out, ld_out,
                          accumulate, err, static_cast<const float*>(bias));
   }
+  return launch_status();
+}
+
+MOE_API int moe_gmm_swiglu(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs,
+                           int64_t ld_rhs, int64_t rhs_group_stride, const int32_t* group_sizes,
+                           const int32_t* valid_rows, int G, int64_t Kdim, int64_t F, int in_dtype,
+                           const void* bias, void* h, int64_t ld_h, void* act, int64_t ld_act,
+                           int64_t M_out, int32_t* err, void* stream) {
+  if (G < 1 || G > kMaxG || M_lhs < 0 || M_out < 0 || M_out > M_lhs || Kdim < 0 || F < 0)
+    return MOE_ERR_ARG;
+  if (M_out > INT32_MAX) return MOE_ERR_ARG;
+  if (in_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (F % 128 || !mult8(Kdim) || !mult8(ld_lhs) || !mult8(ld_rhs) || !mult8(rhs_group_stride) ||
+      !mult8(ld_act) || (h && !mult8(ld_h)))
+    return MOE_ERR_ARG;
+  if (ld_lhs < Kdim || ld_rhs < 2 * F || ld_act < F || (h && ld_h < 2 * F)) return MOE_ERR_ARG;
+  if (ld_lhs > kMaxLd || ld_rhs > kMaxLd) return MOE_ERR_ARG;
+  if (M_out == 0 || F == 0) return MOE_OK;
+  if (!lhs || !rhs || !group_sizes || !act || !aligned16(lhs) || !aligned16(rhs) ||
+      !aligned16(act) || (h && !aligned16(h)) || (bias && !aligned16(bias)))
+    return MOE_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t N = 2 * F;
+  MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
+             rhs_group_stride, group_sizes, G, M_out, Kdim, N, h, ld_h, 0, 0, err, valid_rows};
+  a.bias = static_cast<const bf16_t*>(bias);
+  a.act = static_cast<bf16_t*>(act);
+  a.ld_act = ld_act;
+  // tiles as moe_gmm's: 128-row tiles for small groups, else 256 x 256
+  const bool short_m = G <= kMaxGShort && M_out < 512 * static_cast<int64_t>(G);
+  const int TMv = short_m ? 128 : 256;
+  const int64_t upper = ((M_out + TMv - 1) / TMv + G) * (N / 256);
+  const unsigned grid = persistent_grid(upper, short_m ? 2 : 1);
+  const int64_t nsteps = Kdim / TK;
+  const bool pair = !short_m && nsteps >= 2 && nsteps % 2 == 0;
+  if (short_m)
+    hipLaunchKernelGGL((gmm_mfma_kernel<true, 128, 256, bf16_t, false, true>), dim3(grid), dim3(NT), 0, st, a);
+  else if (pair)
+    hipLaunchKernelGGL((gmm_mfma_kernel<true, 256, 256, bf16_t, true, true>), dim3(grid), dim3(NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((gmm_mfma_kernel<true, 256, 256, bf16_t, false, true>), dim3(grid), dim3(NT), 0, st, a);
   return launch_status();
 }
 

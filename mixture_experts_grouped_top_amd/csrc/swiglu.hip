@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const TH* __restrict__ h0,
       ra[u].get(a);
       rb[u].get(b);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) o[q] = a[q] / (1.0f + expf(-a[q])) * b[q];
+      for (int q = 0; q < 8; ++q) o[q] = swiglu_f32(a[q], b[q]);
       store8_nt(act + i * 8, o);
     }
   }

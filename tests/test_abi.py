@@ -41,7 +41,7 @@ def test_header_declares_the_abi():
                  "moe_abi_version", "moe_aux_loss_workspace", "moe_aux_loss",
                  "moe_aux_loss_bwd", "moe_group_sum_workspace", "moe_group_sum",
                  "moe_fp8_scale_workspace", "moe_fp8_amax_scale", "moe_fp8_padded_rows",
-                 "moe_fp8_quantize", "moe_gmm_fp8", "moe_tgmm_fp8"]:
+                 "moe_fp8_quantize", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gmm_swiglu"]:
         assert name in d, name
 
 
@@ -117,6 +117,16 @@ def test_argument_checks_return_before_launch(lib):
     assert gmm(ld=32) == -1
     assert gmm(G=5000) == -1
     assert gmm(bias=ctypes.c_void_p(18)) == -1      # misaligned bias
+    # gmm_swiglu: F not a multiple of 128, float32 inputs, weight row stride below 2F,
+    # act row stride below F, misaligned act
+    def swi(F=128, it=1, ldr=256, lda=128, act=P):
+        return lib.moe_gmm_swiglu(P, 64, 64, P, ldr, 64 * ldr, P, None, 2, 64, F, it, None, None,
+                                  0, act, lda, 64, None, None)
+    assert swi(F=64, ldr=128, lda=64) == -1
+    assert swi(it=0) == -2
+    assert swi(ldr=248) == -1
+    assert swi(lda=120) == -1
+    assert swi(act=ctypes.c_void_p(24)) == -1
     # group sum: N not a multiple of 8, G too large, missing or short workspace, bad dtype
     W = ctypes.c_void_p(256)
     assert lib.moe_group_sum(P, 12, 1, P, None, 2, 10, 12, P, 0, 0, W, 1 << 20, None, None) == -1

@@ -378,6 +378,62 @@ def test_gmm_valid_rows(gpu_lib, case):
     assert_close(host(out), want, TOL_F32, "gmm valid_rows")
 
 
+SWI_CASES = [
+    # group sizes, valid rows, K, F, bias, write h, extra output rows
+    ([300, 0, 257, 128, 1000], None, 264, 256, False, True, 7),      # 128-row tiles
+    ([300, 0, 257, 128, 1000], [299, 0, 1, 0, 613], 264, 384, True, True, 0),
+    ([1024, 1024], None, 512, 256, True, True, 5),                     # 256-row pair tiles
+    ([1024, 1024], [1000, 3], 544, 128, False, False, 0),              # 256-row tiles, odd steps
+    ([0, 0, 128], None, 40, 128, True, True, 9),                       # one full step and a tail
+]
+
+
+@pytest.mark.parametrize("case", SWI_CASES, ids=[str(i) for i in range(len(SWI_CASES))])
+def test_gmm_swiglu(gpu_lib, case):
+    """The fused up-projection with the SwiGLU epilogue: h and act equal
+    moe_gmm into h followed by moe_swiglu on its halves bit for bit, and the
+    oracle (product, bias, SwiGLU of the bf16-rounded h) within tolerance;
+    rows past the groups are zero."""
+    gs, valid, K, F, with_bias, write_h, extra = case
+    gs = np.array(gs, dtype=np.int32)
+    G = len(gs)
+    S = int(gs.sum())
+    M = S + extra
+    g = np.random.default_rng(K + F + G)
+    lhs = _draw(g, (M, K), "bf16")
+    wi = _draw(g, (G, K, 2 * F), "bf16")
+    bias = _draw(g, (G, 2 * F), "bf16") if with_bias else None
+    vr = None
+    lhs0 = lhs.copy()
+    if valid is not None:
+        vr = np.array(valid, dtype=np.int32)
+        off = np.concatenate([[0], np.cumsum(gs)])
+        for e in range(G):
+            lhs0[off[e] + vr[e]:off[e + 1]] = 0
+    x_d, w_d = dev(lhs, torch.bfloat16), dev(wi, torch.bfloat16)
+    b_d = dev(bias, torch.bfloat16) if with_bias else None
+    v_d = dev_i32(vr) if vr is not None else None
+    h = poison(torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda")) if write_h else None
+    act = poison(torch.empty((M, F), dtype=torch.bfloat16, device="cuda"))
+    gpu_lib.moe_gmm_swiglu(x_d, w_d, dev_i32(gs), act=act, h=h, bias=b_d, valid_rows=v_d)
+    # the two-call path on the same inputs
+    h2 = gpu_lib.moe_gmm(x_d, w_d, dev_i32(gs), bias=b_d, valid_rows=v_d)
+    a2 = gpu_lib.moe_swiglu(h2[:, :F], h2[:, F:])
+    if write_h:
+        assert torch.equal(h.view(torch.int16), h2.view(torch.int16))
+    assert torch.equal(act.view(torch.int16), a2.view(torch.int16))
+    want_h = oracle.gmm(lhs0, wi, gs, bias=bias, rows_out=M)
+    hb = ms.bf16_round(want_h)
+    want_act = oracle.swiglu(hb[:, :F], hb[:, F:])
+    got = host(act)
+    assert_close(got[:S], want_act[:S], TOL_BF16, "gmm_swiglu act")
+    assert (got[S:] == 0).all()
+    if write_h:
+        gh = host(h)
+        assert_close(gh[:S], want_h[:S], TOL_BF16, "gmm_swiglu h")
+        assert (gh[S:] == 0).all()
+
+
 @pytest.mark.parametrize("it", ["bf16", "f32"])
 def test_tgmm_valid_rows(gpu_lib, it):
     """With valid_rows the contraction stops after each group's first
