@@ -39,9 +39,11 @@ __device__ __forceinline__ float swiglu_f32(float g, float u) {
 
 // Wave 0 scans the group sizes: row_base[g] (rows clipped to max_rows) and,
 // if tile_base != nullptr, tile_base[g] = tiles of groups < g, where a group
-// of n rows owns ceil(n / BM) * ntn tiles.
+// of n rows owns ceil(n / BM) * ntn tiles when cls_lo <= n <= cls_hi, else
+// none.
 __device__ inline void scan_groups(const int32_t* __restrict__ gsz, int G, int64_t max_rows, int BMv,
-                            int ntn, int* row_base, int* tile_base, int32_t* err) {
+                            int ntn, int* row_base, int* tile_base, int32_t* err,
+                            int cls_lo = 0, int cls_hi = 0x7fffffff) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
   int64_t rows_run = 0;
@@ -63,7 +65,8 @@ __device__ inline void scan_groups(const int32_t* __restrict__ gsz, int G, int64
     if (start > max_rows) start = max_rows;
     if (end > max_rows) end = max_rows;
     const int neff = static_cast<int>(end - start);
-    int t = tile_base ? ((neff + BMv - 1) / BMv) * ntn : 0;
+    // only groups of cls_lo .. cls_hi rows own tiles (a launch for one size class)
+    int t = tile_base && neff >= cls_lo && neff <= cls_hi ? ((neff + BMv - 1) / BMv) * ntn : 0;
     int tincl = t;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {

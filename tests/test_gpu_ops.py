@@ -269,6 +269,9 @@ GS = {
     "max_groups": [(i * 5) % 4 for i in range(1024)],
     # skewed short contractions over many tiles per workgroup
     "skewed": [(i * 37) % 300 for i in range(64)],
+    # mostly small groups (128-row tiles) with some above 384 rows (256-row
+    # tiles in a launch of their own)
+    "mixed": [30, 700, 0, 385, 384, 1100, 5, 0, 129, 40],
 }
 
 GMM_CASES = [
@@ -292,6 +295,9 @@ GMM_CASES = [
     ("one_group", 200, 264, 0, 0, True, "bf16", "bf16", True),
     ("one_group", 1024, 264, 3, 0, False, "bf16", "bf16", False),  # long pipelined run
     ("one_group", 1024, 136, 3, 0, True, "bf16", "f32", True),
+    ("mixed", 264, 520, 3, 0, False, "bf16", "bf16", False),
+    ("mixed", 256, 264, 0, 0, True, "bf16", "f32", True),
+    ("mixed", 200, 136, 0, 0, False, "bf16", "f32", True),
     ("two_big", 264, 520, 0, 0, True, "bf16", "bf16", False),
     ("two_big", 136, 520, 5, 0, False, "bf16", "f32", True),
     ("one_group", 96, 264, 0, 0, True, "bf16", "f32", True),
@@ -385,6 +391,7 @@ SWI_CASES = [
     ([1024, 1024], None, 512, 256, True, True, 5),                     # 256-row pair tiles
     ([1024, 1024], [1000, 3], 544, 128, False, False, 0),              # 256-row tiles, odd steps
     ([0, 0, 128], None, 40, 128, True, True, 9),                       # one full step and a tail
+    ([30, 700, 0, 385, 384, 1100, 5, 0, 129, 40], None, 264, 128, True, True, 3),   # both size classes
 ]
 
 
