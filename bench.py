@@ -227,13 +227,13 @@ def traffic_summary(bench_fetch, bench_write, copy_fetch, copy_write):
            "calibration": {"copy_bytes_each_way": known, "fetch_scale": round(f_fetch, 4),
                            "write_scale": round(f_write, 4), "kernel": COPY_KERNEL},
            "commands": [
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_bench_fetch -o p "
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_bench_fetch -o p "
                "-- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-kernel-events",
-               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_bench_write -o p "
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_bench_write -o p "
                "-- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-kernel-events",
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o p "
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_copy_fetch -o p "
                "-- python bench.py --copy-calibration",
-               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o p "
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_copy_write -o p "
                "-- python bench.py --copy-calibration"],
            "kernels": {}}
     for kind, name in KERNEL_NAME.items():
@@ -288,7 +288,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
