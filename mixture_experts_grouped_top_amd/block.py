@@ -142,8 +142,22 @@ class MoEPlan:
                 dtype=torch.uint8, device=dev)
         if s.fp8:
             self._init_fp8(dev)
-        # router weight gradient kept in float32 (a [D, E] reduction over all tokens)
+        # router weight gradient kept in float32 (a [D, E] reduction over all tokens).
+        # With few output tiles (E is narrow) the token rows are split into
+        # n_split blocks, each a tgmm group with its own float32 partial, and the
+        # partials are added in block order (group sum), so that the reduction
+        # spreads over the chip instead of a few workgroups.
         self.d_Wg = torch.empty((1, s.D, s.E), **f32) if router else None
+        self.n_split = max(1, min(16, s.T // 512)) if router else 1
+        if self.n_split > 1:
+            per = s.T // self.n_split
+            sizes = [per] * (self.n_split - 1) + [s.T - per * (self.n_split - 1)]
+            self.gs_split = torch.tensor(sizes, **i32)
+            self.gs_one = torch.tensor([self.n_split], **i32)
+            self.d_Wg_part = torch.empty((self.n_split, s.D, s.E), **f32)
+            self.split_ws = torch.empty(
+                max(B.moe_group_sum_workspace(self.n_split, 1, s.D * s.E), 256),
+                dtype=torch.uint8, device=dev)
         self.recorder = None   # optional callable(kind, flops, bytes) -> context manager
 
     def _init_fp8(self, dev):
@@ -476,7 +490,14 @@ class MoEPlan:
             B.moe_aux_loss_bwd(self.logits, self.aux_counts, s.K, s.aux_alpha, s.score,
                                d_logits=self.d_logits, accumulate=True, stream=stream)
         if Wg is not None and self.router:
-            B.moe_tgmm(x, self.d_logits, self.gs_T, out=self.d_Wg, err=self.err, stream=stream)
+            if self.n_split > 1:
+                B.moe_tgmm(x, self.d_logits, self.gs_split, out=self.d_Wg_part, err=self.err,
+                           stream=stream)
+                B.moe_group_sum(self.d_Wg_part.view(self.n_split, -1), self.gs_one,
+                                out=self.d_Wg.view(1, -1), workspace=self.split_ws, err=self.err,
+                                stream=stream)
+            else:
+                B.moe_tgmm(x, self.d_logits, self.gs_T, out=self.d_Wg, err=self.err, stream=stream)
             B.moe_gmm(self.d_logits, Wg.unsqueeze(0), self.gs_T, trans_rhs=True, out=self.dx,
                       accumulate=True, err=self.err, stream=stream)
         return self.dx
