@@ -239,6 +239,27 @@ int moe_gmm_swiglu(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* r
                    int64_t ld_h, void* act, int64_t ld_act, int64_t M_out, int32_t* err,
                    void* stream);
 
+/* moe_gmm_swiglu_bwd: the d_act GEMM of the backward with the SwiGLU
+ * backward in its epilogue (the gradient counterpart of moe_gmm_swiglu).
+ * For each group (rows as moe_gmm's), with wo[g] = rhs + g*rhs_group_stride
+ * viewed as [F, Kdim] (row stride ld_rhs) and used transposed:
+ *     d_act = bf16(lhs[o_g + i, :Kdim] . wo[g]^T)                    [rows, F]
+ *     d_h0 = d_act * h1 * s * (1 + h0 * (1 - s)),  d_h1 = d_act * h0 * s,
+ *   s = sigmoid(h0), from the forward's h0, h1 (row stride ld_h), written to
+ *   d_h0, d_h1 (row stride ld_dh; both may be halves of one [rows, 2F]
+ *   buffer).  Equal, bit for bit, to moe_gmm(trans_rhs) into a bf16 d_act
+ *   followed by moe_swiglu_bwd.  Rows in [sum(group_sizes), M_out) of d_h0
+ *   and d_h1 are zero-filled.  valid_rows as in moe_gmm.  bf16 only (lhs,
+ *   rhs, h0, h1, d_h0, d_h1);
+ *   F > 128 and Kdim > 32 (smaller shapes use the two calls); F, Kdim, ld_*
+ *   and strides multiples of 8; 16-byte aligned pointers; G <= 1024.
+ */
+int moe_gmm_swiglu_bwd(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs,
+                       int64_t ld_rhs, int64_t rhs_group_stride, const int32_t* group_sizes,
+                       const int32_t* valid_rows, int G, int64_t Kdim, int64_t F, int in_dtype,
+                       const void* h0, const void* h1, int64_t ld_h, void* d_h0, void* d_h1,
+                       int64_t ld_dh, int64_t M_out, int32_t* err, void* stream);
+
 /* moe_tgmm: transposed grouped GEMM [MT-Chunk: tgmm, output
  * (num_local_groups, in_size, out_size), zero-initialised empty groups].
  *   out[g] (+)= lhs[rows of g, :Kdim]^T . rhs[rows of g, :N]   -> [Kdim, N]

@@ -11,6 +11,7 @@ from ._binding import (MOE_BF16, MOE_BIAS_LOGIT, MOE_BIAS_SELECT, MOE_DERR_EXPER
                        MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS, MOE_F32, MOE_SIGMOID, MOE_SOFTMAX,
                        SIGNATURES, MoeError, load, moe_aux_loss, moe_aux_loss_bwd,
                        moe_aux_loss_workspace, moe_combine, moe_combine_bwd, moe_gmm, moe_gmm_swiglu,
+                       moe_gmm_swiglu_bwd,
                        moe_group_sum, moe_group_sum_workspace, ABI_VERSION,
                        MOE_FP8_E4M3, MOE_FP8_E5M2, moe_fp8_scale_workspace, moe_fp8_amax_scale,
                        moe_fp8_padded_rows, moe_fp8_quantize, moe_gmm_fp8, moe_tgmm_fp8,
@@ -23,7 +24,7 @@ __all__ = [
     "load", "MoeError", "LIB_PATH", "SIGNATURES", "moe_route", "moe_route_bwd", "moe_rows_bound",
     "moe_aux_loss_workspace", "moe_aux_loss", "moe_aux_loss_bwd", "MOE_BIAS_LOGIT",
     "MOE_BIAS_SELECT",
-    "moe_permute_workspace", "moe_permute", "moe_permute_bwd", "moe_gmm", "moe_gmm_swiglu", "moe_tgmm",
+    "moe_permute_workspace", "moe_permute", "moe_permute_bwd", "moe_gmm", "moe_gmm_swiglu", "moe_gmm_swiglu_bwd", "moe_tgmm",
     "moe_group_sum_workspace", "moe_group_sum", "ABI_VERSION", "MOE_FP8_E4M3", "MOE_FP8_E5M2",
     "moe_fp8_scale_workspace", "moe_fp8_amax_scale", "moe_fp8_padded_rows", "moe_fp8_quantize",
     "moe_gmm_fp8", "moe_tgmm_fp8",

@@ -22,7 +22,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
 MOE_FP8_E4M3, MOE_FP8_E5M2 = 0, 1
-ABI_VERSION = 8   # moe_abi_version() of the library these signatures describe
+ABI_VERSION = 9   # moe_abi_version() of the library these signatures describe
 
 # Entry points (name -> (restype, argtypes)); must match include/moe.h.
 _P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -44,6 +44,8 @@ SIGNATURES = {
                      _P, _P]),
     "moe_gmm_swiglu": (_I, [_P, _L, _L, _P, _L, _L, _P, _P, _I, _L, _L, _I, _P, _P, _L, _P, _L, _L,
                             _P, _P]),
+    "moe_gmm_swiglu_bwd": (_I, [_P, _L, _L, _P, _L, _L, _P, _P, _I, _L, _L, _I, _P, _P, _L, _P, _P,
+                                _L, _L, _P, _P]),
     "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
     "moe_group_sum_workspace": (_S, [_L, _I, _L]),
     "moe_group_sum": (_I, [_P, _L, _I, _P, _P, _I, _L, _L, _P, _I, _I, _P, _S, _P, _P]),
@@ -355,6 +357,8 @@ def moe_gmm_swiglu(lhs, wi, group_sizes, act=None, h=None, rows_out: Optional[in
         h = torch.empty((M_out, F2), dtype=lhs.dtype, device=lhs.device)
     if act.shape[0] != M_out or (h is not None and h.shape[0] != M_out):
         raise MoeError("h and act must have rows_out rows")
+    if act.dtype != torch.bfloat16 or (h is not None and h.dtype != torch.bfloat16):
+        raise MoeError("h and act must be bfloat16")
     ld_act = _rowmajor(act, "act")
     ld_h = _rowmajor(h, "h") if h is not None else 0
     _check(load().moe_gmm_swiglu(_ptr(lhs), M_lhs, ld_lhs, _ptr(wi), wi.stride(1), wi.stride(0),
@@ -362,6 +366,44 @@ def moe_gmm_swiglu(lhs, wi, group_sizes, act=None, h=None, rows_out: Optional[in
                                  _ptr(bias), _ptr(h), ld_h, _ptr(act), ld_act, M_out, _ptr(err),
                                  _stream(stream)), "moe_gmm_swiglu")
     return h, act
+
+
+def moe_gmm_swiglu_bwd(d_y, wo, group_sizes, h0, h1, d_h0=None, d_h1=None,
+                       rows_out: Optional[int] = None, valid_rows=None, err=None, stream=None):
+    """d_act[rows of g] = d_y[rows of g] . wo[g]^T (wo [G, F, K], 3-D view with
+    unit last stride), rounded to bf16, then the SwiGLU backward with the
+    forward's h0, h1 ([M, F] 2-D views sharing one row stride) into d_h0,
+    d_h1 ([M, F] views sharing one row stride).  Returns (d_h0, d_h1)."""
+    M_lhs, Kd = d_y.shape
+    ld_lhs = _rowmajor(d_y, "d_y")
+    if wo.dim() != 3 or wo.stride(2) != 1:
+        raise MoeError("wo must be a 3-D view with unit last stride")
+    G, F, K2 = wo.shape
+    if K2 != Kd:
+        raise MoeError("contracting dimensions differ")
+    if group_sizes.numel() != G:
+        raise MoeError("group_sizes must have one entry per rhs group")
+    if d_y.dtype != wo.dtype:
+        raise MoeError("d_y and wo dtypes differ")
+    M_out = M_lhs if rows_out is None else rows_out
+    if d_h0 is None:
+        d_h0 = torch.empty((M_out, F), dtype=d_y.dtype, device=d_y.device)
+    if d_h1 is None:
+        d_h1 = torch.empty((M_out, F), dtype=d_y.dtype, device=d_y.device)
+    for t, n in ((h0, "h0"), (h1, "h1"), (d_h0, "d_h0"), (d_h1, "d_h1")):
+        if t.dim() != 2 or t.shape[0] < M_out or t.shape[1] != F:
+            raise MoeError(f"{n} must be [rows_out, F]")
+        if t.dtype != torch.bfloat16:
+            raise MoeError(f"{n} must be bfloat16")
+    ld_h, ld_dh = _rowmajor(h0, "h0"), _rowmajor(d_h0, "d_h0")
+    if _rowmajor(h1, "h1") != ld_h or _rowmajor(d_h1, "d_h1") != ld_dh:
+        raise MoeError("h0/h1 and d_h0/d_h1 must share their row strides")
+    _check(load().moe_gmm_swiglu_bwd(_ptr(d_y), M_lhs, ld_lhs, _ptr(wo), wo.stride(1), wo.stride(0),
+                                     _ptr(group_sizes), _ptr(valid_rows), G, Kd, F,
+                                     _dtype_code(d_y), _ptr(h0), _ptr(h1), ld_h, _ptr(d_h0),
+                                     _ptr(d_h1), ld_dh, M_out, _ptr(err), _stream(stream)),
+           "moe_gmm_swiglu_bwd")
+    return d_h0, d_h1
 
 
 def moe_tgmm(lhs, rhs, group_sizes, out=None, out_dtype=None, accumulate: bool = False, err=None,

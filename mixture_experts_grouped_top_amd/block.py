@@ -378,6 +378,15 @@ class MoEPlan:
         return self.y
 
     @property
+    def swiglu_bwd_epilogue(self) -> bool:
+        """The d_act GEMM applies the SwiGLU backward in its epilogue (bf16,
+        h kept in bf16, i.e. no float32 partials of a chunked up-projection,
+        d_ff above 128, d_model above one contraction step)."""
+        s = self.s
+        return (s.dtype == torch.bfloat16 and s.n_chunks == 1 and s.F > 128 and s.D > 32
+                and s.F % 8 == 0)
+
+    @property
     def swiglu_epilogue(self) -> bool:
         """The fused up-projection computes act in its epilogue (one launch,
         bf16, d_ff a multiple of 128, no contraction chunks)."""
@@ -426,17 +435,26 @@ class MoEPlan:
         gs = self.group_sizes
         R = self.kept_rows
         nb = self._bytes() if self.recorder is not None else {}
-        with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
-            B.moe_gmm(self.d_y_sorted, wo, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_act, err=self.err,
-                      stream=stream)
+        if self.swiglu_bwd_epilogue:
+            # d_act stays in registers: its GEMM's epilogue applies the SwiGLU
+            # backward with h0, h1 and writes d_h0, d_h1
+            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+                B.moe_gmm_swiglu_bwd(self.d_y_sorted, wo, gs, self.h0, self.h1, d_h0=self.d_h0,
+                                     d_h1=self.d_h1, valid_rows=self.vrows, err=self.err,
+                                     stream=stream)
+        else:
+            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+                B.moe_gmm(self.d_y_sorted, wo, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_act, err=self.err,
+                          stream=stream)
         with self._rec("tgmm", 2.0 * R * s.D * s.F):
             # padding rows of each group (past its kept rows) are zero in
             # d_y_sorted and x_sorted: the weight gradients stop at counts
             B.moe_tgmm(self.act, self.d_y_sorted, gs, out=self.d_wo, err=self.err, stream=stream,
                        valid_rows=self.idx["counts"])
-        with self._rec("swiglu_bwd", nbytes=nb.get("swiglu_bwd", 0)):
-            B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
-                             stream=stream)
+        if not self.swiglu_bwd_epilogue:
+            with self._rec("swiglu_bwd", nbytes=nb.get("swiglu_bwd", 0)):
+                B.moe_swiglu_bwd(self.h0, self.h1, self.d_act, d_h0=self.d_h0, d_h1=self.d_h1,
+                                 stream=stream)
         if s.fused_wi:
             # d_x_sorted = [d_h0 | d_h1] . [wi_0 | wi_1]^T in one contraction
             # over 2F; d_wi = x_sorted^T [d_h0 | d_h1] in one tgmm

@@ -37,6 +37,15 @@ __device__ __forceinline__ float swiglu_f32(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
+// Gradients of SwiGLU for an upstream gradient d: d_g = d u s (1 + g (1 - s)),
+// d_u = d g s with s = sigmoid(g).  One definition for the backward pass and
+// the fused d_act epilogue.
+__device__ __forceinline__ void swiglu_bwd_f32(float g, float u, float d, float& dg, float& du) {
+  const float s = 1.0f / (1.0f + expf(-g));
+  dg = d * u * s * (1.0f + g * (1.0f - s));
+  du = d * g * s;
+}
+
 // Wave 0 scans the group sizes: row_base[g] (rows clipped to max_rows) and,
 // if tile_base != nullptr, tile_base[g] = tiles of groups < g, where a group
 // of n rows owns ceil(n / BM) * ntn tiles when cls_lo <= n <= cls_hi, else

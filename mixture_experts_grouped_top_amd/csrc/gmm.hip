@@ -474,6 +474,12 @@ struct MfmaArgs {
   bf16_t* act = nullptr;             // gmm with the SwiGLU epilogue: act [M, F]
   int64_t ld_act = 0;
   int cls_lo = 0, cls_hi = 0x7fffffff;   // gmm: only groups of cls_lo .. cls_hi rows own tiles
+  // gmm with the SwiGLU-backward epilogue: h0/h1 [M, N] (row stride ld_h) are
+  // read, out is d_h0 and dh1 d_h1 (row stride ld_out)
+  const bf16_t* h0 = nullptr;
+  const bf16_t* h1 = nullptr;
+  int64_t ld_h = 0;
+  bf16_t* dh1 = nullptr;
 };
 
 // MFMAs of one substep (q = 0 .. NM-1) with NO other operations between
@@ -943,6 +949,79 @@ __device__ __forceinline__ void store_tile_swiglu(const Acc<TM, TN>& acc, char* 
   }
 }
 
+// Epilogue of the d_act GEMM with the SwiGLU backward: the tile's value is
+// d_act (rounded to bf16, as the stored d_act the SwiGLU backward pass reads),
+// combined with the forward's h0, h1 into d_h0, d_h1.  Staged per wave as in
+// store_tile; rows >= rz have zero d_act; rows >= rv and columns >= cv are
+// not written.
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile_swiglu_bwd(const Acc<TM, TN>& acc, char* lds, bf16_t* d0,
+                                                      bf16_t* d1, int64_t ld_d, const bf16_t* h0,
+                                                      const bf16_t* h1, int64_t ld_h, int rv,
+                                                      int cv, int rz) {
+  constexpr int WC = TN / 2;
+  constexpr int SROW = WC * 4 + 16;
+  constexpr int CPR = WC / 8;
+  constexpr int NQ = 32 * CPR / 64;
+  constexpr int QB = NQ < 2 ? NQ : 2;          // chunks whose loads are in flight together
+  static_assert(4 * 32 * SROW <= Stages<TM, TN>::kBytes, "epilogue slabs fit in the stage buffers");
+  const int tid = opaque_tid();
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  char* slab = lds + w * 32 * SROW;
+  const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * WC;
+#pragma unroll
+  for (int i = 0; i < Acc<TM, TN>::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < Acc<TM, TN>::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = 32 * j + (lane & 31);
+        *reinterpret_cast<float*>(slab + row * SROW + col * 4) = acc.v[i][j][r];
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q0 = 0; q0 < NQ; q0 += QB) {
+      float ga[QB][8], ha[QB][8], hb[QB][8];
+      bool ok[QB];
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        const int chunk = lane + 64 * (q0 + u);
+        const int row = chunk / CPR, c8 = chunk % CPR;
+        const int grow = wr + 32 * i + row, gcol = wc + 8 * c8;
+        ok[u] = grow < rv && gcol < cv;
+        const float4 lo = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32);
+        const float4 hi = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
+        const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ga[u][e] = grow < rz ? bf16_to_f32(f32_to_bf16(v[e])) : 0.f;
+        const int64_t hoff = static_cast<int64_t>(ok[u] ? grow : 0) * ld_h + (ok[u] ? gcol : 0);
+        load8(h0 + hoff, ha[u]);
+        load8(h1 + hoff, hb[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        if (!ok[u]) continue;
+        const int chunk = lane + 64 * (q0 + u);
+        const int row = chunk / CPR, c8 = chunk % CPR;
+        const int64_t doff = static_cast<int64_t>(wr + 32 * i + row) * ld_d + wc + 8 * c8;
+        float o0[8], o1[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) swiglu_bwd_f32(ha[u][e], hb[u][e], ga[u][e], o0[e], o1[e]);
+        store8_nt(d0 + doff, o0);
+        store8_nt(d1 + doff, o1);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  __syncthreads();   // the stages are refilled by the next tile
+}
+
 // Groups of more rows than this take 256-row tiles even when most groups are
 // small (a launch of their own).  On a DeepSeek-V3-shaped skewed load this
 // saves 9-11% on the launches whose contraction (7168) exceeds the output
@@ -957,10 +1036,12 @@ struct MaxG {
   static constexpr int value = TM <= 128 ? kMaxGShort : kMaxG;
 };
 
-template <bool B_COLK, int TM, int TN, typename TO, bool PAIR, bool SWI = false>
+template <bool B_COLK, int TM, int TN, typename TO, bool PAIR, bool SWI = false, bool SWB = false>
 __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArgs a) {
   static_assert(!SWI || (B_COLK && TN == 256 && std::is_same<TO, bf16_t>::value),
                 "the SwiGLU epilogue takes a [K, 2F] rhs and bf16 outputs");
+  static_assert(!SWB || (!SWI && std::is_same<TO, bf16_t>::value),
+                "the SwiGLU-backward epilogue writes bf16 d_h0, d_h1");
   static_assert(!PAIR || Stages<TM, TN>::NS == 4, "pair loading uses the four-step ring");
   using OA = std::conditional_t<PAIR, PairRow<TM>, Operand<false, TM>>;
   // the rhs keeps single-step units even in the pair pipeline: a transposed
@@ -1021,14 +1102,23 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
       B.setup(B_COLK ? bg + col0 : bg + col0 * a.ld_rhs, a.ld_rhs, cv);
       if constexpr (PAIR) contract2(smem, A, B, a.Kdim, acc, fa, fb);
       else contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
-      store_tile(acc, smem, out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate,
-                 a.bias ? a.bias + g * a.N + col0 : nullptr, 1.f, vr);
+      if constexpr (SWB)
+        store_tile_swiglu_bwd(acc, smem, out + row0 * a.ld_out + col0,
+                              a.dh1 + row0 * a.ld_out + col0, a.ld_out,
+                              a.h0 + row0 * a.ld_h + col0, a.h1 + row0 * a.ld_h + col0, a.ld_h,
+                              rv, cv, vr);
+      else
+        store_tile(acc, smem, out + row0 * a.ld_out + col0, a.ld_out, rv, cv, a.accumulate,
+                   a.bias ? a.bias + g * a.N + col0 : nullptr, 1.f, vr);
     }
   }
   if (a.cls_lo > 0) return;   // the launch of the small-group class zeroes the rest
   if constexpr (SWI) {
     if (out) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
     zero_rows(a.act, a.ld_act, a.N / 2, row_base[a.G], a.M);
+  } else if constexpr (SWB) {
+    zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
+    zero_rows(a.dh1, a.ld_out, a.N, row_base[a.G], a.M);
   } else {
     if (!a.accumulate) zero_rows(out, a.ld_out, a.N, row_base[a.G], a.M);
   }
@@ -1618,6 +1708,62 @@ MOE_API int moe_gmm_swiglu(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const
     hipLaunchKernelGGL((gmm_mfma_kernel<true, 256, 256, bf16_t, true, true>), dim3(grid), dim3(NT), 0, st, a);
   else
     hipLaunchKernelGGL((gmm_mfma_kernel<true, 256, 256, bf16_t, false, true>), dim3(grid), dim3(NT), 0, st, a);
+  return launch_status();
+}
+
+MOE_API int moe_gmm_swiglu_bwd(const void* lhs, int64_t M_lhs, int64_t ld_lhs, const void* rhs,
+                               int64_t ld_rhs, int64_t rhs_group_stride,
+                               const int32_t* group_sizes, const int32_t* valid_rows, int G,
+                               int64_t Kdim, int64_t F, int in_dtype, const void* h0,
+                               const void* h1, int64_t ld_h, void* d_h0, void* d_h1,
+                               int64_t ld_dh, int64_t M_out, int32_t* err, void* stream) {
+  if (G < 1 || G > kMaxG || M_lhs < 0 || M_out < 0 || M_out > M_lhs || Kdim < 0 || F < 0)
+    return MOE_ERR_ARG;
+  if (M_out > INT32_MAX) return MOE_ERR_ARG;
+  if (in_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!mult8(Kdim) || !mult8(F) || !mult8(ld_lhs) || !mult8(ld_rhs) || !mult8(rhs_group_stride) ||
+      !mult8(ld_h) || !mult8(ld_dh))
+    return MOE_ERR_ARG;
+  if (F <= 128 || Kdim <= TK) return MOE_ERR_ARG;   // the narrow tile shapes are not offered
+  if (ld_lhs < Kdim || ld_rhs < Kdim || ld_h < F || ld_dh < F) return MOE_ERR_ARG;
+  if (ld_lhs > kMaxLd || ld_rhs > kMaxLd) return MOE_ERR_ARG;
+  if (M_out == 0) return MOE_OK;
+  if (!lhs || !rhs || !group_sizes || !h0 || !h1 || !d_h0 || !d_h1 || !aligned16(lhs) ||
+      !aligned16(rhs) || !aligned16(h0) || !aligned16(h1) || !aligned16(d_h0) || !aligned16(d_h1))
+    return MOE_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MfmaArgs a{static_cast<const bf16_t*>(lhs), ld_lhs, static_cast<const bf16_t*>(rhs), ld_rhs,
+             rhs_group_stride, group_sizes, G, M_out, Kdim, F, d_h0, ld_dh, 0, 0, err, valid_rows};
+  a.h0 = static_cast<const bf16_t*>(h0);
+  a.h1 = static_cast<const bf16_t*>(h1);
+  a.ld_h = ld_h;
+  a.dh1 = static_cast<bf16_t*>(d_h1);
+  // tiles as moe_gmm's with a transposed rhs
+  const bool short_m = G <= kMaxGShort && M_out < 512 * static_cast<int64_t>(G);
+  const int64_t nsteps = Kdim / TK;
+  const bool pair = nsteps >= 2 && nsteps % 2 == 0;
+  if (short_m) {
+    const int64_t upper = ((M_out + 127) / 128 + G) * ((F + 255) / 256);
+    const unsigned grid = persistent_grid(upper, 2);
+    if (G > 1 && Kdim >= F) {
+      MfmaArgs b = a;
+      b.cls_lo = kSplitRows + 1;
+      const unsigned grid_big = persistent_grid(((M_out + 255) / 256 + G) * ((F + 255) / 256), 1);
+      if (pair)
+        hipLaunchKernelGGL((gmm_mfma_kernel<false, 256, 256, bf16_t, true, false, true>), dim3(grid_big), dim3(NT), 0, st, b);
+      else
+        hipLaunchKernelGGL((gmm_mfma_kernel<false, 256, 256, bf16_t, false, false, true>), dim3(grid_big), dim3(NT), 0, st, b);
+      a.cls_hi = kSplitRows;
+    }
+    hipLaunchKernelGGL((gmm_mfma_kernel<false, 128, 256, bf16_t, false, false, true>), dim3(grid), dim3(NT), 0, st, a);
+  } else {
+    const int64_t upper = ((M_out + 255) / 256 + G) * ((F + 255) / 256);
+    const unsigned grid = persistent_grid(upper, 1);
+    if (pair)
+      hipLaunchKernelGGL((gmm_mfma_kernel<false, 256, 256, bf16_t, true, false, true>), dim3(grid), dim3(NT), 0, st, a);
+    else
+      hipLaunchKernelGGL((gmm_mfma_kernel<false, 256, 256, bf16_t, false, false, true>), dim3(grid), dim3(NT), 0, st, a);
+  }
   return launch_status();
 }
 

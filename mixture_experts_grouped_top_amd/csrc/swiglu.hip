@@ -81,11 +81,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const TH* __restrict__ 
       rb[u].get(b);
       rg[u].get(g);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float s = 1.0f / (1.0f + expf(-a[q]));
-        o0[q] = g[q] * b[q] * s * (1.0f + a[q] * (1.0f - s));
-        o1[q] = g[q] * a[q] * s;
-      }
+      for (int q = 0; q < 8; ++q) swiglu_bwd_f32(a[q], b[q], g[q], o0[q], o1[q]);
       const int64_t od = strided8(static_cast<uint32_t>(i), cpr, ld_d);
       store8_nt(d0 + od, o0);
       store8_nt(d1 + od, o1);

@@ -41,7 +41,8 @@ def test_header_declares_the_abi():
                  "moe_abi_version", "moe_aux_loss_workspace", "moe_aux_loss",
                  "moe_aux_loss_bwd", "moe_group_sum_workspace", "moe_group_sum",
                  "moe_fp8_scale_workspace", "moe_fp8_amax_scale", "moe_fp8_padded_rows",
-                 "moe_fp8_quantize", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gmm_swiglu"]:
+                 "moe_fp8_quantize", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gmm_swiglu",
+                 "moe_gmm_swiglu_bwd"]:
         assert name in d, name
 
 
@@ -127,6 +128,14 @@ def test_argument_checks_return_before_launch(lib):
     assert swi(ldr=248) == -1
     assert swi(lda=120) == -1
     assert swi(act=ctypes.c_void_p(24)) == -1
+    # gmm_swiglu_bwd: narrow F, short contraction, float32, h row stride below F
+    def swb(F=256, K=64, it=1, ldh=256):
+        return lib.moe_gmm_swiglu_bwd(P, 64, 64, P, 64, 64 * F, P, None, 2, K, F, it, P, P, ldh,
+                                      P, P, F, 64, None, None)
+    assert swb(F=128, ldh=128) == -1
+    assert swb(K=32) == -1
+    assert swb(it=0) == -2
+    assert swb(ldh=248) == -1
     # group sum: N not a multiple of 8, G too large, missing or short workspace, bad dtype
     W = ctypes.c_void_p(256)
     assert lib.moe_group_sum(P, 12, 1, P, None, 2, 10, 12, P, 0, 0, W, 1 << 20, None, None) == -1

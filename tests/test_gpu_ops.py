@@ -441,6 +441,63 @@ def test_gmm_swiglu(gpu_lib, case):
         assert (gh[S:] == 0).all()
 
 
+SWB_CASES = [
+    # group sizes, valid rows, K (d_model), F, fused [rows, 2F] layouts, extra output rows
+    ([300, 0, 257, 128, 1000], None, 264, 264, False, 7),            # 128-row tiles, ragged F
+    ([30, 700, 0, 385, 384, 1100, 5, 0, 129, 40], [30, 650, 0, 385, 300, 1100, 1, 0, 129, 40],
+     520, 256, True, 0),                                              # both size classes
+    ([1024, 1024], None, 512, 384, True, 5),                          # 256-row pair tiles
+    ([1024, 1024], [1000, 3], 544, 256, False, 0),                    # odd steps
+]
+
+
+@pytest.mark.parametrize("case", SWB_CASES, ids=[str(i) for i in range(len(SWB_CASES))])
+def test_gmm_swiglu_bwd(gpu_lib, case):
+    """The d_act GEMM with the SwiGLU backward epilogue equals moe_gmm into a
+    bf16 d_act followed by moe_swiglu_bwd bit for bit, and the oracle within
+    tolerance; rows past the groups are zero."""
+    gs, valid, K, F, fused, extra = case
+    gs = np.array(gs, dtype=np.int32)
+    G = len(gs)
+    S = int(gs.sum())
+    M = S + extra
+    g = np.random.default_rng(K + F + 3 * G)
+    dy = _draw(g, (M, K), "bf16")
+    wo = _draw(g, (G, F, K), "bf16")          # used transposed: [F, K] per group
+    h = ms.bf16_round(_draw(g, (M, 2 * F), "bf16") * 3)
+    vr = None
+    dy0 = dy.copy()
+    if valid is not None:
+        vr = np.array(valid, dtype=np.int32)
+        off = np.concatenate([[0], np.cumsum(gs)])
+        for e in range(G):
+            dy0[off[e] + vr[e]:off[e + 1]] = 0
+    dy_d, wo_d = dev(dy, torch.bfloat16), dev(wo, torch.bfloat16)
+    v_d = dev_i32(vr) if vr is not None else None
+    if fused:
+        hd = dev(h, torch.bfloat16)
+        h0, h1 = hd[:, :F], hd[:, F:]
+        dh = poison(torch.empty((M, 2 * F), dtype=torch.bfloat16, device="cuda"))
+        d0, d1 = dh[:, :F], dh[:, F:]
+    else:
+        h0, h1 = dev(h[:, :F], torch.bfloat16), dev(h[:, F:], torch.bfloat16)
+        d0 = poison(torch.empty((M, F), dtype=torch.bfloat16, device="cuda"))
+        d1 = poison(torch.empty((M, F), dtype=torch.bfloat16, device="cuda"))
+    gpu_lib.moe_gmm_swiglu_bwd(dy_d, wo_d, dev_i32(gs), h0, h1, d_h0=d0, d_h1=d1, valid_rows=v_d)
+    da = gpu_lib.moe_gmm(dy_d, wo_d, dev_i32(gs), trans_rhs=True, valid_rows=v_d)
+    w0, w1 = gpu_lib.moe_swiglu_bwd(h0, h1, da)
+    # rows of the groups bit for bit (rows past them are zero in both, the
+    # two-call path's possibly as -0 from a zero d_act times a negative h)
+    assert torch.equal(d0.contiguous()[:S].view(torch.int16), w0[:S].view(torch.int16))
+    assert torch.equal(d1.contiguous()[:S].view(torch.int16), w1[:S].view(torch.int16))
+    want_da = ms.bf16_round(oracle.gmm(dy0, wo, gs, trans_rhs=True, rows_out=M))
+    o0, o1 = oracle.swiglu_bwd(h[:, :F], h[:, F:], want_da)
+    g0, g1 = host(d0.contiguous()), host(d1.contiguous())
+    assert_close(g0[:S], o0[:S], TOL_BF16, "d_h0")
+    assert_close(g1[:S], o1[:S], TOL_BF16, "d_h1")
+    assert (g0[S:] == 0).all() and (g1[S:] == 0).all()
+
+
 @pytest.mark.parametrize("it", ["bf16", "f32"])
 def test_tgmm_valid_rows(gpu_lib, it):
     """With valid_rows the contraction stops after each group's first
