@@ -144,10 +144,11 @@ class LaunchRecorder:
 # (the rocprofv3 summary is matched on this name).
 # These are the 256 x 256 tile variants the Mixtral-8x7B shape runs on.
 KERNEL_NAME = {
-    "gmm_nn": "gmm_mfma_kernel<true, 256, 256, unsigned short, true, false>",
-    "gmm_nt": "gmm_mfma_kernel<false, 256, 256, unsigned short, true, false>",
+    "gmm_nn": "gmm_mfma_kernel<true, 256, 256, unsigned short, true, false, false>",
+    "gmm_nt": "gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, false>",
     "tgmm": "tgmm_mfma_kernel<256, 256, unsigned short>",
-    "gmm_up_chunk": "gmm_mfma_kernel<true, 128, 256, float, false, false>",
+    "gmm_nt_swiglu_bwd": "gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, true>",
+    "gmm_up_chunk": "gmm_mfma_kernel<true, 128, 256, float, false, false, false>",
 }
 
 

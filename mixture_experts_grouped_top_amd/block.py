@@ -438,7 +438,7 @@ class MoEPlan:
         if self.swiglu_bwd_epilogue:
             # d_act stays in registers: its GEMM's epilogue applies the SwiGLU
             # backward with h0, h1 and writes d_h0, d_h1
-            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+            with self._rec("gmm_nt_swiglu_bwd", 2.0 * R * s.D * s.F):
                 B.moe_gmm_swiglu_bwd(self.d_y_sorted, wo, gs, self.h0, self.h1, d_h0=self.d_h0,
                                      d_h1=self.d_h1, valid_rows=self.vrows, err=self.err,
                                      stream=stream)
