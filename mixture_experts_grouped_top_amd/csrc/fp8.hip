@@ -126,10 +126,12 @@ int amax_blocks(int64_t elems, int G) {
 // rows of a tile are two 64-row tiles of the groups' 64-row tiling (which
 // may belong to two groups), so every row segment of both copies a tile
 // writes is a whole 128-byte line, written by one workgroup at one time.
-// Each thread converts 4 consecutive rows x 16 columns (eight 16-byte
-// loads in flight), stores them row-wise, and writes one dword per column
-// (its 4 rows) into an LDS tile that is read back along columns for the
-// transposed copy.
+// Each thread converts 8 consecutive rows x 8 columns (one 16-byte bf16
+// load per row, eight in flight); the 16 lanes that share its rows read
+// whole lines of each row (256 contiguous bytes of bf16) and write one
+// whole 128-byte line of the row-wise copy.  A thread writes its 8 rows of
+// each of its columns (two dwords) into an LDS tile that is read back
+// along columns for the transposed copy.
 // Transposed layouts:
 //   qt_gs == 0: one [cols, P] matrix, the 64-row tile rt of the groups'
 //               tiling at columns 64 rt (a group's rows, then zeros up to
@@ -151,8 +153,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   const int nrt = tile_base[G];                       // 64-row tiles
   const int64_t total = static_cast<int64_t>((nrt + 1) / 2) * ntc;
   const int tid = threadIdx.x;
-  const int rg = tid >> 3, cg = tid & 7;               // rows 4 rg .. + 3, columns 16 cg .. + 15
-  const int half = rg >> 4;                            // which 64-row tile of the pair
+  const int rg = tid >> 4, cg = tid & 15;              // rows 8 rg .. + 7, columns 8 cg .. + 7
+  const int half = rg >> 3;                            // which 64-row tile of the pair
   auto group_of = [&](int rt) {
     int lo = 0, hi = G - 1;   // largest g with tile_base[g] <= rt
     while (lo < hi) {
@@ -169,51 +171,48 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     const int g = tile_ok ? group_of(rt) : 0;
     const int r_in = tile_ok ? 64 * (rt - tile_base[g]) : 0;     // first group row of the tile
     const int rv = tile_ok ? min(64, row_base[g + 1] - row_base[g] - r_in) : 0;
-    const int lr = 4 * (rg & 15);                      // first of the thread's rows in its tile
-    const int64_t col = static_cast<int64_t>(ct) * 128 + 16 * cg;
-    const bool col_ok = col < cols, two = col + 8 < cols;
+    const int lr = 8 * (rg & 7);                       // first of the thread's rows in its tile
+    const int64_t col = static_cast<int64_t>(ct) * 128 + 8 * cg;
+    const bool col_ok = col < cols;                    // cols is a multiple of 8
     const float s = scale[per_group ? g : 0];
-    // eight loads (two per row), a lane with nothing to load reads x[0..7]
-    Raw8<T> raw[4][2];
+    // eight loads, one per row; a lane with nothing to load reads x[0..7]
+    Raw8<T> raw[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const bool ok = col_ok && lr + i < rv;
       const T* p = x + (static_cast<int64_t>(row_base[g]) + r_in + lr + i) * ld + col;
-      raw[i][0].load(ok ? p : x);
-      raw[i][1].load(ok && two ? p + 8 : x);
+      raw[i].load(ok ? p : x);
     }
-    uint32_t w[4][4];
+    uint32_t w[8][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const bool ok = col_ok && lr + i < rv;
-      float v[16];
-      raw[i][0].get(v);
-      raw[i][1].get(v + 8);
+      float v[8];
+      raw[i].get(v);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 2; ++k) {
         const uint32_t c = pack4_fp8<FMT>(__fmul_rn(v[4 * k], s), __fmul_rn(v[4 * k + 1], s),
                                           __fmul_rn(v[4 * k + 2], s), __fmul_rn(v[4 * k + 3], s));
-        w[i][k] = ok && (k < 2 || two) ? c : 0u;
+        w[i][k] = ok ? c : 0u;
       }
       if (q && ok) {
+        // 8-byte aligned: col and ld_q are multiples of 8
         uint8_t* d = q + (static_cast<int64_t>(row_base[g]) + r_in + lr + i) * ld_q + col;
-        // rows are 16-byte aligned when ld_q is a multiple of 16, else 8-byte
-        if (two && !(ld_q & 15)) {
-          *reinterpret_cast<uint4*>(d) = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
-        } else {
-          *reinterpret_cast<uint2*>(d) = make_uint2(w[i][0], w[i][1]);
-          if (two) *reinterpret_cast<uint2*>(d + 8) = make_uint2(w[i][2], w[i][3]);
-        }
+        *reinterpret_cast<uint2*>(d) = make_uint2(w[i][0], w[i][1]);
       }
     }
     if (qt) {
-      // column 16 cg + e, rows 4 rg .. + 3 as one dword (row 4 rg in the low byte)
+      // column 8 cg + e, rows 8 rg .. + 7 as two dwords (row 8 rg in the low byte)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < 8; ++e) {
         const int sh = 8 * (e & 3);
-        const uint32_t b0 = (w[0][e >> 2] >> sh) & 0xFFu, b1 = (w[1][e >> 2] >> sh) & 0xFFu;
-        const uint32_t b2 = (w[2][e >> 2] >> sh) & 0xFFu, b3 = (w[3][e >> 2] >> sh) & 0xFFu;
-        tr[16 * cg + e][rg] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo |= ((w[i][e >> 2] >> sh) & 0xFFu) << (8 * i);
+          hi |= ((w[i + 4][e >> 2] >> sh) & 0xFFu) << (8 * i);
+        }
+        *reinterpret_cast<uint2*>(&tr[8 * cg + e][2 * rg]) = make_uint2(lo, hi);
       }
       __syncthreads();
       // thread: tile column tid / 2, the 64 rows of tile 2 pr + (tid & 1)
