@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import gc
 import hashlib
 import json
 import os
@@ -98,6 +99,29 @@ def to_gpu(inp, dtype):
     return out
 
 
+class _Bracket:
+    """Context manager recording a start and an end event around launches."""
+
+    __slots__ = ("rec", "kind", "flops", "nbytes", "s")
+
+    def __init__(self, rec, kind, flops, nbytes):
+        self.rec, self.kind, self.flops, self.nbytes = rec, kind, flops, nbytes
+
+    def __enter__(self):
+        rec = self.rec
+        if rec.active:
+            self.s = rec.torch.cuda.Event(enable_timing=True)
+            self.s.record(rec.torch.cuda.current_stream())
+
+    def __exit__(self, *exc):
+        rec = self.rec
+        if rec.active:
+            e = rec.torch.cuda.Event(enable_timing=True)
+            e.record(rec.torch.cuda.current_stream())
+            rec.items.append((self.kind, self.flops, self.nbytes, self.s, e))
+        return False
+
+
 class LaunchRecorder:
     """Brackets launches with events on the stream they are issued on."""
 
@@ -108,21 +132,7 @@ class LaunchRecorder:
         self.active = False
 
     def __call__(self, kind, flops=0.0, nbytes=0.0):
-        rec = self
-
-        class _Ctx:
-            def __enter__(self_):
-                if rec.active:
-                    self_.s = rec.torch.cuda.Event(enable_timing=True)
-                    self_.s.record(rec.torch.cuda.current_stream())
-
-            def __exit__(self_, *exc):
-                if rec.active:
-                    e = rec.torch.cuda.Event(enable_timing=True)
-                    e.record(rec.torch.cuda.current_stream())
-                    rec.items.append((kind, flops, nbytes, self_.s, e))
-                return False
-        return _Ctx()
+        return _Bracket(self, kind, flops, nbytes)
 
     def summary(self):
         agg = {}
@@ -334,6 +344,10 @@ def main():
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    # no cyclic garbage collection inside the timed region (as timeit does):
+    # a collection pass stalls the launching thread for tens of milliseconds
+    gc.collect()
+    gc.disable()
     rec.active = True
     start.record()
     for _ in range(args.steps):
@@ -341,6 +355,7 @@ def main():
     end.record()
     torch.cuda.synchronize()
     rec.active = False
+    gc.enable()
     ms_step = start.elapsed_time(end) / args.steps
     err = int(plan.err.item())
     flops = 18.0 * R * w.D * w.F
