@@ -962,8 +962,7 @@ __device__ __forceinline__ void store_tile_swiglu_bwd(const Acc<TM, TN>& acc, ch
   constexpr int WC = TN / 2;
   constexpr int SROW = WC * 4 + 16;
   constexpr int CPR = WC / 8;
-  constexpr int NQ = 32 * CPR / 64;
-  constexpr int QB = NQ < 2 ? NQ : 2;          // chunks whose loads are in flight together
+  constexpr int NQ = 32 * CPR / 64;            // chunks per lane per slab
   static_assert(4 * 32 * SROW <= Stages<TM, TN>::kBytes, "epilogue slabs fit in the stage buffers");
   const int tid = opaque_tid();
   const int lane = tid & 63;
@@ -972,6 +971,21 @@ __device__ __forceinline__ void store_tile_swiglu_bwd(const Acc<TM, TN>& acc, ch
   const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * WC;
 #pragma unroll
   for (int i = 0; i < Acc<TM, TN>::FM; ++i) {
+    // every h0, h1 chunk of the slab is requested before the slab is
+    // staged, so their latency overlaps the staging (one wait per slab;
+    // requesting the next slab's chunks during this slab's stores, in the
+    // same registers, was 12% slower on the Mixtral-8x7B shape)
+    Raw8<bf16_t> ra[NQ], rb[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int chunk = lane + 64 * q;
+      const int row = chunk / CPR, c8 = chunk % CPR;
+      const int grow = wr + 32 * i + row, gcol = wc + 8 * c8;
+      const bool ok = grow < rv && gcol < cv;
+      const int64_t hoff = static_cast<int64_t>(ok ? grow : 0) * ld_h + (ok ? gcol : 0);
+      ra[q].load(h0 + hoff);
+      rb[q].load(h1 + hoff);
+    }
 #pragma unroll
     for (int j = 0; j < Acc<TM, TN>::FN; ++j)
 #pragma unroll
@@ -984,33 +998,22 @@ __device__ __forceinline__ void store_tile_swiglu_bwd(const Acc<TM, TN>& acc, ch
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int q0 = 0; q0 < NQ; q0 += QB) {
-      float ga[QB][8], ha[QB][8], hb[QB][8];
-      bool ok[QB];
-#pragma unroll
-      for (int u = 0; u < QB; ++u) {
-        const int chunk = lane + 64 * (q0 + u);
-        const int row = chunk / CPR, c8 = chunk % CPR;
-        const int grow = wr + 32 * i + row, gcol = wc + 8 * c8;
-        ok[u] = grow < rv && gcol < cv;
+    for (int q = 0; q < NQ; ++q) {
+      const int chunk = lane + 64 * q;
+      const int row = chunk / CPR, c8 = chunk % CPR;
+      const int grow = wr + 32 * i + row, gcol = wc + 8 * c8;
+      if (grow < rv && gcol < cv) {
         const float4 lo = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32);
         const float4 hi = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
         const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        float ga[8], ha[8], hb[8], o0[8], o1[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ga[u][e] = grow < rz ? bf16_to_f32(f32_to_bf16(v[e])) : 0.f;
-        const int64_t hoff = static_cast<int64_t>(ok[u] ? grow : 0) * ld_h + (ok[u] ? gcol : 0);
-        load8(h0 + hoff, ha[u]);
-        load8(h1 + hoff, hb[u]);
-      }
+        for (int e = 0; e < 8; ++e) ga[e] = grow < rz ? bf16_to_f32(f32_to_bf16(v[e])) : 0.f;
+        ra[q].get(ha);
+        rb[q].get(hb);
 #pragma unroll
-      for (int u = 0; u < QB; ++u) {
-        if (!ok[u]) continue;
-        const int chunk = lane + 64 * (q0 + u);
-        const int row = chunk / CPR, c8 = chunk % CPR;
-        const int64_t doff = static_cast<int64_t>(wr + 32 * i + row) * ld_d + wc + 8 * c8;
-        float o0[8], o1[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) swiglu_bwd_f32(ha[u][e], hb[u][e], ga[u][e], o0[e], o1[e]);
+        for (int e = 0; e < 8; ++e) swiglu_bwd_f32(ha[e], hb[e], ga[e], o0[e], o1[e]);
+        const int64_t doff = static_cast<int64_t>(grow) * ld_d + gcol;
         store8_nt(d0 + doff, o0);
         store8_nt(d1 + doff, o1);
       }
