@@ -348,14 +348,16 @@ def main():
     # a collection pass stalls the launching thread for tens of milliseconds
     gc.collect()
     gc.disable()
-    rec.active = True
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    rec.active = False
-    gc.enable()
+    try:
+        rec.active = True
+        start.record()
+        for _ in range(args.steps):
+            step()
+        end.record()
+        torch.cuda.synchronize()
+        rec.active = False
+    finally:
+        gc.enable()
     ms_step = start.elapsed_time(end) / args.steps
     err = int(plan.err.item())
     flops = 18.0 * R * w.D * w.F
