@@ -180,6 +180,10 @@ GMM8_CASES = [
     ([800, 0, 900], 512, 520, "e5m2", "e5m2", "bf16", True, True),
     ([(i * 7) % 3 for i in range(1000)], 64, 136, "e4m3", "e4m3", "f32", False, False),
     ([0, 0, 0], 64, 64, "e4m3", "e4m3", "f32", False, False),
+    # 256-row tiles (groups of 512 rows or more on average): an odd number
+    # of full contraction steps and a ragged one, and a ragged step alone
+    ([700, 600], 224, 264, "e4m3", "e4m3", "bf16", True, False),
+    ([600, 520], 32, 136, "e5m2", "e4m3", "f32", False, True),
 ]
 
 
