@@ -785,7 +785,7 @@ struct Stages {
 // (in bounds, no partial sum, bias or scale) takes a path without per-chunk
 // tests.  The LDS is the operand stages, free once the contraction has ended
 // with a barrier.
-template <int TM, int TN, typename TO>
+template <int TM, int TN, typename TO, bool PF = true>
 __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO* o, int64_t ldo,
                                            int rv, int cv, int accumulate,
                                            const bf16_t* bias = nullptr, float scale = 1.f,
@@ -805,6 +805,20 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
                      wc + WC <= cv;
 #pragma unroll
   for (int i = 0; i < Acc<TM, TN>::FM; ++i) {
+    // partial sums (PF): all of the slab's old values are requested before
+    // the slab is staged (one load round trip per slab, overlapping the
+    // staging); the FP8 tgmm, which is slower with it (its epilogue
+    // spills more), loads them chunk by chunk
+    Raw8<TO> prev[PF ? NQ : 1];
+    if (PF && accumulate) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int chunk = lane + 64 * q;
+        const int grow = wr + 32 * i + chunk / CPR, gcol = wc + 8 * (chunk % CPR);
+        const bool ok = grow < rv && gcol < cv;
+        prev[q].load(ok ? o + static_cast<int64_t>(grow) * ldo + gcol : o);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < Acc<TM, TN>::FN; ++j)
 #pragma unroll
@@ -843,7 +857,8 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
       if (grow < rv && gcol < cv) {
         if (accumulate) {
           float old[8];
-          load8(p, old);
+          if constexpr (PF) prev[q].get(old);
+          else load8(p, old);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += old[e];
         }
@@ -1487,8 +1502,9 @@ __global__ __launch_bounds__(NT, TM >= 256 ? 1 : 2) void tgmm_fp8_kernel(Fp8Args
     A.setup(a.lhs + m0 * a.ld_lhs + c0, a.ld_lhs, mv);
     B.setup(a.rhs + n0 * a.ld_rhs + c0, a.ld_rhs, nv);
     contract_f8<F8Tile<TM>::NS>(smem, A, B, kc, acc, fa, fb);
-    store_tile(static_cast<const Acc<TM, TN>&>(acc), smem, out + g * a.out_gs + m0 * a.ld_out + n0,
-               a.ld_out, mv, nv, a.accumulate, nullptr, scale);
+    store_tile<TM, TN, TO, false>(static_cast<const Acc<TM, TN>&>(acc), smem,
+                                  out + g * a.out_gs + m0 * a.ld_out + n0, a.ld_out, mv, nv,
+                                  a.accumulate, nullptr, scale);
   }
 }
 
