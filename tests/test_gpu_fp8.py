@@ -95,6 +95,29 @@ def test_fp8_quantize(gpu_lib, case):
     assert (got_t[:, used:] == 0xAA).all()
 
 
+def test_fp8_quantize_many_tiles(gpu_lib):
+    """More 128 x 128 tiles than the quantizer's grid holds workgroups, so
+    each workgroup takes several tiles (ragged groups and columns)."""
+    gs = np.array([2500, 0, 1, 4095, 3000, 129, 5000, 64, 5211], dtype=np.int32)
+    G, cols = len(gs), 2176
+    g = np.random.default_rng(11)
+    rows = int(gs.sum())
+    x = _draw(g, (rows, cols), "bf16", spread=2.0)
+    xd = dev(x, torch.bfloat16)
+    sc = gpu_lib.moe_fp8_amax_scale(xd, "e4m3")
+    P = gpu_lib.moe_fp8_padded_rows(rows, G)
+    tiles = (P // 64 + 1) // 2 * ((cols + 127) // 128)
+    assert tiles > 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    q = torch.full((rows, cols), 0xAA, dtype=torch.uint8, device="cuda")
+    qt = torch.full((cols, P), 0xAA, dtype=torch.uint8, device="cuda")
+    gpu_lib.moe_fp8_quantize(xd, dev_i32(gs), sc[1], "e4m3", q=q, qt=qt)
+    s, _ = F8.scales(F8.amax_groups(x), "e4m3")
+    want = F8.quantize(x, "e4m3", s[0])
+    assert (host(q) == want).all()
+    used = 64 * int(((gs + 63) // 64).sum())
+    assert (host(qt)[:, :used] == _padded_t(want, gs, P)[:, :used]).all()
+
+
 def _all_bf16():
     """Every finite bf16 value below 1e30 in magnitude (as float32; the
     float32 products with the test scales stay finite)."""
