@@ -1,5 +1,5 @@
 // SwiGLU gating of the expert FFN and its backward, elementwise over
-// [rows, F], two groups of 8 elements per thread per step (HBM-bound).  The two inputs
+// [rows, F], four groups of 8 elements per thread per step (HBM-bound).  The two inputs
 // are the gate and up projection outputs named in the TransformerEngine MoE
 // block pull request's commit notes (gate_proj_out, up_proj_out).
 #include "common.h"
@@ -9,7 +9,7 @@ namespace {
 
 // Grid-stride over groups of kU x 8 elements per thread: all loads of a
 // group are issued (streaming hint) before any is used.
-constexpr int kU = 2;
+constexpr int kU = 4;
 
 // Element group i (8 elements) of a [rows, F] matrix with row stride ld
 // (cpr = F / 8 groups per row; i < 2^31 is checked on the host).
