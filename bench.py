@@ -2,6 +2,7 @@
 """MoE expert-FFN forward+backward throughput on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+                    [--extra-workloads deepseek_v3] [--fp8] [--fused-wi]
 
 A step is one pass of the whole path over one batch of synthetic input:
 router GEMM, top-k routing, permute, the up-projection grouped GEMMs,
@@ -11,19 +12,26 @@ transposed, transposed grouped GEMMs for the expert weight gradients,
 SwiGLU backward, permute backward, routing backward and the router GEMM
 backward).  Inputs are resident in HBM before the timed region starts.
 
-`value` is expert-FFN TFLOP/s: 18 * R * d_model * d_ff algorithmic flops per
-step (R = kept routed rows; padding rows and the router GEMM excluded)
-divided by the step time.  Prints ONE JSON line on stdout; everything else
-goes to stderr.
+`value` is expert-FFN TFLOP/s of the headline workload (Mixtral-8x7B
+shape by default): 18 * R * d_model * d_ff algorithmic flops per step
+(R = kept routed rows; padding rows and the router GEMM excluded) divided
+by the step time, which is taken over K steps with no other events in the
+stream.  A second pass of the same steps brackets every expert GEMM and
+memory-bound call with events, each after a 1 GiB scratch write that
+evicts the 256 MB memory-side cache, and classifies each kind of call by
+its own roofline: MFMA-bound when flops / peak exceeds algorithmic bytes /
+HBM bandwidth, else HBM-bound.  Extra workloads (the DeepSeek-V3 shape by
+default) are measured the same way and reported under "workloads".
+Prints ONE JSON line on stdout; everything else goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
-import concurrent.futures as cf
 import gc
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -35,6 +43,7 @@ METRIC = "MoE FFN fwd+bwd grouped-GEMM TFLOP/s and % of bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+FLUSH_BYTES = 1 << 30          # scratch written before each bracketed call (> 256 MB MALL)
 
 
 def log(*a):
@@ -46,61 +55,32 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--kernel-steps", type=int, default=5,
+                   help="steps of the second pass that times each call after a cache flush")
     p.add_argument("--workload", default="mixtral")
-    p.add_argument("--cpu-tokens", type=int, default=2048,
-                   help="tokens of the workload the CPU oracle baseline runs on")
+    p.add_argument("--extra-workloads", default="deepseek_v3",
+                   help="comma-separated workloads reported under 'workloads' ('' = none)")
+    p.add_argument("--cpu-tokens", type=int, default=0,
+                   help="tokens of the headline workload the CPU oracle runs on (0 = all)")
     p.add_argument("--fused-wi", action="store_true",
                    help="one [E, D, 2F] up-projection weight [wi_0 | wi_1]")
     p.add_argument("--fp8", action="store_true",
                    help="FP8 expert GEMMs (e4m3 forward, e5m2 backward, current scaling)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
-                   help="do not bracket the expert GEMM launches with events")
+                   help="skip the per-call pass (only the step timing runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain row copy of known size (for scaling HBM counters)")
-    p.add_argument("--traffic-summary", nargs=4, metavar=("BENCH_FETCH", "BENCH_WRITE",
-                                                           "COPY_FETCH", "COPY_WRITE"),
+    p.add_argument("--traffic-summary", nargs=5,
+                   metavar=("WORKLOAD", "BENCH_FETCH", "BENCH_WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="turn four rocprofv3 --pmc counter_collection.csv files into "
-                        "profiles/gmm_mixtral_traffic.json and exit")
+                        "profiles/<workload>_traffic.json and exit")
     return p.parse_args()
 
 
-def gen_inputs(w, threads: int):
-    """Seeded inputs (CPU), generated per expert in parallel."""
-    import numpy as np
-    import moe_synth as ms
-    t0 = time.time()
-    with cf.ThreadPoolExecutor(threads) as ex:
-        futs = {name: [ex.submit(ms.gen_expert_weight, w, name, e) for e in range(w.E)]
-                for name in ("wi_0", "wi_1", "wo")}
-        x = ms.gen_x(w)
-        dy = ms.gen_dy(w)
-        Wg = ms.gen_gate(w) if w.logits == "gemm" else None
-        logits = ms.gen_uniform_logits(w) if w.logits == "uniform" else None
-        bias = ms.gen_logit_bias(w)
-        weights = {k: [f.result() for f in v] for k, v in futs.items()}
-    log(f"[bench] generated inputs in {time.time() - t0:.1f}s")
-    return dict(x=x, dy=dy, Wg=Wg, logits=logits, bias=bias, **weights)
-
-
-def to_gpu(inp, dtype):
-    import numpy as np
-    import torch
-
-    def up(a):
-        t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
-        return t.to(dtype) if dtype != torch.float32 else t
-
-    out = {k: up(inp[k]) if inp[k] is not None else None for k in ("x", "dy", "Wg")}
-    for k in ("wi_0", "wi_1", "wo"):
-        out[k] = torch.stack([up(a) for a in inp[k]])
-    for k in ("logits", "bias"):   # float32 router inputs
-        out[k] = torch.from_numpy(inp[k]).cuda() if inp[k] is not None else None
-    return out
-
-
 class _Bracket:
-    """Context manager recording a start and an end event around launches."""
+    """Context manager: optional cache flush, then a start and an end event
+    around the launches inside it."""
 
     __slots__ = ("rec", "kind", "flops", "nbytes", "s")
 
@@ -110,6 +90,8 @@ class _Bracket:
     def __enter__(self):
         rec = self.rec
         if rec.active:
+            if rec.flush is not None:
+                rec.flush.fill_(float(len(rec.items) & 1023))
             self.s = rec.torch.cuda.Event(enable_timing=True)
             self.s.record(rec.torch.cuda.current_stream())
 
@@ -125,16 +107,17 @@ class _Bracket:
 class LaunchRecorder:
     """Brackets launches with events on the stream they are issued on."""
 
-    def __init__(self):
+    def __init__(self, flush=None):
         import torch
         self.torch = torch
         self.items = []
         self.active = False
+        self.flush = flush
 
     def __call__(self, kind, flops=0.0, nbytes=0.0):
         return _Bracket(self, kind, flops, nbytes)
 
-    def summary(self):
+    def summary(self, peak_tflops):
         agg = {}
         for kind, flops, nbytes, s, e in self.items:
             ms = s.elapsed_time(e)
@@ -144,60 +127,85 @@ class LaunchRecorder:
             a["flops"] += flops
             a["bytes"] += nbytes
         for a in agg.values():
+            sec = a["ms"] * 1e-3
             a["avg_ms"] = a["ms"] / a["launches"]
-            a["tflops"] = a["flops"] / (a["ms"] * 1e-3) / 1e12
-            a["gbs"] = a["bytes"] / (a["ms"] * 1e-3) / 1e9
+            a["tflops"] = a["flops"] / sec / 1e12
+            a["gbs"] = a["bytes"] / sec / 1e9
+            # the roofline that bounds this kind of call: the larger of its
+            # compute time at the MFMA peak and its traffic time at the HBM peak
+            t_mfma = a["flops"] / (peak_tflops * 1e12)
+            t_hbm = a["bytes"] / (PEAK_HBM_GBS * 1e9)
+            a["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
+            a["frac"] = max(t_mfma, t_hbm) / sec if sec > 0 else 0.0
         return agg
 
 
-# Kernel symbol behind each recorded launch kind for the bf16 workloads
-# (the rocprofv3 summary is matched on this name).
-# These are the 256 x 256 tile variants the Mixtral-8x7B shape runs on.
+# Kernel symbol behind a recorded launch kind, per workload (for the
+# rocprofv3 summaries and the PMC traffic of the dominant kernel).  Kinds
+# launched as two kernels (a size-class split) have no single symbol.
 KERNEL_NAME = {
-    "gmm_nn": "gmm_mfma_kernel<true, 256, 256, unsigned short, true, false, false>",
-    "gmm_nt": "gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, false>",
-    "tgmm": "tgmm_mfma_kernel<256, 256, unsigned short>",
-    "gmm_nt_swiglu_bwd": "gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, true>",
-    "gmm_up_chunk": "gmm_mfma_kernel<true, 128, 256, float, false, false, false>",
+    "mixtral": {
+        "gmm_nn": "gmm_mfma_kernel<true, 256, 256, unsigned short, true, false, false>",
+        "gmm_nt": "gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, false>",
+        "tgmm": "tgmm_mfma_kernel<256, 256, unsigned short>",
+        "gmm_nt_swiglu_bwd": "gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, true>",
+    },
+    "deepseek_v3": {
+        "tgmm": "tgmm_mfma_kernel<128, 256, unsigned short>",
+    },
+}
+# Memory-bound kinds: the symbol prefix of the kernel that moves their data.
+MEM_KERNEL_PREFIX = {
+    "permute": "permute_scatter_kernel",
+    "combine": "gather_sum_kernel<unsigned short, true",
+    "permute_bwd": "gather_sum_kernel<unsigned short, false",
+    "combine_bwd": "combine_bwd_kernel<unsigned short",
+    "swiglu": "swiglu_kernel<unsigned short",
+    "swiglu_bwd": "swiglu_bwd_kernel<unsigned short",
 }
 
 
 def kernel_source_digest() -> str:
-    """Digest of the grouped-GEMM source and the helpers it includes, with
-    comments and blank lines removed, so that counters stay tied to the code
-    they were taken on."""
+    """Digest of every HIP source and header of the library, with comments
+    and blank lines removed, so that counters stay tied to the code they
+    were taken on."""
     import re
     csrc = os.path.join(ROOT, "mixture_experts_grouped_top_amd", "csrc")
     text = ""
-    for name in ("gmm.hip", "common.h"):
-        with open(os.path.join(csrc, name)) as f:
-            text += f.read()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name)) as f:
+                text += f.read()
     text = re.sub(r"//[^\n]*", "", text)
     code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def traffic_from_profiles(kind: str, workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed PMC
-    summary (taken on the Mixtral-8x7B shape), or None if absent, taken on a
-    different kernel source or for another workload."""
-    if workload != "mixtral":
-        return None
-    path = os.path.join(ROOT, "profiles", "gmm_mixtral_traffic.json")
+def traffic_json(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+
+
+def traffic_for(workload: str, kind: str):
+    """Calibrated HBM bytes per launch of the kernel behind `kind` from the
+    committed PMC summary, or None (absent, or taken on other sources)."""
     try:
-        with open(path) as f:
+        with open(traffic_json(workload)) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    k = d.get("kernels", {}).get(kind)
-    if not k or d.get("gmm_source_sha256_16") != kernel_source_digest():
+    if d.get("source_sha256_16") != kernel_source_digest():
         return None
-    return k.get("hbm_bytes_per_launch")
+    ks = d.get("kernels", {})
+    name = KERNEL_NAME.get(workload, {}).get(kind)
+    if name is None and kind in MEM_KERNEL_PREFIX:
+        hits = [k for k in ks if k.startswith(MEM_KERNEL_PREFIX[kind])]
+        name = hits[0] if len(hits) == 1 else None
+    k = ks.get(name) if name else None
+    return None if k is None else k.get("hbm_bytes_per_dispatch")
 
 
 COPY_ROWS, COPY_COLS = 32768, 16384      # bf16 rows copied by the calibration run (1 GiB)
 COPY_KERNEL = "permute_scatter_kernel"
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gmm_mixtral_traffic.json")
 
 
 def copy_calibration():
@@ -215,103 +223,112 @@ def copy_calibration():
     log(f"[bench] copy calibration: {COPY_ROWS}x{COPY_COLS} bf16, 3 copies")
 
 
-def _pmc_per_dispatch(path, counter, name_part):
+def _pmc_per_dispatch(path, counter):
+    """{kernel symbol: [counter value summed over its dimensions, per dispatch]}"""
     import csv
     per = {}
     for r in csv.DictReader(open(path)):
-        if r["Counter_Name"] != counter or name_part not in r["Kernel_Name"]:
+        if r["Counter_Name"] != counter:
             continue
-        d = int(r["Dispatch_Id"])
-        per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
-    return list(per.values())
+        key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
 
 
-def traffic_summary(bench_fetch, bench_write, copy_fetch, copy_write):
-    """Average FETCH_SIZE / WRITE_SIZE (KiB) per dispatch of each GEMM kernel,
-    scaled by known_bytes / measured_bytes of the copy kernel."""
+def traffic_summary(workload, bench_fetch, bench_write, copy_fetch, copy_write):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB) per dispatch of every kernel of a
+    bench run, scaled by known_bytes / measured_bytes of the copy kernel."""
     known = COPY_ROWS * COPY_COLS * 2
-    cf = _pmc_per_dispatch(copy_fetch, "FETCH_SIZE", COPY_KERNEL)
-    cw = _pmc_per_dispatch(copy_write, "WRITE_SIZE", COPY_KERNEL)
-    f_fetch = known / (1024.0 * sum(cf) / len(cf))
-    f_write = known / (1024.0 * sum(cw) / len(cw))
-    out = {"gmm_source_sha256_16": kernel_source_digest(),
+
+    def copy_avg(path, counter):
+        v = [x for k, xs in _pmc_per_dispatch(path, counter).items() if COPY_KERNEL in k for x in xs]
+        return sum(v) / len(v)
+    f_fetch = known / (1024.0 * copy_avg(copy_fetch, "FETCH_SIZE"))
+    f_write = known / (1024.0 * copy_avg(copy_write, "WRITE_SIZE"))
+    bench_cmd = (f"python bench.py --workload {workload} --extra-workloads '' --steps 2 "
+                 "--warmup 1 --no-cpu-baseline --no-kernel-events")
+    out = {"workload": workload, "source_sha256_16": kernel_source_digest(),
            "calibration": {"copy_bytes_each_way": known, "fetch_scale": round(f_fetch, 4),
                            "write_scale": round(f_write, 4), "kernel": COPY_KERNEL},
            "commands": [
-               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_bench_fetch -o p "
-               "-- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-kernel-events",
-               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_bench_write -o p "
-               "-- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-kernel-events",
+               f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch -o p -- {bench_cmd}",
+               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write -o p -- {bench_cmd}",
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_copy_fetch -o p "
                "-- python bench.py --copy-calibration",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_copy_write -o p "
                "-- python bench.py --copy-calibration"],
            "kernels": {}}
-    for kind, name in KERNEL_NAME.items():
-        f = _pmc_per_dispatch(bench_fetch, "FETCH_SIZE", name)
-        wv = _pmc_per_dispatch(bench_write, "WRITE_SIZE", name)
-        if not f or not wv:
+    fetch = _pmc_per_dispatch(bench_fetch, "FETCH_SIZE")
+    write = _pmc_per_dispatch(bench_write, "WRITE_SIZE")
+    for name in sorted(set(fetch) & set(write)):
+        if name.startswith(("at::", "void at::", "__amd")):
             continue
+        f, wv = fetch[name], write[name]
         fk, wk = sum(f) / len(f), sum(wv) / len(wv)
-        out["kernels"][kind] = {
+        out["kernels"][name] = {
             "dispatches": len(f), "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
-            "hbm_bytes_per_launch": round(1024.0 * (fk * f_fetch + wk * f_write))}
-    with open(TRAFFIC_JSON, "w") as fh:
+            "hbm_bytes_per_dispatch": round(1024.0 * (fk * f_fetch + wk * f_write))}
+    with open(traffic_json(workload), "w") as fh:
         json.dump(out, fh, indent=1)
-    log(f"[bench] wrote {TRAFFIC_JSON}")
+    log(f"[bench] wrote {traffic_json(workload)}")
 
 
-def cpu_baseline(w, inp, tokens: int):
-    """The float64 oracle, as it stands, on the first `tokens` tokens."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, host, tokens: int):
+    """The float64 oracle, as it stands, on the first `tokens` tokens (all
+    if 0) of the workload, with the expert weights regenerated on the host."""
     import numpy as np
+    import moe_synth as ms
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    T = min(tokens, w.T)
+    T = w.T if tokens <= 0 else min(tokens, w.T)
     sl = slice(0, T)
-    wi0, wi1, wo = (np.stack(inp[k]) for k in ("wi_0", "wi_1", "wo"))
-    kw = dict(score=w.score, renorm=w.renorm, bias=inp["bias"])
+    wi0, wi1, wo = (ms.gen_expert_weights(w, k) for k in ("wi_0", "wi_1", "wo"))
+    kw = dict(score=w.score, renorm=w.renorm, bias=host["bias"])
     t0 = time.perf_counter()
-    f = oracle.moe_forward(inp["x"][sl], wi0, wi1, wo, w.K, Wg=inp["Wg"],
-                           logits=None if inp["logits"] is None else inp["logits"][sl],
+    f = oracle.moe_forward(host["x"][sl], wi0, wi1, wo, w.K, Wg=host["Wg"],
+                           logits=None if host["logits"] is None else host["logits"][sl],
                            align=w.align, capacity=w.capacity, n_chunks=w.n_chunks, **kw)
-    oracle.moe_backward(f, inp["dy"][sl], inp["x"][sl], wi0, wi1, wo, w.K, Wg=inp["Wg"], **kw)
+    oracle.moe_backward(f, host["dy"][sl], host["x"][sl], wi0, wi1, wo, w.K, Wg=host["Wg"], **kw)
     dt = time.perf_counter() - t0
     R = int((f["perm"]["row_of_slot"] >= 0).sum())
     flops = 18.0 * R * w.D * w.F
+    what = "all" if T == w.T else f"the first {T} of"
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"float64 oracle forward+backward on the first {T} of {w.T} tokens "
-                      f"({R} routed rows, all {w.E} experts) of the same workload; "
-                      f"{dt:.1f} s wall"}
+            "kind": "oracle", "cpu": cpu_model(),
+            "sample": f"float64 oracle forward+backward on {what} {w.T} tokens ({R} routed "
+                      f"rows, all {w.E} experts) of the same workload; {dt:.1f} s wall"}
 
 
-def main():
-    args = parse()
-    if args.traffic_summary:
-        traffic_summary(*args.traffic_summary)
-        return
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the library has no multi-GPU path)", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
+def measure(name: str, args, headline: bool) -> dict:
+    """Generate a workload on the GPU, time its step, then time each call."""
     import torch
     import moe_synth as ms
     import mixture_experts_grouped_top_amd as moe
 
-    moe.load()
-    w = ms.get_workload(args.workload)
+    w = ms.get_workload(name)
     dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
-    threads = min(16, len(os.sched_getaffinity(0)))
-    inp = gen_inputs(w, threads)
-    g = to_gpu(inp, dtype)
+    t0 = time.time()
+    g = ms.device_inputs(w, threads=min(16, len(os.sched_getaffinity(0))))
+    host = g.pop("host")
+    log(f"[bench] {name}: generated inputs in {time.time() - t0:.1f}s")
     g["wi"] = None
     if args.fused_wi:
         g["wi"] = torch.cat([g.pop("wi_0"), g.pop("wi_1")], dim=2).contiguous()
@@ -327,90 +344,146 @@ def main():
     def step():
         plan.forward(g["x"], g["wi_0"], g["wi_1"], g["wo"], Wg=g["Wg"], logits=g["logits"],
                      bias=g["bias"], wi=g["wi"])
-        plan.backward(g["dy"], g["x"], g["wi_0"], g["wi_1"], g["wo"], Wg=g["Wg"], bias=g["bias"],
-                      wi=g["wi"])
+        plan.backward(g["dy"], g["x"], g["wi_0"], g["wi_1"], g["wo"], Wg=g["Wg"],
+                      bias=g["bias"], wi=g["wi"])
 
-    # one untimed step to learn the kept row count (dropping) for the flop count
+    # one untimed step to read back the routed counts (flops and bytes labels)
     step()
     torch.cuda.synchronize()
-    R = int(plan.idx["counts"].sum().item())
+    counts = plan.idx["counts"]
+    R = int(counts.sum().item())
     plan.kept_rows_override = R
     plan.padded_rows_override = int(plan.idx["group_offsets"][-1].item())
+    plan.nonempty_groups_override = int((counts > 0).sum().item())
     for _ in range(max(0, args.warmup - 1)):
         step()
-    rec = LaunchRecorder()
-    if not args.no_kernel_events:
-        plan.recorder = rec
     torch.cuda.synchronize()
+
+    # pass 1: the step time, nothing but the path's own launches in the stream
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    # no cyclic garbage collection inside the timed region (as timeit does):
-    # a collection pass stalls the launching thread for tens of milliseconds
     gc.collect()
-    gc.disable()
+    gc.disable()   # a collection pass stalls the launching thread (as timeit does)
     try:
-        rec.active = True
         start.record()
         for _ in range(args.steps):
             step()
         end.record()
         torch.cuda.synchronize()
-        rec.active = False
     finally:
         gc.enable()
     ms_step = start.elapsed_time(end) / args.steps
     err = int(plan.err.item())
     flops = 18.0 * R * w.D * w.F
     tflops = flops / (ms_step * 1e-3) / 1e12
-    log(f"[bench] {args.workload}: {ms_step:.3f} ms/step, {tflops:.1f} TFLOP/s, R={R}, err={err}")
+    log(f"[bench] {name}: {ms_step:.3f} ms/step, {tflops:.1f} TFLOP/s, R={R}, "
+        f"padded rows={plan.padded_rows}, non-empty experts={plan.nonempty_groups}, err={err}")
 
-    kernels = rec.summary()
+    # pass 2: every expert GEMM and memory-bound call bracketed by events,
+    # each after a cache-evicting scratch write
+    kernels = {}
+    if not args.no_kernel_events and args.kernel_steps > 0:
+        scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        rec = LaunchRecorder(flush=scratch)
+        plan.recorder = rec
+        gc.collect()
+        gc.disable()
+        try:
+            rec.active = True
+            for _ in range(args.kernel_steps):
+                step()
+            torch.cuda.synchronize()
+            rec.active = False
+        finally:
+            gc.enable()
+        plan.recorder = None
+        kernels = rec.summary(peak)
+        del scratch
     roofline = None
-    gemm = {k: v for k, v in kernels.items() if v["flops"] > 0}
-    if gemm:
-        kind = max(gemm, key=lambda k: gemm[k]["ms"])
-        k = gemm[kind]
-        ach = k["tflops"]
+    if kernels:
+        kind = max(kernels, key=lambda k: kernels[k]["ms"])
+        k = kernels[kind]
+        if k["bound"] == "mfma":
+            ach, pk, unit = k["tflops"], peak, "TFLOP/s"
+        else:
+            ach, pk, unit = k["gbs"], PEAK_HBM_GBS, "GB/s"
         plain = not (args.fused_wi or args.fp8)
-        traffic = traffic_from_profiles(kind, args.workload) if plain else None
-        label = KERNEL_NAME.get(kind, kind) if args.workload == "mixtral" and plain else kind
-        roofline = {"bound": "mfma", "kernel": label,
-                    "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": traffic,
+        roofline = {"bound": k["bound"], "kind": kind,
+                    "kernel": KERNEL_NAME.get(name, {}).get(kind, kind) if plain else kind,
+                    "achieved": round(ach, 2), "peak": pk, "unit": unit,
+                    "frac": round(ach / pk, 4),
+                    "traffic": traffic_for(name, kind) if plain else None,
                     "avg_launch_ms": round(k["avg_ms"], 4),
-                    "flops_per_launch": k["flops"] / k["launches"]}
+                    "flops_per_launch": k["flops"] / k["launches"],
+                    "algorithmic_bytes_per_launch": round(k["bytes"] / k["launches"])}
     for kk, v in kernels.items():
-        rate = (f"{v['tflops']:.1f} TFLOP/s" if v["flops"] else
-                f"{v['gbs']:.0f} GB/s ({100 * v['gbs'] / PEAK_HBM_GBS:.0f}% of HBM)")
-        log(f"[bench]   {kk:12s} {v['launches']:4d} launches  avg {v['avg_ms']:.3f} ms  {rate}")
-    cpu = None
-    if not args.no_cpu_baseline:
-        t0 = time.time()
-        cpu = cpu_baseline(w, inp, args.cpu_tokens)
-        log(f"[bench] cpu baseline: {cpu} ({time.time() - t0:.1f}s)")
-
-    out = {
-        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("fp8 e4m3/e5m2 GEMM operands, bf16 activations" if args.fp8 else
-                  "bf16" if dtype == torch.bfloat16 else "f32"),
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights; no dataset)",
+        log(f"[bench]   {kk:18s} {v['launches']:3d} launches  avg {v['avg_ms']:.3f} ms  "
+            f"{v['tflops']:7.1f} TFLOP/s  {v['gbs']:6.0f} GB/s  bound {v['bound']} "
+            f"({100 * v['frac']:.0f}% of it)")
+    rec_out = {
+        "ms_per_step": round(ms_step, 4), "tflops": round(tflops, 3),
+        "mfma_peak_frac": round(tflops / peak, 4), "device_error_flags": err, "dtype": w.dtype,
         "config": {"workload": w.name, "tokens": w.T, "d_model": w.D, "d_ff": w.F,
                    "experts": w.E, "top_k": w.K, "score": w.score, "renorm": w.renorm,
                    "align_size": w.align, "capacity": w.capacity, "chunks": w.n_chunks,
-                   "fused_wi": bool(args.fused_wi), "fp8": bool(args.fp8), "routed_rows": R},
-        "mfma_peak_frac": round(tflops / peak, 4),
+                   "fused_wi": bool(args.fused_wi), "fp8": bool(args.fp8), "routed_rows": R,
+                   "padded_rows": plan.padded_rows, "nonempty_experts": plan.nonempty_groups},
         "roofline": roofline,
-        "cpu_baseline": cpu,
-        "device_error_flags": err,
-        "kernels": {k: ({"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
-                         "tflops": round(v["tflops"], 2)} if v["flops"] else
-                        {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
+        "kernels": {kk: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
+                         "tflops": round(v["tflops"], 2),
                          "algorithmic_bytes": int(v["bytes"] / v["launches"]),
-                         "gbs": round(v["gbs"], 1),
-                         "hbm_frac": round(v["gbs"] / PEAK_HBM_GBS, 4)})
-                    for k, v in kernels.items()},
+                         "gbs": round(v["gbs"], 1), "bound": v["bound"],
+                         "roofline_frac": round(v["frac"], 4),
+                         "traffic": traffic_for(name, kk)}
+                    for kk, v in kernels.items()},
+    }
+    del plan, g
+    gc.collect()
+    torch.cuda.empty_cache()
+    if headline and not args.no_cpu_baseline:
+        t1 = time.time()
+        rec_out["cpu_baseline"] = cpu_baseline(w, host, args.cpu_tokens)
+        log(f"[bench] cpu baseline: {rec_out['cpu_baseline']} ({time.time() - t1:.1f}s)")
+    return rec_out
+
+
+def main():
+    args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import mixture_experts_grouped_top_amd as moe
+    moe.load()
+    head = measure(args.workload, args, headline=True)
+    extras = {}
+    for name in [n for n in args.extra_workloads.split(",") if n and n != args.workload]:
+        extras[name] = measure(name, args, headline=False)
+        extras[name]["cpu_baseline"] = None
+        extras[name]["cpu_baseline_note"] = (
+            "not run: the oracle's per-expert float64 weights alone (256 experts x 3 x "
+            "7168 x 2048) take minutes to form on the host; the headline workload's "
+            "baseline is the one reported")
+    out = {
+        "metric": METRIC, "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": ("fp8 e4m3/e5m2 GEMM operands, bf16 activations" if args.fp8 else
+                  head["dtype"]),
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights; no dataset)",
+        "config": head["config"],
+        "mfma_peak_frac": head["mfma_peak_frac"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head.get("cpu_baseline"),
+        "device_error_flags": head["device_error_flags"],
+        "kernels": head["kernels"],
+        "workloads": extras,
     }
     print(json.dumps(out), flush=True)
 

@@ -279,6 +279,28 @@ int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t ld_rhs,
              int64_t out_group_stride, int out_dtype, int accumulate, int32_t* err,
              void* stream);
 
+/* Workspace bytes moe_router_bwd needs (256-byte aligned device memory). */
+size_t moe_router_bwd_workspace(int64_t T, int64_t D, int E);
+
+/* moe_router_bwd: backward of the router GEMM logits = x . Wg (the gate
+ * projection of the [TE-MoE] block; [MT-ES] review: [B, S, E] ->
+ * [B, S, num_exp]), with the float32 d_logits of moe_route_bwd /
+ * moe_aux_loss_bwd:
+ *     d_Wg  = x^T . d_logits               [D, E] float32, fully written
+ *     dx  (+)= d_logits . Wg^T             [T, D] in dx_dtype
+ *   x [T, D] and Wg [D, E] contiguous bf16; d_logits [T, E] contiguous
+ *   float32; dx contiguous, added to when accumulate_dx != 0 (the token
+ *   gradient of the expert path is already there).  The products are those
+ *   of float32 arithmetic: d_logits is split exactly into three bf16 planes
+ *   (hi + mid + lo == d_logits) that the bf16 MFMA GEMMs contract with x and
+ *   with three copies of Wg, accumulating in float32; d_Wg's per-block
+ *   partial sums are added in a fixed order (deterministic).  Requires
+ *   D a multiple of 8, 1 <= E <= 1024, 16-byte aligned x, Wg, dx.
+ */
+int moe_router_bwd(const void* x, const void* Wg, const float* d_logits, int64_t T, int64_t D,
+                   int E, float* d_Wg, void* dx, int dx_dtype, int accumulate_dx,
+                   void* workspace, size_t ws_bytes, int32_t* err, void* stream);
+
 /* Workspace bytes moe_group_sum needs: (ceil(M / 256) + G) * N float32
  * partial rows (16-byte aligned device memory). */
 size_t moe_group_sum_workspace(int64_t M, int G, int64_t N);

@@ -12,7 +12,8 @@ from ._binding import (MOE_BF16, MOE_BIAS_LOGIT, MOE_BIAS_SELECT, MOE_DERR_EXPER
                        SIGNATURES, MoeError, load, moe_aux_loss, moe_aux_loss_bwd,
                        moe_aux_loss_workspace, moe_combine, moe_combine_bwd, moe_gmm, moe_gmm_swiglu,
                        moe_gmm_swiglu_bwd,
-                       moe_group_sum, moe_group_sum_workspace, ABI_VERSION,
+                       moe_group_sum, moe_group_sum_workspace, moe_router_bwd,
+                       moe_router_bwd_workspace, ABI_VERSION,
                        MOE_FP8_E4M3, MOE_FP8_E5M2, moe_fp8_scale_workspace, moe_fp8_amax_scale,
                        moe_fp8_padded_rows, moe_fp8_quantize, moe_gmm_fp8, moe_tgmm_fp8,
                        moe_permute, moe_permute_bwd, moe_permute_workspace, moe_route,
@@ -25,7 +26,8 @@ __all__ = [
     "moe_aux_loss_workspace", "moe_aux_loss", "moe_aux_loss_bwd", "MOE_BIAS_LOGIT",
     "MOE_BIAS_SELECT",
     "moe_permute_workspace", "moe_permute", "moe_permute_bwd", "moe_gmm", "moe_gmm_swiglu", "moe_gmm_swiglu_bwd", "moe_tgmm",
-    "moe_group_sum_workspace", "moe_group_sum", "ABI_VERSION", "MOE_FP8_E4M3", "MOE_FP8_E5M2",
+    "moe_group_sum_workspace", "moe_group_sum", "moe_router_bwd", "moe_router_bwd_workspace",
+    "ABI_VERSION", "MOE_FP8_E4M3", "MOE_FP8_E5M2",
     "moe_fp8_scale_workspace", "moe_fp8_amax_scale", "moe_fp8_padded_rows", "moe_fp8_quantize",
     "moe_gmm_fp8", "moe_tgmm_fp8",
     "moe_swiglu", "moe_swiglu_bwd", "moe_combine", "moe_combine_bwd", "MoEPlan", "MoEShape",

@@ -22,7 +22,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
 MOE_FP8_E4M3, MOE_FP8_E5M2 = 0, 1
-ABI_VERSION = 9   # moe_abi_version() of the library these signatures describe
+ABI_VERSION = 10  # moe_abi_version() of the library these signatures describe
 
 # Entry points (name -> (restype, argtypes)); must match include/moe.h.
 _P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -48,6 +48,8 @@ SIGNATURES = {
                                 _L, _L, _P, _P]),
     "moe_tgmm": (_I, [_P, _L, _P, _L, _P, _P, _I, _L, _L, _L, _I, _P, _L, _L, _I, _I, _P, _P]),
     "moe_group_sum_workspace": (_S, [_L, _I, _L]),
+    "moe_router_bwd_workspace": (_S, [_L, _L, _I]),
+    "moe_router_bwd": (_I, [_P, _P, _P, _L, _L, _I, _P, _P, _I, _I, _P, _S, _P, _P]),
     "moe_group_sum": (_I, [_P, _L, _I, _P, _P, _I, _L, _L, _P, _I, _I, _P, _S, _P, _P]),
     "moe_fp8_scale_workspace": (_S, [_L, _L, _I]),
     "moe_fp8_amax_scale": (_I, [_P, _L, _I, _L, _L, _I, _I, _P, _P, _S, _P]),
@@ -138,6 +140,17 @@ def _rowmajor(t: torch.Tensor, name: str):
 def _contig(t: torch.Tensor, name: str):
     if not t.is_contiguous():
         raise MoeError(f"{name} must be contiguous")
+
+
+def _i32vec(t: Optional[torch.Tensor], n: int, name: str, optional: bool = False):
+    """A contiguous int32 vector of n entries (group sizes, valid rows)."""
+    if t is None:
+        if optional:
+            return
+        raise MoeError(f"{name} is required")
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.dim() != 1 or t.numel() != n:
+        raise MoeError(f"{name} must be a contiguous int32 vector of {n} entries "
+                       f"(got {t.dtype}, shape {tuple(t.shape)})")
 
 
 # ----------------------------------------------------------------- routing
@@ -304,8 +317,8 @@ def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: 
     N = rhs.shape[1] if trans_rhs else rhs.shape[2]
     if (rhs.shape[2] if trans_rhs else rhs.shape[1]) != Kd:
         raise MoeError("contracting dimensions differ")
-    if group_sizes.numel() != G:
-        raise MoeError("group_sizes must have one entry per rhs group")
+    _i32vec(group_sizes, G, "group_sizes")
+    _i32vec(valid_rows, G, "valid_rows", optional=True)
     if lhs.dtype != rhs.dtype:
         raise MoeError("lhs and rhs dtypes differ")
     if bias is not None:
@@ -316,6 +329,10 @@ def moe_gmm(lhs, rhs, group_sizes, trans_rhs: bool = False, out=None, rows_out: 
         M_out = M_lhs if rows_out is None else rows_out
         odt = lhs.dtype if out_dtype is None else out_dtype
         out = torch.empty((M_out, N), dtype=odt, device=lhs.device)
+    if out.dim() != 2 or out.shape[1] != N:
+        raise MoeError(f"out must be [rows, {N}] (got {tuple(out.shape)})")
+    if out_dtype is not None and out.dtype != out_dtype:
+        raise MoeError("out does not have out_dtype")
     M_out = out.shape[0]
     ld_out = _rowmajor(out, "out")
     _check(load().moe_gmm(_ptr(lhs), M_lhs, ld_lhs, _ptr(rhs), rhs.stride(1), rhs.stride(0),
@@ -342,8 +359,8 @@ def moe_gmm_swiglu(lhs, wi, group_sizes, act=None, h=None, rows_out: Optional[in
     if F2 % 2:
         raise MoeError("wi must have 2F columns")
     F = F2 // 2
-    if group_sizes.numel() != G:
-        raise MoeError("group_sizes must have one entry per rhs group")
+    _i32vec(group_sizes, G, "group_sizes")
+    _i32vec(valid_rows, G, "valid_rows", optional=True)
     if lhs.dtype != wi.dtype:
         raise MoeError("lhs and wi dtypes differ")
     if bias is not None:
@@ -355,8 +372,10 @@ def moe_gmm_swiglu(lhs, wi, group_sizes, act=None, h=None, rows_out: Optional[in
         act = torch.empty((M_out, F), dtype=lhs.dtype, device=lhs.device)
     if h is None and write_h:
         h = torch.empty((M_out, F2), dtype=lhs.dtype, device=lhs.device)
-    if act.shape[0] != M_out or (h is not None and h.shape[0] != M_out):
-        raise MoeError("h and act must have rows_out rows")
+    if act.dim() != 2 or act.shape[0] != M_out or act.shape[1] != F:
+        raise MoeError("act must be [rows_out, F]")
+    if h is not None and (h.dim() != 2 or h.shape[0] != M_out or h.shape[1] != F2):
+        raise MoeError("h must be [rows_out, 2F]")
     if act.dtype != torch.bfloat16 or (h is not None and h.dtype != torch.bfloat16):
         raise MoeError("h and act must be bfloat16")
     ld_act = _rowmajor(act, "act")
@@ -381,8 +400,8 @@ def moe_gmm_swiglu_bwd(d_y, wo, group_sizes, h0, h1, d_h0=None, d_h1=None,
     G, F, K2 = wo.shape
     if K2 != Kd:
         raise MoeError("contracting dimensions differ")
-    if group_sizes.numel() != G:
-        raise MoeError("group_sizes must have one entry per rhs group")
+    _i32vec(group_sizes, G, "group_sizes")
+    _i32vec(valid_rows, G, "valid_rows", optional=True)
     if d_y.dtype != wo.dtype:
         raise MoeError("d_y and wo dtypes differ")
     M_out = M_lhs if rows_out is None else rows_out
@@ -415,20 +434,66 @@ def moe_tgmm(lhs, rhs, group_sizes, out=None, out_dtype=None, accumulate: bool =
     M2, N = rhs.shape
     if M2 != M:
         raise MoeError("lhs and rhs row counts differ")
+    if lhs.dtype != rhs.dtype:
+        raise MoeError("lhs and rhs dtypes differ")
     G = group_sizes.numel()
+    _i32vec(group_sizes, G, "group_sizes")
+    _i32vec(valid_rows, G, "valid_rows", optional=True)
     if out is None:
         odt = lhs.dtype if out_dtype is None else out_dtype
         out = torch.empty((G, Kd, N), dtype=odt, device=lhs.device)
-    if out.dim() != 3 or out.stride(2) != 1 or out.shape[0] != G:
-        raise MoeError("out must be [G, K, N] with unit last stride")
-    if valid_rows is not None and valid_rows.numel() != G:
-        raise MoeError("valid_rows must have one entry per group")
+    if out.dim() != 3 or out.stride(2) != 1 or tuple(out.shape) != (G, Kd, N):
+        raise MoeError(f"out must be [{G}, {Kd}, {N}] with unit last stride "
+                       f"(got {tuple(out.shape)})")
+    if out_dtype is not None and out.dtype != out_dtype:
+        raise MoeError("out does not have out_dtype")
     _check(load().moe_tgmm(_ptr(lhs), _rowmajor(lhs, "lhs"), _ptr(rhs), _rowmajor(rhs, "rhs"),
                            _ptr(group_sizes), _ptr(valid_rows), G, M, Kd, N, _dtype_code(lhs),
                            _ptr(out),
                            out.stride(1), out.stride(0), _dtype_code(out), int(bool(accumulate)),
                            _ptr(err), _stream(stream)), "moe_tgmm")
     return out
+
+
+def moe_router_bwd_workspace(T: int, D: int, E: int) -> int:
+    return load().moe_router_bwd_workspace(T, D, E)
+
+
+def moe_router_bwd(x, Wg, d_logits, d_Wg=None, dx=None, accumulate_dx: bool = False,
+                   dx_dtype=None, workspace=None, err=None, stream=None):
+    """Router-GEMM backward: d_Wg = x^T . d_logits [D, E] float32 and
+    dx (+)= d_logits . Wg^T [T, D] (x [T, D], Wg [D, E] bf16; d_logits
+    [T, E] float32; all contiguous).  Returns (d_Wg, dx)."""
+    T, D = x.shape
+    D2, E = Wg.shape
+    if D2 != D or tuple(d_logits.shape) != (T, E):
+        raise MoeError("x [T, D], Wg [D, E] and d_logits [T, E] do not match")
+    if x.dtype != torch.bfloat16 or Wg.dtype != torch.bfloat16:
+        raise MoeError("x and Wg must be bfloat16")
+    if d_logits.dtype != torch.float32:
+        raise MoeError("d_logits must be float32")
+    for t, n in ((x, "x"), (Wg, "Wg"), (d_logits, "d_logits")):
+        _contig(t, n)
+    if d_Wg is None:
+        d_Wg = torch.empty((D, E), dtype=torch.float32, device=x.device)
+    if tuple(d_Wg.shape) != (D, E) or d_Wg.dtype != torch.float32:
+        raise MoeError("d_Wg must be [D, E] float32")
+    _contig(d_Wg, "d_Wg")
+    if dx is None:
+        if accumulate_dx:
+            raise MoeError("accumulate_dx needs dx")
+        dx = torch.empty((T, D), dtype=x.dtype if dx_dtype is None else dx_dtype, device=x.device)
+    if tuple(dx.shape) != (T, D):
+        raise MoeError("dx must be [T, D]")
+    _contig(dx, "dx")
+    ws_bytes = moe_router_bwd_workspace(T, D, E)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    _check(load().moe_router_bwd(_ptr(x), _ptr(Wg), _ptr(d_logits), T, D, E, _ptr(d_Wg),
+                                 _ptr(dx), _dtype_code(dx), int(bool(accumulate_dx)),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _ptr(err), _stream(stream)), "moe_router_bwd")
+    return d_Wg, dx
 
 
 def moe_group_sum_workspace(M: int, G: int, N: int) -> int:
@@ -446,8 +511,8 @@ def moe_group_sum(x, group_sizes, out=None, out_dtype=torch.float32, accumulate:
     _contig(out, "out")
     if tuple(out.shape) != (G, N):
         raise MoeError("out must be [G, N]")
-    if valid_rows is not None and valid_rows.numel() != G:
-        raise MoeError("valid_rows must have one entry per group")
+    _i32vec(group_sizes, G, "group_sizes")
+    _i32vec(valid_rows, G, "valid_rows", optional=True)
     ws_bytes = moe_group_sum_workspace(M, G, N)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)

@@ -121,7 +121,7 @@ class MoEPlan:
             self.d_h1 = torch.empty((self.rows, s.F), **act)
         self.d_x_sorted = torch.empty((self.rows, s.D), **act)
         self.dx = torch.empty((s.T, s.D), **act)
-        self.d_logits = torch.empty((s.T, s.E), **act)
+        self.d_logits = torch.empty((s.T, s.E), **f32)
         if s.fused_wi:
             self.d_wi = torch.empty((s.E, s.D, 2 * s.F), **act)
             self.d_wi_0, self.d_wi_1 = self.d_wi[:, :, :s.F], self.d_wi[:, :, s.F:]
@@ -142,22 +142,12 @@ class MoEPlan:
                 dtype=torch.uint8, device=dev)
         if s.fp8:
             self._init_fp8(dev)
-        # router weight gradient kept in float32 (a [D, E] reduction over all tokens).
-        # With few output tiles (E is narrow) the token rows are split into
-        # n_split blocks, each a tgmm group with its own float32 partial, and the
-        # partials are added in block order (group sum), so that the reduction
-        # spreads over the chip instead of a few workgroups.
+        # router GEMM backward in float32 (d_logits is float32; its products
+        # with x and Wg are exact-split bf16 MFMA contractions)
         self.d_Wg = torch.empty((1, s.D, s.E), **f32) if router else None
-        self.n_split = max(1, min(16, s.T // 512)) if router else 1
-        if self.n_split > 1:
-            per = s.T // self.n_split
-            sizes = [per] * (self.n_split - 1) + [s.T - per * (self.n_split - 1)]
-            self.gs_split = torch.tensor(sizes, **i32)
-            self.gs_one = torch.tensor([self.n_split], **i32)
-            self.d_Wg_part = torch.empty((self.n_split, s.D, s.E), **f32)
-            self.split_ws = torch.empty(
-                max(B.moe_group_sum_workspace(self.n_split, 1, s.D * s.E), 256),
-                dtype=torch.uint8, device=dev)
+        if router and s.dtype == torch.bfloat16:
+            self.router_ws = torch.empty(max(B.moe_router_bwd_workspace(s.T, s.D, s.E), 256),
+                                         dtype=torch.uint8, device=dev)
         self.recorder = None   # optional callable(kind, flops, bytes) -> context manager
 
     def _init_fp8(self, dev):
@@ -214,7 +204,7 @@ class MoEPlan:
         xq, _, sx = q["x"]
         for name, h in (("wi_0", self.h0), ("wi_1", self.h1)):
             _, wt, sw = q[name]
-            with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+            with self._rec("gmm_nn", 2.0 * R * s.D * s.F, self._gb("gmm", s.D, s.F, in_b=1)):
                 B.moe_gmm_fp8(xq, "e4m3", sx[2], wt, "e4m3", sw[2], gs, valid_rows=self.vrows, out=h, bias=mb.get(name),
                               err=self.err, stream=stream)
         with self._rec("swiglu", nbytes=self._bytes().get("swiglu", 0) if self.recorder else 0):
@@ -222,7 +212,7 @@ class MoEPlan:
         self._quant("act", self.act, "e4m3", stream)
         aq, _, sa = q["act"]
         _, wt, sw = q["wo"]
-        with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+        with self._rec("gmm_nn", 2.0 * R * s.D * s.F, self._gb("gmm", s.F, s.D, in_b=1)):
             B.moe_gmm_fp8(aq, "e4m3", sa[2], wt, "e4m3", sw[2], gs, valid_rows=self.vact, out=self.y_sorted,
                           bias=mb.get("wo"), err=self.err, stream=stream)
 
@@ -232,11 +222,11 @@ class MoEPlan:
         self._quant("d_y_sorted", self.d_y_sorted, "e5m2", stream)
         dq, dqt, sd = q["d_y_sorted"]
         wor, _, swo = q["wo"]
-        with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+        with self._rec("gmm_nt", 2.0 * R * s.D * s.F, self._gb("gmm", s.D, s.F, in_b=1)):
             B.moe_gmm_fp8(dq, "e5m2", sd[2], wor, "e4m3", swo[2], gs, valid_rows=self.vrows, out=self.d_act, err=self.err,
                           stream=stream)
         _, aqt, sa = q["act"]
-        with self._rec("tgmm", 2.0 * R * s.D * s.F):
+        with self._rec("tgmm", 2.0 * R * s.D * s.F, self._gb("tgmm", s.F, s.D, in_b=1)):
             B.moe_tgmm_fp8(aqt, "e4m3", sa[2], dqt, "e5m2", sd[2], gs, self.rows, out=self.d_wo,
                            valid_rows=cnt, err=self.err, stream=stream)
         with self._rec("swiglu_bwd", nbytes=self._bytes().get("swiglu_bwd", 0) if self.recorder else 0):
@@ -248,10 +238,11 @@ class MoEPlan:
             self._quant(gname, dh, "e5m2", stream)
             hq, hqt, sh = q[gname]
             wr, _, sw = q[wname]
-            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+            with self._rec("gmm_nt", 2.0 * R * s.D * s.F,
+                           self._gb("gmm", s.F, s.D, in_b=1, rd_out=i > 0)):
                 B.moe_gmm_fp8(hq, "e5m2", sh[2], wr, "e4m3", sw[2], gs, valid_rows=self.vrows, out=self.d_x_sorted,
                               accumulate=i > 0, err=self.err, stream=stream)
-            with self._rec("tgmm", 2.0 * R * s.D * s.F):
+            with self._rec("tgmm", 2.0 * R * s.D * s.F, self._gb("tgmm", s.D, s.F, in_b=1)):
                 B.moe_tgmm_fp8(xqt, "e4m3", sx[2], hqt, "e5m2", sh[2], gs, self.rows, out=dw,
                                valid_rows=cnt, err=self.err, stream=stream)
 
@@ -275,10 +266,14 @@ class MoEPlan:
     def vact(self):
         return None if self.s.mlp_bias else self.idx["counts"]
 
-    # Routed rows the expert GEMMs must process (the algorithmic work); set
-    # by the caller when dropping makes it smaller than T*K (it is only used
-    # to label recorded launches with their flops).
+    # Counts of the routed data, set by a caller that has read them back from
+    # the device (kept routed rows, rows of the groups including align
+    # padding, non-empty groups); they only label recorded launches with
+    # their algorithmic flops and bytes.  Defaults: no dropping, no padding,
+    # every group non-empty.
     kept_rows_override: Optional[int] = None
+    padded_rows_override: Optional[int] = None
+    nonempty_groups_override: Optional[int] = None
 
     @property
     def kept_rows(self) -> int:
@@ -286,13 +281,37 @@ class MoEPlan:
             return self.kept_rows_override
         return self.s.T * self.s.K
 
-    # Rows of the sorted buffers that belong to groups (kept rows plus
-    # align_size padding); only used to label recorded launches.
-    padded_rows_override: Optional[int] = None
-
     @property
     def padded_rows(self) -> int:
         return self.rows if self.padded_rows_override is None else self.padded_rows_override
+
+    @property
+    def nonempty_groups(self) -> int:
+        return self.s.E if self.nonempty_groups_override is None else self.nonempty_groups_override
+
+    @property
+    def _eb(self) -> int:
+        return torch.finfo(self.s.dtype).bits // 8
+
+    def _gb(self, kind: str, K: int, N: int, out_b: Optional[int] = None, in_b: Optional[int] = None,
+            rd_out: bool = False, extra: int = 0) -> float:
+        """Algorithmic HBM bytes of one grouped-GEMM launch (0 unless
+        recording): each operand read once and the output written once.
+          gmm:  the kept lhs rows (padding rows are not read), the weights of
+                the non-empty groups, and every row of the groups written
+                (read too when accumulating);
+          tgmm: the kept rows of both operands and every group's [K, N]
+                block (empty groups are written as zero)."""
+        if self.recorder is None:
+            return 0.0
+        b = self._eb if in_b is None else in_b
+        ob = self._eb if out_b is None else out_b
+        R, Rp = self.kept_rows, self.padded_rows
+        if kind == "gmm":
+            n = R * K * b + self.nonempty_groups * K * N * b + Rp * N * ob * (2 if rd_out else 1)
+        else:
+            n = R * (K + N) * b + self.s.E * K * N * ob
+        return float(n + extra)
 
     def _bytes(self) -> dict:
         """Algorithmic HBM bytes of the memory-bound calls (each tensor read or
@@ -351,25 +370,27 @@ class MoEPlan:
             for i in range(s.n_chunks):
                 xs = self.x_sorted[:, i * c:(i + 1) * c]
                 last = i == s.n_chunks - 1   # the biases enter once, with the last chunk
-                with self._rec("gmm_up_chunk", 2.0 * R * c * s.F):
+                with self._rec("gmm_up_chunk", 2.0 * R * c * s.F,
+                               self._gb("gmm", c, s.F, out_b=4, rd_out=i > 0)):
                     B.moe_gmm(xs, wi_0[:, i * c:(i + 1) * c, :], gs, valid_rows=self.vrows, out=self.h0,
                               accumulate=i > 0, err=self.err, stream=stream,
                               bias=mb.get("wi_0") if last else None)
-                with self._rec("gmm_up_chunk", 2.0 * R * c * s.F):
+                with self._rec("gmm_up_chunk", 2.0 * R * c * s.F,
+                               self._gb("gmm", c, s.F, out_b=4, rd_out=i > 0)):
                     B.moe_gmm(xs, wi_1[:, i * c:(i + 1) * c, :], gs, valid_rows=self.vrows, out=self.h1,
                               accumulate=i > 0, err=self.err, stream=stream,
                               bias=mb.get("wi_1") if last else None)
         else:
-            with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+            with self._rec("gmm_nn", 2.0 * R * s.D * s.F, self._gb("gmm", s.D, s.F)):
                 B.moe_gmm(self.x_sorted, wi_0, gs, valid_rows=self.vrows, out=self.h0, err=self.err, stream=stream,
                           bias=mb.get("wi_0"))
-            with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+            with self._rec("gmm_nn", 2.0 * R * s.D * s.F, self._gb("gmm", s.D, s.F)):
                 B.moe_gmm(self.x_sorted, wi_1, gs, valid_rows=self.vrows, out=self.h1, err=self.err, stream=stream,
                           bias=mb.get("wi_1"))
         if not self.swiglu_epilogue:   # else the up-projection's epilogue wrote act
             with self._rec("swiglu", nbytes=nb.get("swiglu", 0)):
                 B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
-        with self._rec("gmm_nn", 2.0 * R * s.D * s.F):
+        with self._rec("gmm_nn", 2.0 * R * s.D * s.F, self._gb("gmm", s.F, s.D)):
             B.moe_gmm(self.act, wo, gs, valid_rows=self.vact, out=self.y_sorted, err=self.err, stream=stream,
                       bias=mb.get("wo"))
         with self._rec("combine", nbytes=nb.get("combine", 0)):
@@ -398,17 +419,19 @@ class MoEPlan:
         if s.n_chunks > 1:
             c = s.D // s.n_chunks
             for i in range(s.n_chunks):
-                with self._rec("gmm_up_chunk", 4.0 * R * c * s.F):
+                with self._rec("gmm_up_chunk", 4.0 * R * c * s.F,
+                               self._gb("gmm", c, 2 * s.F, out_b=4, rd_out=i > 0)):
                     B.moe_gmm(self.x_sorted[:, i * c:(i + 1) * c], wi[:, i * c:(i + 1) * c, :],
                               gs, valid_rows=self.vrows, out=self.h, accumulate=i > 0, err=self.err, stream=stream,
                               bias=b_wi if i == s.n_chunks - 1 else None)
         elif self.swiglu_epilogue:
             # one launch: h (kept for the backward) and act = SwiGLU(h) from its epilogue
-            with self._rec("gmm_nn", 4.0 * R * s.D * s.F):
+            with self._rec("gmm_nn", 4.0 * R * s.D * s.F,
+                           self._gb("gmm", s.D, 2 * s.F, extra=self.padded_rows * s.F * self._eb)):
                 B.moe_gmm_swiglu(self.x_sorted, wi, gs, act=self.act, h=self.h, valid_rows=self.vrows,
                                  bias=b_wi, err=self.err, stream=stream)
         else:
-            with self._rec("gmm_nn", 4.0 * R * s.D * s.F):
+            with self._rec("gmm_nn", 4.0 * R * s.D * s.F, self._gb("gmm", s.D, 2 * s.F)):
                 B.moe_gmm(self.x_sorted, wi, gs, valid_rows=self.vrows, out=self.h, err=self.err, stream=stream,
                           bias=b_wi)
 
@@ -438,15 +461,16 @@ class MoEPlan:
         if self.swiglu_bwd_epilogue:
             # d_act stays in registers: its GEMM's epilogue applies the SwiGLU
             # backward with h0, h1 and writes d_h0, d_h1
-            with self._rec("gmm_nt_swiglu_bwd", 2.0 * R * s.D * s.F):
+            with self._rec("gmm_nt_swiglu_bwd", 2.0 * R * s.D * s.F,
+                           self._gb("gmm", s.D, s.F, extra=3 * self.padded_rows * s.F * self._eb)):
                 B.moe_gmm_swiglu_bwd(self.d_y_sorted, wo, gs, self.h0, self.h1, d_h0=self.d_h0,
                                      d_h1=self.d_h1, valid_rows=self.vrows, err=self.err,
                                      stream=stream)
         else:
-            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+            with self._rec("gmm_nt", 2.0 * R * s.D * s.F, self._gb("gmm", s.D, s.F)):
                 B.moe_gmm(self.d_y_sorted, wo, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_act, err=self.err,
                           stream=stream)
-        with self._rec("tgmm", 2.0 * R * s.D * s.F):
+        with self._rec("tgmm", 2.0 * R * s.D * s.F, self._gb("tgmm", s.F, s.D)):
             # padding rows of each group (past its kept rows) are zero in
             # d_y_sorted and x_sorted: the weight gradients stop at counts
             B.moe_tgmm(self.act, self.d_y_sorted, gs, out=self.d_wo, err=self.err, stream=stream,
@@ -458,23 +482,23 @@ class MoEPlan:
         if s.fused_wi:
             # d_x_sorted = [d_h0 | d_h1] . [wi_0 | wi_1]^T in one contraction
             # over 2F; d_wi = x_sorted^T [d_h0 | d_h1] in one tgmm
-            with self._rec("gmm_nt", 4.0 * R * s.D * s.F):
+            with self._rec("gmm_nt", 4.0 * R * s.D * s.F, self._gb("gmm", 2 * s.F, s.D)):
                 B.moe_gmm(self.d_h, wi, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_x_sorted, err=self.err,
                           stream=stream)
-            with self._rec("tgmm", 4.0 * R * s.D * s.F):
+            with self._rec("tgmm", 4.0 * R * s.D * s.F, self._gb("tgmm", s.D, 2 * s.F)):
                 B.moe_tgmm(xs, self.d_h, gs, out=self.d_wi, err=self.err, stream=stream,
                            valid_rows=self.idx["counts"])
         else:
-            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+            with self._rec("gmm_nt", 2.0 * R * s.D * s.F, self._gb("gmm", s.F, s.D)):
                 B.moe_gmm(self.d_h0, wi_0, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_x_sorted, err=self.err,
                           stream=stream)
-            with self._rec("gmm_nt", 2.0 * R * s.D * s.F):
+            with self._rec("gmm_nt", 2.0 * R * s.D * s.F, self._gb("gmm", s.F, s.D, rd_out=True)):
                 B.moe_gmm(self.d_h1, wi_1, gs, valid_rows=self.vrows, trans_rhs=True, out=self.d_x_sorted,
                           accumulate=True, err=self.err, stream=stream)
-            with self._rec("tgmm", 2.0 * R * s.D * s.F):
+            with self._rec("tgmm", 2.0 * R * s.D * s.F, self._gb("tgmm", s.D, s.F)):
                 B.moe_tgmm(xs, self.d_h0, gs, out=self.d_wi_0, err=self.err, stream=stream,
                            valid_rows=self.idx["counts"])
-            with self._rec("tgmm", 2.0 * R * s.D * s.F):
+            with self._rec("tgmm", 2.0 * R * s.D * s.F, self._gb("tgmm", s.D, s.F)):
                 B.moe_tgmm(xs, self.d_h1, gs, out=self.d_wi_1, err=self.err, stream=stream,
                            valid_rows=self.idx["counts"])
 
@@ -508,16 +532,16 @@ class MoEPlan:
             B.moe_aux_loss_bwd(self.logits, self.aux_counts, s.K, s.aux_alpha, s.score,
                                d_logits=self.d_logits, accumulate=True, stream=stream)
         if Wg is not None and self.router:
-            if self.n_split > 1:
-                B.moe_tgmm(x, self.d_logits, self.gs_split, out=self.d_Wg_part, err=self.err,
-                           stream=stream)
-                B.moe_group_sum(self.d_Wg_part.view(self.n_split, -1), self.gs_one,
-                                out=self.d_Wg.view(1, -1), workspace=self.split_ws, err=self.err,
-                                stream=stream)
+            if s.dtype == torch.bfloat16:
+                B.moe_router_bwd(x, Wg, self.d_logits, d_Wg=self.d_Wg[0], dx=self.dx,
+                                 accumulate_dx=True, workspace=self.router_ws, err=self.err,
+                                 stream=stream)
             else:
-                B.moe_tgmm(x, self.d_logits, self.gs_T, out=self.d_Wg, err=self.err, stream=stream)
-            B.moe_gmm(self.d_logits, Wg.unsqueeze(0), self.gs_T, trans_rhs=True, out=self.dx,
-                      accumulate=True, err=self.err, stream=stream)
+                # float32 workloads: the float32 GEMM kernels take d_logits as is
+                B.moe_tgmm(x, self.d_logits, self.gs_T, out=self.d_Wg, err=self.err,
+                           stream=stream)
+                B.moe_gmm(self.d_logits, Wg.unsqueeze(0), self.gs_T, trans_rhs=True,
+                          out=self.dx, accumulate=True, err=self.err, stream=stream)
         return self.dx
 
     def expert_flops(self, kept_rows: Optional[int] = None) -> float:

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["abi.hip", "route.hip", "permute.hip", "swiglu.hip", "gmm.hip", "groupsum.hip", "fp8.hip"]
+SOURCES = ["abi.hip", "route.hip", "permute.hip", "swiglu.hip", "gmm.hip", "groupsum.hip", "fp8.hip",
+           "router_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

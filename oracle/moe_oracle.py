@@ -147,6 +147,31 @@ def route(logits, K: int, score: str = SOFTMAX, renorm: bool = True, bias=None,
     return ids.astype(np.int32), w
 
 
+def route_weights(logits, ids, score: str = SOFTMAX, renorm: bool = True, bias=None,
+                  bias_mode: str = LOGIT) -> np.ndarray:
+    """Routing weights of a given selection ids [T, K] (float64 [T, K]): the
+    weights ``route`` assigns once its experts are chosen.  The scores are
+    those of the float32 logits plus the bias for bias_mode "logit", of the
+    logits alone for "select" (the bias only moved the selection); softmax
+    over all E experts or the logistic function; the K selected scores,
+    divided by their sum when renorm is set (same pull request, fused top-K
+    router)."""
+    z = biased_logits_f32(logits, bias if bias_mode == LOGIT else None).astype(np.float64)
+    sel = np.asarray(ids, dtype=np.int64)
+    if score == SOFTMAX:
+        # softmax scores of the selected experts: exp(z_e - max) / sum_all
+        m = z.max(axis=1, keepdims=True)
+        num = np.exp(np.take_along_axis(z, sel, axis=1) - m)
+        sc = num / np.exp(z - m).sum(axis=1, keepdims=True)
+    elif score == SIGMOID:
+        sc = 1.0 / (1.0 + np.exp(-np.take_along_axis(z, sel, axis=1)))
+    else:
+        raise ValueError(score)
+    if renorm:
+        sc = sc / sc.sum(axis=1, keepdims=True)
+    return sc
+
+
 def route_bwd(logits, ids, d_w, score: str = SOFTMAX, renorm: bool = True, bias=None,
               bias_mode: str = LOGIT):
     """Gradient of the routing weights with respect to the router logits,

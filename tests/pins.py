@@ -122,6 +122,31 @@ def _py_scores(z_row, score):
     return [1.0 / (1.0 + math.exp(-v)) for v in z_row]
 
 
+def check_route_weights_of_given_ids(seed=11):
+    """Weights of an arbitrary (not top-K) selection, per token with the math
+    module: every score mode, with and without renorm, a logit bias that
+    enters the scores and a selection-only bias that does not."""
+    g = _rng(seed)
+    T, E, K = 20, 9, 3
+    z = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    bias = (g.standard_normal(E) * 0.4).astype(np.float32)
+    ids = np.stack([g.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    for score in ("softmax", "sigmoid"):
+        for renorm in (True, False):
+            for mode, b in (("logit", None), ("logit", bias), ("select", bias)):
+                w = oracle.route_weights(z, ids, score, renorm, b, mode)
+                for t in range(T):
+                    zz = [float(np.float32(z[t, e]) + (np.float32(b[e]) if b is not None and
+                                                      mode == "logit" else 0))
+                          for e in range(E)]
+                    p = _py_scores(zz, score)
+                    ws = [p[e] for e in ids[t]]
+                    if renorm:
+                        tot = sum(ws)
+                        ws = [v / tot for v in ws]
+                    np.testing.assert_allclose(w[t], ws, rtol=1e-12)
+
+
 def check_route_select_bias(seed=4):
     """Selection-only bias: the key is score + bias, the weights the plain
     scores of the selected experts.  Brute force per token, and with a zero

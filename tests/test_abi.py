@@ -42,7 +42,7 @@ def test_header_declares_the_abi():
                  "moe_aux_loss_bwd", "moe_group_sum_workspace", "moe_group_sum",
                  "moe_fp8_scale_workspace", "moe_fp8_amax_scale", "moe_fp8_padded_rows",
                  "moe_fp8_quantize", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gmm_swiglu",
-                 "moe_gmm_swiglu_bwd"]:
+                 "moe_gmm_swiglu_bwd", "moe_router_bwd", "moe_router_bwd_workspace"]:
         assert name in d, name
 
 
@@ -164,7 +164,53 @@ def test_argument_checks_return_before_launch(lib):
                            None, None) == -3
     assert lib.moe_permute(P, 1, 16, 64, P, 2, 4, 0, 0, 0, P, 32, P, P, P, P, P, None, 0,
                            None, None) == -5
+    # router backward: D not a multiple of 8, E too large, bad dx dtype, short workspace
+    W2 = ctypes.c_void_p(1 << 20)
+    ws = moe.moe_router_bwd_workspace(64, 64, 8)
+    assert ws >= 256 + 64 * 24 * 2 * 2
+    assert lib.moe_router_bwd(P, P, P, 64, 60, 8, P, P, 1, 1, W2, ws, None, None) == -1
+    assert lib.moe_router_bwd(P, P, P, 64, 64, 1025, P, P, 1, 1, W2, 1 << 30, None, None) == -1
+    assert lib.moe_router_bwd(P, P, P, 64, 64, 8, P, P, 7, 1, W2, ws, None, None) == -2
+    assert lib.moe_router_bwd(P, P, P, 64, 64, 8, P, P, 1, 1, W2, ws - 1, None, None) == -5
+    assert lib.moe_router_bwd(P, P, P, 64, 64, 8, P, P, 1, 1, ctypes.c_void_p(16), ws, None,
+                              None) == -5
     # combine: D not a multiple of 8
     assert lib.moe_combine(P, 1, 4, 12, 2, 8, P, P, P, None) == -1
     assert lib.moe_swiglu(P, P, 3, 4, 8, 8, P, 1, None) == -2
     assert lib.moe_swiglu(P, P, 1, 4, 16, 8, P, 1, None) == -1      # row stride below F
+
+
+def test_binding_rejects_bad_shapes_and_index_dtypes(lib):
+    """The binding checks shapes and index vectors before any pointer is
+    taken (CPU tensors: a check that passed would fail later on the device
+    check, with another message)."""
+    import torch
+    bf = torch.bfloat16
+    lhs = torch.zeros((64, 32), dtype=bf)
+    rhs = torch.zeros((2, 32, 48), dtype=bf)
+    gs = torch.tensor([30, 34], dtype=torch.int32)
+
+    def raises(match, fn, *a, **kw):
+        with pytest.raises(moe.MoeError, match=match):
+            fn(*a, **kw)
+
+    raises("group_sizes must be a contiguous int32", moe.moe_gmm, lhs, rhs, gs.long())
+    raises("group_sizes must be a contiguous int32", moe.moe_gmm, lhs, rhs, gs[:1])
+    raises("valid_rows must be a contiguous int32", moe.moe_gmm, lhs, rhs, gs,
+           valid_rows=torch.tensor([1, 2, 3], dtype=torch.int32))
+    raises("out must be", moe.moe_gmm, lhs, rhs, gs, out=torch.zeros((64, 40), dtype=bf))
+    raises("out must be", moe.moe_gmm, lhs, rhs, gs, out=torch.zeros((64, 48, 1), dtype=bf))
+    raises("out does not have out_dtype", moe.moe_gmm, lhs, rhs, gs,
+           out=torch.zeros((64, 48), dtype=bf), out_dtype=torch.float32)
+    x2 = torch.zeros((64, 48), dtype=bf)
+    raises("out must be", moe.moe_tgmm, lhs, x2, gs, out=torch.zeros((2, 32, 40), dtype=bf))
+    raises("out must be", moe.moe_tgmm, lhs, x2, gs, out=torch.zeros((3, 32, 48), dtype=bf))
+    raises("group_sizes must be a contiguous int32", moe.moe_tgmm, lhs, x2, gs.long())
+    raises("valid_rows must be a contiguous int32", moe.moe_tgmm, lhs, x2, gs,
+           valid_rows=gs.long())
+    raises("dtypes differ", moe.moe_tgmm, lhs, x2.float(), gs)
+    raises("group_sizes must be a contiguous int32", moe.moe_group_sum, x2, gs.long())
+    wi = torch.zeros((2, 32, 256), dtype=bf)
+    raises("act must be", moe.moe_gmm_swiglu, lhs, wi, gs, act=torch.zeros((64, 64), dtype=bf))
+    raises("h must be", moe.moe_gmm_swiglu, lhs, wi, gs, h=torch.zeros((64, 128), dtype=bf))
+    raises("group_sizes must be a contiguous int32", moe.moe_gmm_swiglu, lhs, wi, gs.long())

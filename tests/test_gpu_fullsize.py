@@ -182,7 +182,8 @@ def test_full_properties(full):
         dx_want += f64(plan.d_logits)[sample] @ f64(dev["Wg"]).T
         # router weight gradient: d_Wg = x^T d_logits (sampled columns)
         dW = f64(dev["x"]).T @ f64(plan.d_logits)
-        assert_close(f64(plan.d_Wg)[0], dW, TOL_GRAD, "d_Wg")
+        # float32 d_logits and exact-split products: float32 accuracy
+        assert_close(f64(plan.d_Wg)[0], dW, TOL_F32, "d_Wg")
     assert_close(f64(plan.dx)[sample], dx_want, TOL_GRAD, "dx")
     # routing gradient is supported on the selected experts (renormalised modes)
     if w.renorm:

@@ -18,6 +18,12 @@ MUTATIONS = {
     "tie_break_higher_id": (
         'order = np.argsort(-key, axis=1, kind="stable")',
         'order = key.shape[1] - 1 - np.argsort(-key[:, ::-1], axis=1, kind="stable")'),
+    "route_weights_renorm_over_all": (
+        "        sc = sc / sc.sum(axis=1, keepdims=True)\n    return sc",
+        "        sc = sc / np.exp(z - z.max(axis=1, keepdims=True)).sum(axis=1, keepdims=True)\n    return sc"),
+    "route_weights_select_bias_in_scores": (
+        "bias if bias_mode == LOGIT else None).astype(np.float64)\n    sel",
+        "bias).astype(np.float64)\n    sel"),
     "renorm_dropped": (
         "    if renorm:\n        w = w / w.sum(axis=1, keepdims=True)\n    return ids",
         "    return ids"),
