@@ -173,6 +173,29 @@ int moe_permute(const void* x, int dtype, int64_t T, int64_t D, const int32_t* t
                 int32_t* row_of_slot, int32_t* slot_of_row, void* workspace, size_t ws_bytes,
                 int32_t* err, void* stream);
 
+/* Scratch words (int32) of moe_permute_noalloc: 262144 (1 MiB per GPU). */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_WORDS 262144
+
+/* moe_permute_noalloc: moe_permute without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results
+ * and errors as moe_permute; it calls no allocating routine.  Its per-block
+ * expert counts live in a static device array of the library (one per GPU,
+ * held until the process ends), so it supports
+ * moe_permute_workspace(T, K, E) <= 4 * MOE_PERMUTE_NOALLOC_SCRATCH_WORDS
+ * bytes (ceil(T K / 1024) * E <= 262144; e.g. T K <= 1M slots with E = 256)
+ * and returns MOE_ERR_WORKSPACE beyond that.  Every call on one GPU shares
+ * that array: calls that may overlap on one GPU (different streams without
+ * ordering, several host threads) race and must be serialised by the
+ * caller.  No entry needs to start at zero (each call writes every entry
+ * it reads).
+ */
+int moe_permute_noalloc(const void* x, int dtype, int64_t T, int64_t D, const int32_t* topk_ids,
+                        int K, int E, int align, int capacity, int capacity_layout,
+                        void* x_sorted, int64_t rows, int32_t* counts, int32_t* group_sizes,
+                        int32_t* group_offsets, int32_t* row_of_slot, int32_t* slot_of_row,
+                        int32_t* err, void* stream);
+
 /* moe_permute_bwd: d_x[t] (+)= sum_j d_x_sorted[row_of_slot[t*K+j]] over kept
  * slots (adjoint of the row gather; the dispatch backward of [TE-MoE]).
  * accumulate != 0 adds into d_x.  d_x_sorted [rows, D], d_x [T, D], both in

@@ -22,7 +22,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
 MOE_FP8_E4M3, MOE_FP8_E5M2 = 0, 1
-ABI_VERSION = 10  # moe_abi_version() of the library these signatures describe
+ABI_VERSION = 11  # moe_abi_version() of the library these signatures describe
 
 # Entry points (name -> (restype, argtypes)); must match include/moe.h.
 _P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -39,6 +39,8 @@ SIGNATURES = {
     "moe_permute_workspace": (_S, [_L, _I, _I]),
     "moe_permute": (_I, [_P, _I, _L, _L, _P, _I, _I, _I, _I, _I, _P, _L, _P, _P, _P, _P, _P,
                          _P, _S, _P, _P]),
+    "moe_permute_noalloc": (_I, [_P, _I, _L, _L, _P, _I, _I, _I, _I, _I, _P, _L, _P, _P, _P, _P,
+                                 _P, _P, _P]),
     "moe_permute_bwd": (_I, [_P, _I, _L, _L, _I, _L, _P, _P, _I, _P]),
     "moe_gmm": (_I, [_P, _L, _L, _P, _L, _L, _I, _P, _P, _I, _L, _L, _I, _P, _P, _L, _L, _I, _I,
                      _P, _P]),
@@ -246,10 +248,12 @@ def moe_permute_workspace(T: int, K: int, E: int) -> int:
 
 def moe_permute(x, topk_ids, E: int, align: int = 0, capacity: int = 0,
                 capacity_layout: bool = False, rows: Optional[int] = None, x_sorted=None,
-                with_rows: bool = True, err=None, workspace=None, out=None, stream=None):
+                with_rows: bool = True, err=None, workspace=None, out=None, stream=None,
+                noalloc: bool = False):
     """Returns dict(x_sorted, counts, group_sizes, group_offsets, row_of_slot,
     slot_of_row).  ``rows`` defaults to moe_rows_bound(...); ``out`` may hold
-    preallocated index tensors under the same keys."""
+    preallocated index tensors under the same keys.  ``noalloc`` calls
+    moe_permute_noalloc (the library's static scratch, no workspace)."""
     T, K = topk_ids.shape
     dev = topk_ids.device
     if rows is None:
@@ -274,6 +278,15 @@ def moe_permute(x, topk_ids, E: int, align: int = 0, capacity: int = 0,
         assert x_sorted.shape[0] == rows and x_sorted.shape[1] == D
     else:
         x_sorted = None
+    if noalloc:
+        _check(load().moe_permute_noalloc(_ptr(x) if x_sorted is not None else None, dt, T, D,
+                                          _ptr(topk_ids), K, E, align, capacity,
+                                          int(bool(capacity_layout)), _ptr(x_sorted), rows,
+                                          _ptr(counts), _ptr(gsz), _ptr(goff), _ptr(ros),
+                                          _ptr(sor), _ptr(err), _stream(stream)),
+               "moe_permute_noalloc")
+        return dict(x_sorted=x_sorted, counts=counts, group_sizes=gsz, group_offsets=goff,
+                    row_of_slot=ros, slot_of_row=sor)
     ws_bytes = moe_permute_workspace(T, K, E)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

@@ -16,7 +16,16 @@
 //              row_of_slot and slot_of_row.
 //   4. scatter one wave per token: read x[token] once, write it to the row
 //              of each kept slot; padding rows are zeroed.
+#include <mutex>
+
 #include "common.h"
+
+// Scratch of moe_permute_noalloc: the per-block expert counts (int32) that
+// moe_permute keeps in its caller's workspace.  One copy per GPU, held until
+// the process ends.  Host code never passes this name to a kernel: it is a
+// host-side stand-in, and the device address comes from hipGetSymbolAddress
+// (scratch_address below).
+static __device__ __align__(256) int32_t scratch[MOE_PERMUTE_NOALLOC_SCRATCH_WORDS];
 
 namespace moe {
 namespace {
@@ -404,11 +413,16 @@ MOE_API size_t moe_permute_workspace(int64_t T, int K, int E) {
   return (bytes + 255) & ~static_cast<size_t>(255);
 }
 
-MOE_API int moe_permute(const void* x, int dtype, int64_t T, int64_t D, const int32_t* topk_ids,
-                        int K, int E, int align, int capacity, int capacity_layout,
-                        void* x_sorted, int64_t rows, int32_t* counts, int32_t* group_sizes,
-                        int32_t* group_offsets, int32_t* row_of_slot, int32_t* slot_of_row,
-                        void* workspace, size_t ws_bytes, int32_t* err, void* stream) {
+namespace moe {
+namespace {
+
+// Argument checks shared by both permute entry points (the workspace is
+// checked by each).
+int permute_check(const void* x, int dtype, int64_t T, int64_t D, const int32_t* topk_ids, int K,
+                  int E, int align, int capacity, int capacity_layout, const void* x_sorted,
+                  int64_t rows, const int32_t* counts, const int32_t* group_sizes,
+                  const int32_t* group_offsets, const int32_t* row_of_slot,
+                  const int32_t* slot_of_row) {
   if (T < 0 || D < 0 || K < 1 || K > 64 || E < 1 || E > kMaxE || align < 0 || capacity < 0)
     return MOE_ERR_ARG;
   if (capacity_layout && capacity <= 0) return MOE_ERR_ARG;
@@ -424,13 +438,19 @@ MOE_API int moe_permute(const void* x, int dtype, int64_t T, int64_t D, const in
     if ((T > 0 && !x) || (D * eb) % 16 || !aligned16(x) || !aligned16(x_sorted))
       return MOE_ERR_ARG;
   }
-  if (ws_bytes < moe_permute_workspace(T, K, E) || !workspace ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255))
-    return MOE_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  return MOE_OK;
+}
+
+// The four permute launches; blockcounts holds ceil(T K / kSlots) x E int32
+// (every entry is written by the hist pass before it is read).
+int permute_launch(const void* x, int dtype, int64_t T, int64_t D, const int32_t* topk_ids, int K,
+                   int E, int align, int capacity, int capacity_layout, void* x_sorted,
+                   int64_t rows, int32_t* counts, int32_t* group_sizes, int32_t* group_offsets,
+                   int32_t* row_of_slot, int32_t* slot_of_row, int32_t* blockcounts,
+                   int32_t* err, hipStream_t st) {
+  const int eb = elem_bytes(dtype);
   const int64_t TK = T * K;
   const int nb = static_cast<int>((TK + kSlots - 1) / kSlots);
-  int32_t* blockcounts = static_cast<int32_t*>(workspace);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   // at least one block, so that counts are zeroed and padding rows marked
@@ -454,6 +474,71 @@ MOE_API int moe_permute(const void* x, int dtype, int64_t T, int64_t D, const in
                        token_blocks);
   }
   return launch_status();
+}
+
+// Device address of `scratch` on the current device, taken once per device
+// (the same array lives at a different address on every GPU).
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64] = {};
+
+int scratch_address(int32_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return MOE_ERR_LAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MOE_ERR_LAUNCH;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  *out = static_cast<int32_t*>(g_scratch_addr[dev]);
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+MOE_API int moe_permute(const void* x, int dtype, int64_t T, int64_t D, const int32_t* topk_ids,
+                        int K, int E, int align, int capacity, int capacity_layout,
+                        void* x_sorted, int64_t rows, int32_t* counts, int32_t* group_sizes,
+                        int32_t* group_offsets, int32_t* row_of_slot, int32_t* slot_of_row,
+                        void* workspace, size_t ws_bytes, int32_t* err, void* stream) {
+  const int rc = permute_check(x, dtype, T, D, topk_ids, K, E, align, capacity, capacity_layout,
+                               x_sorted, rows, counts, group_sizes, group_offsets, row_of_slot,
+                               slot_of_row);
+  if (rc != MOE_OK) return rc;
+  if (ws_bytes < moe_permute_workspace(T, K, E) || !workspace ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return MOE_ERR_WORKSPACE;
+  return permute_launch(x, dtype, T, D, topk_ids, K, E, align, capacity, capacity_layout,
+                        x_sorted, rows, counts, group_sizes, group_offsets, row_of_slot,
+                        slot_of_row, static_cast<int32_t*>(workspace), err,
+                        static_cast<hipStream_t>(stream));
+}
+
+MOE_API int moe_permute_noalloc(const void* x, int dtype, int64_t T, int64_t D,
+                                const int32_t* topk_ids, int K, int E, int align, int capacity,
+                                int capacity_layout, void* x_sorted, int64_t rows,
+                                int32_t* counts, int32_t* group_sizes, int32_t* group_offsets,
+                                int32_t* row_of_slot, int32_t* slot_of_row, int32_t* err,
+                                void* stream) {
+  int rc = permute_check(x, dtype, T, D, topk_ids, K, E, align, capacity, capacity_layout,
+                         x_sorted, rows, counts, group_sizes, group_offsets, row_of_slot,
+                         slot_of_row);
+  if (rc != MOE_OK) return rc;
+  if (moe_permute_workspace(T, K, E) > sizeof(int32_t) * MOE_PERMUTE_NOALLOC_SCRATCH_WORDS)
+    return MOE_ERR_WORKSPACE;
+  int32_t* blockcounts = nullptr;
+  rc = scratch_address(&blockcounts);
+  if (rc != MOE_OK) return rc;
+  return permute_launch(x, dtype, T, D, topk_ids, K, E, align, capacity, capacity_layout,
+                        x_sorted, rows, counts, group_sizes, group_offsets, row_of_slot,
+                        slot_of_row, blockcounts, err, static_cast<hipStream_t>(stream));
 }
 
 // Slot batch of the token-centric kernels for top-K routing.

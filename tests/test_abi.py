@@ -42,7 +42,8 @@ def test_header_declares_the_abi():
                  "moe_aux_loss_bwd", "moe_group_sum_workspace", "moe_group_sum",
                  "moe_fp8_scale_workspace", "moe_fp8_amax_scale", "moe_fp8_padded_rows",
                  "moe_fp8_quantize", "moe_gmm_fp8", "moe_tgmm_fp8", "moe_gmm_swiglu",
-                 "moe_gmm_swiglu_bwd", "moe_router_bwd", "moe_router_bwd_workspace"]:
+                 "moe_gmm_swiglu_bwd", "moe_router_bwd", "moe_router_bwd_workspace",
+                 "moe_permute_noalloc"]:
         assert name in d, name
 
 
@@ -174,6 +175,11 @@ def test_argument_checks_return_before_launch(lib):
     assert lib.moe_router_bwd(P, P, P, 64, 64, 8, P, P, 1, 1, W2, ws - 1, None, None) == -5
     assert lib.moe_router_bwd(P, P, P, 64, 64, 8, P, P, 1, 1, ctypes.c_void_p(16), ws, None,
                               None) == -5
+    # permute without a workspace: past its static scratch (ceil(T K / 1024) E > 262144 words)
+    assert lib.moe_permute_noalloc(P, 1, 131073, 64, P, 8, 256, 0, 0, 0, P, 131073 * 8, P, P, P,
+                                   P, P, None, None) == -5
+    assert lib.moe_permute_noalloc(P, 1, 16, 64, P, 2, 4, 0, 0, 0, P, 31, P, P, P, P, P, None,
+                                   None) == -3
     # combine: D not a multiple of 8
     assert lib.moe_combine(P, 1, 4, 12, 2, 8, P, P, P, None) == -1
     assert lib.moe_swiglu(P, P, 3, 4, 8, 8, P, 1, None) == -2
