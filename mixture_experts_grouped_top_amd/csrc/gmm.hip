@@ -67,10 +67,10 @@ __device__ __forceinline__ void blocked_tile(int l, int mtiles, int ntiles, int&
 
 // Linear tile index of a persistent workgroup's it-th tile: the grid's
 // workgroups on XCD x (b % 8 == x) take a contiguous run of indices.
-__device__ __forceinline__ int64_t xcd_tile(int it) {
-  const int b = blockIdx.x, g = gridDim.x;
+__device__ __forceinline__ int64_t xcd_index(int it, int b, int g) {
   return static_cast<int64_t>(it) * g + (b & 7) * (g >> 3) + (b >> 3);
 }
+__device__ __forceinline__ int64_t xcd_tile(int it) { return xcd_index(it, blockIdx.x, gridDim.x); }
 
 template <typename TO>
 __device__ __forceinline__ void store_out(TO* p, float v, int accumulate) {
@@ -1142,16 +1142,59 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
   }
 }
 
+// Rows of group g that the weight-gradient contraction covers: its rows
+// (clipped to the buffer), or the first valid[g] of them.
+__device__ __forceinline__ int tgmm_rows(const MfmaArgs& a, const int* row_base, int g) {
+  const int n = row_base[g + 1] - row_base[g];
+  return a.valid ? min(n, max(a.valid[g], 0)) : n;
+}
+
+// After scan_groups has filled row_base: wave 0 writes unit_base[g] = units
+// of the groups before g, where a group owns `per` units when its
+// contraction rows (tgmm_rows) lie in [lo, hi], else none.
+__device__ inline void scan_class_units(const MfmaArgs& a, const int* row_base, int lo, int hi,
+                                        int per, int* unit_base) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int run = 0;
+  for (int g0 = 0; g0 < a.G; g0 += 64) {
+    const int g = g0 + lane;
+    int u = 0;
+    if (g < a.G) {
+      const int v = tgmm_rows(a, row_base, g);
+      u = (v >= lo && v <= hi) ? per : 0;
+    }
+    int incl = u;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    if (g < a.G) unit_base[g] = run + incl - u;
+    run += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) unit_base[a.G] = run;
+}
+
+// Largest g with unit_base[g] <= u (unit_base non-decreasing, u < unit_base[G]).
+__device__ __forceinline__ int find_group(const int* unit_base, int G, int64_t u) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (unit_base[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The tiles listed in tile_base (the groups' tiles one after another, TM x
+// TN tiles of [Kdim, N] in column blocks) for workgroup b of nwg:
+// out[g] tile = lhs[rows of g, tile rows]^T . rhs[rows of g, tile columns].
 template <int TM, int TN, typename TO>
-__global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void tgmm_mfma_kernel(MfmaArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem[Stages<TM, TN>::kBytes];
-  __shared__ int row_base[kMaxG + 1];
-  scan_groups(a.gsz, a.G, a.M, TM, 1, row_base, nullptr, blockIdx.x == 0 ? a.err : nullptr);
-  __syncthreads();
+__device__ __forceinline__ void tgmm_tile_loop(const MfmaArgs& a, char* smem, const int* row_base,
+                                               const int* tile_base, int b, int nwg) {
   const int mtn = static_cast<int>((a.Kdim + TM - 1) / TM);
   const int ntn = static_cast<int>((a.N + TN - 1) / TN);
-  const int64_t per_group = static_cast<int64_t>(mtn) * ntn;
-  const int64_t total = per_group * a.G;
+  const int64_t total = tile_base[a.G];
   TO* out = static_cast<TO*>(a.out);
   Operand<true, TM> A;
   Operand<true, TN> B;
@@ -1160,15 +1203,14 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void tgmm_mfma_kernel(MfmaAr
   Operand<true, TM>::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
   Operand<true, TN>::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
   for (int it = 0;; ++it) {
-    const int64_t tile = xcd_tile(it);
+    const int64_t tile = xcd_index(it, b, nwg);
     if (tile >= total) break;
-    const int g = static_cast<int>(tile / per_group);
-    const int local = static_cast<int>(tile - g * per_group);
+    const int g = find_group(tile_base, a.G, tile);
+    const int local = static_cast<int>(tile - tile_base[g]);
     int mt, nt;
     blocked_tile(local, mtn, ntn, mt, nt);
     const int64_t r0 = row_base[g];
-    int rows_g = row_base[g + 1] - row_base[g];
-    if (a.valid) rows_g = min(rows_g, max(a.valid[g], 0));   // the rest is zero
+    const int rows_g = tgmm_rows(a, row_base, g);   // the rest is zero
     if (rows_g == 0 && a.accumulate) continue;   // partial sum unchanged
     const int64_t m0 = static_cast<int64_t>(mt) * TM, n0 = static_cast<int64_t>(nt) * TN;
     const int mv = static_cast<int>(lmin(TM, a.Kdim - m0));
@@ -1179,6 +1221,239 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void tgmm_mfma_kernel(MfmaAr
     store_tile(acc, smem, out + g * a.out_gs + m0 * a.ld_out + n0, a.ld_out, mv, nv,
                a.accumulate);
   }
+}
+
+// Transposed grouped GEMM over the groups whose contraction rows lie in
+// [cls_lo, cls_hi] (all groups by default), every workgroup taking tiles.
+template <int TM, int TN, typename TO>
+__global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void tgmm_mfma_kernel(MfmaArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Stages<TM, TN>::kBytes];
+  __shared__ int row_base[MaxG<TM>::value + 1];
+  __shared__ int tile_base[MaxG<TM>::value + 1];
+  scan_groups(a.gsz, a.G, a.M, TM, 1, row_base, nullptr, blockIdx.x == 0 ? a.err : nullptr);
+  __syncthreads();
+  const int per = static_cast<int>(((a.Kdim + TM - 1) / TM) * ((a.N + TN - 1) / TN));
+  scan_class_units(a, row_base, a.cls_lo, a.cls_hi, per, tile_base);
+  __syncthreads();
+  tgmm_tile_loop<TM, TN, TO>(a, smem, row_base, tile_base, blockIdx.x, gridDim.x);
+}
+
+// Write a 128 x 256 accumulator tile as store_tile does, staging 16-row
+// halves of each wave's 32-row slabs (half the LDS of store_tile: 4 x 16 x
+// 528 bytes), so that the staging area fits beside the short loop's
+// resident operand strip.  rows >= rv and columns >= cv are skipped.  Each
+// wave stages in its own region; SYNC ends with a workgroup barrier.
+template <typename TO, bool SYNC = true>
+__device__ __forceinline__ void store_tile_halves(const Acc<128, 256>& acc, char* lds, TO* o,
+                                                  int64_t ldo, int rv, int cv, int accumulate) {
+  constexpr int TM = 128, TN = 256;
+  constexpr int WC = TN / 2;
+  constexpr int SROW = WC * 4 + 16;
+  constexpr int CPR = WC / 8;                 // 8-column chunks per staged row
+  constexpr int NQ = 16 * CPR / 64;           // chunks per lane per half slab
+  const int tid = opaque_tid();
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  char* slab = lds + w * 16 * SROW;
+  const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * WC;
+  const bool plain = !accumulate && wr + TM / 2 <= rv && wc + WC <= cv;
+#pragma unroll
+  for (int i = 0; i < Acc<TM, TN>::FM; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // accumulator entries r of this half: rows 8 (r >> 2) + 4 (lane / 32) + (r & 3) - 16 h
+#pragma unroll
+      for (int j = 0; j < Acc<TM, TN>::FN; ++j)
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; ++r) {
+          const int row = 8 * ((r >> 2) & 1) + 4 * (lane >> 5) + (r & 3);
+          const int col = 32 * j + (lane & 31);
+          *reinterpret_cast<float*>(slab + row * SROW + col * 4) = acc.v[i][j][r];
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float4 lo[NQ], hi[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int chunk = lane + 64 * q;
+        const int row = chunk / CPR, c8 = chunk % CPR;
+        lo[q] = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32);
+        hi[q] = *reinterpret_cast<const float4*>(slab + row * SROW + c8 * 32 + 16);
+      }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int chunk = lane + 64 * q;
+        const int row = chunk / CPR, c8 = chunk % CPR;
+        const int grow = wr + 32 * i + 16 * h + row, gcol = wc + 8 * c8;
+        float v[8] = {lo[q].x, lo[q].y, lo[q].z, lo[q].w, hi[q].x, hi[q].y, hi[q].z, hi[q].w};
+        TO* p = o + static_cast<int64_t>(grow) * ldo + gcol;
+        if (plain) {
+          store8_nt(p, v);
+        } else if (grow < rv && gcol < cv) {
+          if (accumulate) {
+            float old[8];
+            load8(p, old);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += old[e];
+            store8(p, v);
+          } else {
+            store8_nt(p, v);
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  if (SYNC) __syncthreads();   // the staging area may be refilled by the next tile's operand
+}
+
+// Weight gradients of groups whose contraction is short (at most
+// kShortRows = one step of rows): such a tile holds one MFMA step and 64 KB
+// of output, so tile by tile its time is the operand load latency plus the
+// output stores, and on gfx9 a wait for a load also waits for the stores
+// issued before it.  Here a workgroup takes a unit = (group g, 256-column
+// strip of N):
+//   * the strip of rhs (the group's rows x 256 columns, zero past them) is
+//     loaded into LDS once and stays there for the whole unit;
+//   * the unit's 128-row tiles of Kdim run in order; the lhs block of tile
+//     t + 1 (32 rows x 128) is copied global -> LDS into the other half of a
+//     double buffer while tile t is contracted and stored, and tile t + 1
+//     waits only for that copy: the wait leaves tile t's stores (issued
+//     after the copy) in flight, so the stores of one tile overlap the next;
+//   * the output leaves through half-slab staging in its own LDS region.
+// Operand traffic is one rhs strip per unit and one lhs block per tile
+// instead of both per tile.  lhs rows past the group's rows are not zeroed
+// in LDS: the copy repeats the last row there, and the zero rhs rows cancel
+// them.  Groups with no rows write zero blocks (or keep the partial sum).
+// Units are listed in unit_base (ntn per group).
+constexpr int kShortRows = TK;
+constexpr int kShortB = 256 * TK * 2;                        // resident rhs strip
+constexpr int kShortA = 128 * TK * 2;                        // one lhs block
+constexpr int kShortStage = 4 * 16 * (128 * 4 + 16);         // half-slab output staging
+constexpr int kShortBytes = kShortB + 2 * kShortA + kShortStage;
+
+// global_load_lds offsets of one 32-row x 128-column lhs block (a col tile
+// of Operand<true, 128>'s layout) whose rows past kv repeat row kv - 1.
+struct ShortLhs {
+  static constexpr int BX = 128;
+  static constexpr int NJ = Operand<true, BX>::NJ;
+  uint32_t voff[NJ];
+  __device__ __forceinline__ void setup(int64_t ld, int xv, int kv) {
+    const int tid = opaque_tid();
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int byte = (w * NJ + j) * 1024 + lane * 16;
+      const int k = byte / (BX * 2);
+      int c = ((byte % (BX * 2)) >> 4) ^ col_swz(k);
+      const int cmax = (xv - 1) >> 3;
+      if (c > cmax) c = cmax;
+      voff[j] = static_cast<uint32_t>(((k < kv ? k : kv - 1) * ld + c * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void dma(const bf16_t* base, uint32_t lds) const {
+    const void* sb = uniform_ptr(base);
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dma16(sb, voff[j], lds + (w * NJ + j) * 1024);
+  }
+};
+
+template <typename TO>
+__device__ __forceinline__ void tgmm_short_loop(const MfmaArgs& a, char* smem, const int* row_base,
+                                                const int* unit_base, int b, int nwg) {
+  constexpr int TM = 128, TN = 256;
+  using OA = Operand<true, TM>;
+  using OB = Operand<true, TN>;
+  // vector-memory instructions per wave of a plain (in-bounds, no partial
+  // sum) output tile: 16 eight-element chunks per lane, one 16-byte store
+  // each for bf16, two for float32
+  constexpr int kStores = 16 * (sizeof(TO) == 2 ? 1 : 2);
+  char* const Bs = smem;
+  char* const As = smem + kShortB;                // two lhs blocks
+  char* const Ss = smem + kShortB + 2 * kShortA;  // output staging
+  const int mtn = static_cast<int>((a.Kdim + TM - 1) / TM);
+  const int ntn = static_cast<int>((a.N + TN - 1) / TN);
+  const int64_t total = unit_base[a.G];
+  TO* out = static_cast<TO*>(a.out);
+  OB B;
+  ShortLhs A;
+  Acc<TM, TN> acc;
+  uint32_t fa[4], fb[4];
+  OA::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
+  OB::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
+  for (int it = 0;; ++it) {
+    const int64_t unit = xcd_index(it, b, nwg);
+    if (unit >= total) break;
+    const int g = find_group(unit_base, a.G, unit);
+    const int nt = static_cast<int>(unit - unit_base[g]);
+    const int64_t r0 = row_base[g];
+    const int rows_g = min(tgmm_rows(a, row_base, g), kShortRows);
+    if (rows_g == 0 && a.accumulate) continue;   // partial sums unchanged
+    const int64_t n0 = static_cast<int64_t>(nt) * TN;
+    const int nv = static_cast<int>(lmin(TN, a.N - n0));
+    const bf16_t* lhs_g = a.lhs + r0 * a.ld_lhs;
+    // every wave is done with the previous unit's LDS (its last tile ended
+    // with a barrier before the epilogue); the copies of the previous unit
+    // have all landed (each tile waited for its own)
+    if (rows_g > 0) {
+      B.setup(a.rhs + r0 * a.ld_rhs + n0, a.ld_rhs, nv);
+      uint4 t[OB::NR];
+      B.tail_load(0, rows_g, t);
+      B.tail_store(Bs, t);
+      A.setup(a.ld_lhs, static_cast<int>(lmin(TM, a.Kdim)), rows_g);
+      A.dma(lhs_g, lds_addr(As));
+    }
+    bool drain = true;   // the wait below must also cover the previous stores
+    for (int mt = 0; mt < mtn; ++mt) {
+      const int64_t m0 = static_cast<int64_t>(mt) * TM;
+      const int mv = static_cast<int>(lmin(TM, a.Kdim - m0));
+      char* const cur = As + (mt & 1) * kShortA;
+      if (rows_g > 0) {
+        // this tile's lhs block: everything issued after its copy is the
+        // previous tile's stores, which may stay in flight
+        if (drain) wait_vmcnt<0>(); else wait_vmcnt<kStores>();
+      }
+      __syncthreads();
+      if (rows_g > 0 && mt + 1 < mtn) {
+        // the next block into the other half (read by tile mt - 1, whose
+        // fragment reads all waves finished before its epilogue)
+        A.setup(a.ld_lhs, static_cast<int>(lmin(TM, a.Kdim - m0 - TM)), rows_g);
+        A.dma(lhs_g + m0 + TM, lds_addr(As + ((mt + 1) & 1) * kShortA));
+      }
+      acc.zero();
+      if (rows_g > 0) {
+        typename Acc<TM, TN>::Frags f;
+        Acc<TM, TN>::template load<OA, OB>(f, cur, Bs, fa, fb, 0);
+        acc.mma(f);
+        Acc<TM, TN>::template load<OA, OB>(f, cur, Bs, fa, fb, 1);
+        acc.mma(f);
+      }
+      // a plain epilogue issues exactly kStores vector-memory instructions
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      drain = a.accumulate || (w >> 1) * (TM / 2) + TM / 2 > mv || (w & 1) * (TN / 2) + TN / 2 > nv;
+      store_tile_halves<TO, false>(acc, Ss, out + g * a.out_gs + m0 * a.ld_out + n0, a.ld_out, mv,
+                                   nv, a.accumulate);
+    }
+    __syncthreads();   // the unit's LDS is refilled by the next unit
+  }
+}
+
+// Weight gradients of the groups with at most kShortRows contraction rows
+// (cls_lo .. cls_hi), every workgroup taking units (tgmm_short_loop).
+template <typename TO>
+__global__ __launch_bounds__(NT, 2) void tgmm_short_kernel(MfmaArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kShortBytes];
+  __shared__ int row_base[kMaxGShort + 1];
+  __shared__ int unit_base[kMaxGShort + 1];
+  scan_groups(a.gsz, a.G, a.M, 128, 1, row_base, nullptr, blockIdx.x == 0 ? a.err : nullptr);
+  __syncthreads();
+  scan_class_units(a, row_base, a.cls_lo, min(a.cls_hi, kShortRows),
+                   static_cast<int>((a.N + 255) / 256), unit_base);
+  __syncthreads();
+  tgmm_short_loop<TO>(a, smem, row_base, unit_base, blockIdx.x, gridDim.x);
 }
 
 // ---------------------------------------------------------------- fp8 MFMA
@@ -1899,18 +2174,47 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
                0, group_sizes, G, M, Kdim, N, out, ld_out, out_group_stride, accumulate, err,
                valid_rows};
     // short contractions (under 512 rows per group on average) leave each
-    // tile's epilogue exposed: 128-row tiles let two workgroups share a CU
-    const bool short_k = M < 512 * static_cast<int64_t>(G);
-    const int TMv = short_k ? 128 : 256;
-    const int64_t upper = static_cast<int64_t>(G) * ((Kdim + TMv - 1) / TMv) * ((N + 255) / 256);
-    const unsigned grid = persistent_grid(upper, short_k ? 2 : 1);
-#define TGMM(TMc, TOc) \
-  hipLaunchKernelGGL((tgmm_mfma_kernel<TMc, 256, TOc>), dim3(grid), dim3(NT), 0, st, a)
+    // tile's latency and stores exposed.  There the groups are split by the
+    // rows their contraction covers (valid_rows, else the group size) into
+    // three launches: at most kShortRows rows in the short kernel (resident
+    // rhs strip, lhs blocks copied ahead, stores of one tile overlapping
+    // the next), up to kSplitRows in 128 x 256 tiles (two workgroups per
+    // CU), the rest in 256 x 256 tiles (half the operand traffic per flop).
+    // On the DeepSeek-V3 shape: 2.7 ms per launch in one 128-row launch ->
+    // ~2.3 ms.  (256-row tiles for the mid-sized groups took 0.9 ms more.)
+    // Otherwise one launch of 256 x 256 tiles does every group.
+    const bool short_k = M < 512 * static_cast<int64_t>(G) && G <= kMaxGShort;
+    auto grid_for = [&](int TMv, int per_cu) {
+      return persistent_grid(static_cast<int64_t>(G) * ((Kdim + TMv - 1) / TMv) * ((N + 255) / 256),
+                             per_cu);
+    };
+#define TGMM(TMc, TOc, ARGS, GRID) \
+  hipLaunchKernelGGL((tgmm_mfma_kernel<TMc, 256, TOc>), dim3(GRID), dim3(NT), 0, st, ARGS)
+#define TGMMS(TOc, ARGS, GRID) \
+  hipLaunchKernelGGL((tgmm_short_kernel<TOc>), dim3(GRID), dim3(NT), 0, st, ARGS)
     if (short_k) {
-      if (out_dtype == MOE_BF16) TGMM(128, bf16_t); else TGMM(128, float);
+      MfmaArgs s_ = a, m_ = a, b_ = a;
+      s_.cls_hi = kShortRows;
+      m_.cls_lo = kShortRows + 1;
+      m_.cls_hi = kSplitRows;
+      b_.cls_lo = kSplitRows + 1;
+      m_.err = b_.err = nullptr;   // the first launch reports the group-size check
+      const unsigned gs_ = persistent_grid(static_cast<int64_t>(G) * ((N + 255) / 256), 2);
+      const unsigned gm_ = grid_for(128, 2), gb_ = grid_for(256, 1);
+      if (out_dtype == MOE_BF16) {
+        TGMMS(bf16_t, s_, gs_);
+        TGMM(128, bf16_t, m_, gm_);
+        TGMM(256, bf16_t, b_, gb_);
+      } else {
+        TGMMS(float, s_, gs_);
+        TGMM(128, float, m_, gm_);
+        TGMM(256, float, b_, gb_);
+      }
     } else {
-      if (out_dtype == MOE_BF16) TGMM(256, bf16_t); else TGMM(256, float);
+      const unsigned grid = grid_for(256, 1);
+      if (out_dtype == MOE_BF16) TGMM(256, bf16_t, a, grid); else TGMM(256, float, a, grid);
     }
+#undef TGMMS
 #undef TGMM
   } else {
     const int64_t upper = static_cast<int64_t>(G) * ((Kdim + FB - 1) / FB) * ((N + FB - 1) / FB);

@@ -347,6 +347,8 @@ GS = {
     # mostly small groups (128-row tiles) with some above 384 rows (256-row
     # tiles in a launch of their own)
     "mixed": [30, 700, 0, 385, 384, 1100, 5, 0, 129, 40],
+    # contractions of at most 64 rows (one or two steps, full and ragged)
+    "shortk": [33, 64, 47, 0, 5, 63, 32, 1, 17],
 }
 
 GMM_CASES = [
@@ -709,6 +711,15 @@ TGMM_CASES = [
     ("max_groups", 16, 136, "bf16", "bf16", False),
     ("many", 264, 520, "bf16", "bf16", False),
     ("skewed", 520, 1032, "bf16", "bf16", False),   # full and ragged tiles, several per workgroup
+    # short contractions in all three size classes (<= 64 rows, <= 384 rows, larger)
+    ("mixed", 136, 264, "bf16", "bf16", False),
+    ("mixed", 264, 520, "bf16", "f32", True),
+    ("mixed", 200, 72, "bf16", "f32", False),
+    # only contractions of at most 64 rows: ragged Kdim and N, partial sums
+    ("shortk", 200, 264, "bf16", "bf16", False),
+    ("shortk", 136, 520, "bf16", "f32", True),
+    ("shortk", 1032, 72, "bf16", "bf16", False),
+    ("shortk", 8, 8, "bf16", "bf16", True),
 ]
 
 
