@@ -2,7 +2,7 @@
 """MoE expert-FFN forward+backward throughput on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
-                    [--extra-workloads deepseek_v3] [--fp8] [--fused-wi]
+                    [--extra-workloads deepseek_v3,token_drop] [--fp8] [--fused-wi]
 
 A step is one pass of the whole path over one batch of synthetic input:
 router GEMM, top-k routing, permute, the up-projection grouped GEMMs,
@@ -20,8 +20,12 @@ stream.  A second pass of the same steps brackets every expert GEMM and
 memory-bound call with events, each after a 1 GiB scratch write that
 evicts the 256 MB memory-side cache, and classifies each kind of call by
 its own roofline: MFMA-bound when flops / peak exceeds algorithmic bytes /
-HBM bandwidth, else HBM-bound.  Extra workloads (the DeepSeek-V3 shape by
-default) are measured the same way and reported under "workloads".
+HBM bandwidth, else HBM-bound.  Extra workloads (the DeepSeek-V3 shape and
+the token-dropping shape by default) are measured the same way and
+reported under "workloads"; a workload with a capacity is also run in the
+capacity-padded batched layout (every expert owns C rows) on the same
+inputs, with the ratio of the two step times and, for context, the
+forward's three GEMMs through the vendor batched GEMM (torch.bmm).
 Prints ONE JSON line on stdout; everything else goes to stderr.
 """
 from __future__ import annotations
@@ -58,7 +62,7 @@ def parse():
     p.add_argument("--kernel-steps", type=int, default=5,
                    help="steps of the second pass that times each call after a cache flush")
     p.add_argument("--workload", default="mixtral")
-    p.add_argument("--extra-workloads", default="deepseek_v3",
+    p.add_argument("--extra-workloads", default="deepseek_v3,token_drop",
                    help="comma-separated workloads reported under 'workloads' ('' = none)")
     p.add_argument("--cpu-tokens", type=int, default=0,
                    help="tokens of the headline workload the CPU oracle runs on (0 = all)")
@@ -140,18 +144,24 @@ class LaunchRecorder:
         return agg
 
 
-# Kernel symbol behind a recorded launch kind, per workload (for the
-# rocprofv3 summaries and the PMC traffic of the dominant kernel).  Kinds
-# launched as two kernels (a size-class split) have no single symbol.
+# Kernel symbols behind a recorded launch kind, per workload (for the
+# rocprofv3 summaries and the PMC traffic): each is launched once per call
+# of that kind, so the call's traffic is the sum of theirs.
 KERNEL_NAME = {
     "mixtral": {
-        "gmm_nn": "gmm_mfma_kernel<true, 256, 256, unsigned short, true, false, false>",
-        "gmm_nt": "gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, false>",
-        "tgmm": "tgmm_mfma_kernel<256, 256, unsigned short>",
-        "gmm_nt_swiglu_bwd": "gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, true>",
+        "gmm_nn": ["gmm_mfma_kernel<true, 256, 256, unsigned short, true, false, false>"],
+        "gmm_nt": ["gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, false>"],
+        "tgmm": ["tgmm_mfma_kernel<256, 256, unsigned short>"],
+        "gmm_nt_swiglu_bwd": ["gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, true>"],
     },
     "deepseek_v3": {
-        "tgmm": "tgmm_mfma_kernel<128, 256, unsigned short>",
+        "tgmm": ["tgmm_short_kernel<unsigned short>", "tgmm_mfma_kernel<128, 256, unsigned short>",
+                 "tgmm_mfma_kernel<256, 256, unsigned short>"],
+        "gmm_nn": ["gmm_mfma_kernel<true, 256, 256, unsigned short, true, false, false>",
+                   "gmm_mfma_kernel<true, 128, 256, unsigned short, false, false, false>"],
+        "gmm_nt": ["gmm_mfma_kernel<false, 128, 256, unsigned short, false, false, false>"],
+        "gmm_nt_swiglu_bwd": ["gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, true>",
+                              "gmm_mfma_kernel<false, 128, 256, unsigned short, false, false, true>"],
     },
 }
 # Memory-bound kinds: the symbol prefix of the kernel that moves their data.
@@ -186,8 +196,9 @@ def traffic_json(workload: str) -> str:
 
 
 def traffic_for(workload: str, kind: str):
-    """Calibrated HBM bytes per launch of the kernel behind `kind` from the
-    committed PMC summary, or None (absent, or taken on other sources)."""
+    """Calibrated HBM bytes per call of `kind` (the sum over the kernels it
+    launches) from the committed PMC summary, or None (absent, taken on
+    other sources, or a kernel missing from it)."""
     try:
         with open(traffic_json(workload)) as f:
             d = json.load(f)
@@ -196,12 +207,17 @@ def traffic_for(workload: str, kind: str):
     if d.get("source_sha256_16") != kernel_source_digest():
         return None
     ks = d.get("kernels", {})
-    name = KERNEL_NAME.get(workload, {}).get(kind)
-    if name is None and kind in MEM_KERNEL_PREFIX:
-        hits = [k for k in ks if k.startswith(MEM_KERNEL_PREFIX[kind])]
-        name = hits[0] if len(hits) == 1 else None
-    k = ks.get(name) if name else None
-    return None if k is None else k.get("hbm_bytes_per_dispatch")
+
+    def find(sym):
+        hits = [k for k in ks if sym in k]
+        return ks[hits[0]]["hbm_bytes_per_dispatch"] if len(hits) == 1 else None
+    names = KERNEL_NAME.get(workload, {}).get(kind)
+    if names is None and kind in MEM_KERNEL_PREFIX:
+        names = [MEM_KERNEL_PREFIX[kind]]
+    if not names:
+        return None
+    vals = [find(n) for n in names]
+    return None if any(v is None for v in vals) else int(sum(vals))
 
 
 COPY_ROWS, COPY_COLS = 32768, 16384      # bf16 rows copied by the calibration run (1 GiB)
@@ -317,14 +333,10 @@ def cpu_baseline(w, host, tokens: int):
                       f"rows, all {w.E} experts) of the same workload; {dt:.1f} s wall"}
 
 
-def measure(name: str, args, headline: bool) -> dict:
-    """Generate a workload on the GPU, time its step, then time each call."""
+def gen_device_inputs(name: str, args):
     import torch
     import moe_synth as ms
-    import mixture_experts_grouped_top_amd as moe
-
     w = ms.get_workload(name)
-    dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     t0 = time.time()
     g = ms.device_inputs(w, threads=min(16, len(os.sched_getaffinity(0))))
     host = g.pop("host")
@@ -334,8 +346,48 @@ def measure(name: str, args, headline: bool) -> dict:
         g["wi"] = torch.cat([g.pop("wi_0"), g.pop("wi_1")], dim=2).contiguous()
         g["wi_0"] = g["wi_1"] = None
         torch.cuda.empty_cache()
+    return w, g, host
+
+
+def vendor_batched_forward(w, g, plan, reps: int = 10) -> dict:
+    """The forward's three expert GEMMs as a dense per-expert batched GEMM
+    from the vendor library (torch.bmm) over the capacity-padded buffers the
+    plan just filled ([E, C, D] x [E, D, F], all operands contiguous), timed
+    like the library's own calls, for context beside them."""
+    import torch
+    E, C, D, F = w.E, w.capacity, w.D, w.F
+    xs = plan.x_sorted[:E * C].view(E, C, D)
+    act = plan.act[:E * C].view(E, C, F)
+    h = torch.empty((E, C, F), dtype=xs.dtype, device=xs.device)
+    y = torch.empty((E, C, D), dtype=xs.dtype, device=xs.device)
+
+    def fwd():
+        torch.bmm(xs, g["wi_0"], out=h)
+        torch.bmm(xs, g["wi_1"], out=h)
+        torch.bmm(act, g["wo"], out=y)
+    fwd()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fwd()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    return {"ms_three_gemms": round(ms, 4), "library": "torch.bmm (hipBLASLt / rocBLAS)",
+            "shape": f"{E} x [{C}, {D}] . [{D}, {F}] (twice) and [{C}, {F}] . [{F}, {D}]"}
+
+
+def measure(name: str, args, headline: bool, inputs=None, capacity_layout: bool = False) -> dict:
+    """Time a workload's step on the GPU, then time each call."""
+    import torch
+    import mixture_experts_grouped_top_amd as moe
+
+    w, g, host = inputs if inputs is not None else gen_device_inputs(name, args)
+    dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     shape = moe.MoEShape(T=w.T, D=w.D, F=w.F, E=w.E, K=w.K, dtype=dtype, score=w.score,
                          renorm=w.renorm, align=w.align, capacity=w.capacity,
+                         capacity_layout=capacity_layout,
                          n_chunks=w.n_chunks, pad_rows_to=w.pad_rows_to,
                          fused_wi=args.fused_wi, fp8=args.fp8)
     plan = moe.MoEPlan(shape)
@@ -376,6 +428,8 @@ def measure(name: str, args, headline: bool) -> dict:
     err = int(plan.err.item())
     flops = 18.0 * R * w.D * w.F
     tflops = flops / (ms_step * 1e-3) / 1e12
+    if capacity_layout:
+        name = f"{name} (capacity layout)"
     log(f"[bench] {name}: {ms_step:.3f} ms/step, {tflops:.1f} TFLOP/s, R={R}, "
         f"padded rows={plan.padded_rows}, non-empty experts={plan.nonempty_groups}, err={err}")
 
@@ -409,10 +463,10 @@ def measure(name: str, args, headline: bool) -> dict:
             ach, pk, unit = k["gbs"], PEAK_HBM_GBS, "GB/s"
         plain = not (args.fused_wi or args.fp8)
         roofline = {"bound": k["bound"], "kind": kind,
-                    "kernel": KERNEL_NAME.get(name, {}).get(kind, kind) if plain else kind,
+                    "kernels": KERNEL_NAME.get(w.name, {}).get(kind, [kind]) if plain else [kind],
                     "achieved": round(ach, 2), "peak": pk, "unit": unit,
                     "frac": round(ach / pk, 4),
-                    "traffic": traffic_for(name, kind) if plain else None,
+                    "traffic": traffic_for(w.name, kind) if plain and not capacity_layout else None,
                     "avg_launch_ms": round(k["avg_ms"], 4),
                     "flops_per_launch": k["flops"] / k["launches"],
                     "algorithmic_bytes_per_launch": round(k["bytes"] / k["launches"])}
@@ -426,7 +480,8 @@ def measure(name: str, args, headline: bool) -> dict:
         "config": {"workload": w.name, "tokens": w.T, "d_model": w.D, "d_ff": w.F,
                    "experts": w.E, "top_k": w.K, "score": w.score, "renorm": w.renorm,
                    "align_size": w.align, "capacity": w.capacity, "chunks": w.n_chunks,
-                   "fused_wi": bool(args.fused_wi), "fp8": bool(args.fp8), "routed_rows": R,
+                   "fused_wi": bool(args.fused_wi), "fp8": bool(args.fp8),
+                   "capacity_layout": bool(capacity_layout), "routed_rows": R,
                    "padded_rows": plan.padded_rows, "nonempty_experts": plan.nonempty_groups},
         "roofline": roofline,
         "kernels": {kk: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
@@ -434,10 +489,14 @@ def measure(name: str, args, headline: bool) -> dict:
                          "algorithmic_bytes": int(v["bytes"] / v["launches"]),
                          "gbs": round(v["gbs"], 1), "bound": v["bound"],
                          "roofline_frac": round(v["frac"], 4),
-                         "traffic": traffic_for(name, kk)}
+                         "traffic": None if capacity_layout else traffic_for(w.name, kk)}
                     for kk, v in kernels.items()},
     }
-    del plan, g
+    if capacity_layout:
+        rec_out["vendor_batched_fwd"] = vendor_batched_forward(w, g, plan)
+    del plan
+    if inputs is None:
+        del g
     gc.collect()
     torch.cuda.empty_cache()
     if headline and not args.no_cpu_baseline:
@@ -464,12 +523,33 @@ def main():
     head = measure(args.workload, args, headline=True)
     extras = {}
     for name in [n for n in args.extra_workloads.split(",") if n and n != args.workload]:
-        extras[name] = measure(name, args, headline=False)
+        import moe_synth as ms
+        inputs = gen_device_inputs(name, args)
+        extras[name] = measure(name, args, headline=False, inputs=inputs)
         extras[name]["cpu_baseline"] = None
         extras[name]["cpu_baseline_note"] = (
             "not run: the oracle's per-expert float64 weights alone (256 experts x 3 x "
             "7168 x 2048) take minutes to form on the host; the headline workload's "
             "baseline is the one reported")
+        if ms.get_workload(name).capacity > 0 and not args.fp8 and not args.fused_wi:
+            # the same step in the capacity-padded batched layout (every expert
+            # C rows), against the compact grouped layout
+            cap = measure(name, args, headline=False, inputs=inputs, capacity_layout=True)
+            g_ms, b_ms = extras[name]["ms_per_step"], cap["ms_per_step"]
+            fw = {k: v for k, v in cap["kernels"].items() if k == "gmm_nn"}
+            extras[name]["capacity_layout"] = cap
+            extras[name]["grouped_vs_batched"] = {
+                "grouped_ms_per_step": g_ms, "batched_ms_per_step": b_ms,
+                "batched_over_grouped": round(b_ms / g_ms, 3),
+                "forward_gemms_ms": {
+                    "grouped": round(3 * extras[name]["kernels"]["gmm_nn"]["avg_ms"], 4)
+                    if "gmm_nn" in extras[name]["kernels"] else None,
+                    "batched_library_kernels": round(3 * fw["gmm_nn"]["avg_ms"], 4)
+                    if fw else None,
+                    "batched_vendor_bmm": cap["vendor_batched_fwd"]["ms_three_gemms"]},
+                "context": "the MaxText grouped-GEMM pull request reports grouped GEMM about "
+                           "1.2x faster than batch GEMM on its hardware (context only)"}
+        del inputs
     out = {
         "metric": METRIC, "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],

@@ -197,3 +197,60 @@ def test_full_properties(full):
         t = getattr(plan, k)
         for e in empty:
             assert int(torch.count_nonzero(t[int(e)])) == 0, (k, e)
+
+
+def test_full_token_drop_capacity_layout():
+    """Token dropping at its full size in the capacity-padded batched layout
+    (every expert owns C rows starting at e C, the dense per-expert batched
+    GEMM of the MaxText grouped-GEMM pull request, Tests): every kept row of
+    every intermediate and gradient equals the compact grouped layout's bit
+    for bit (the kernels' per-row contraction order does not depend on the
+    row's position), the padding rows carry zeros, the block outputs and
+    weight gradients are identical, and sampled experts match the oracle."""
+    w = ms.get_workload("token_drop")
+    dev = ms.device_inputs(w, threads=16)
+    h = dev["host"]
+    plans = {}
+    for lay in (False, True):
+        shape = MoEShape(T=w.T, D=w.D, F=w.F, E=w.E, K=w.K, score=w.score, renorm=w.renorm,
+                         capacity=w.capacity, capacity_layout=lay)
+        p = MoEPlan(shape)
+        p.forward(dev["x"], dev["wi_0"], dev["wi_1"], dev["wo"], logits=dev["logits"])
+        p.backward(dev["dy"], dev["x"], dev["wi_0"], dev["wi_1"], dev["wo"])
+        plans[lay] = p
+    torch.cuda.synchronize()
+    pc, pb = plans[False], plans[True]
+    assert pb.rows == w.E * w.capacity
+    ros_c, ros_b = host(pc.idx["row_of_slot"]), host(pb.idx["row_of_slot"])
+    kept = ros_c >= 0
+    assert ((ros_b >= 0) == kept).all()
+    ids, wts = oracle.route(h["logits"], w.K, w.score, w.renorm, h["bias"])
+    Pb = oracle.permute(None, ids, w.E, 0, w.capacity, capacity_layout=True, rows=pb.lhs_rows)
+    for k in ("counts", "group_sizes", "group_offsets", "row_of_slot", "slot_of_row"):
+        assert (host(pb.idx[k]) == Pb[k]).all(), k
+    rc = torch.from_numpy(ros_c[kept]).long().cuda()
+    rb = torch.from_numpy(ros_b[kept]).long().cuda()
+    for name in ("x_sorted", "h0", "h1", "act", "y_sorted", "d_y_sorted", "d_h0", "d_h1",
+                 "d_x_sorted"):
+        a, c = getattr(pc, name)[rc], getattr(pb, name)[rb]
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16)), name
+    # padding rows of the capacity layout (past each expert's kept rows)
+    pad = torch.from_numpy(host(pb.idx["slot_of_row"]) < 0).cuda()
+    for name in ("x_sorted", "d_y_sorted", "d_x_sorted"):
+        assert int(torch.count_nonzero(getattr(pb, name)[pad])) == 0, name
+    for name in ("y", "dx", "d_wi_0", "d_wi_1", "d_wo"):
+        assert torch.equal(getattr(pc, name).view(torch.int16), getattr(pb, name).view(torch.int16)), name
+    for name in ("d_w", "d_logits"):
+        assert torch.equal(getattr(pc, name), getattr(pb, name)), name
+    # the oracle on sampled experts, rows of the capacity layout
+    for e in sampled_experts(Pb["counts"]):
+        g = _group_oracle(w, dev, Pb, wts, e)
+        rows = slice(g["o"], g["o"] + g["n"])
+        for k in ("h0", "h1", "act", "y_sorted"):
+            assert_close(f64(getattr(pb, k)[rows]), g[k], TOL_BF16, f"{k} expert {e}")
+        for k in ("d_y_sorted", "d_h0", "d_h1", "d_x_sorted"):
+            assert_close(f64(getattr(pb, k)[rows]), g[k], TOL_GRAD, f"{k} expert {e}")
+        for k in ("d_wo", "d_wi_0", "d_wi_1"):
+            assert_close(f64(getattr(pb, k)[e]), g[k], TOL_GRAD, f"{k} expert {e}")
+    del plans, pc, pb, dev
+    torch.cuda.empty_cache()
