@@ -349,6 +349,71 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
   const int rl = slot_rows(ros + t * K, K);
   const float wl = lane < K ? wts[t * K + lane] : 0.f;
   const T* g = dy + t * D;
+  if (K <= kJB && rows > 0) {
+    // One batch holds every slot: software-pipelined over the lane's chunks
+    // (the loads of chunk i + 1 are in flight while chunk i is scaled,
+    // stored and dotted).  Past the lane's last chunk the issues re-read
+    // its first chunk (dy row t and row 0 of y_sorted), so every wait
+    // leaves the next chunk's loads in flight.
+    int r[kJB];
+    float wv[kJB], dot[kJB];
+    const T* pr[kJB];
+#pragma unroll
+    for (int q = 0; q < kJB; ++q) {
+      r[q] = q < K ? lane_value(rl, q) : -1;
+      wv[q] = r[q] >= 0 ? lane_value(wl, q) : 0.f;
+      dot[q] = 0.f;
+      pr[q] = ys + static_cast<int64_t>(r[q] < 0 ? 0 : r[q]) * D;
+    }
+    const int64_t c0 = static_cast<int64_t>(lane) * 8;
+    const int nch = c0 < D ? static_cast<int>((D - c0 + 511) / 512) : 0;
+    Raw8<T> ga, gb, ra[kJB], rb[kJB];
+    auto issue = [&](Raw8<T>& gv, Raw8<T>(&raw)[kJB], int i) {
+      const int64_t c = i < nch ? c0 + 512 * static_cast<int64_t>(i) : c0;
+      gv.load(g + c);
+#pragma unroll
+      for (int q = 0; q < kJB; ++q) raw[q].load(pr[q] + c);
+    };
+    auto finish = [&](const Raw8<T>& gv, const Raw8<T>(&raw)[kJB], int i) {
+      const int64_t c = c0 + 512 * static_cast<int64_t>(i);
+      float a[8];
+      gv.get(a);
+#pragma unroll
+      for (int q = 0; q < kJB; ++q) {
+        if (r[q] < 0) continue;
+        float b[8], o[8];
+        raw[q].get(b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o[e] = wv[q] * a[e];
+          dot[q] = fmaf(a[e], b[e], dot[q]);
+        }
+        store8_nt(d_ys + static_cast<int64_t>(r[q]) * D + c, o);
+      }
+    };
+    if (nch > 0) {
+      issue(ga, ra, 0);
+      int i = 0;
+      for (; i + 2 <= nch; i += 2) {
+        issue(gb, rb, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(ga, ra, i);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(ga, ra, i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        finish(gb, rb, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i < nch) finish(ga, ra, i);
+    }
+#pragma unroll
+    for (int q = 0; q < kJB; ++q) {
+      if (q >= K) break;
+      const float sdot = wave_sum(dot[q]);
+      if (lane == 0) d_w[t * K + q] = r[q] >= 0 ? sdot : 0.f;
+    }
+    return;
+  }
   for (int j0 = 0; j0 < K; j0 += kJB) {
     int r[kJB];
     float wv[kJB], dot[kJB];
