@@ -378,6 +378,51 @@ def vendor_batched_forward(w, g, plan, reps: int = 10) -> dict:
             "shape": f"{E} x [{C}, {D}] . [{D}, {F}] (twice) and [{C}, {F}] . [{F}, {D}]"}
 
 
+def vendor_dense_gemm(w, g, plan, R: int, reps: int = 5) -> dict:
+    """The up-projection's product (rows x D . D x F per expert) through the
+    vendor library on an even split of the routed rows (C = R / E rows per
+    expert, from x_sorted): a batched NN GEMM (torch.bmm over [E, C, D] x
+    [E, D, F], the layout the library's gmm_nn call reads) and, per expert,
+    the NT form (torch.mm against a [F, D] copy of the weight, both operands
+    contraction-contiguous, as nn.Linear multiplies).  Each call follows the same cache-evicting
+    scratch write as the library's bracketed calls; for context beside the
+    library's gmm_nn."""
+    import torch
+    E, D, F = w.E, w.D, w.F
+    C = R // E
+    xs = plan.x_sorted[:E * C].view(E, C, D)
+    wi = g["wi_0"]
+    wt = wi.transpose(1, 2).contiguous()
+    h = torch.empty((E, C, F), dtype=xs.dtype, device=xs.device)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        tot = 0.0
+        for i in range(reps):
+            scratch.fill_(float(i))
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            tot += s.elapsed_time(e)
+        return tot / reps
+
+    def nt():
+        for e_ in range(E):
+            torch.mm(xs[e_], wt[e_].t(), out=h[e_])
+    ms_nn = timed(lambda: torch.bmm(xs, wi, out=h))
+    ms_nt = timed(nt)
+    flops = 2.0 * E * C * D * F
+    del wt, h, scratch
+    torch.cuda.empty_cache()
+    return {"shape": f"{E} x [{C}, {D}] . [{D}, {F}]", "library": "torch (hipBLASLt / rocBLAS)",
+            "bmm_nn_ms": round(ms_nn, 4), "bmm_nn_tflops": round(flops / ms_nn / 1e9, 1),
+            "linear_nt_ms": round(ms_nt, 4), "linear_nt_tflops": round(flops / ms_nt / 1e9, 1)}
+
+
 def measure(name: str, args, headline: bool, inputs=None, capacity_layout: bool = False) -> dict:
     """Time a workload's step on the GPU, then time each call."""
     import torch
@@ -494,6 +539,14 @@ def measure(name: str, args, headline: bool, inputs=None, capacity_layout: bool 
     }
     if capacity_layout:
         rec_out["vendor_batched_fwd"] = vendor_batched_forward(w, g, plan)
+    if (headline and not capacity_layout and w.dtype == "bf16" and not args.fp8
+            and not args.fused_wi and w.E <= 16):
+        v = vendor_dense_gemm(w, g, plan, R)
+        if "gmm_nn" in kernels:
+            v["library_gmm_nn_ms"] = round(kernels["gmm_nn"]["avg_ms"], 4)
+            v["library_gmm_nn_tflops"] = round(kernels["gmm_nn"]["tflops"], 1)
+        rec_out["vendor_dense_gemm"] = v
+        log(f"[bench] vendor dense GEMM context: {v}")
     del plan
     if inputs is None:
         del g
@@ -563,6 +616,7 @@ def main():
         "cpu_baseline": head.get("cpu_baseline"),
         "device_error_flags": head["device_error_flags"],
         "kernels": head["kernels"],
+        "vendor_dense_gemm": head.get("vendor_dense_gemm"),
         "workloads": extras,
     }
     print(json.dumps(out), flush=True)

@@ -1314,9 +1314,9 @@ __device__ __forceinline__ void store_tile_halves(const Acc<128, 256>& acc, char
 // of output, so tile by tile its time is the operand load latency plus the
 // output stores, and on gfx9 a wait for a load also waits for the stores
 // issued before it.  Here a workgroup takes a unit = (group g, 256-column
-// strip of N):
+// strip of N), or one of up to four runs of its consecutive tiles:
 //   * the strip of rhs (the group's rows x 256 columns, zero past them) is
-//     loaded into LDS once and stays there for the whole unit;
+//     loaded into LDS once and stays there for the whole unit (run);
 //   * the unit's 128-row tiles of Kdim run in order; the lhs block of tile
 //     t + 1 (32 rows x 128) is copied global -> LDS into the other half of a
 //     double buffer while tile t is contracted and stored, and tile t + 1
@@ -1376,7 +1376,25 @@ __device__ __forceinline__ void tgmm_short_loop(const MfmaArgs& a, char* smem, c
   char* const Ss = smem + kShortB + 2 * kShortA;  // output staging
   const int mtn = static_cast<int>((a.Kdim + TM - 1) / TM);
   const int ntn = static_cast<int>((a.N + TN - 1) / TN);
-  const int64_t total = unit_base[a.G];
+  // A unit's tiles may be taken in `parts` runs of consecutive tiles by
+  // different workgroups: with units a few times the grid, whole units
+  // leave the last round part-empty (1264 units on 512 workgroups: three
+  // rounds of work for 2.47).  parts (1 .. 4) minimises rounds / parts, a
+  // unit's length in rounds, with 2% of a unit charged per extra part for
+  // its second rhs strip load and pipeline start.
+  const int64_t units = unit_base[a.G];
+  int parts = 1;
+  {
+    int64_t best = (units + nwg - 1) / nwg * 100;
+    for (int p = 2; p <= 4 && p <= mtn; ++p) {
+      const int64_t c = (units * p + nwg - 1) / nwg * 100 / p + 2 * (p - 1);
+      if (c < best) {
+        best = c;
+        parts = p;
+      }
+    }
+  }
+  const int64_t total = units * parts;
   TO* out = static_cast<TO*>(a.out);
   OB B;
   ShortLhs A;
@@ -1385,8 +1403,11 @@ __device__ __forceinline__ void tgmm_short_loop(const MfmaArgs& a, char* smem, c
   OA::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
   OB::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
   for (int it = 0;; ++it) {
-    const int64_t unit = xcd_index(it, b, nwg);
-    if (unit >= total) break;
+    const int64_t vunit = xcd_index(it, b, nwg);
+    if (vunit >= total) break;
+    const int64_t unit = vunit / parts;   // the parts of a unit are adjacent: one XCD
+    const int part = static_cast<int>(vunit - unit * parts);
+    const int mt_lo = part * mtn / parts, mt_hi = (part + 1) * mtn / parts;
     const int g = find_group(unit_base, a.G, unit);
     const int nt = static_cast<int>(unit - unit_base[g]);
     const int64_t r0 = row_base[g];
@@ -1403,25 +1424,26 @@ __device__ __forceinline__ void tgmm_short_loop(const MfmaArgs& a, char* smem, c
       uint4 t[OB::NR];
       B.tail_load(0, rows_g, t);
       B.tail_store(Bs, t);
-      A.setup(a.ld_lhs, static_cast<int>(lmin(TM, a.Kdim)), rows_g);
-      A.dma(lhs_g, lds_addr(As));
+      const int64_t mlo = static_cast<int64_t>(mt_lo) * TM;
+      A.setup(a.ld_lhs, static_cast<int>(lmin(TM, a.Kdim - mlo)), rows_g);
+      A.dma(lhs_g + mlo, lds_addr(As));
     }
     bool drain = true;   // the wait below must also cover the previous stores
-    for (int mt = 0; mt < mtn; ++mt) {
+    for (int mt = mt_lo; mt < mt_hi; ++mt) {
       const int64_t m0 = static_cast<int64_t>(mt) * TM;
       const int mv = static_cast<int>(lmin(TM, a.Kdim - m0));
-      char* const cur = As + (mt & 1) * kShortA;
+      char* const cur = As + ((mt - mt_lo) & 1) * kShortA;
       if (rows_g > 0) {
         // this tile's lhs block: everything issued after its copy is the
         // previous tile's stores, which may stay in flight
         if (drain) wait_vmcnt<0>(); else wait_vmcnt<kStores>();
       }
       __syncthreads();
-      if (rows_g > 0 && mt + 1 < mtn) {
+      if (rows_g > 0 && mt + 1 < mt_hi) {
         // the next block into the other half (read by tile mt - 1, whose
         // fragment reads all waves finished before its epilogue)
         A.setup(a.ld_lhs, static_cast<int>(lmin(TM, a.Kdim - m0 - TM)), rows_g);
-        A.dma(lhs_g + m0 + TM, lds_addr(As + ((mt + 1) & 1) * kShortA));
+        A.dma(lhs_g + m0 + TM, lds_addr(As + ((mt + 1 - mt_lo) & 1) * kShortA));
       }
       acc.zero();
       if (rows_g > 0) {
