@@ -155,7 +155,8 @@ KERNEL_NAME = {
         "gmm_nt_swiglu_bwd": ["gmm_mfma_kernel<false, 256, 256, unsigned short, true, false, true>"],
     },
     "deepseek_v3": {
-        "tgmm": ["tgmm_short_kernel<unsigned short>", "tgmm_mfma_kernel<128, 256, unsigned short>",
+        "tgmm": ["tgmm_short_kernel<unsigned short>", "tgmm_strip_kernel<2, unsigned short>",
+                 "tgmm_strip_kernel<4, unsigned short>", "tgmm_mfma_kernel<128, 256, unsigned short>",
                  "tgmm_mfma_kernel<256, 256, unsigned short>"],
         "gmm_nn": ["gmm_mfma_kernel<true, 256, 256, unsigned short, true, false, false>",
                    "gmm_mfma_kernel<true, 128, 256, unsigned short, false, false, false>"],

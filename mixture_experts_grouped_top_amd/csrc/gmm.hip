@@ -1478,6 +1478,223 @@ __global__ __launch_bounds__(NT, 2) void tgmm_short_kernel(MfmaArgs a) {
   tgmm_short_loop<TO>(a, smem, row_base, unit_base, blockIdx.x, gridDim.x);
 }
 
+// Weight gradients of groups whose contraction takes S steps (S = 2: 33 ..
+// 64 rows, S = 4: 65 .. 128 rows): the short kernel's scheme with a
+// resident rhs strip of S steps, where the output staging has no LDS of its
+// own.  Per unit (group, 256-column strip, or a run of its tiles):
+//   * the rhs strip (the group's rows x 256, zero past them) goes into LDS
+//     through registers once;
+//   * the lhs block of each 128-row tile of Kdim (S steps of 32 rows x 128,
+//     rows past the group's repeating its last row, which the zero strip
+//     rows cancel) is copied global -> LDS one tile ahead, into the other
+//     half of a double buffer;
+//   * once every wave has read its fragments of a tile's block, the block is
+//     free and the tile's epilogue stages its output there, each wave in
+//     its own quarter; the next tile's block is already in the other half,
+//     so its wait leaves the stores of this tile in flight (they are the
+//     youngest vector-memory instructions of the wave).
+// LDS: S = 2: 32 KB strip + 2 x 16 KB blocks, two workgroups per CU;
+// S = 4: 64 KB + 2 x 32 KB, one workgroup per CU.
+template <int S>
+struct Strip {
+  static constexpr int kStepB = 256 * TK * 2;     // one strip step (32 rows x 256)
+  static constexpr int kStepA = 128 * TK * 2;     // one lhs block step (32 rows x 128)
+  static constexpr int kB = S * kStepB;
+  static constexpr int kA = S * kStepA;
+  static constexpr int kBytes = kB + 2 * kA;
+  static constexpr int kWaveStage = kA / 4;       // a wave's staging bytes in a free block
+  static constexpr int kRows = kWaveStage / 512;  // float32 rows of 128 columns per staging round
+};
+
+// Write a 128 x 256 accumulator tile through a wave's own staging region of
+// ROWS x 128 float32 (unpadded 512-byte rows; in rows with bit 2 set the
+// 8-column chunks are swapped with the ones 32 columns away, so the two
+// half-waves of a write, 4 rows apart, hit different banks).  rows >= rv
+// and columns >= cv are skipped.  No workgroup barrier: the region is the
+// wave's alone until the caller's next barrier.
+template <typename TO, int ROWS>
+__device__ __forceinline__ void store_tile_staged(const Acc<128, 256>& acc, char* region, TO* o,
+                                                  int64_t ldo, int rv, int cv, int accumulate) {
+  constexpr int TM = 128, WC = 128;
+  constexpr int CPR = WC / 8;                 // 8-column chunks per staged row
+  constexpr int NQ = ROWS * CPR / 64;         // chunks per lane per round
+  constexpr int RPS = 32 / ROWS;              // rounds per 32-row slab
+  static_assert(ROWS == 8 || ROWS == 16, "staging rounds of 8 or 16 rows");
+  const int tid = opaque_tid();
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = (w >> 1) * (TM / 2), wc = (w & 1) * WC;
+  const bool plain = !accumulate && wr + TM / 2 <= rv && wc + WC <= cv;
+#pragma unroll
+  for (int i = 0; i < Acc<TM, 256>::FM; ++i)
+#pragma unroll
+    for (int h = 0; h < RPS; ++h) {
+      // entries r of this round: rows 8 (r >> 2) + 4 (lane / 32) + (r & 3) - ROWS h
+#pragma unroll
+      for (int j = 0; j < Acc<TM, 256>::FN; ++j)
+#pragma unroll
+        for (int r = ROWS / 2 * h; r < ROWS / 2 * (h + 1); ++r) {
+          const int row = 8 * ((r >> 2) - ROWS / 8 * h) + 4 * (lane >> 5) + (r & 3);
+          const int col = (32 * j + (lane & 31)) ^ (row & 4 ? 32 : 0);
+          *reinterpret_cast<float*>(region + row * 512 + col * 4) = acc.v[i][j][r];
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float4 lo[NQ], hi[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int chunk = lane + 64 * q;
+        const int row = chunk / CPR, c8 = (chunk % CPR) ^ (row & 4 ? 4 : 0);
+        lo[q] = *reinterpret_cast<const float4*>(region + row * 512 + c8 * 32);
+        hi[q] = *reinterpret_cast<const float4*>(region + row * 512 + c8 * 32 + 16);
+      }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int chunk = lane + 64 * q;
+        const int row = chunk / CPR, c8 = chunk % CPR;
+        const int grow = wr + 32 * i + ROWS * h + row, gcol = wc + 8 * c8;
+        float v[8] = {lo[q].x, lo[q].y, lo[q].z, lo[q].w, hi[q].x, hi[q].y, hi[q].z, hi[q].w};
+        TO* p = o + static_cast<int64_t>(grow) * ldo + gcol;
+        if (plain) {
+          store8_nt(p, v);
+        } else if (grow < rv && gcol < cv) {
+          if (accumulate) {
+            float old[8];
+            load8(p, old);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += old[e];
+            store8(p, v);
+          } else {
+            store8_nt(p, v);
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+template <int S, typename TO>
+__device__ __forceinline__ void tgmm_strip_loop(const MfmaArgs& a, char* smem, const int* row_base,
+                                                const int* unit_base, int b, int nwg) {
+  constexpr int TM = 128, TN = 256;
+  using OA = Operand<true, TM>;
+  using OB = Operand<true, TN>;
+  using C = Strip<S>;
+  // vector-memory instructions per wave of a plain output tile (as in the
+  // short kernel)
+  constexpr int kStores = 16 * (sizeof(TO) == 2 ? 1 : 2);
+  char* const Bs = smem;
+  char* const As = smem + C::kB;                  // two lhs blocks
+  const int mtn = static_cast<int>((a.Kdim + TM - 1) / TM);
+  const int ntn = static_cast<int>((a.N + TN - 1) / TN);
+  // runs of a unit's tiles, chosen as in the short kernel
+  const int64_t units = unit_base[a.G];
+  int parts = 1;
+  {
+    int64_t best = (units + nwg - 1) / nwg * 100;
+    for (int p = 2; p <= 4 && p <= mtn; ++p) {
+      const int64_t c = (units * p + nwg - 1) / nwg * 100 / p + 2 * (p - 1);
+      if (c < best) {
+        best = c;
+        parts = p;
+      }
+    }
+  }
+  const int64_t total = units * parts;
+  TO* out = static_cast<TO*>(a.out);
+  OB B;
+  ShortLhs A;
+  Acc<TM, TN> acc;
+  uint32_t fa[4], fb[4];
+  OA::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
+  OB::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int it = 0;; ++it) {
+    const int64_t vunit = xcd_index(it, b, nwg);
+    if (vunit >= total) break;
+    const int64_t unit = vunit / parts;
+    const int part = static_cast<int>(vunit - unit * parts);
+    const int mt_lo = part * mtn / parts, mt_hi = (part + 1) * mtn / parts;
+    const int g = find_group(unit_base, a.G, unit);
+    const int nt = static_cast<int>(unit - unit_base[g]);
+    const int64_t r0 = row_base[g];
+    // the class holds groups of more than 32 (S / 2) rows: every step up
+    // to ns has rows, and steps past ns are neither loaded nor multiplied
+    const int rows_g = min(tgmm_rows(a, row_base, g), TK * S);
+    const int ns = (rows_g + TK - 1) / TK;
+    const int64_t n0 = static_cast<int64_t>(nt) * TN;
+    const int nv = static_cast<int>(lmin(TN, a.N - n0));
+    const bf16_t* lhs_g = a.lhs + r0 * a.ld_lhs;
+    // every wave is done with the previous unit's LDS (barrier at its end)
+    B.setup(a.rhs + r0 * a.ld_rhs + n0, a.ld_rhs, nv);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (s < ns) {
+        uint4 t[OB::NR];
+        B.tail_load(s, rows_g - TK * s, t);
+        B.tail_store(Bs + s * C::kStepB, t);
+      }
+    auto copy_block = [&](int mt, char* dst) {
+      const int64_t m0 = static_cast<int64_t>(mt) * TM;
+      const int mv = static_cast<int>(lmin(TM, a.Kdim - m0));
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if (s < ns) {
+          A.setup(a.ld_lhs, mv, min(TK, rows_g - TK * s));
+          A.dma(lhs_g + static_cast<int64_t>(TK) * s * a.ld_lhs + m0,
+                lds_addr(dst + s * C::kStepA));
+        }
+    };
+    copy_block(mt_lo, As);
+    bool drain = true;   // the wait below must also cover the previous stores
+    for (int mt = mt_lo; mt < mt_hi; ++mt) {
+      const int64_t m0 = static_cast<int64_t>(mt) * TM;
+      const int mv = static_cast<int>(lmin(TM, a.Kdim - m0));
+      char* const cur = As + ((mt - mt_lo) & 1) * C::kA;
+      // this tile's block: everything issued after its copy is the previous
+      // tile's stores, which may stay in flight
+      if (drain) wait_vmcnt<0>(); else wait_vmcnt<kStores>();
+      __syncthreads();   // the block (and strip) visible; the other half's staging done
+      if (mt + 1 < mt_hi) copy_block(mt + 1, As + ((mt + 1 - mt_lo) & 1) * C::kA);
+      acc.zero();
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if (s < ns) {
+          typename Acc<TM, TN>::Frags f;
+          Acc<TM, TN>::template load<OA, OB>(f, cur + s * C::kStepA, Bs + s * C::kStepB, fa, fb, 0);
+          acc.mma(f);
+          Acc<TM, TN>::template load<OA, OB>(f, cur + s * C::kStepA, Bs + s * C::kStepB, fa, fb, 1);
+          acc.mma(f);
+        }
+      __syncthreads();   // every wave has its fragments: the block becomes staging
+      // a plain epilogue issues exactly kStores vector-memory instructions
+      drain = a.accumulate || (w >> 1) * (TM / 2) + TM / 2 > mv || (w & 1) * (TN / 2) + TN / 2 > nv;
+      store_tile_staged<TO, C::kRows>(acc, cur + w * C::kWaveStage,
+                                      out + g * a.out_gs + m0 * a.ld_out + n0, a.ld_out, mv, nv,
+                                      a.accumulate);
+    }
+    __syncthreads();   // the unit's LDS is refilled by the next unit
+  }
+}
+
+// Weight gradients of the groups with 32 S / 2 + 1 .. 32 S contraction rows
+// (cls_lo .. cls_hi), every workgroup taking units (tgmm_strip_loop).
+template <int S, typename TO>
+__global__ __launch_bounds__(NT, S <= 2 ? 2 : 1) void tgmm_strip_kernel(MfmaArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[Strip<S>::kBytes];
+  __shared__ int row_base[kMaxGShort + 1];
+  __shared__ int unit_base[kMaxGShort + 1];
+  scan_groups(a.gsz, a.G, a.M, 128, 1, row_base, nullptr, nullptr);
+  __syncthreads();
+  scan_class_units(a, row_base, max(a.cls_lo, TK * S / 2 + 1), min(a.cls_hi, TK * S),
+                   static_cast<int>((a.N + 255) / 256), unit_base);
+  __syncthreads();
+  tgmm_strip_loop<S, TO>(a, smem, row_base, unit_base, blockIdx.x, gridDim.x);
+}
+
 // ---------------------------------------------------------------- fp8 MFMA
 //
 // FP8 operands (the quantization=fp8 run of the MaxText grouped-GEMM pull
@@ -2214,21 +2431,35 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
   hipLaunchKernelGGL((tgmm_mfma_kernel<TMc, 256, TOc>), dim3(GRID), dim3(NT), 0, st, ARGS)
 #define TGMMS(TOc, ARGS, GRID) \
   hipLaunchKernelGGL((tgmm_short_kernel<TOc>), dim3(GRID), dim3(NT), 0, st, ARGS)
+#define TGMMR(Sc, TOc, ARGS, GRID) \
+  hipLaunchKernelGGL((tgmm_strip_kernel<Sc, TOc>), dim3(GRID), dim3(NT), 0, st, ARGS)
+#ifndef STRIP_MAX
+#define STRIP_MAX 128
+#endif
     if (short_k) {
-      MfmaArgs s_ = a, m_ = a, b_ = a;
+      MfmaArgs s_ = a, r2_ = a, r4_ = a, m_ = a, b_ = a;
       s_.cls_hi = kShortRows;
-      m_.cls_lo = kShortRows + 1;
+      r2_.cls_lo = kShortRows + 1;
+      r2_.cls_hi = 2 * kShortRows;
+      r4_.cls_lo = 2 * kShortRows + 1;
+      r4_.cls_hi = 4 * kShortRows;
+      m_.cls_lo = STRIP_MAX + 1;
       m_.cls_hi = kSplitRows;
       b_.cls_lo = kSplitRows + 1;
-      m_.err = b_.err = nullptr;   // the first launch reports the group-size check
-      const unsigned gs_ = persistent_grid(static_cast<int64_t>(G) * ((N + 255) / 256), 2);
+      r2_.err = r4_.err = m_.err = b_.err = nullptr;   // the first launch checks the group sizes
+      const int64_t units = static_cast<int64_t>(G) * ((N + 255) / 256);
+      const unsigned gs_ = persistent_grid(units, 2), g4_ = persistent_grid(units, 1);
       const unsigned gm_ = grid_for(128, 2), gb_ = grid_for(256, 1);
       if (out_dtype == MOE_BF16) {
         TGMMS(bf16_t, s_, gs_);
+        if (STRIP_MAX >= 64) TGMMR(2, bf16_t, r2_, gs_);
+        if (STRIP_MAX >= 128) TGMMR(4, bf16_t, r4_, g4_);
         TGMM(128, bf16_t, m_, gm_);
         TGMM(256, bf16_t, b_, gb_);
       } else {
         TGMMS(float, s_, gs_);
+        if (STRIP_MAX >= 64) TGMMR(2, float, r2_, gs_);
+        if (STRIP_MAX >= 128) TGMMR(4, float, r4_, g4_);
         TGMM(128, float, m_, gm_);
         TGMM(256, float, b_, gb_);
       }
@@ -2236,6 +2467,7 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
       const unsigned grid = grid_for(256, 1);
       if (out_dtype == MOE_BF16) TGMM(256, bf16_t, a, grid); else TGMM(256, float, a, grid);
     }
+#undef TGMMR
 #undef TGMMS
 #undef TGMM
   } else {

@@ -349,6 +349,8 @@ GS = {
     "mixed": [30, 700, 0, 385, 384, 1100, 5, 0, 129, 40],
     # contractions of at most 64 rows (one or two steps, full and ragged)
     "shortk": [33, 64, 47, 0, 5, 63, 32, 1, 17],
+    # contractions of 65 .. 128 rows (three or four steps), beside shorter ones
+    "midk": [65, 128, 96, 0, 97, 100, 127, 3, 70, 40],
 }
 
 GMM_CASES = [
@@ -576,12 +578,17 @@ def test_gmm_swiglu_bwd(gpu_lib, case):
 
 
 @pytest.mark.parametrize("it", ["bf16", "f32"])
-def test_tgmm_valid_rows(gpu_lib, it):
+@pytest.mark.parametrize("sizes", [
+    ([300, 0, 257, 128, 1000], [299, 0, 1, 0, 613]),
+    # valid rows in the 33..64 and 65..128 classes, groups longer than that
+    ([200, 150, 100, 90, 64, 256], [33, 65, 100, 64, 40, 128]),
+], ids=["classes_short_mid_large", "classes_two_and_four_steps"])
+def test_tgmm_valid_rows(gpu_lib, it, sizes):
     """With valid_rows the contraction stops after each group's first
     valid_rows[g] rows: rows past them (garbage here) must not contribute,
     and the result equals the oracle over the rows with the rest zeroed."""
-    gs = np.array([300, 0, 257, 128, 1000], dtype=np.int32)
-    valid = np.array([299, 0, 1, 0, 613], dtype=np.int32)
+    gs = np.array(sizes[0], dtype=np.int32)
+    valid = np.array(sizes[1], dtype=np.int32)
     Kd, N = 264, 136
     g = np.random.default_rng(11)
     M = int(gs.sum())
@@ -720,6 +727,11 @@ TGMM_CASES = [
     ("shortk", 136, 520, "bf16", "f32", True),
     ("shortk", 1032, 72, "bf16", "bf16", False),
     ("shortk", 8, 8, "bf16", "bf16", True),
+    # contractions of 65 .. 128 rows: ragged Kdim and N, partial sums, f32 out
+    ("midk", 200, 264, "bf16", "bf16", False),
+    ("midk", 136, 520, "bf16", "f32", True),
+    ("midk", 1032, 72, "bf16", "bf16", False),
+    ("midk", 8, 8, "bf16", "f32", False),
 ]
 
 
