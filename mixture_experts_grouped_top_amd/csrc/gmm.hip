@@ -805,12 +805,14 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
                      wc + WC <= cv;
 #pragma unroll
   for (int i = 0; i < Acc<TM, TN>::FM; ++i) {
-    // partial sums (PF): all of the slab's old values are requested before
-    // the slab is staged (one load round trip per slab, overlapping the
-    // staging); the FP8 tgmm, which is slower with it (its epilogue
-    // spills more), loads them chunk by chunk
-    Raw8<TO> prev[PF ? NQ : 1];
-    if (PF && accumulate) {
+    // bf16 partial sums (PF): all of the slab's old values are requested
+    // before the slab is staged (one load round trip per slab, overlapping
+    // the staging, 32 registers); float32 partial sums (64 registers, which
+    // the 256 x 256 epilogues would spill) and the FP8 tgmm, which is
+    // slower with it, load them chunk by chunk
+    constexpr bool kPre = PF && sizeof(TO) == 2;
+    Raw8<TO> prev[kPre ? NQ : 1];
+    if (kPre && accumulate) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int chunk = lane + 64 * q;
@@ -857,7 +859,7 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
       if (grow < rv && gcol < cv) {
         if (accumulate) {
           float old[8];
-          if constexpr (PF) prev[q].get(old);
+          if constexpr (kPre) prev[q].get(old);
           else load8(p, old);
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] += old[e];
