@@ -32,9 +32,17 @@ def f64(t):
 
 
 def sampled_experts(counts):
+    """The largest, the smallest and the median non-empty expert, and the
+    smallest expert of each contraction-length class that the weight
+    gradients launch separately (33..64, 65..128, 129..384 rows), when the
+    load has one."""
     nz = np.where(counts > 0)[0]
     order = nz[np.argsort(counts[nz], kind="stable")]
     picks = {int(order[-1]), int(order[0]), int(order[len(order) // 2])}
+    for lo, hi in ((33, 64), (65, 128), (129, 384)):
+        inside = [int(e) for e in order if lo <= counts[e] <= hi]
+        if inside:
+            picks.add(inside[0])
     return sorted(picks)
 
 
