@@ -2417,13 +2417,14 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
     // short contractions (under 512 rows per group on average) leave each
     // tile's latency and stores exposed.  There the groups are split by the
     // rows their contraction covers (valid_rows, else the group size) into
-    // three launches: at most kShortRows rows in the short kernel (resident
+    // five launches: at most kShortRows rows in the short kernel (resident
     // rhs strip, lhs blocks copied ahead, stores of one tile overlapping
-    // the next), up to kSplitRows in 128 x 256 tiles (two workgroups per
-    // CU), the rest in 256 x 256 tiles (half the operand traffic per flop).
-    // On the DeepSeek-V3 shape: 2.7 ms per launch in one 128-row launch ->
-    // ~2.3 ms.  (256-row tiles for the mid-sized groups took 0.9 ms more.)
-    // Otherwise one launch of 256 x 256 tiles does every group.
+    // the next), 33..64 and 65..128 rows in the strip kernels (the same
+    // scheme over two and four steps), up to kSplitRows in 128 x 256 tiles
+    // (two workgroups per CU), the rest in 256 x 256 tiles (half the operand
+    // traffic per flop).  On the DeepSeek-V3 shape: 2.7 ms per launch in one
+    // 128-row launch -> 2.4 ms.  (256-row tiles for the mid-sized groups took
+    // 0.9 ms more.)  Otherwise one launch of 256 x 256 tiles does every group.
     const bool short_k = M < 512 * static_cast<int64_t>(G) && G <= kMaxGShort;
     auto grid_for = [&](int TMv, int per_cu) {
       return persistent_grid(static_cast<int64_t>(G) * ((Kdim + TMv - 1) / TMv) * ((N + 255) / 256),
@@ -2435,9 +2436,6 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
   hipLaunchKernelGGL((tgmm_short_kernel<TOc>), dim3(GRID), dim3(NT), 0, st, ARGS)
 #define TGMMR(Sc, TOc, ARGS, GRID) \
   hipLaunchKernelGGL((tgmm_strip_kernel<Sc, TOc>), dim3(GRID), dim3(NT), 0, st, ARGS)
-#ifndef STRIP_MAX
-#define STRIP_MAX 128
-#endif
     if (short_k) {
       MfmaArgs s_ = a, r2_ = a, r4_ = a, m_ = a, b_ = a;
       s_.cls_hi = kShortRows;
@@ -2445,7 +2443,7 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
       r2_.cls_hi = 2 * kShortRows;
       r4_.cls_lo = 2 * kShortRows + 1;
       r4_.cls_hi = 4 * kShortRows;
-      m_.cls_lo = STRIP_MAX + 1;
+      m_.cls_lo = 4 * kShortRows + 1;
       m_.cls_hi = kSplitRows;
       b_.cls_lo = kSplitRows + 1;
       r2_.err = r4_.err = m_.err = b_.err = nullptr;   // the first launch checks the group sizes
@@ -2454,14 +2452,14 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
       const unsigned gm_ = grid_for(128, 2), gb_ = grid_for(256, 1);
       if (out_dtype == MOE_BF16) {
         TGMMS(bf16_t, s_, gs_);
-        if (STRIP_MAX >= 64) TGMMR(2, bf16_t, r2_, gs_);
-        if (STRIP_MAX >= 128) TGMMR(4, bf16_t, r4_, g4_);
+        TGMMR(2, bf16_t, r2_, gs_);
+        TGMMR(4, bf16_t, r4_, g4_);
         TGMM(128, bf16_t, m_, gm_);
         TGMM(256, bf16_t, b_, gb_);
       } else {
         TGMMS(float, s_, gs_);
-        if (STRIP_MAX >= 64) TGMMR(2, float, r2_, gs_);
-        if (STRIP_MAX >= 128) TGMMR(4, float, r4_, g4_);
+        TGMMR(2, float, r2_, gs_);
+        TGMMR(4, float, r4_, g4_);
         TGMM(128, float, m_, gm_);
         TGMM(256, float, b_, gb_);
       }
