@@ -1330,6 +1330,25 @@ __device__ __forceinline__ void store_tile_halves(const Acc<128, 256>& acc, char
 // in LDS: the copy repeats the last row there, and the zero rhs rows cancel
 // them.  Groups with no rows write zero blocks (or keep the partial sum).
 // Units are listed in unit_base (ntn per group).
+// Runs a unit's mtn tiles are taken in, by different workgroups of the
+// persistent grid of nwg: with units a few times the grid, whole units leave
+// the last round part-empty (1264 units on 512 workgroups: three rounds of
+// work for 2.47).  The run count (1 .. 4, at most mtn) minimises rounds /
+// runs, a unit's length in rounds, with 2% of a unit charged per extra run
+// for its second rhs strip load and pipeline start.
+__device__ __forceinline__ int unit_runs(int64_t units, int nwg, int mtn) {
+  int parts = 1;
+  int64_t best = (units + nwg - 1) / nwg * 100;
+  for (int p = 2; p <= 4 && p <= mtn; ++p) {
+    const int64_t c = (units * p + nwg - 1) / nwg * 100 / p + 2 * (p - 1);
+    if (c < best) {
+      best = c;
+      parts = p;
+    }
+  }
+  return parts;
+}
+
 constexpr int kShortRows = TK;
 constexpr int kShortB = 256 * TK * 2;                        // resident rhs strip
 constexpr int kShortA = 128 * TK * 2;                        // one lhs block
@@ -1378,24 +1397,8 @@ __device__ __forceinline__ void tgmm_short_loop(const MfmaArgs& a, char* smem, c
   char* const Ss = smem + kShortB + 2 * kShortA;  // output staging
   const int mtn = static_cast<int>((a.Kdim + TM - 1) / TM);
   const int ntn = static_cast<int>((a.N + TN - 1) / TN);
-  // A unit's tiles may be taken in `parts` runs of consecutive tiles by
-  // different workgroups: with units a few times the grid, whole units
-  // leave the last round part-empty (1264 units on 512 workgroups: three
-  // rounds of work for 2.47).  parts (1 .. 4) minimises rounds / parts, a
-  // unit's length in rounds, with 2% of a unit charged per extra part for
-  // its second rhs strip load and pipeline start.
   const int64_t units = unit_base[a.G];
-  int parts = 1;
-  {
-    int64_t best = (units + nwg - 1) / nwg * 100;
-    for (int p = 2; p <= 4 && p <= mtn; ++p) {
-      const int64_t c = (units * p + nwg - 1) / nwg * 100 / p + 2 * (p - 1);
-      if (c < best) {
-        best = c;
-        parts = p;
-      }
-    }
-  }
+  const int parts = unit_runs(units, nwg, mtn);
   const int64_t total = units * parts;
   TO* out = static_cast<TO*>(a.out);
   OB B;
@@ -1592,19 +1595,8 @@ __device__ __forceinline__ void tgmm_strip_loop(const MfmaArgs& a, char* smem, c
   char* const As = smem + C::kB;                  // two lhs blocks
   const int mtn = static_cast<int>((a.Kdim + TM - 1) / TM);
   const int ntn = static_cast<int>((a.N + TN - 1) / TN);
-  // runs of a unit's tiles, chosen as in the short kernel
   const int64_t units = unit_base[a.G];
-  int parts = 1;
-  {
-    int64_t best = (units + nwg - 1) / nwg * 100;
-    for (int p = 2; p <= 4 && p <= mtn; ++p) {
-      const int64_t c = (units * p + nwg - 1) / nwg * 100 / p + 2 * (p - 1);
-      if (c < best) {
-        best = c;
-        parts = p;
-      }
-    }
-  }
+  const int parts = unit_runs(units, nwg, mtn);
   const int64_t total = units * parts;
   TO* out = static_cast<TO*>(a.out);
   OB B;
