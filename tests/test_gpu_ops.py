@@ -351,6 +351,8 @@ GS = {
     "shortk": [33, 64, 47, 0, 5, 63, 32, 1, 17],
     # contractions of 65 .. 128 rows (three or four steps), beside shorter ones
     "midk": [65, 128, 96, 0, 97, 100, 127, 3, 70, 40],
+    # 900 groups of 0 .. 128 rows: every short class, group tables near their limit
+    "many_short": [(i * 37) % 129 for i in range(900)],
 }
 
 GMM_CASES = [
@@ -732,6 +734,8 @@ TGMM_CASES = [
     ("midk", 136, 520, "bf16", "f32", True),
     ("midk", 1032, 72, "bf16", "bf16", False),
     ("midk", 8, 8, "bf16", "f32", False),
+    ("many_short", 136, 264, "bf16", "bf16", False),
+    ("many_short", 72, 136, "bf16", "f32", True),
 ]
 
 
