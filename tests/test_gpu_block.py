@@ -219,6 +219,57 @@ def check_backward_fp8(w, inp, plan, f, b):
         assert (host(getattr(plan, k))[empty] == 0).all()
 
 
+def test_chain_fp8_steps(chain):
+    """Each FP8 GEMM of the chain against the oracle on the GPU's own codes
+    and scales (its inputs as quantized in the chain, dequantized in
+    float64), at the bf16 tolerance: the loose chain tolerances above come
+    only from quantizing differently computed intermediates, not from the
+    GEMMs."""
+    w, inp, plan, f, b = chain
+    if not plan.s.fp8:
+        return
+    from oracle import fp8 as F8
+    gs = f["perm"]["group_sizes"].astype(np.int64)
+    counts = host(plan.idx["counts"]).astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(gs)])
+    rows = plan.rows
+    kept = np.zeros(rows, dtype=bool)
+    for e in range(len(gs)):
+        kept[off[e]:off[e] + counts[e]] = True
+    assert kept.any()
+
+    def deq(name, fmt):
+        qr, _, sc = plan.q8[name]
+        si = host(sc[2]).astype(np.float64)
+        return F8.dequantize(host(qr), fmt, si if si.size > 1 else si[0])
+
+    def valid_only(a):
+        a = a.copy()
+        a[~kept[:a.shape[0]]] = 0
+        return a
+
+    X, A = deq("x", "e4m3"), deq("act", "e4m3")
+    DY = deq("d_y_sorted", "e5m2")
+    DH = [deq("d_h0", "e5m2"), deq("d_h1", "e5m2")]
+    W = {k: deq(k, "e4m3") for k in ("wi_0", "wi_1", "wo")}
+    mlp = inp["mlp"] or {}
+    # forward: y_sorted from the quantized act (rows past the kept ones are
+    # not read unless MLP biases make them non-zero)
+    A_in = A if plan.vact is None else valid_only(A)
+    y = oracle.gmm(A_in, W["wo"], gs, rows_out=rows, bias=mlp.get("wo"))
+    assert_close(host(plan.y_sorted)[kept], y[kept], TOL_BF16, "y_sorted on the chain's codes")
+    # backward: d_act, d_wo, d_x_sorted, d_wi_0, d_wi_1
+    d_act = oracle.gmm(DY, W["wo"], gs, trans_rhs=True, rows_out=rows)
+    assert_close(host(plan.d_act)[kept], d_act[kept], TOL_BF16, "d_act on the chain's codes")
+    assert_close(host(plan.d_wo), oracle.tgmm(valid_only(A), DY, gs), TOL_BF16,
+                 "d_wo on the chain's codes")
+    d_x = sum(oracle.gmm(DH[i], W[f"wi_{i}"], gs, trans_rhs=True, rows_out=rows) for i in range(2))
+    assert_close(host(plan.d_x_sorted)[kept], d_x[kept], TOL_BF16, "d_x_sorted on the chain's codes")
+    for i in range(2):
+        assert_close(host(getattr(plan, f"d_wi_{i}")), oracle.tgmm(valid_only(X), DH[i], gs),
+                     TOL_BF16, f"d_wi_{i} on the chain's codes")
+
+
 def test_chain_deterministic():
     """Two runs of the whole chain give bitwise-identical outputs (all
     reductions are ordered; no float atomics)."""
