@@ -2,7 +2,7 @@
 """MoE expert-FFN forward+backward throughput on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
-                    [--extra-workloads deepseek_v3,token_drop] [--fp8] [--fused-wi]
+                    [--extra-workloads deepseek_v3,token_drop] [--fp8] [--fused-wi] [--graph]
 
 A step is one pass of the whole path over one batch of synthetic input:
 router GEMM, top-k routing, permute, the up-projection grouped GEMMs,
@@ -16,7 +16,8 @@ backward).  Inputs are resident in HBM before the timed region starts.
 shape by default): 18 * R * d_model * d_ff algorithmic flops per step
 (R = kept routed rows; padding rows and the router GEMM excluded) divided
 by the step time, which is taken over K steps with no other events in the
-stream.  A second pass of the same steps brackets every expert GEMM and
+stream (with --graph, K replays of one step captured into a HIP graph).
+A second pass of the same steps brackets every expert GEMM and
 memory-bound call with events, each after a 1 GiB scratch write that
 evicts the 256 MB memory-side cache, and classifies each kind of call by
 its own roofline: MFMA-bound when flops / peak exceeds algorithmic bytes /
@@ -70,6 +71,8 @@ def parse():
                    help="one [E, D, 2F] up-projection weight [wi_0 | wi_1]")
     p.add_argument("--fp8", action="store_true",
                    help="FP8 expert GEMMs (e4m3 forward, e5m2 backward, current scaling)")
+    p.add_argument("--graph", action="store_true",
+                   help="time the steps as replays of one step captured into a HIP graph")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="skip the per-call pass (only the step timing runs)")
@@ -456,6 +459,17 @@ def measure(name: str, args, headline: bool, inputs=None, capacity_layout: bool 
     for _ in range(max(0, args.warmup - 1)):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # the step's launches captured once (the plan owns every buffer, so
+        # the capture allocates nothing) and replayed as one graph
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        run()
+        torch.cuda.synchronize()
 
     # pass 1: the step time, nothing but the path's own launches in the stream
     start = torch.cuda.Event(enable_timing=True)
@@ -465,7 +479,7 @@ def measure(name: str, args, headline: bool, inputs=None, capacity_layout: bool 
     try:
         start.record()
         for _ in range(args.steps):
-            step()
+            run()
         end.record()
         torch.cuda.synchronize()
     finally:
@@ -527,7 +541,8 @@ def measure(name: str, args, headline: bool, inputs=None, capacity_layout: bool 
                    "experts": w.E, "top_k": w.K, "score": w.score, "renorm": w.renorm,
                    "align_size": w.align, "capacity": w.capacity, "chunks": w.n_chunks,
                    "fused_wi": bool(args.fused_wi), "fp8": bool(args.fp8),
-                   "capacity_layout": bool(capacity_layout), "routed_rows": R,
+                   "capacity_layout": bool(capacity_layout), "graph": bool(args.graph),
+                   "routed_rows": R,
                    "padded_rows": plan.padded_rows, "nonempty_experts": plan.nonempty_groups},
         "roofline": roofline,
         "kernels": {kk: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
