@@ -346,10 +346,12 @@ int moe_group_sum(const void* in, int64_t ld_in, int in_dtype, const int32_t* gr
 /* ------------------------------------------------------------------- FP8
  * The quantization=fp8 recipe of [MT-GG] (current-tensor scaling, e4m3 in
  * the forward, e5m2 in the backward, two quantized copies of each operand)
- * with the per-expert weight amax of [TE-MoE] commit notes.  Every FP8 GEMM
- * below takes both operands contraction-contiguous; the quantizer writes the
- * transposed copy a GEMM needs.  FP8 buffers are bytes; strides in bytes
- * (= elements).
+ * with the per-expert weight amax of [TE-MoE] commit notes.  moe_tgmm_fp8
+ * takes both operands contraction-contiguous (the quantizer writes the
+ * transposed copies of activations and gradients); moe_gmm_fp8 reads its
+ * weight operand in either orientation, so one row-wise copy of a weight
+ * serves the forward and the d_lhs product.  FP8 buffers are bytes; strides
+ * in bytes (= elements).
  */
 
 /* Workspace bytes of moe_fp8_amax_scale (16-byte aligned device memory). */
@@ -383,7 +385,7 @@ int64_t moe_fp8_padded_rows(int64_t rows, int G);
  *     to the group's next multiple of 64 are zero (the layout moe_tgmm_fp8
  *     reads).  qt_group_stride > 0: group g at qt + g * qt_group_stride as
  *     [cols, n_g] with row stride ld_qt (>= n_g); only the group's rows are
- *     written (the per-expert weight copy moe_gmm_fp8 reads).
+ *     written (a per-expert transposed weight copy).
  *   cols, ld, ld_q multiples of 8; ld_qt, qt_group_stride multiples of 16;
  *   16-byte aligned pointers.
  */
@@ -392,12 +394,15 @@ int moe_fp8_quantize(const void* x, int64_t ld, int dtype, int64_t rows, int64_t
                      void* q, int64_t ld_q, void* qt, int64_t ld_qt, int64_t qt_group_stride,
                      int32_t* err, void* stream);
 
-/* moe_gmm_fp8: grouped GEMM on FP8 operands (bf16 MFMA semantics of moe_gmm
- * with trans_rhs = 1):
- *   out[o_g + i, :] (+)= sa * sb[g] * lhs[o_g + i, :Kdim] . B_g^T (+ bias[g])
+/* moe_gmm_fp8: grouped GEMM on FP8 operands (the semantics of moe_gmm):
+ *   out[o_g + i, :] (+)= sa * sb[g] * lhs[o_g + i, :Kdim] . B_g (+ bias[g])
  *   lhs [M_lhs, Kdim] FP8 (lhs_fmt, row stride ld_lhs), sa = lhs_scale_inv[0];
- *   B_g = rhs + g * rhs_group_stride as [N, Kdim] (row stride ld_rhs, rhs_fmt),
- *   sb = rhs_scale_inv (device, [G]: per expert).  Products are exact and
+ *   trans_rhs = 1: B_g^T = rhs + g * rhs_group_stride as [N, Kdim] (row stride
+ *   ld_rhs >= Kdim); trans_rhs = 0: B_g as [Kdim, N] (row stride ld_rhs >= N,
+ *   each row spanning ld_rhs bytes: the chunk holding column N - 1 is read
+ *   whole), both in rhs_fmt; sb = rhs_scale_inv (device, [G]: per expert).  So
+ *   one row-wise copy of a [K, N] weight serves both the forward (trans_rhs =
+ *   0) and the d_lhs product (trans_rhs = 1).  Products are exact and
  *   accumulated in float32 by v_mfma_f32_32x32x64_f8f6f4; the scales are
  *   applied to the float32 sums.  valid_rows, bias: as in moe_gmm.  Output rows
  *   and accumulate as in moe_gmm.  Kdim, ld_lhs, ld_rhs, rhs_group_stride
@@ -405,7 +410,8 @@ int moe_fp8_quantize(const void* x, int64_t ld, int dtype, int64_t rows, int64_t
  */
 int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_fmt,
                 const float* lhs_scale_inv, const void* rhs, int64_t ld_rhs,
-                int64_t rhs_group_stride, int rhs_fmt, const float* rhs_scale_inv,
+                int64_t rhs_group_stride, int trans_rhs, int rhs_fmt,
+                const float* rhs_scale_inv,
                 const int32_t* group_sizes, const int32_t* valid_rows, int G, int64_t Kdim,
                 int64_t N, const void* bias,
                 void* out, int64_t M_out, int64_t ld_out, int out_dtype, int accumulate,

@@ -22,7 +22,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_BIAS_LOGIT, MOE_BIAS_SELECT = 0, 1
 MOE_DERR_EXPERT_ID, MOE_DERR_GROUP_SIZES, MOE_DERR_ROWS = 1, 2, 4
 MOE_FP8_E4M3, MOE_FP8_E5M2 = 0, 1
-ABI_VERSION = 11  # moe_abi_version() of the library these signatures describe
+ABI_VERSION = 12  # moe_abi_version() of the library these signatures describe
 
 # Entry points (name -> (restype, argtypes)); must match include/moe.h.
 _P, _I, _L, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -57,8 +57,8 @@ SIGNATURES = {
     "moe_fp8_amax_scale": (_I, [_P, _L, _I, _L, _L, _I, _I, _P, _P, _S, _P]),
     "moe_fp8_padded_rows": (_L, [_L, _I]),
     "moe_fp8_quantize": (_I, [_P, _L, _I, _L, _L, _P, _I, _P, _I, _I, _P, _L, _P, _L, _L, _P, _P]),
-    "moe_gmm_fp8": (_I, [_P, _L, _L, _I, _P, _P, _L, _L, _I, _P, _P, _P, _I, _L, _L, _P, _P, _L,
-                         _L, _I, _I, _P, _P]),
+    "moe_gmm_fp8": (_I, [_P, _L, _L, _I, _P, _P, _L, _L, _I, _I, _P, _P, _P, _I, _L, _L, _P, _P,
+                         _L, _L, _I, _I, _P, _P]),
     "moe_tgmm_fp8": (_I, [_P, _L, _I, _P, _P, _L, _I, _P, _P, _P, _I, _L, _L, _L, _P, _L, _L, _I,
                           _I, _P, _P]),
     "moe_swiglu": (_I, [_P, _P, _I, _L, _L, _L, _P, _I, _P]),
@@ -593,14 +593,16 @@ def moe_fp8_quantize(x, group_sizes, scale, fmt, per_group: bool = False, q=None
 
 def moe_gmm_fp8(lhs, lhs_fmt, lhs_scale_inv, rhs, rhs_fmt, rhs_scale_inv, group_sizes, out=None,
                 rows_out: Optional[int] = None, out_dtype=torch.bfloat16, accumulate: bool = False,
-                bias=None, err=None, stream=None, valid_rows=None):
-    """out[rows of g] (+)= sa sb[g] lhs[rows of g] . rhs[g]^T (+ bias[g]);
-    lhs uint8 [M, K] (2-D view), rhs uint8 [G, N, K] (3-D view, unit last
-    stride), scale_inv tensors float32 on the device."""
+                bias=None, err=None, stream=None, valid_rows=None, trans_rhs: bool = True):
+    """out[rows of g] (+)= sa sb[g] lhs[rows of g] . B_g (+ bias[g]); lhs
+    uint8 [M, K] (2-D view); rhs uint8 3-D view with unit last stride:
+    [G, N, K] holding B_g^T (trans_rhs) or [G, K, N] holding B_g; scale_inv
+    tensors float32 on the device."""
     M_lhs, Kd = lhs.shape
-    if rhs.dim() != 3 or rhs.stride(2) != 1 or rhs.shape[2] != Kd:
-        raise MoeError("rhs must be a [G, N, K] view with unit last stride")
-    G, N = rhs.shape[0], rhs.shape[1]
+    if rhs.dim() != 3 or rhs.stride(2) != 1 or rhs.shape[2 if trans_rhs else 1] != Kd:
+        raise MoeError("rhs must be a [G, N, K] (trans_rhs) or [G, K, N] view with unit last "
+                       "stride")
+    G, N = rhs.shape[0], rhs.shape[1 if trans_rhs else 2]
     if out is None:
         out = torch.empty((M_lhs if rows_out is None else rows_out, N), dtype=out_dtype,
                           device=lhs.device)
@@ -608,7 +610,8 @@ def moe_gmm_fp8(lhs, lhs_fmt, lhs_scale_inv, rhs, rhs_fmt, rhs_scale_inv, group_
         _contig(bias, "bias")
     _check(load().moe_gmm_fp8(_ptr(lhs), M_lhs, _rowmajor(lhs, "lhs"), _fmt(lhs_fmt),
                               _ptr(lhs_scale_inv), _ptr(rhs), rhs.stride(1), rhs.stride(0),
-                              _fmt(rhs_fmt), _ptr(rhs_scale_inv), _ptr(group_sizes),
+                              int(bool(trans_rhs)), _fmt(rhs_fmt), _ptr(rhs_scale_inv),
+                              _ptr(group_sizes),
                               _ptr(valid_rows), G, Kd, N,
                               _ptr(bias), _ptr(out), out.shape[0], _rowmajor(out, "out"),
                               _dtype_code(out), int(bool(accumulate)), _ptr(err),

@@ -165,10 +165,10 @@ class MoEPlan:
                                  ("d_h1", self.rows, F)):
             q[name] = (torch.empty((rows, cols), **u8), torch.empty((cols, self.P8), **u8),
                        torch.empty((3, 1), **f32))
-        # weights [E, a, b]: row-wise [E, a, b] and per-expert transposed [E, b, a]
+        # weights [E, a, b]: the row-wise copy only; the forward reads it as
+        # [K, N] and the d_lhs product as [N, K]
         for name, a, b in (("wi_0", D, F), ("wi_1", D, F), ("wo", F, D)):
-            q[name] = (torch.empty((E, a, b), **u8), torch.empty((E, b, a), **u8),
-                       torch.empty((3, E), **f32))
+            q[name] = (torch.empty((E, a, b), **u8), None, torch.empty((3, E), **f32))
         self.w_rows = {D: torch.full((E,), D, dtype=torch.int32, device=dev),
                        F: torch.full((E,), F, dtype=torch.int32, device=dev)}
         ws = max(B.moe_fp8_scale_workspace(self.lhs_rows, max(D, F), 1),
@@ -186,14 +186,14 @@ class MoEPlan:
                                stream=stream)
 
     def _quant_weight(self, name, w, stream):
-        qr, qt, sc = self.q8[name]
+        qr, _, sc = self.q8[name]
         E, a, b = w.shape
         w2 = w.reshape(E * a, b)
-        with self._rec("fp8_quantize", nbytes=w.numel() * (2 * w.element_size() + 2)):
+        # algorithmic bytes: w read twice (amax, quantize), one FP8 copy written
+        with self._rec("fp8_quantize", nbytes=w.numel() * (2 * w.element_size() + 1)):
             B.moe_fp8_amax_scale(w2, "e4m3", G=E, scales=sc, workspace=self.f8_ws, stream=stream)
             B.moe_fp8_quantize(w2, self.w_rows[a], sc[1], "e4m3", per_group=True,
-                               q=qr.view(E * a, b), qt=qt, qt_group_stride=a * b, ld_qt=a,
-                               err=self.err, stream=stream)
+                               q=qr.view(E * a, b), err=self.err, stream=stream)
 
     def _forward_fp8(self, wi_0, wi_1, wo, mb, stream):
         s, q = self.s, self.q8
@@ -203,18 +203,18 @@ class MoEPlan:
             self._quant_weight(name, w, stream)
         xq, _, sx = q["x"]
         for name, h in (("wi_0", self.h0), ("wi_1", self.h1)):
-            _, wt, sw = q[name]
+            wr, _, sw = q[name]
             with self._rec("gmm_nn", 2.0 * R * s.D * s.F, self._gb("gmm", s.D, s.F, in_b=1)):
-                B.moe_gmm_fp8(xq, "e4m3", sx[2], wt, "e4m3", sw[2], gs, valid_rows=self.vrows, out=h, bias=mb.get(name),
-                              err=self.err, stream=stream)
+                B.moe_gmm_fp8(xq, "e4m3", sx[2], wr, "e4m3", sw[2], gs, valid_rows=self.vrows, out=h, bias=mb.get(name),
+                              trans_rhs=False, err=self.err, stream=stream)
         with self._rec("swiglu", nbytes=self._bytes().get("swiglu", 0) if self.recorder else 0):
             B.moe_swiglu(self.h0, self.h1, act=self.act, stream=stream)
         self._quant("act", self.act, "e4m3", stream)
         aq, _, sa = q["act"]
-        _, wt, sw = q["wo"]
+        wr, _, sw = q["wo"]
         with self._rec("gmm_nn", 2.0 * R * s.D * s.F, self._gb("gmm", s.F, s.D, in_b=1)):
-            B.moe_gmm_fp8(aq, "e4m3", sa[2], wt, "e4m3", sw[2], gs, valid_rows=self.vact, out=self.y_sorted,
-                          bias=mb.get("wo"), err=self.err, stream=stream)
+            B.moe_gmm_fp8(aq, "e4m3", sa[2], wr, "e4m3", sw[2], gs, valid_rows=self.vact, out=self.y_sorted,
+                          bias=mb.get("wo"), trans_rhs=False, err=self.err, stream=stream)
 
     def _backward_fp8(self, stream):
         s, q = self.s, self.q8

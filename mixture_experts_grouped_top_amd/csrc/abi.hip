@@ -13,4 +13,4 @@ MOE_API const char* moe_status_string(int status) {
   }
 }
 
-MOE_API int moe_abi_version(void) { return 11; }
+MOE_API int moe_abi_version(void) { return 12; }

@@ -1752,6 +1752,106 @@ struct Fp8Args {
   const bf16_t* bias;    // gmm: [G, N] or null
 };
 
+// A contraction-major FP8 operand of BX = 256 columns: element (x, k) at
+// byte k * ld + x of the source (a [K, N] weight as stored), one step = 64
+// contraction rows.  LDS rows of 256 bytes; the 16-byte chunk c of row k sits
+// at position c ^ 2 (k & 7).  A transposing read (ds_read_b64_tr_b8) lets
+// each 16-lane group address an 8-row x 16-byte block (lane 2 r + q: row r,
+// bytes 8 q .. 8 q + 7) and gives lane j the bytes of column j for rows
+// 0..7, in row order.  The 32 lanes of a half-wave read the same 8 rows of
+// 32 columns, two chunks per row, which the swizzle places on 16 distinct
+// chunk positions (all 64 banks).  Fragment (i, s) of lane l: column
+// xw + 32 i + l % 32, contraction rows 32 s + 16 (l / 32) + 0..15 in order,
+// the bytes a row-tile fragment holds for the same k, so the two layouts
+// feed one MFMA.  Columns past the valid extent are clamped to the last
+// valid chunk (their products land in columns that are never stored); the
+// chunk holding column xv - 1 is read whole, which stays inside the row's
+// ld bytes because ld is a multiple of 16.
+template <int BX>
+struct F8Col {
+  static_assert(BX == 256, "the swizzle spans 16 chunk positions");
+  static constexpr int kBytes = BX * TK * 2;      // 64 rows x BX bytes
+  static constexpr int NJ = kBytes / 1024 / 4;    // DMA instructions per wave per stage
+  static constexpr int NR = kBytes / 16 / NT;     // register path: chunks per thread
+  static constexpr int CPR = BX / 16;             // chunks per row
+  const bf16_t* base;     // FP8 bytes in two-byte units
+  int64_t ld;             // row stride in units
+  int xv;                 // valid columns (>= 1)
+  uint32_t voff[NJ];
+
+  __device__ __forceinline__ static int swz(int k) { return (k & 7) << 1; }
+  __device__ __forceinline__ void setup(const bf16_t* b, int64_t ld_, int xv_) {
+    base = b;
+    ld = ld_;
+    xv = xv_;
+    const int tid = opaque_tid();
+    const int lane = tid & 63, w = tid >> 6;
+    const int cmax = (xv - 1) >> 4;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int byte = (w * NJ + j) * 1024 + lane * 16;
+      const int k = byte / BX;
+      int c = ((byte % BX) >> 4) ^ swz(k);
+      if (c > cmax) c = cmax;
+      voff[j] = static_cast<uint32_t>(k * ld * 2 + c * 16);
+    }
+  }
+  __device__ __forceinline__ const bf16_t* step_base(int kt) const {
+    return base + static_cast<int64_t>(kt) * (2 * TK) * ld;
+  }
+  __device__ __forceinline__ void dma_one(const void* sb, int j, uint32_t lds) const {
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    dma16(sb, voff[j], lds + (w * NJ + j) * 1024);
+  }
+  __device__ __forceinline__ void dma(int kt, uint32_t lds) const {
+    const void* sb = uniform_ptr(step_base(kt));
+    const uint32_t w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dma16(sb, voff[j], lds + (w * NJ + j) * 1024);
+  }
+  // Register path for a partial step of kv < TK units (2 kv contraction rows).
+  __device__ __forceinline__ void tail_load(int kt, int kv, uint4 (&r)[NR]) const {
+    const char* b = reinterpret_cast<const char*>(step_base(kt));
+    const int tid = opaque_tid();
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int q = tid + i * NT;
+      const int k = q / CPR, c = q % CPR;
+      const bool ok = k < 2 * kv && c * 16 < xv;
+      const char* p = b + static_cast<int64_t>(k) * ld * 2 + c * 16;
+      r[i] = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void tail_store(char* lds, const uint4 (&r)[NR]) const {
+    const int tid = opaque_tid();
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int q = tid + i * NT;
+      const int k = q / CPR, c = q % CPR;
+      *reinterpret_cast<uint4*>(lds + k * BX + ((c ^ swz(k)) << 4)) = r[i];
+    }
+  }
+  __device__ __forceinline__ static void frag_base(int xw, uint32_t (&fb)[4]) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, j = lane & 15;
+    const int r = j >> 1, q = j & 1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int c = (xw + 32 * t + 16 * (g & 1)) >> 4;
+      fb[t] = static_cast<uint32_t>((16 * (g >> 1) + r) * BX + ((c ^ (2 * r)) << 4) + 8 * q);
+    }
+  }
+  __device__ __forceinline__ static bf16x8 frag(const char* lds, const uint32_t (&fb)[4], int i, int s) {
+    typedef int i32x2v __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) i32x2v lds_i32x2;
+    const char* p = lds + fb[i] + s * 32 * BX;
+    const i32x2v lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+    const i32x2v hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p + 8 * BX));
+    const i32x4v v = {lo[0], lo[1], hi[0], hi[1]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
 // Contraction over nfull full steps and kv trailing units (< TK) of A and B
 // (both row operands), NS-stage ring.  Every step issues one DMA block, the
 // source clamped to the last full step past the end, so the wait before
@@ -1917,10 +2017,12 @@ struct F8Tile {
 };
 
 // Grouped GEMM, ragged rows: out[rows of g] (+)= sa sb[g] A[rows of g] B_g^T
-// (+ bias[g]), B_g = rhs + g rhs_gs as [N, K].
-template <int FA, int FB, typename TO, int TM>
+// (+ bias[g]), B_g = rhs + g rhs_gs as [N, K], or with B_KN as [K, N] read
+// through transposing LDS reads.
+template <int FA, int FB, typename TO, int TM, bool B_KN = false>
 __global__ __launch_bounds__(NT, TM >= 256 ? 1 : 2) void gmm_fp8_kernel(Fp8Args a) {
   constexpr int TN = kF8TN;
+  using OB = std::conditional_t<B_KN, F8Col<TN>, Operand<false, TN>>;
   __shared__ __attribute__((aligned(1024))) char smem[F8Tile<TM>::kBytes];
   __shared__ int row_base[kMaxGShort + 1];
   __shared__ int tile_base[kMaxGShort + 1];
@@ -1930,11 +2032,11 @@ __global__ __launch_bounds__(NT, TM >= 256 ? 1 : 2) void gmm_fp8_kernel(Fp8Args 
   const int total = tile_base[a.G];
   TO* out = static_cast<TO*>(a.out);
   Operand<false, TM> A;
-  Operand<false, TN> B;
+  OB B;
   Acc8<TM, TN, FA, FB> acc;
   uint32_t fa[4], fb[4];
   Operand<false, TM>::frag_base(((threadIdx.x >> 6) >> 1) * (TM / 2), fa);
-  Operand<false, TN>::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
+  OB::frag_base(((threadIdx.x >> 6) & 1) * (TN / 2), fb);
   const float sa = a.sinv_a[0];
   for (int it = 0;; ++it) {
     const int64_t tile = xcd_tile(it);
@@ -1957,7 +2059,8 @@ __global__ __launch_bounds__(NT, TM >= 256 ? 1 : 2) void gmm_fp8_kernel(Fp8Args 
     const int vr = a.valid ? max(0, min(rv, min(rows_g, max(a.valid[g], 0)) - mt * TM)) : rv;
     acc.set_live_rows(vr);
     A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, max(vr, 1));
-    B.setup(a.rhs + g * a.rhs_gs + col0 * a.ld_rhs, a.ld_rhs, cv);
+    if constexpr (B_KN) B.setup(a.rhs + g * a.rhs_gs + col0 / 2, a.ld_rhs, cv);
+    else B.setup(a.rhs + g * a.rhs_gs + col0 * a.ld_rhs, a.ld_rhs, cv);
     if constexpr (F8Tile<TM>::NS == 4) contract_f8_db<4>(smem, A, B, a.Kdim, acc, fa, fb);
     else contract_f8<F8Tile<TM>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
     store_tile(static_cast<const Acc<TM, TN>&>(acc), smem, out + row0 * a.ld_out + col0, a.ld_out,
@@ -2476,7 +2579,8 @@ MOE_API int moe_tgmm(const void* lhs, int64_t ld_lhs, const void* rhs, int64_t l
 
 MOE_API int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_fmt,
                         const float* lhs_scale_inv, const void* rhs, int64_t ld_rhs,
-                        int64_t rhs_group_stride, int rhs_fmt, const float* rhs_scale_inv,
+                        int64_t rhs_group_stride, int trans_rhs, int rhs_fmt,
+                        const float* rhs_scale_inv,
                         const int32_t* group_sizes, const int32_t* valid_rows, int G, int64_t Kdim,
                         int64_t N,
                         const void* bias, void* out, int64_t M_out, int64_t ld_out, int out_dtype,
@@ -2491,7 +2595,7 @@ MOE_API int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_
   if (Kdim % 16 || ld_lhs % 16 || ld_rhs % 16 || rhs_group_stride % 16 || !mult8(N) ||
       !mult8(ld_out))
     return MOE_ERR_ARG;
-  if (ld_lhs < Kdim || ld_rhs < Kdim || ld_out < N) return MOE_ERR_ARG;
+  if (ld_lhs < Kdim || ld_rhs < (trans_rhs ? Kdim : N) || ld_out < N) return MOE_ERR_ARG;
   if (ld_lhs / 2 > kMaxLd || ld_rhs / 2 > kMaxLd) return MOE_ERR_ARG;
   if (M_out == 0 || N == 0) return MOE_OK;
   if (!lhs || !rhs || !group_sizes || !out || !lhs_scale_inv || !rhs_scale_inv ||
@@ -2507,8 +2611,13 @@ MOE_API int moe_gmm_fp8(const void* lhs, int64_t M_lhs, int64_t ld_lhs, int lhs_
   const int TMv = big ? 256 : 128;
   const int64_t upper = ((M_out + TMv - 1) / TMv + G) * ((N + kF8TN - 1) / kF8TN);
   const unsigned grid = persistent_grid(upper, big ? 1 : 2);
-#define G8T(FA, FB, TO, TMV) \
-  hipLaunchKernelGGL((gmm_fp8_kernel<FA, FB, TO, TMV>), dim3(grid), dim3(NT), 0, st, a)
+#define G8T(FA, FB, TO, TMV)                                                                   \
+  do {                                                                                         \
+    if (trans_rhs)                                                                             \
+      hipLaunchKernelGGL((gmm_fp8_kernel<FA, FB, TO, TMV>), dim3(grid), dim3(NT), 0, st, a);    \
+    else                                                                                       \
+      hipLaunchKernelGGL((gmm_fp8_kernel<FA, FB, TO, TMV, true>), dim3(grid), dim3(NT), 0, st, a); \
+  } while (0)
 #define G8(FA, FB, TO) do { if (big) G8T(FA, FB, TO, 256); else G8T(FA, FB, TO, 128); } while (0)
 #define G8O(FA, FB) \
   do { if (out_dtype == MOE_BF16) G8(FA, FB, bf16_t); else G8(FA, FB, float); } while (0)

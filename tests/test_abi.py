@@ -149,10 +149,13 @@ def test_argument_checks_return_before_launch(lib):
     assert lib.moe_fp8_amax_scale(P, 64, 1, 64, 64, 1, 7, P, W, 1 << 20, None) == -1
     assert lib.moe_fp8_amax_scale(P, 64, 1, 65, 64, 2, 0, P, W, 1 << 20, None) == -1
     assert lib.moe_fp8_amax_scale(P, 64, 1, 64, 64, 1, 0, P, None, 0, None) == -5
-    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 40, 40 * 64, 0, P, P, None, 2, 40, 64, None, P, 64,
-                           64, 1, 0, None, None) == -1
-    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 64, 64 * 64, 0, P, P, None, 1001, 64, 64, None, P,
+    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 40, 40 * 64, 1, 0, P, P, None, 2, 40, 64, None, P,
                            64, 64, 1, 0, None, None) == -1
+    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 64, 64 * 64, 1, 0, P, P, None, 1001, 64, 64, None,
+                           P, 64, 64, 1, 0, None, None) == -1
+    # [K, N] weight (trans_rhs = 0): its row stride must cover N
+    assert lib.moe_gmm_fp8(P, 64, 64, 0, P, P, 64, 64 * 96, 0, 0, P, P, None, 2, 64, 96, None, P,
+                           64, 96, 1, 0, None, None) == -1
     assert lib.moe_fp8_padded_rows(100, 3) == 64 * (2 + 2)
     assert lib.moe_fp8_quantize(P, 64, 1, 100, 64, P, 3, P, 0, 0, None, 0, P, 128, 0, None,
                                 None) == -1

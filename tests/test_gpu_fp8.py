@@ -210,8 +210,22 @@ GMM8_CASES = [
 ]
 
 
+def _kn(qb, fill=0x7F):
+    """[G, N, K] codes as a [G, K, N] view whose rows are padded to a multiple
+    of 16 bytes with NaN codes (0x7F: NaN in e4m3, a NaN in e5m2 too), which
+    only products in columns past N may see."""
+    G, N, K = qb.shape
+    npad = 16 * ((N + 15) // 16)
+    buf = np.full((G, K, npad), fill, dtype=np.uint8)
+    buf[:, :, :N] = qb.transpose(0, 2, 1)
+    return _u8(buf)[:, :, :N]
+
+
+@pytest.mark.parametrize("trans", [True, False], ids=["nk", "kn"])
 @pytest.mark.parametrize("case", GMM8_CASES, ids=[f"G{len(c[0])}-{c[1]}x{c[2]}-{c[3]}{c[4]}-{c[5]}-a{int(c[6])}-b{int(c[7])}" for c in GMM8_CASES])
-def test_gmm_fp8(gpu_lib, case):
+def test_gmm_fp8(gpu_lib, case, trans):
+    """Both weight orientations: B_g^T stored [N, K] (trans_rhs) or B_g stored
+    [K, N] and read through transposing LDS reads."""
     gs, K, N, fa, fb, ot, acc, with_bias = case
     gs = np.array(gs, dtype=np.int32)
     G = len(gs)
@@ -227,8 +241,8 @@ def test_gmm_fp8(gpu_lib, case):
     bias = ms.bf16_round(g.standard_normal((G, N)).astype(np.float32)) if with_bias else None
     out = dev(P, TD[ot]) if acc else poison(torch.empty((M, N), dtype=TD[ot], device="cuda"))
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    gpu_lib.moe_gmm_fp8(_u8(qa), fa, dev(sa), _u8(qb), fb, dev(sb), dev_i32(gs), out=out,
-                        accumulate=acc, err=err,
+    gpu_lib.moe_gmm_fp8(_u8(qa), fa, dev(sa), _u8(qb) if trans else _kn(qb), fb, dev(sb),
+                        dev_i32(gs), out=out, accumulate=acc, err=err, trans_rhs=trans,
                         bias=None if bias is None else dev(bias, torch.bfloat16))
     A = F8.dequantize(qa, fa, sa[0])
     B = F8.dequantize(qb, fb, sb)
@@ -248,8 +262,9 @@ FP8_VALID = {
 }
 
 
+@pytest.mark.parametrize("trans", [True, False], ids=["nk", "kn"])
 @pytest.mark.parametrize("case", list(FP8_VALID))
-def test_gmm_fp8_valid_rows(gpu_lib, case):
+def test_gmm_fp8_valid_rows(gpu_lib, case, trans):
     """FP8 gmm skips lhs rows past valid_rows (garbage codes here)."""
     gs = np.array(FP8_VALID[case][0], dtype=np.int32)
     valid = np.array(FP8_VALID[case][1], dtype=np.int32)
@@ -263,8 +278,9 @@ def test_gmm_fp8_valid_rows(gpu_lib, case):
     for e in range(G):
         qa0[off[e] + valid[e]:off[e + 1]] = 0
     sa, sb = np.float32([0.03]), np.full(G, 0.5, np.float32)
-    out = gpu_lib.moe_gmm_fp8(_u8(qa), "e4m3", dev(sa), _u8(qb), "e4m3", dev(sb), dev_i32(gs),
-                              out_dtype=torch.float32, valid_rows=dev_i32(valid))
+    out = gpu_lib.moe_gmm_fp8(_u8(qa), "e4m3", dev(sa), _u8(qb) if trans else _kn(qb), "e4m3",
+                              dev(sb), dev_i32(gs), out_dtype=torch.float32,
+                              valid_rows=dev_i32(valid), trans_rhs=trans)
     want = oracle.gmm(F8.dequantize(qa0, "e4m3", sa[0]), F8.dequantize(qb, "e4m3", sb), gs,
                       trans_rhs=True)
     assert_close(host(out), want, TOL_F32, "gmm_fp8 valid_rows")
