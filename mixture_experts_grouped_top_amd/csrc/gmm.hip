@@ -179,7 +179,10 @@ struct Operand {
   const bf16_t* base;
   int64_t ld;
   int xv;                 // valid x extent (>= 1)
-  int64_t split;          // col tile: elements added to the columns of its second half
+  // col tile: 0, or the distance of a second column range: the tile's columns
+  // then come in 64-wide blocks alternating between the two ranges (block
+  // 2 p: columns 64 p .. of the first, block 2 p + 1: the same of the second)
+  int64_t split;
   uint32_t voff[NJ];      // byte offsets of this lane's DMA chunks
 
   __device__ __forceinline__ void setup(const bf16_t* b, int64_t ld_, int xv_, int64_t split_ = 0) {
@@ -202,12 +205,17 @@ struct Operand {
         int c = ((byte % (BX * 2)) >> 4) ^ col_swz(k);
         const int cmax = (xv - 1) >> 3;
         if (c > cmax) c = cmax;
-        voff[j] = static_cast<uint32_t>((k * ld + c * 8 + (c >= BX / 16 ? split : 0)) * 2);
+        voff[j] = static_cast<uint32_t>((k * ld + col_of(c)) * 2);
       }
     }
   }
   __device__ __forceinline__ const bf16_t* step_base(int kt) const {
     return COLK ? base + static_cast<int64_t>(kt) * TK * ld : base + static_cast<int64_t>(kt) * TK;
+  }
+  // col tile: source column (elements from base) of the tile's 8-column chunk c
+  __device__ __forceinline__ int64_t col_of(int c) const {
+    const int b = c >> 3;   // 64-column block
+    return c * 8 + (split ? (b & 1) * split - 64 * ((b + 1) >> 1) : 0);
   }
   // DMA instruction j (< NJ) of step kt; sb = uniform_ptr(step_base(kt)).
   __device__ __forceinline__ void dma_one(const void* sb, int j, uint32_t lds) const {
@@ -236,7 +244,7 @@ struct Operand {
       } else {
         const int k = q / (BX / 8), c = q % (BX / 8);
         ok = k < kv && c * 8 < xv;
-        p = b + k * ld + c * 8 + (c >= BX / 16 ? split : 0);
+        p = b + k * ld + col_of(c);
       }
       r[i] = ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
     }
@@ -882,43 +890,40 @@ __device__ __forceinline__ void store_tile(const Acc<TM, TN>& acc, char* lds, TO
   __syncthreads();   // the stages are refilled by the next tile
 }
 
-// Epilogue of the fused up-projection with SwiGLU: tile columns [0, TN/2)
-// are gate columns, [TN/2, TN) the up columns of the same d_ff range, so
-// waves 2p and 2p + 1 hold the two halves of the same rows.  Per 32-row
-// slab all four waves stage their float32 block in LDS; each wave writes its
-// own half to h (h0: gate rows, h1: up rows; bias added, rows >= rz zero)
-// and the pair computes act = silu(g) * u on the bf16-rounded h values (as
-// the SwiGLU pass over h does), each wave half of the slab's chunks.
+// Epilogue of the fused up-projection with SwiGLU.  The tile's columns come
+// in 64-wide blocks alternating gate and up columns of the same d_ff range
+// (block 2 p: gate columns f0 + 64 p .., block 2 p + 1: the up columns of the
+// same d_ff), so the 128 columns of each wave hold the gate and up values of
+// 64 d_ff columns and no wave needs another's: per 32-row slab it stages its
+// block in its own LDS region (as store_tile), writes its rows of h0 and h1
+// (bias added, rows >= rz zero) and act = silu(g) * u on the bf16-rounded h
+// values (as the SwiGLU pass over h does).
 template <int TM, int TN>
 __device__ __forceinline__ void store_tile_swiglu(const Acc<TM, TN>& acc, char* lds, bf16_t* h0,
                                                   bf16_t* h1, int64_t ld_h, bf16_t* act,
                                                   int64_t ld_act, int rv, const bf16_t* b0,
                                                   const bf16_t* b1, int rz) {
-  constexpr int WC = TN / 2;
+  constexpr int WC = TN / 2;                  // columns per wave: 64 gate, 64 up
+  constexpr int HC = WC / 2;                  // d_ff columns per wave
   constexpr int SROW = WC * 4 + 16;
-  constexpr int CPR = WC / 8;                 // 8-column chunks per slab row
-  constexpr int NQ = 32 * CPR / 64;           // h chunks per lane per slab
-  constexpr int NA = NQ / 2;                  // act chunks per lane per slab
+  constexpr int CPR = HC / 8;                 // 8-column chunks per row of one half
+  constexpr int NQ = 32 * CPR / 64;           // chunks per lane per slab
   static_assert(4 * 32 * SROW <= Stages<TM, TN>::kBytes, "epilogue slabs fit in the stage buffers");
   const int tid = opaque_tid();
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int up = w & 1;
   char* slab = lds + w * 32 * SROW;
-  const char* sg = lds + (w & ~1) * 32 * SROW;   // the pair's gate slab
-  const char* su = sg + 32 * SROW;               // and its up slab
   const int wr = (w >> 1) * (TM / 2);
-  bf16_t* hw = up ? h1 : h0;
-  const bf16_t* bw = up ? b1 : b0;
-  auto value = [&](const char* sl, int row, int c8, int grow, const bf16_t* bias, float v[8]) {
-    const float4 lo = *reinterpret_cast<const float4*>(sl + row * SROW + c8 * 32);
-    const float4 hi = *reinterpret_cast<const float4*>(sl + row * SROW + c8 * 32 + 16);
+  const int fw = (w & 1) * HC;                // the wave's first d_ff column in the tile
+  auto value = [&](int row, int col, int grow, const bf16_t* bias, float v[8]) {
+    const float4 lo = *reinterpret_cast<const float4*>(slab + row * SROW + col * 4);
+    const float4 hi = *reinterpret_cast<const float4*>(slab + row * SROW + col * 4 + 16);
     v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = grow < rz ? v[e] : 0.f;
     if (bias) {
       float b[8];
-      load8(bias + 8 * c8, b);
+      load8(bias, b);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] += b[e];
     }
@@ -933,37 +938,34 @@ __device__ __forceinline__ void store_tile_swiglu(const Acc<TM, TN>& acc, char* 
         const int col = 32 * j + (lane & 31);
         *reinterpret_cast<float*>(slab + row * SROW + col * 4) = acc.v[i][j][r];
       }
-    __syncthreads();   // both halves of these rows are staged
-    if (hw) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int chunk = lane + 64 * q;
-        const int row = chunk / CPR, c8 = chunk % CPR;
-        const int grow = wr + 32 * i + row;
-        if (grow < rv) {
-          float v[8];
-          value(slab, row, c8, grow, bw, v);
-          store8_nt(hw + static_cast<int64_t>(grow) * ld_h + 8 * c8, v);
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < NA; ++q) {
-      const int chunk = up * (32 * CPR / 2) + lane + 64 * q;
+    for (int q = 0; q < NQ; ++q) {
+      const int chunk = lane + 64 * q;
       const int row = chunk / CPR, c8 = chunk % CPR;
       const int grow = wr + 32 * i + row;
       if (grow < rv) {
+        const int f = fw + 8 * c8;
         float g[8], u[8], o[8];
-        value(sg, row, c8, grow, b0, g);
-        value(su, row, c8, grow, b1, u);
+        value(row, 8 * c8, grow, b0 ? b0 + f : nullptr, g);
+        value(row, HC + 8 * c8, grow, b1 ? b1 + f : nullptr, u);
+        if (h0) {
+          store8_nt(h0 + static_cast<int64_t>(grow) * ld_h + f, g);
+          store8_nt(h1 + static_cast<int64_t>(grow) * ld_h + f, u);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           o[e] = swiglu_f32(bf16_to_f32(f32_to_bf16(g[e])), bf16_to_f32(f32_to_bf16(u[e])));
-        store8_nt(act + static_cast<int64_t>(grow) * ld_act + 8 * c8, o);
+        store8_nt(act + static_cast<int64_t>(grow) * ld_act + f, o);
       }
     }
-    __syncthreads();   // the slabs are rewritten (and, after the last, refilled by the next tile)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+  __syncthreads();   // the stages are refilled by the next tile
 }
 
 // Epilogue of the d_act GEMM with the SwiGLU backward: the tile's value is
@@ -1107,9 +1109,10 @@ __global__ __launch_bounds__(NT, TM <= 128 ? 2 : 1) void gmm_mfma_kernel(MfmaArg
     A.setup(a.lhs + row0 * a.ld_lhs, a.ld_lhs, max(vr, 1));
     const bf16_t* bg = a.rhs + g * a.rhs_gs;
     if constexpr (SWI) {
-      // gate columns F0 .. F0 + TN/2 of wi and the up columns F + F0 ..
+      // d_ff columns f0 .. f0 + TN/2 of wi's gate half and of its up half
+      // (F further), in 64-wide blocks alternating gate and up
       const int64_t F = a.N / 2, f0 = static_cast<int64_t>(nt) * (TN / 2);
-      B.setup(bg + f0, a.ld_rhs, TN, F - TN / 2);
+      B.setup(bg + f0, a.ld_rhs, TN, F);
       if constexpr (PAIR) contract2(smem, A, B, a.Kdim, acc, fa, fb);
       else contract<Stages<TM, TN>::NS>(smem, A, B, a.Kdim, acc, fa, fb);
       bf16_t* h = static_cast<bf16_t*>(a.out);
