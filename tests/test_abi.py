@@ -223,3 +223,34 @@ def test_binding_rejects_bad_shapes_and_index_dtypes(lib):
     raises("act must be", moe.moe_gmm_swiglu, lhs, wi, gs, act=torch.zeros((64, 64), dtype=bf))
     raises("h must be", moe.moe_gmm_swiglu, lhs, wi, gs, h=torch.zeros((64, 128), dtype=bf))
     raises("group_sizes must be a contiguous int32", moe.moe_gmm_swiglu, lhs, wi, gs.long())
+
+
+def test_header_serves_plain_c_callers(tmp_path, lib):
+    """include/moe.h compiles as strict C99 and C++17 with every warning an
+    error, and a C program linked against libmoe.so through it calls the
+    library (host-side entry points only: no GPU is touched)."""
+    src = tmp_path / "caller.c"
+    src.write_text(
+        '#include "moe.h"\n'
+        "#include <stdio.h>\n"
+        "int main(void) {\n"
+        "  const int64_t rows = moe_rows_bound(4096, 8, 256, 128, 0, 0);\n"
+        "  printf(\"%d %lld %s\\n\", moe_abi_version(), (long long)rows, moe_status_string(MOE_ERR_ARG));\n"
+        "  return 0;\n"
+        "}\n")
+    inc = os.path.join(ROOT, "include")
+    libdir = os.path.dirname(moe.LIB_PATH)
+    exe = tmp_path / "caller"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc,
+                    str(src), "-o", str(exe), os.path.join(libdir, "libmoe.so"),
+                    f"-Wl,-rpath,{libdir}"], check=True, capture_output=True, text=True)
+    cpp = tmp_path / "caller.cpp"
+    cpp.write_text('#include "moe.h"\nint main() { return moe_abi_version() > 0 ? 0 : 1; }\n')
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", inc,
+                    "-fsyntax-only", str(cpp)], check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    ver, rows, msg = r.stdout.split(" ", 2)
+    assert int(ver) == lib.moe_abi_version()
+    assert int(rows) == lib.moe_rows_bound(4096, 8, 256, 128, 0, 0)
+    assert msg.strip().startswith("invalid argument")
