@@ -514,7 +514,18 @@ def measure(name: str, args, headline: bool, inputs=None, capacity_layout: bool 
         kernels = rec.summary(peak)
         del scratch
     roofline = None
+    step_roofline = None
     if kernels:
+        # the step's floor: each recorded call at its own roofline (the larger
+        # of its flops at the MFMA peak and its algorithmic bytes at 8 TB/s)
+        floor_ms = 1e3 * sum(max(v["flops"] / (peak * 1e12), v["bytes"] / (PEAK_HBM_GBS * 1e9))
+                             for v in kernels.values()) / args.kernel_steps
+        step_roofline = {
+            "floor_ms": round(floor_ms, 4), "frac": round(floor_ms / ms_step, 4),
+            "calls": "expert GEMMs, permute, SwiGLU, combine and their backward (the router "
+                     "GEMM and routing, a few tens of microseconds, are not recorded)"}
+        log(f"[bench]   step floor {floor_ms:.3f} ms at each call's roofline: "
+            f"{100 * floor_ms / ms_step:.1f}% of the measured step")
         kind = max(kernels, key=lambda k: kernels[k]["ms"])
         k = kernels[kind]
         if k["bound"] == "mfma":
@@ -545,6 +556,7 @@ def measure(name: str, args, headline: bool, inputs=None, capacity_layout: bool 
                    "routed_rows": R,
                    "padded_rows": plan.padded_rows, "nonempty_experts": plan.nonempty_groups},
         "roofline": roofline,
+        "step_roofline": step_roofline,
         "kernels": {kk: {"launches": v["launches"], "avg_ms": round(v["avg_ms"], 4),
                          "tflops": round(v["tflops"], 2),
                          "algorithmic_bytes": int(v["bytes"] / v["launches"]),
@@ -629,6 +641,7 @@ def main():
         "config": head["config"],
         "mfma_peak_frac": head["mfma_peak_frac"],
         "roofline": head["roofline"],
+        "step_roofline": head.get("step_roofline"),
         "cpu_baseline": head.get("cpu_baseline"),
         "device_error_flags": head["device_error_flags"],
         "kernels": head["kernels"],
