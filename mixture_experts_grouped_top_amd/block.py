@@ -410,9 +410,15 @@ class MoEPlan:
     @property
     def swiglu_epilogue(self) -> bool:
         """The fused up-projection computes act in its epilogue (one launch,
-        bf16, d_ff a multiple of 128, no contraction chunks)."""
+        bf16, d_ff a multiple of 128, no contraction chunks), when groups
+        average 512 rows or more: there the library's 256-row tiles hide the
+        epilogue behind long contractions.  With smaller groups (128-row
+        tiles, a weight-streaming launch) the epilogue is exposed and the
+        plain product plus the SwiGLU pass is faster (DeepSeek-V3 shape:
+        4.39 ms against 3.89 + 0.15 ms)."""
         s = self.s
-        return s.fused_wi and s.n_chunks == 1 and s.dtype == torch.bfloat16 and s.F % 128 == 0
+        return (s.fused_wi and s.n_chunks == 1 and s.dtype == torch.bfloat16 and s.F % 128 == 0
+                and s.T * s.K >= 512 * s.E)
 
     def _up_fused(self, wi, gs, R, stream, b_wi=None):
         s = self.s

@@ -89,6 +89,9 @@ WORKLOADS = {
                  zipf_s=1.5, n_forced_empty=4, n_chunks=4, pad_rows_to=128, seed=3),
         # Same structure at oracle-friendly sizes: several tiles and ragged tails.
         Workload("mini_mixtral", 600, 256, 384, 8, 2, "bf16", "softmax", True),
+        # groups of 512 rows or more on average (the 256-row tile regime, where
+        # the fused up-projection applies SwiGLU in its epilogue)
+        Workload("mini_mixtral_512", 2400, 256, 384, 8, 2, "bf16", "softmax", True),
         Workload("mini_deepseek", 300, 256, 192, 32, 8, "bf16", "sigmoid", True,
                  align=128, zipf_s=1.2, n_forced_empty=4),
         Workload("mini_token_drop", 700, 192, 160, 32, 1, "bf16", "softmax", False,

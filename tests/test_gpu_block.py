@@ -19,7 +19,7 @@ CHAIN = ["tiny", "mini_mixtral", "mini_deepseek", "mini_token_drop", "mini_chunk
          "mini_dsv3_router", "mini_mixtral_aux", "tiny_grouped", "tiny_bias", "mini_bias_align",
          "mini_bias_chunked"]
 # the same chain with the fused [wi_0 | wi_1] up-projection weight
-FUSED = ["tiny", "mini_mixtral", "mini_deepseek", "mini_chunked", "mini_bias_align",
+FUSED = ["tiny", "mini_mixtral", "mini_mixtral_512", "mini_deepseek", "mini_chunked", "mini_bias_align",
          "mini_bias_chunked"]
 # the same chain with FP8 expert GEMMs
 FP8 = ["tiny", "mini_mixtral", "mini_deepseek", "mini_token_drop", "mini_align8",
@@ -155,6 +155,8 @@ def test_chain_routing_and_permutation(chain):
 def test_chain_forward(chain):
     w, inp, plan, f, b = chain
     tol = TOL_F32 if w.dtype == "f32" else TOL_BF16
+    if plan.s.fused_wi and w.name == "mini_mixtral_512":
+        assert plan.swiglu_epilogue   # this chain covers the fused SwiGLU epilogue
     rows = plan.rows
     if plan.s.fp8:
         # identical inputs give identical codes and scales

@@ -22,7 +22,8 @@ CASES = [("tiny", False, False), ("mini_mixtral", False, False), ("mini_deepseek
          ("mini_token_drop", False, False), ("mini_chunked", False, False),
          ("mini_dsv3_router", False, False), ("mini_mixtral_aux", False, False),
          ("tiny_bias", False, False), ("mini_bias_chunked", False, False),
-         ("mini_deepseek", True, False), ("mini_mixtral", False, True),
+         ("mini_deepseek", True, False), ("mini_mixtral_512", True, False),
+         ("mini_mixtral", False, True),
          ("mini_deepseek", False, True)]
 
 # step outputs poisoned before each replay
